@@ -1,0 +1,496 @@
+"""Pins of the CPU oracle to facts fixed outside the oracle itself.
+
+Each test checks the oracle against something it cannot agree with by
+construction: published known-answer vectors, an independent RNG engine,
+closed-form distributions, the dense head (the p = c special case), brute
+force on tiny inputs, or the parameter counts printed on the pages.
+"""
+import itertools
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+from oracle import flashhead_ref as ref
+from two_stage_retrieval_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+
+
+# --------------------------------------------------------------------------
+# Philox4x32-10 and the uniform / Gumbel transforms
+# --------------------------------------------------------------------------
+
+def _kat_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([int(x, 16) for x in line.split()])
+    return rows
+
+
+def test_philox_known_answers():
+    rows = _kat_rows()
+    assert len(rows) == 3
+    for r in rows:
+        out = ref.philox4x32_10(([r[0]], [r[1]], [r[2]], [r[3]]),
+                                ([r[4]], [r[5]]))
+        assert [int(o[0]) for o in out] == r[6:10]
+
+
+@pytest.fixture(scope="module")
+def rocrand_engine(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path_factory.mktemp("philox") / "philox_rocrand")
+    src = os.path.join(HERE, "host", "philox_rocrand.cpp")
+    subprocess.run([hipcc, "-O1", "-x", "hip", "--offload-arch=gfx950",
+                    "-I/opt/rocm/include", src, "-o", exe], check=True,
+                   capture_output=True)
+    return exe
+
+
+@pytest.mark.parametrize("seed,stream", [(0, 0), (0x123456789ABCDEF, 1),
+                                         ((7 << 32) | 3, 0), (2**64 - 1, 1)])
+def test_philox_words_match_rocrand_engine(rocrand_engine, seed, stream):
+    """rocRAND's Philox engine (host build of its header) is an independent
+    implementation; skipping 4*((stream << 32) + (idx >> 2)) + (idx & 3)
+    outputs lands it on our counter (idx >> 2, stream, 0, 0), word idx & 3."""
+    idx = [0, 1, 2, 3, 4, 5, 6, 7, 63, 64, 1000, 8015, 128255, 2**31 + 5]
+    out = subprocess.run([rocrand_engine, str(seed), str(stream)] +
+                         [str(i) for i in idx], check=True,
+                         capture_output=True, text=True).stdout.split()
+    assert [int(x) for x in out] == [int(w) for w in
+                                     ref.philox_words(seed, stream, idx)]
+
+
+def test_uniform_is_odd_multiple_of_2_pow_minus_24():
+    w = np.array([0, 1, 511, 512, 2**31, 2**32 - 1], dtype=np.uint64)
+    u = ref.uniform_open01(w)
+    n = u * 2.0 ** 24
+    assert np.all(n == np.round(n)) and np.all(n.astype(np.int64) % 2 == 1)
+    assert np.all(u > 0) and np.all(u < 1)
+    assert u[0] == 2.0 ** -24 and u[-1] == 1 - 2.0 ** -24
+    # exact in fp32
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)
+
+
+def test_gumbel_noise_is_standard_gumbel():
+    g = ref.gumbel(12345, 0, np.arange(200_000))
+    ks = stats.kstest(g, stats.gumbel_r.cdf)
+    assert ks.pvalue > 1e-3
+    # different streams / seeds give different noise
+    assert not np.array_equal(g[:64], ref.gumbel(12345, 1, np.arange(64)))
+    assert not np.array_equal(g[:64], ref.gumbel(12346, 0, np.arange(64)))
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+def test_round_to_bf16_known_values():
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -1 - 2.0 ** -7,
+                  1 + 2.0 ** -8 + 2.0 ** -30, 0.0, 3.0e-39])
+    y = ref.round_to_bf16(x)
+    assert y[0] == 1.0
+    assert y[1] == 1.0                       # tie -> even
+    assert y[2] == 1 + 2.0 ** -6             # tie -> even (upwards)
+    assert y[3] == -1 - 2.0 ** -7            # exact
+    assert y[4] == 1 + 2.0 ** -7             # above the tie
+    assert y[5] == 0.0
+    assert y[6] == round(3.0e-39 / 2.0 ** -133) * 2.0 ** -133
+
+
+def test_round_to_bf16_matches_bit_rounding_of_fp32():
+    """The generator's fp32 bit-level RNE is an independent implementation."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(100_000) *
+         np.exp(rng.uniform(-30, 30, 100_000))).astype(np.float32)
+    a = ref.bf16_bits_of(ref.round_to_bf16(x.astype(np.float64)))
+    b = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(a, b)
+    assert np.array_equal(ref.decode_bf16(b),
+                          synth.bf16_bits_to_f32(b).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# validation
+# --------------------------------------------------------------------------
+
+def test_validate_rejects_bad_tables_and_arguments():
+    c2t = np.arange(24).reshape(6, 4)
+    ref.validate(24, 6, 4, c2t, p=2, tau=0.7)
+    bad = c2t.copy()
+    bad[0, 0] = 5                             # duplicate of token 5
+    with pytest.raises(ValueError, match="permutation"):
+        ref.validate(24, 6, 4, bad)
+    bad = c2t.copy()
+    bad[1, 1] = 24
+    with pytest.raises(ValueError, match="out of"):
+        ref.validate(24, 6, 4, bad)
+    with pytest.raises(ValueError):
+        ref.validate(25, 6, 4, c2t)
+    with pytest.raises(ValueError):
+        ref.validate(24, 4, 6, c2t)
+    for p in (0, 7):
+        with pytest.raises(ValueError):
+            ref.validate(24, 6, 4, c2t, p=p)
+    for tau in (0.0, -1.0, math.inf, math.nan):
+        with pytest.raises(ValueError):
+            ref.validate(24, 6, 4, c2t, tau=tau)
+
+
+# --------------------------------------------------------------------------
+# stage 1: brute force on tiny inputs
+# --------------------------------------------------------------------------
+
+def _py_dot(a, b):
+    s = 0.0
+    for x, y in zip(a, b):
+        s += float(x) * float(y)
+    return s
+
+
+def test_stage1_scores_bruteforce():
+    rng = np.random.default_rng(1)
+    C = rng.standard_normal((7, 5))
+    h = rng.standard_normal(5)
+    got = ref.stage1_scores(C, h)
+    want = [_py_dot(C[k], h) for k in range(7)]
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_stage1_int4_scores_bruteforce_and_closed_form():
+    rng = np.random.default_rng(2)
+    q = rng.integers(-8, 8, size=(5, 256)).astype(np.int8)
+    s = ref.round_to_bf16(rng.uniform(0.001, 0.1, size=(5, 2)))
+    h = rng.standard_normal(256)
+    got = ref.stage1_scores_int4(q, s, h)
+    want = []
+    for k in range(5):
+        acc = 0.0
+        for g in range(2):
+            inner = _py_dot(q[k, g * 128:(g + 1) * 128],
+                            h[g * 128:(g + 1) * 128])
+            acc += s[k, g] * inner
+        want.append(acc)
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-12)
+    deq = q.astype(np.float64) * np.repeat(s, 128, axis=1)
+    assert np.allclose(got, deq @ h, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# selection, candidates, decode: brute force and hand-made ties
+# --------------------------------------------------------------------------
+
+def _tiny_head(seed=0, c=6, b=4, d=8):
+    rng = np.random.default_rng(seed)
+    v = c * b
+    E = rng.standard_normal((v, d))
+    c2t = rng.permutation(v).reshape(c, b)
+    C = rng.standard_normal((c, d))
+    return E, c2t, C
+
+
+def test_candidates_match_bruteforce_enumeration():
+    for seed in range(20):
+        E, c2t, C = _tiny_head(seed)
+        rng = np.random.default_rng(100 + seed)
+        scores = np.round(rng.standard_normal(6), 1)   # ties happen
+        for p in range(1, 7):
+            S, _, _ = ref.select_clusters(scores, p)
+            T = ref.candidate_tokens(S, c2t)
+            want = []
+            for t in range(24):
+                k = [kk for kk in range(6) if t in list(c2t[kk])][0]
+                rank = sum(1 for j in range(6)
+                           if scores[j] > scores[k] or
+                           (scores[j] == scores[k] and j < k))
+                if rank < p:
+                    want.append(t)
+            assert sorted(T.tolist()) == want
+            assert len(set(T.tolist())) == p * 4
+
+
+def test_step_token_matches_bruteforce():
+    for seed in range(10):
+        E, c2t, C = _tiny_head(seed, d=5)
+        h = np.random.default_rng(50 + seed).standard_normal(5)
+        rows = ref.rows_accessor(E, "f32")
+        for p in (1, 2, 4, 6):
+            r = ref.flashhead_step(lambda i: E[i], c2t, h, p, C_f64=C)
+            sc = [_py_dot(C[k], h) for k in range(6)]
+            ks = sorted(range(6), key=lambda k: (-sc[k], k))[:p]
+            best, best_t = -math.inf, None
+            for k in ks:
+                for t in c2t[k]:
+                    z = _py_dot(E[t], h)
+                    if z > best or (z == best and t < best_t):
+                        best, best_t = z, int(t)
+            assert r.token == best_t
+        del rows
+
+
+def test_tie_rules_and_margins():
+    S, keys, m1 = ref.select_clusters(np.array([1.0, 3.0, 3.0, 2.0]), 2)
+    assert sorted(S.tolist()) == [1, 2] and m1 == 1.0
+    S, keys, m1 = ref.select_clusters(np.array([1.0, 3.0, 3.0, 2.0]), 1)
+    assert S.tolist() == [1] and m1 == 0.0
+    S, keys, m1 = ref.select_clusters(np.array([1.0, 3.0, 3.0, 2.0]), 4)
+    assert m1 == math.inf
+    S, keys, m1 = ref.select_clusters(np.array([2.5, 5.0, 1.0, 3.0]), 2)
+    assert sorted(S.tolist()) == [1, 3] and m1 == 0.5
+    tok, m2, lse, _ = ref.decode_tokens([7, 3, 9], [5.0, 5.0, 1.0])
+    assert tok == 3 and m2 == 0.0
+    tok, m2, lse, _ = ref.decode_tokens([7, 3, 9], [5.0, 4.5, 1.0])
+    assert tok == 7 and m2 == 0.5
+    assert lse == pytest.approx(special.logsumexp([5.0, 4.5, 1.0]))
+
+
+# --------------------------------------------------------------------------
+# the p = c special case reduces to the dense head (Formulas 1-3)
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny_workload():
+    head = synth.make_head(0)
+    H = synth.make_hidden(head, 256)
+    return head, H
+
+
+def test_p_equals_c_greedy_is_dense_argmax(tiny_workload):
+    head, H = tiny_workload
+    wl = head.wl
+    E64 = head.E.astype(np.float64)
+    C64 = head.C_given.astype(np.float64)
+    rows = ref.rows_accessor(head.E, "f32")
+    Z = E64 @ H.astype(np.float64).T                 # library matmul
+    for i in range(H.shape[0]):
+        r = ref.flashhead_step(rows, head.c2t, H[i].astype(np.float64),
+                               wl.c, C_f64=C64)
+        assert r.token == int(np.argmax(Z[:, i]))     # first max = lowest id
+
+
+def test_p_equals_c_sample_is_dense_sample(tiny_workload):
+    head, H = tiny_workload
+    wl = head.wl
+    C64 = head.C_given.astype(np.float64)
+    rows = ref.rows_accessor(head.E, "f32")
+    seeds = synth.make_seeds(3, 32)
+    for tau in (0.7, 1.0):
+        for i in range(32):
+            h = H[i].astype(np.float64)
+            r = ref.flashhead_step(rows, head.c2t, h, wl.c, C_f64=C64,
+                                   mode="sample", tau=tau,
+                                   seed=int(seeds[i]))
+            tok, _, lse, _ = ref.dense_head(rows, wl.v, h, "sample", tau,
+                                            int(seeds[i]))
+            assert r.token == tok
+            z = head.E.astype(np.float64) @ h
+            assert r.lse == pytest.approx(special.logsumexp(z / tau),
+                                          rel=1e-12)
+
+
+def test_flashhead_matches_dense_often_on_tiny_workload(tiny_workload):
+    """Information only about the synthetic data: containment well above
+    chance (1/8 of the vocabulary is probed at p=8)."""
+    head, H = tiny_workload
+    C64 = head.C_given.astype(np.float64)
+    rows = ref.rows_accessor(head.E, "f32")
+    Z = head.E.astype(np.float64) @ H.astype(np.float64).T
+    hits = 0
+    for i in range(H.shape[0]):
+        r = ref.flashhead_step(rows, head.c2t, H[i].astype(np.float64), 8,
+                               C_f64=C64)
+        hits += r.token == int(np.argmax(Z[:, i]))
+    assert hits / H.shape[0] > 0.3
+
+
+# --------------------------------------------------------------------------
+# sampling distributions (exact enumeration / closed forms)
+# --------------------------------------------------------------------------
+
+def _chisq_pvalue(counts, probs):
+    counts = np.asarray(counts, dtype=np.float64)
+    exp = np.asarray(probs) * counts.sum()
+    keep = exp >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    ex = np.append(exp[keep], exp[~keep].sum())
+    if ex[-1] == 0:
+        obs, ex = obs[:-1], ex[:-1]
+    return stats.chisquare(obs, ex).pvalue
+
+
+def _plackett_luce_set_probs(w, p):
+    """P(unordered set) under successive sampling without replacement."""
+    W = w.sum()
+    out = {}
+    for seq in itertools.permutations(range(len(w)), p):
+        pr, rem = 1.0, W
+        for k in seq:
+            pr *= w[k] / rem
+            rem -= w[k]
+        key = tuple(sorted(seq))
+        out[key] = out.get(key, 0.0) + pr
+    return out
+
+
+@pytest.mark.parametrize("p,tau", [(2, 0.7), (3, 1.0)])
+def test_gumbel_top_p_is_sampling_without_replacement(p, tau):
+    s = np.array([0.3, -0.4, 1.1, 0.0, 0.8, -1.2])
+    probs = _plackett_luce_set_probs(np.exp(s / tau), p)
+    keys = sorted(probs)
+    counts = dict.fromkeys(keys, 0)
+    n = 20000
+    for i in range(n):
+        S, _, _ = ref.select_clusters(s, p, "sample", tau, seed=i)
+        counts[tuple(sorted(S.tolist()))] += 1
+    pv = _chisq_pvalue([counts[k] for k in keys], [probs[k] for k in keys])
+    assert pv > 1e-3
+
+
+def test_gumbel_max_is_softmax_sample():
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal(16) * 1.5
+    tau = 0.7
+    T = np.arange(16)
+    n = 20000
+    counts = np.zeros(16)
+    for i in range(n):
+        tok, _, _, _ = ref.decode_tokens(T, z, "sample", tau, seed=10**6 + i)
+        counts[tok] += 1
+    pv = _chisq_pvalue(counts, special.softmax(z / tau))
+    assert pv > 1e-3
+
+
+def test_marginal_over_cluster_draws_matches_exact_enumeration():
+    """v=24, c=6, b=4, p=2: P(t) = sum_S P(S) softmax_{T(S)}(z/tau)_t."""
+    E, c2t, C = _tiny_head(3, d=6)
+    h = np.random.default_rng(4).standard_normal(6) * 0.8
+    tau = 1.0
+    s = C @ h
+    z = E @ h
+    set_probs = _plackett_luce_set_probs(np.exp(s / tau), 2)
+    marg = np.zeros(24)
+    for S, pS in set_probs.items():
+        T = ref.candidate_tokens(np.array(S), c2t)
+        marg[T] += pS * special.softmax(z[T] / tau)
+    assert marg.sum() == pytest.approx(1.0)
+    counts = np.zeros(24)
+    for i in range(20000):
+        r = ref.flashhead_step(lambda idx: E[idx], c2t, h, 2, C_f64=C,
+                               mode="sample", tau=tau, seed=i)
+        counts[r.token] += 1
+    assert _chisq_pvalue(counts, marg) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# prepare-time data: centroid means and the INT4 quantizer
+# --------------------------------------------------------------------------
+
+def test_centroid_means_are_unit_cluster_directions():
+    rng = np.random.default_rng(11)
+    v, c, b, d = 64, 8, 8, 32
+    E = rng.standard_normal((v, d))
+    c2t = rng.permutation(v).reshape(c, b)
+    # cluster 3: identical rows -> centroid is that row's direction
+    E[c2t[3]] = E[c2t[3][0]]
+    # cluster 5: rows cancel -> zero centroid
+    E[c2t[5][1::2]] = -E[c2t[5][0::2]]
+    got = ref.centroid_means(lambda i: E[i], c2t)
+    # independent route: sort rows by cluster, segment sums via reduceat
+    owner = np.empty(v, dtype=np.int64)
+    owner[c2t.reshape(-1)] = np.repeat(np.arange(c), b)
+    order = np.argsort(owner, kind="stable")
+    sums = np.add.reduceat(E[order], np.arange(0, v, b), axis=0)
+    for k in range(c):
+        n = np.linalg.norm(sums[k])
+        if k == 5:
+            assert np.all(got[k] == 0)
+            continue
+        want = ref.round_to_bf16(sums[k] / n)
+        assert np.array_equal(got[k], want)
+        assert abs(np.linalg.norm(got[k]) - 1) < 2 ** -7
+    row = E[c2t[3][0]]
+    assert np.array_equal(got[3], ref.round_to_bf16(row / np.linalg.norm(row)))
+    # order of tokens inside a cluster does not matter
+    c2t2 = c2t[:, ::-1]
+    assert np.array_equal(ref.centroid_means(lambda i: E[i], c2t2), got)
+
+
+def test_int4_quantizer_definition_and_roundtrip_bound():
+    rng = np.random.default_rng(12)
+    C = ref.round_to_bf16(rng.standard_normal((9, 256)) *
+                          np.array([0.01, 3.0])[np.arange(256) // 128])
+    C[4, :128] = 0.0                                 # all-zero group
+    C[5, 128:] = 0.0
+    C[5, 130] = -0.5                                 # single element group
+    q, s = ref.int4_quantize(C)
+    assert q.dtype == np.int8 and q.min() >= -8 and q.max() <= 7
+    G = C.reshape(9, 2, 128)
+    amax = np.abs(G).max(axis=2)
+    assert np.array_equal(s, ref.round_to_bf16(amax / 7))
+    assert s[4, 0] == 0 and np.all(q[4, :128] == 0)
+    assert q[5, 130] == -7 and np.all(np.delete(q[5, 128:], 2) == 0)
+    deq = q.astype(np.float64) * np.repeat(s, 128, axis=1)
+    err = np.abs(C - deq)
+    assert np.all(err <= np.repeat(s, 128, axis=1) / 2 + 1e-15)
+    # the largest element of every non-zero group codes to +-7
+    for k in range(9):
+        for g in range(2):
+            if s[k, g] > 0:
+                assert np.abs(q[k, g * 128:(g + 1) * 128]).max() == 7
+    # round half to even on an exact tie: value 2.5*s codes to 2
+    Ct = np.zeros((1, 128))
+    Ct[0, 0], Ct[0, 1] = 7.0, 2.5
+    qt, st = ref.int4_quantize(Ct)
+    assert st[0, 0] == 1.0 and qt[0, 0] == 7 and qt[0, 1] == 2
+
+
+# --------------------------------------------------------------------------
+# work model ([paper] Table 8 parameter counts)
+# --------------------------------------------------------------------------
+
+def test_active_params_match_the_pages():
+    vals = {}
+    with open(os.path.join(GOLDEN, "active_params_llama32_1b.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, x = line.split()
+                vals[k] = float(x)
+    v, d, c, p = (int(vals[k]) for k in ("v", "d", "c", "p"))
+    b = v // c
+    assert c * b == v == 128256 and b == 16
+    act = ref.active_head_params(c, d, p, b)
+    assert act == 33_193_984
+    assert round(act / 1e6) == vals["active_params_millions"]
+    assert round(v * d / 1e6) == vals["dense_params_millions"]
+    assert round(100 * (1 - act / (v * d)), 1) == vals["reduction_percent"]
+
+
+# --------------------------------------------------------------------------
+# generator (input plumbing shared by both sides)
+# --------------------------------------------------------------------------
+
+def test_generator_tables_and_determinism():
+    head = synth.make_head(0, cache=False)
+    wl = head.wl
+    ref.validate(wl.v, wl.c, wl.b, head.c2t)
+    head2 = synth.make_head(0, cache=False)
+    assert np.array_equal(head.E, head2.E)
+    assert np.array_equal(head.c2t, head2.c2t)
+    nrm = np.linalg.norm(head.C_given, axis=1)
+    assert np.allclose(nrm, 1, atol=1e-5)
+    H1 = synth.make_hidden(head, 10)
+    H2 = synth.make_hidden(head, 4, offset=6)
+    assert np.array_equal(H1[6:], H2)
+    small = synth.make_head(1, c=32, b=16, d=128, cache=False)
+    assert small.E.dtype == np.uint16 and small.E.shape == (512, 128)
+    ref.validate(512, 32, 16, small.c2t)
