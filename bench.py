@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashHead two-stage retrieval head on one MI355X.
+
+One step = one call of the head on one batch of synthetic hidden vectors:
+stage-1 centroid scores, cluster selection, stage-2 candidate logits and the
+decode.  Default workload: the Llama-3.2-1B head shape (v=128256, d=2048,
+c=8016 clusters of b=16, p=512 probes), bf16, batch 1, greedy.
+
+Timing
+  cold (headline): before every call a 1 GiB buffer is streamed through the
+      GPU (untimed) so that neither L2 nor the 256 MB Infinity Cache holds
+      the head's data; the call is bracketed by HIP events on its stream.
+  warm: K back-to-back calls between two events.
+  kernels: HIP events recorded exactly around each kernel by the library
+      (flashhead_profile_begin/_end) during a separate cold pass.
+The dense head z = E h with the same decode runs on the same GPU with the
+same protocol.  The CPU oracle is timed on a bounded sample on the host.
+Inputs are resident in HBM before any timed region.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "head µs/call + achieved HBM GB/s vs dense E·h, v=128256 d=2048 p=512"
+HBM_PEAK_GBS = 8000.0
+PAGES_TPOT_H_US = 400.0   # the paper page's Table 3 FlashHead TPOT^H (0.40 ms)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, B, U, int4):
+    """Bytes the method must move per call (stage 1 + candidates + io)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    s1 = (wl.c * wl.d // 2 + wl.c * (wl.d // 128) * 2) if int4 else wl.c * wl.d * e
+    stage1 = s1 + B * wl.d * e + B * wl.c * 4
+    stage2 = U * wl.b * wl.d * e + U * wl.b * 4 + B * wl.d * e + B * wl.p * 4 + B * 4
+    total = s1 + U * wl.b * wl.d * e + U * wl.b * 4 + B * wl.d * e + B * 4
+    return total, stage1, stage2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--tau", type=float, default=1.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(batch rows shard across GPUs with no exchange; see the design "
+              "notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from two_stage_retrieval_amd import binding as fhb
+    from two_stage_retrieval_amd import synth
+
+    wl = synth.workload(args.workload)
+    B = args.batch or wl.batches[0]
+    int4 = wl.quant == "int4_g128"
+    sample = wl.mode == "sample"
+    tau = args.tau if sample else 1.0
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    head = synth.make_head(wl)
+    nvec = max(B * 64, 1024 if B == 1 else B * 8)
+    H = synth.make_hidden(head, nvec)
+    log(f"[bench] generated workload {wl.name} in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    E_dev = to_dev(head.E)
+    H_dev = to_dev(H)
+    C_init = to_dev(head.C_given) if head.C_given is not None else None
+    fh = fhb.FlashHead(E_dev, head.c2t, C_init,
+                       quant=fhb.FH_QUANT_INT4_G128 if int4 else fhb.FH_QUANT_NONE,
+                       max_batch=B, max_p=wl.p)
+    nb = nvec // B
+    batches = [H_dev[i * B:(i + 1) * B] for i in range(nb)]
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    seeds = [torch.from_numpy(synth.make_seeds(i, B).view(np.int64)).to(dev)
+             for i in range(nb)]
+    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    flush.zero_()
+    torch.cuda.synchronize()
+    log(f"[bench] prepared in {time.time() - t0:.1f}s")
+
+    def call(i):
+        x = batches[i % nb]
+        if sample:
+            fh.sample(x, wl.p, tau, seeds[i % nb], out=out)
+        else:
+            fh.greedy(x, wl.p, out=out)
+
+    dense = None if args.no_dense else fhb.DenseHead(E_dev, max_batch=B)
+
+    def call_dense(i):
+        x = batches[i % nb]
+        if sample:
+            dense(x, fhb.FH_MODE_SAMPLE, tau, seeds[i % nb], out=out)
+        else:
+            dense(x, out=out)
+
+    def time_cold(fn, K):
+        ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            flush.add_(1.0)
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+    def time_warm(fn, K):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(K):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / K
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        call(i)
+        if dense:
+            call_dense(i)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    cold = time_cold(call, K)
+    warm = time_warm(call, K)
+    log(f"[bench] flashhead cold p50 {statistics.median(cold):.2f} us, warm {warm:.2f} us")
+
+    # per-kernel durations (events around each kernel), cold
+    fhb.flashhead_profile_begin(fh.handle, K)
+    time_cold(call, K)
+    stage_ms, ncalls = fhb.flashhead_profile_end(fh.handle)
+    kern_us = [x * 1e3 for x in stage_ms]
+    log(f"[bench] kernels us: stage1 {kern_us[0]:.2f} select {kern_us[1]:.2f} "
+        f"stage2 {kern_us[2]:.2f} over {ncalls} calls")
+
+    dense_cold = dense_warm = None
+    if dense:
+        dense_cold = time_cold(call_dense, K)
+        dense_warm = time_warm(call_dense, K)
+        log(f"[bench] dense cold p50 {statistics.median(dense_cold):.2f} us, warm {dense_warm:.2f} us")
+
+    # union of selected clusters per batch (U = p at batch 1)
+    U = wl.p
+    if B > 1:
+        us = []
+        for i in range(min(nb, 8)):
+            dbg = {"clusters": torch.empty(B, wl.p, dtype=torch.int32, device=dev)}
+            if sample:
+                fh.sample(batches[i], wl.p, tau, seeds[i], out=out, debug=dbg)
+            else:
+                fh.greedy(batches[i], wl.p, out=out, debug=dbg)
+            us.append(len(np.unique(dbg["clusters"].cpu().numpy())))
+        U = int(round(statistics.mean(us)))
+    total_b, s1_b, s2_b = algorithmic_bytes(wl, B, U, int4)
+    cold_p50 = statistics.median(cold)
+    cold_p90 = float(np.percentile(cold, 90))
+    gbs = total_b / (cold_p50 * 1e-6) / 1e9
+    # dominant kernel: the longer of the two streaming stages
+    dom = 2 if kern_us[2] >= kern_us[0] else 0
+    dom_bytes = s2_b if dom == 2 else s1_b
+    dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "stage2_gather" if dom == 2 else "stage1_scores",
+                "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": dom_bytes, "avg_launch_us": round(kern_us[dom], 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head, H, wl, B, int4, sample, tau, args.cpu_seconds)
+
+    dense_p50 = statistics.median(dense_cold) if dense_cold else None
+    res = {
+        "metric": METRIC,
+        "value": round(cold_p50, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(cold_p50 / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": (round(cold_p50 / PAGES_TPOT_H_US, 4)
+                        if args.workload == 1 and B == 1 else None),
+        "vs_baseline_note": "value / the paper page's FlashHead TPOT^H of 400 us "
+                            "(Table 3, other hardware): context only",
+        "dtype": wl.dtype if not int4 else "int4+bf16",
+        "data": "synthetic (seeded generator, pages' head shapes)",
+        "config": {"workload": f"{wl.name} {'sample' if sample else 'greedy'} B={B}",
+                   "v": wl.v, "d": wl.d, "c": wl.c, "b": wl.b, "p": wl.p,
+                   "batch": B, "timing": "cold (1 GiB flush before each call)"},
+        "achieved_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": total_b,
+        "union_clusters": U,
+        "cold_p90_us": round(cold_p90, 3),
+        "warm_us": round(warm, 3),
+        "kernels_us": {"stage1": round(kern_us[0], 3), "select": round(kern_us[1], 3),
+                       "stage2": round(kern_us[2], 3)},
+        "dense_us_cold": round(dense_p50, 3) if dense_p50 else None,
+        "dense_us_warm": round(dense_warm, 3) if dense_warm else None,
+        "speedup_vs_dense": round(dense_p50 / cold_p50, 3) if dense_p50 else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    fh.close()
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(head, H, wl, B, int4, sample, tau, seconds):
+    """The oracle as it stands, on the host cores, over a bounded sample."""
+    from oracle import flashhead_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    t0 = time.time()
+    rows = ref.rows_accessor(head.E, wl.dtype)
+    if head.C_given is not None:
+        C64 = ref.as_f64(head.C_given, wl.dtype)
+    else:
+        C64 = ref.centroid_means(rows, head.c2t)
+    q4 = ref.int4_quantize(C64) if int4 else None
+    log(f"[bench] oracle prepare {time.time() - t0:.1f}s")
+    H64 = ref.as_f64(H, wl.dtype)
+    times = []
+    start = time.time()
+    n = 0
+    while time.time() - start < seconds and n < len(H64):
+        t = time.perf_counter()
+        for r in range(B):
+            ref.flashhead_step(rows, head.c2t, H64[(n * B + r) % len(H64)], wl.p,
+                               C_f64=C64, int4=q4, mode="sample" if sample else "greedy",
+                               tau=tau, seed=r)
+        times.append((time.perf_counter() - t) * 1e6)
+        n += 1
+    return {"value": round(statistics.median(times), 1), "unit": "us/call", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} calls of batch {B} on the same workload (float64 numpy oracle), "
+                      f"median per call"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/*
+ * flashhead.h -- C ABI of the MI355X (gfx950) FlashHead two-stage retrieval
+ * classification head.
+ *
+ * What the calls compute (sources are the FlashHead pages):
+ *   - "FlashHead: Efficient Drop-In Replacement for the Classification Head
+ *     in Language Model Inference", reading notes (dihengye.cn), sections
+ *     "Overall architecture", "Module 1" .. "Module 4", "Key formulas" 1-7,
+ *     "Figure 1";
+ *   - the FlashHead paper page (thelatestinai.com, arXiv 2603.14591),
+ *     abstract and Figure 1 caption.
+ *
+ * The head replaces the dense logits z = E h (Formula 1) at one decode step:
+ *   stage 1  s = C h over c unit-norm centroids (Figure 1), optionally with
+ *            INT4 centroids (Module 3);
+ *   select   p clusters: the p largest s (greedy, Module 2) or p draws
+ *            without replacement from softmax(s / tau) (sampling, Module 2);
+ *   stage 2  the p*b candidate tokens C2T[S[i / b], i mod b] (Module 1: the
+ *            dense equal-size c x b table), their exact logits E_t h, then an
+ *            argmax (Formula 2) or a temperature sample over the candidates
+ *            (Formula 3).
+ * The head returns token ids, not a distribution over the vocabulary (the
+ * notes' Module 4: the full distribution is only reachable by Monte Carlo).
+ *
+ * Conventions shared by every call
+ *   - Device pointers are HIP device memory of the current device; host
+ *     pointers are ordinary host memory.  `stream` is a hipStream_t (NULL =
+ *     the default stream).
+ *   - Matrices are row-major.  E is v x d with a row stride of `lde`
+ *     elements; H is B x d, contiguous.  dtype FH_DTYPE_F32 means float32
+ *     storage, FH_DTYPE_BF16 means bfloat16 storage (uint16 bit patterns);
+ *     H always has E's dtype.  All arithmetic accumulates in fp32.
+ *   - Alignment: E, C and H base addresses must be 16-byte aligned and a row
+ *     (d * element size, and lde * element size) a multiple of 16 bytes.
+ *   - Ties: a larger value wins, then the lower index (cluster or token id).
+ *   - Random numbers: Philox4x32-10 keyed by a per-row 64-bit seed, counter
+ *     (idx >> 2, stream, 0, 0), word idx & 3; stream 0 draws per cluster id,
+ *     stream 1 per token id; Gumbel noise -log(-log u) with
+ *     u = (2 * (x >> 9) + 1) * 2^-24.
+ *   - Inputs must be finite; the library does not scan them.
+ *   - Calls on one handle must not overlap in time (the handle owns the
+ *     workspace); calls are asynchronous on `stream`, make no allocation and
+ *     no host synchronisation, and leave the workspace ready for the next
+ *     call.  Errors found at enqueue time return synchronously and enqueue
+ *     nothing.
+ */
+#ifndef FLASHHEAD_H
+#define FLASHHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes: 0 = success, negative = error. */
+#define FH_OK 0
+#define FH_ERR_INVALID_ARG (-1)     /* NULL pointer, size or range error     */
+#define FH_ERR_NOT_PERMUTATION (-2) /* C2T is not a permutation of [0, v)    */
+#define FH_ERR_UNSUPPORTED (-3)     /* dtype, alignment or shape not handled */
+#define FH_ERR_HIP (-4)             /* a HIP runtime call failed             */
+#define FH_ERR_OOM (-5)             /* device allocation failed (prepare)    */
+
+#define FH_DTYPE_F32 0
+#define FH_DTYPE_BF16 1
+
+#define FH_QUANT_NONE 0
+#define FH_QUANT_INT4_G128 1 /* stage-1 centroids as 4-bit codes, groups of
+                                128 columns, one bf16 scale per group        */
+
+#define FH_MODE_GREEDY 0
+#define FH_MODE_SAMPLE 1
+
+/* Limits of this implementation. */
+#define FH_MAX_BATCH 64     /* rows per call                               */
+#define FH_MAX_C 32768      /* clusters                                    */
+#define FH_MAX_ROW_BYTES 8192 /* d * element size (bf16: d <= 4096)        */
+
+typedef struct fh_handle fh_handle;
+
+/*
+ * Description of a prepared head.  Stage-1 centroids C and the table C2T
+ * come from the offline equal-size spherical k-means (notes, Module 1 and
+ * Formulas 4-5); this library takes them as inputs, or computes C from E and
+ * C2T by Formula 5 when C is NULL.
+ */
+typedef struct fh_desc {
+  int64_t v;          /* vocabulary size; must equal c * b                 */
+  int32_t d;          /* hidden size                                       */
+  int32_t c;          /* number of clusters (1..FH_MAX_C)                  */
+  int32_t b;          /* tokens per cluster                                */
+  int32_t dtype;      /* FH_DTYPE_F32 or FH_DTYPE_BF16 (E, C, H)           */
+  int64_t lde;        /* row stride of E in elements (>= d)                */
+  const void* E;      /* device, v x lde; read during prepare only: the
+                         handle keeps its own cluster-major copy (row
+                         k*b + j = E[C2T[k, j]], v x d), so E may be freed
+                         or changed after prepare returns                  */
+  const int32_t* c2t; /* host, c x b; must be a permutation of [0, v);
+                         copied at prepare                                 */
+  const void* C;      /* device, c x d contiguous in dtype, unit-norm rows,
+                         or NULL to compute C = unit(mean of cluster rows)
+                         (Formula 5; bf16 by round-to-nearest-even when
+                         dtype is bf16); copied at prepare                 */
+  int32_t quant;      /* FH_QUANT_NONE or FH_QUANT_INT4_G128 (needs bf16,
+                         d a multiple of 128)                              */
+  int32_t max_batch;  /* largest B passed to later calls (1..FH_MAX_BATCH) */
+  int32_t max_p;      /* largest p passed to later calls (1..c)            */
+  void* stream;       /* hipStream_t for prepare's own work                */
+} fh_desc;
+
+/*
+ * Optional debug outputs (device pointers, each may be NULL).  They cost
+ * extra writes and exist for tests and analysis.
+ *   scores      B x c   stage-1 scores s = C h (before any noise)
+ *   clusters    B x p   selected cluster ids, ascending per row
+ *   cand_ids    B x p*b candidate token ids; row r lists, for the j-th
+ *                       selected cluster in ascending cluster order, its b
+ *                       tokens C2T[k, 0..b) at [j*b, j*b + b)
+ *   cand_logits B x p*b exact logits of cand_ids (fp32)
+ */
+typedef struct fh_debug {
+  float* scores;
+  int32_t* clusters;
+  int32_t* cand_ids;
+  float* cand_logits;
+} fh_debug;
+
+/*
+ * One-time preparation (notes: "Implementation details" -- the head stores
+ * the centroid matrix and the C2T map).  Validates the description, checks
+ * that C2T is a permutation of [0, v) (FH_ERR_NOT_PERMUTATION otherwise),
+ * copies C2T and C to device memory owned by the handle (or computes C),
+ * builds the INT4 codes when asked, allocates the workspace, and waits for
+ * `stream` to finish.  On error *out is set to NULL and nothing is kept.
+ */
+int flashhead_prepare(const fh_desc* desc, fh_handle** out);
+
+/* Frees everything the handle owns (not E).  NULL is accepted. */
+void flashhead_destroy(fh_handle* h);
+
+/*
+ * Greedy decode step for B rows (notes, Module 2 greedy mode and Formula 2):
+ * per row r, S = the p clusters with the largest C h_r, then
+ * out_tokens[r] = argmax over the p*b candidates of E_t h_r.
+ *   H          device, B x d in the handle's dtype
+ *   B          1..max_batch;  p  1..max_p
+ *   out_tokens device, B int32
+ *   dbg        optional debug outputs (NULL for none)
+ */
+int flashhead_greedy(fh_handle* h, const void* H, int32_t B, int32_t p,
+                     int32_t* out_tokens, const fh_debug* dbg, void* stream);
+
+/*
+ * Sampling decode step (notes, Module 2 sampling mode and Formula 3; the
+ * paper's abstract, innovation 3).  Per row r with key seeds[r]:
+ * S = the p largest s_k / tau + G0(k) (Gumbel-top-p: p successive draws
+ * without replacement from softmax(s / tau)), then out_tokens[r] = the
+ * candidate with the largest z_t / tau + G1(t) (Gumbel-max: one draw from
+ * the softmax of z / tau over the candidates).
+ *   tau        finite, > 0; the same temperature scales both stages
+ *   seeds      device, B uint64 Philox keys (e.g. (step << 32) | row)
+ *   out_lse    device, B fp32 log sum_{t in candidates} exp(z_t / tau), or
+ *              NULL (the normaliser of p(t | h, S), the summand of
+ *              Formula 7)
+ */
+int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p,
+                     float tau, const uint64_t* seeds, int32_t* out_tokens,
+                     float* out_lse, const fh_debug* dbg, void* stream);
+
+/*
+ * The dense head it replaces (Formula 1 followed by Formula 2 or 3), as the
+ * in-library comparison: z = E h_r over all v tokens, then argmax or the
+ * Gumbel-max sample with stream-1 noise keyed by token id (so that
+ * flashhead_sample with p = c returns the same ids).
+ *   workspace  device memory of dense_head_workspace_bytes(B) bytes, zero
+ *              filled before its first use; every call leaves it zeroed
+ *   out_lse    optional, as for flashhead_sample (over all v tokens)
+ */
+size_t dense_head_workspace_bytes(int32_t B);
+int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype,
+               int64_t lde, const void* H, int32_t B, int32_t mode,
+               float tau, const uint64_t* seeds, int32_t* out_tokens,
+               float* out_lse, void* workspace, void* stream);
+
+/* Static text for a status code. */
+const char* flashhead_status_string(int status);
+
+/*
+ * Prepare-time data, copied to host memory (synchronous):
+ *   flashhead_export_centroids  c x d in the handle's dtype
+ *   flashhead_export_int4       codes: ceil(c/16) * (d/128) tiles of 1024
+ *     bytes; tile (t, g) lane l (0..63) owns row 16t + (l mod 16) and
+ *     columns 128g + 32(l div 16) + [0, 32); its 16 bytes hold those 32
+ *     codes, byte j = column 2j (low nibble) and column 2j + 1 (high
+ *     nibble), two's complement.  scales: ceil(c/16) * (d/128) * 16 bf16,
+ *     scale of (row 16t + i, group g) at index (t * (d/128) + g) * 16 + i.
+ *     Rows past c are zero.
+ */
+int flashhead_export_centroids(const fh_handle* h, void* dst_host);
+int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
+                          uint16_t* scales_host);
+
+/* Sizes of a prepared head: what = 0 v, 1 d, 2 c, 3 b, 4 dtype, 5 quant,
+ * 6 max_batch, 7 max_p, 8 device bytes owned by the handle, 9 the selection
+ * self-check flag (non-zero if a selection ever produced a count other than
+ * p; reading it synchronises with the device and clears it). */
+int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
+
+/*
+ * Per-kernel timing for measurement (not for the decode loop).
+ * flashhead_profile_begin creates 6 HIP events per call for the next
+ * max_calls decode calls on this handle; each of those calls records them
+ * exactly around its stage-1, select and stage-2 kernels (on the call's
+ * stream).  flashhead_profile_end waits for the recorded events, writes the
+ * average duration in milliseconds of each of the three kernels per call to
+ * stage_ms[0..2] and the number of recorded calls to *calls, and releases
+ * the events.
+ */
+int flashhead_profile_begin(fh_handle* h, int32_t max_calls);
+int flashhead_profile_end(fh_handle* h, double* stage_ms, int32_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHHEAD_H */

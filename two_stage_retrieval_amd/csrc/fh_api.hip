@@ -1,0 +1,504 @@
+// C ABI of libflashhead: argument validation, the prepared handle and its
+// workspace, the host INT4 quantizer, and the enqueue of each decode step.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "fh_internal.h"
+
+using namespace fh;
+
+struct fh_handle {
+  int64_t v = 0;
+  int d = 0, c = 0, b = 0, dtype = 0, quant = 0, max_batch = 0, max_p = 0;
+  int esize = 0;
+  int64_t row_bytes = 0;  // d * esize: rows of C and of the cluster-major copy
+  int device = 0;
+  void* C = nullptr;          // c x d
+  int32_t* c2t = nullptr;     // c x b
+  uint8_t* Ec = nullptr;      // cluster-major copy of E (v x d)
+  uint8_t* q4 = nullptr;      // INT4 tiles
+  uint16_t* q4s = nullptr;    // INT4 scales
+  int ntiles = 0, groups = 0;
+  // workspace (left zeroed / consistent by every call)
+  float* keys = nullptr;      // max_batch x c
+  int32_t* sel = nullptr;     // max_batch x max_p
+  uint64_t* best = nullptr;   // max_batch
+  uint32_t* counters = nullptr;
+  float2* lse_part = nullptr; // max_batch x kMaxGrid
+  uint64_t* masks = nullptr;  // c
+  uint32_t* error = nullptr;  // 1
+  int64_t bytes = 0;
+  std::vector<void*> allocs;
+  // per-kernel timing (flashhead_profile_begin / _end)
+  std::vector<hipEvent_t> prof_ev;  // 6 per recorded call
+  int prof_cap = 0, prof_calls = 0;
+};
+
+namespace {
+
+constexpr int kMaxGrid = 8192;       // largest grid.x of a decode launch
+constexpr int kDenseMaxGrid = 2048;  // dense launches loop inside
+
+int esize_of(int dtype) { return dtype == FH_DTYPE_F32 ? 4 : dtype == FH_DTYPE_BF16 ? 2 : 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+void drop_profile(fh_handle* h) {
+  for (hipEvent_t e : h->prof_ev) (void)hipEventDestroy(e);
+  h->prof_ev.clear();
+  h->prof_cap = h->prof_calls = 0;
+}
+
+void free_handle(fh_handle* h) {
+  if (!h) return;
+  drop_profile(h);
+  for (void* p : h->allocs) (void)hipFree(p);
+  delete h;
+}
+
+template <typename T>
+hipError_t alloc(fh_handle* h, T** p, size_t bytes) {
+  void* q = nullptr;
+  const hipError_t e = hipMalloc(&q, bytes < 16 ? 16 : bytes);
+  if (e != hipSuccess) return e;
+  h->allocs.push_back(q);
+  h->bytes += (int64_t)bytes;
+  *p = static_cast<T*>(q);
+  return hipSuccess;
+}
+
+// nearest bf16 value of a double (8 significant bits), ties to even
+double round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e = 0;
+  (void)frexp(x, &e);
+  const int se = (e - 8) > -133 ? (e - 8) : -133;
+  return ldexp(nearbyint(ldexp(x, -se)), se);
+}
+uint16_t bf16_bits(double x) {
+  const float f = (float)x;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+double bf16_value(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Symmetric per-group INT4 codes (groups of 128 columns): scale = bf16(amax/7),
+// code = round-half-even(x / scale) clipped to [-8, 7]; packed in 16-row tiles.
+void quantize_int4(const uint16_t* C, int c, int d, std::vector<uint8_t>& codes,
+                   std::vector<uint16_t>& scales, int* ntiles_out, int* groups_out) {
+  const int G = d / 128, ntiles = (c + 15) / 16;
+  codes.assign((size_t)ntiles * G * 1024, 0);
+  scales.assign((size_t)ntiles * G * 16, 0);
+  std::vector<int8_t> q(128);
+  for (int k = 0; k < c; ++k) {
+    const int t = k / 16, rin = k % 16;
+    for (int g = 0; g < G; ++g) {
+      const uint16_t* src = C + (size_t)k * d + (size_t)g * 128;
+      double amax = 0.0;
+      for (int j = 0; j < 128; ++j) amax = fmax(amax, fabs(bf16_value(src[j])));
+      const double s = round_bf16(amax / 7.0);
+      for (int j = 0; j < 128; ++j) {
+        double qq = s > 0.0 ? nearbyint(bf16_value(src[j]) / s) : 0.0;
+        qq = qq < -8.0 ? -8.0 : (qq > 7.0 ? 7.0 : qq);
+        q[j] = (int8_t)qq;
+      }
+      scales[((size_t)t * G + g) * 16 + rin] = bf16_bits(s);
+      for (int quarter = 0; quarter < 4; ++quarter) {
+        const int lane = quarter * 16 + rin;
+        uint8_t* dst = codes.data() + (((size_t)t * G + g) * 64 + lane) * 16;
+        for (int j = 0; j < 16; ++j) {
+          const int col = quarter * 32 + 2 * j;
+          dst[j] = (uint8_t)((q[col] & 0xF) | ((q[col + 1] & 0xF) << 4));
+        }
+      }
+    }
+  }
+  *ntiles_out = ntiles;
+  *groups_out = G;
+}
+
+int check_device(const fh_handle* h) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FH_ERR_HIP;
+  return dev == h->device ? FH_OK : FH_ERR_INVALID_ARG;
+}
+
+#define FH_TRY(expr)                                              \
+  do {                                                            \
+    const hipError_t e_ = (expr);                                 \
+    if (e_ != hipSuccess) return e_ == hipErrorOutOfMemory ? FH_ERR_OOM : FH_ERR_HIP; \
+  } while (0)
+
+int prepare_impl(const fh_desc* ds, fh_handle* h) {
+  hipStream_t s = static_cast<hipStream_t>(ds->stream);
+  FH_TRY(hipGetDevice(&h->device));
+  const int64_t v = ds->v;
+  const int c = ds->c, b = ds->b, d = ds->d;
+  FH_TRY(alloc(h, &h->c2t, (size_t)v * 4));
+  FH_TRY(hipMemcpyAsync(h->c2t, ds->c2t, (size_t)v * 4, hipMemcpyHostToDevice, s));
+  FH_TRY(alloc(h, &h->C, (size_t)c * h->row_bytes));
+  const uint8_t* E = static_cast<const uint8_t*>(ds->E);
+  const int64_t lde_bytes = ds->lde * h->esize;
+  if (ds->C)
+    FH_TRY(hipMemcpyAsync(h->C, ds->C, (size_t)c * h->row_bytes, hipMemcpyDeviceToDevice, s));
+  else
+    FH_TRY(launch_centroid_means(E, lde_bytes, h->dtype, d, h->c2t, c, b, h->C, s));
+  FH_TRY(alloc(h, &h->Ec, (size_t)v * h->row_bytes));
+  FH_TRY(launch_cluster_major_copy(E, lde_bytes, h->c2t, v, h->row_bytes, h->Ec, s));
+  if (h->quant == FH_QUANT_INT4_G128) {
+    std::vector<uint16_t> hostC((size_t)c * d);
+    FH_TRY(hipMemcpyAsync(hostC.data(), h->C, hostC.size() * 2, hipMemcpyDeviceToHost, s));
+    FH_TRY(hipStreamSynchronize(s));
+    std::vector<uint8_t> codes;
+    std::vector<uint16_t> scales;
+    quantize_int4(hostC.data(), c, d, codes, scales, &h->ntiles, &h->groups);
+    FH_TRY(alloc(h, &h->q4, codes.size()));
+    FH_TRY(alloc(h, &h->q4s, scales.size() * 2));
+    FH_TRY(hipMemcpyAsync(h->q4, codes.data(), codes.size(), hipMemcpyHostToDevice, s));
+    FH_TRY(hipMemcpyAsync(h->q4s, scales.data(), scales.size() * 2, hipMemcpyHostToDevice, s));
+    FH_TRY(hipStreamSynchronize(s));  // host vectors die at scope end
+  }
+  const int mb = h->max_batch;
+  FH_TRY(alloc(h, &h->keys, (size_t)mb * c * 4));
+  FH_TRY(alloc(h, &h->sel, (size_t)mb * h->max_p * 4));
+  FH_TRY(alloc(h, &h->best, (size_t)mb * 8));
+  FH_TRY(alloc(h, &h->counters, (size_t)mb * 4));
+  FH_TRY(alloc(h, &h->lse_part, (size_t)mb * kMaxGrid * 8));
+  FH_TRY(alloc(h, &h->masks, (size_t)c * 8));
+  FH_TRY(alloc(h, &h->error, 4));
+  FH_TRY(hipMemsetAsync(h->sel, 0, (size_t)mb * h->max_p * 4, s));
+  FH_TRY(hipMemsetAsync(h->best, 0, (size_t)mb * 8, s));
+  FH_TRY(hipMemsetAsync(h->counters, 0, (size_t)mb * 4, s));
+  FH_TRY(hipMemsetAsync(h->masks, 0, (size_t)c * 8, s));
+  FH_TRY(hipMemsetAsync(h->error, 0, 4, s));
+  FH_TRY(hipStreamSynchronize(s));
+  return FH_OK;
+}
+
+int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
+              const uint64_t* seeds, int32_t* out, float* out_lse, const fh_debug* dbg,
+              void* stream) {
+  if (!h || !H || !out) return FH_ERR_INVALID_ARG;
+  if (B < 1 || B > h->max_batch || p < 1 || p > h->max_p || p > h->c) return FH_ERR_INVALID_ARG;
+  if (mode == FH_MODE_SAMPLE && (!seeds || !(tau > 0.0f) || !isfinite(tau)))
+    return FH_ERR_INVALID_ARG;
+  if (!aligned16(H)) return FH_ERR_UNSUPPORTED;
+  if (dbg && ((dbg->cand_ids == nullptr) != (dbg->cand_logits == nullptr)))
+    return FH_ERR_INVALID_ARG;
+  {
+    const int st = check_device(h);
+    if (st != FH_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Timing tm[3];
+  const Timing* t1 = nullptr;
+  const Timing* t2 = nullptr;
+  const Timing* t3 = nullptr;
+  if (h->prof_calls < h->prof_cap) {
+    const size_t e = (size_t)h->prof_calls++ * 6;
+    for (int i = 0; i < 3; ++i) tm[i] = Timing{h->prof_ev[e + 2 * i], h->prof_ev[e + 2 * i + 1]};
+    t1 = &tm[0];
+    t2 = &tm[1];
+    t3 = &tm[2];
+  }
+  const bool sample = mode == FH_MODE_SAMPLE;
+  const float inv_tau = sample ? 1.0f / tau : 1.0f;
+  const int nchunk = (int)(h->row_bytes / 16);
+
+  // stage 1: selection keys per (row, cluster)
+  if (h->quant == FH_QUANT_INT4_G128) {
+    Int4Args a{};
+    a.codes = h->q4;
+    a.scales = h->q4s;
+    a.ntiles = h->ntiles;
+    a.groups = h->groups;
+    a.c = h->c;
+    a.d = h->d;
+    a.H = static_cast<const uint16_t*>(H);
+    a.keys_out = h->keys;
+    a.key_stride = h->c;
+    a.dbg_scores = dbg ? dbg->scores : nullptr;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    if (launch_int4_gemv(a, B, s, t1) != hipSuccess) return FH_ERR_HIP;
+  } else {
+    RowdotArgs a{};
+    a.base = static_cast<const uint8_t*>(h->C);
+    a.row_bytes = h->row_bytes;
+    a.nchunk = nchunk;
+    a.H = static_cast<const uint8_t*>(H);
+    a.h_bytes = h->row_bytes;
+    a.nrows = h->c;
+    a.keys_out = h->keys;
+    a.key_stride = h->c;
+    a.dbg_scores = dbg ? dbg->scores : nullptr;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    if (launch_rowdot(a, kRowScores, h->dtype, B, rowdot_grid(h->c, nchunk, kRowScores), s,
+                      t1) != hipSuccess)
+      return FH_ERR_HIP;
+  }
+  // select p clusters per row
+  {
+    SelectArgs a{};
+    a.keys = h->keys;
+    a.key_stride = h->c;
+    a.c = h->c;
+    a.p = p;
+    a.sel = h->sel;
+    a.sel_stride = h->max_p;
+    a.masks = nullptr;
+    a.error = h->error;
+    if (launch_select(a, B, s, t2) != hipSuccess) return FH_ERR_HIP;
+  }
+  if (dbg && dbg->clusters) {
+    if (hipMemcpy2DAsync(dbg->clusters, (size_t)p * 4, h->sel, (size_t)h->max_p * 4,
+                         (size_t)p * 4, B, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return FH_ERR_HIP;
+  }
+  // stage 2: candidate logits + decode
+  {
+    RowdotArgs a{};
+    a.base = h->Ec;
+    a.row_bytes = h->row_bytes;
+    a.nchunk = nchunk;
+    a.H = static_cast<const uint8_t*>(H);
+    a.h_bytes = h->row_bytes;
+    a.nrows = (int64_t)p * h->b;
+    a.sel = h->sel;
+    a.sel_stride = h->max_p;
+    a.c2t = h->c2t;
+    a.b = h->b;
+    a.nclusters = h->c;
+    a.best = h->best;
+    a.counters = h->counters;
+    a.lse_part = h->lse_part;
+    a.out_tokens = out;
+    a.out_lse = out_lse;
+    a.dbg_ids = dbg ? dbg->cand_ids : nullptr;
+    a.dbg_logits = dbg ? dbg->cand_logits : nullptr;
+    a.dbg_stride = (int64_t)p * h->b;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    const int gx = rowdot_grid(a.nrows, nchunk, kRowGather);
+    if (gx > kMaxGrid) return FH_ERR_UNSUPPORTED;
+    if (launch_rowdot(a, kRowGather, h->dtype, B, gx, s, t3) != hipSuccess) return FH_ERR_HIP;
+  }
+  return FH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flashhead_status_string(int status) {
+  switch (status) {
+    case FH_OK: return "ok";
+    case FH_ERR_INVALID_ARG: return "invalid argument";
+    case FH_ERR_NOT_PERMUTATION: return "C2T is not a permutation of [0, v)";
+    case FH_ERR_UNSUPPORTED: return "unsupported dtype, alignment or shape";
+    case FH_ERR_HIP: return "HIP runtime error";
+    case FH_ERR_OOM: return "device out of memory";
+    default: return "unknown status";
+  }
+}
+
+int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
+  if (!out) return FH_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!ds || !ds->E || !ds->c2t) return FH_ERR_INVALID_ARG;
+  if (ds->c < 1 || ds->b < 1 || ds->d < 1 || ds->v != (int64_t)ds->c * ds->b)
+    return FH_ERR_INVALID_ARG;
+  if (ds->max_batch < 1 || ds->max_batch > FH_MAX_BATCH) return FH_ERR_INVALID_ARG;
+  if (ds->max_p < 1 || ds->max_p > ds->c) return FH_ERR_INVALID_ARG;
+  if (ds->lde < ds->d) return FH_ERR_INVALID_ARG;
+  if (ds->v > (int64_t)INT32_MAX) return FH_ERR_UNSUPPORTED;
+  const int es = esize_of(ds->dtype);
+  if (!es) return FH_ERR_UNSUPPORTED;
+  if (ds->c > FH_MAX_C) return FH_ERR_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)ds->d * es;
+  if (row_bytes % 16 || (ds->lde * es) % 16 || row_bytes > FH_MAX_ROW_BYTES)
+    return FH_ERR_UNSUPPORTED;
+  if (!aligned16(ds->E) || (ds->C && !aligned16(ds->C))) return FH_ERR_UNSUPPORTED;
+  if (ds->quant != FH_QUANT_NONE && ds->quant != FH_QUANT_INT4_G128) return FH_ERR_UNSUPPORTED;
+  if (ds->quant == FH_QUANT_INT4_G128 && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
+    return FH_ERR_UNSUPPORTED;
+  // C2T must be a permutation of [0, v) (equal-size clusters, dense table)
+  {
+    std::vector<uint8_t> seen((size_t)ds->v, 0);
+    for (int64_t i = 0; i < ds->v; ++i) {
+      const int32_t t = ds->c2t[i];
+      if (t < 0 || (int64_t)t >= ds->v || seen[(size_t)t]) return FH_ERR_NOT_PERMUTATION;
+      seen[(size_t)t] = 1;
+    }
+  }
+  fh_handle* h = new (std::nothrow) fh_handle();
+  if (!h) return FH_ERR_OOM;
+  h->v = ds->v;
+  h->d = ds->d;
+  h->c = ds->c;
+  h->b = ds->b;
+  h->dtype = ds->dtype;
+  h->quant = ds->quant;
+  h->max_batch = ds->max_batch;
+  h->max_p = ds->max_p;
+  h->esize = es;
+  h->row_bytes = row_bytes;
+  const int st = prepare_impl(ds, h);
+  if (st != FH_OK) {
+    (void)hipStreamSynchronize(static_cast<hipStream_t>(ds->stream));
+    free_handle(h);
+    return st;
+  }
+  *out = h;
+  return FH_OK;
+}
+
+void flashhead_destroy(fh_handle* h) { free_handle(h); }
+
+int flashhead_greedy(fh_handle* h, const void* H, int32_t B, int32_t p, int32_t* out_tokens,
+                     const fh_debug* dbg, void* stream) {
+  return step_impl(h, H, B, p, FH_MODE_GREEDY, 1.0f, nullptr, out_tokens, nullptr, dbg, stream);
+}
+
+int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p, float tau,
+                     const uint64_t* seeds, int32_t* out_tokens, float* out_lse,
+                     const fh_debug* dbg, void* stream) {
+  return step_impl(h, H, B, p, FH_MODE_SAMPLE, tau, seeds, out_tokens, out_lse, dbg, stream);
+}
+
+size_t dense_head_workspace_bytes(int32_t B) {
+  if (B < 1) return 0;
+  const size_t nb = (size_t)B;
+  return nb * 8 + ((nb * 4 + 15) / 16) * 16 + nb * kDenseMaxGrid * 8;
+}
+
+int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, const void* H,
+               int32_t B, int32_t mode, float tau, const uint64_t* seeds, int32_t* out_tokens,
+               float* out_lse, void* workspace, void* stream) {
+  if (!E || !H || !out_tokens || !workspace) return FH_ERR_INVALID_ARG;
+  if (v < 1 || d < 1 || lde < d || B < 1 || B > FH_MAX_BATCH) return FH_ERR_INVALID_ARG;
+  if (mode != FH_MODE_GREEDY && mode != FH_MODE_SAMPLE) return FH_ERR_INVALID_ARG;
+  if (mode == FH_MODE_SAMPLE && (!seeds || !(tau > 0.0f) || !isfinite(tau)))
+    return FH_ERR_INVALID_ARG;
+  if (v > (int64_t)INT32_MAX) return FH_ERR_UNSUPPORTED;
+  const int es = esize_of(dtype);
+  if (!es) return FH_ERR_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)d * es;
+  if (row_bytes % 16 || (lde * es) % 16 || row_bytes > FH_MAX_ROW_BYTES) return FH_ERR_UNSUPPORTED;
+  if (!aligned16(E) || !aligned16(H) || !aligned16(workspace)) return FH_ERR_UNSUPPORTED;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t nb = (size_t)B;
+  RowdotArgs a{};
+  a.base = static_cast<const uint8_t*>(E);
+  a.row_bytes = lde * es;
+  a.nchunk = (int)(row_bytes / 16);
+  a.H = static_cast<const uint8_t*>(H);
+  a.h_bytes = row_bytes;
+  a.nrows = v;
+  a.best = reinterpret_cast<uint64_t*>(ws);
+  a.counters = reinterpret_cast<uint32_t*>(ws + nb * 8);
+  a.lse_part = reinterpret_cast<float2*>(ws + nb * 8 + ((nb * 4 + 15) / 16) * 16);
+  a.out_tokens = out_tokens;
+  a.out_lse = out_lse;
+  a.sample = mode == FH_MODE_SAMPLE;
+  a.inv_tau = a.sample ? 1.0f / tau : 1.0f;
+  a.seeds = seeds;
+  const int gx = rowdot_grid(v, a.nchunk, kRowDense);
+  if (gx > kDenseMaxGrid) return FH_ERR_UNSUPPORTED;
+  if (launch_rowdot(a, kRowDense, dtype, B, gx, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FH_ERR_HIP;
+  return FH_OK;
+}
+
+int flashhead_export_centroids(const fh_handle* h, void* dst) {
+  if (!h || !dst) return FH_ERR_INVALID_ARG;
+  if (hipMemcpy(dst, h->C, (size_t)h->c * h->row_bytes, hipMemcpyDeviceToHost) != hipSuccess)
+    return FH_ERR_HIP;
+  return FH_OK;
+}
+
+int flashhead_export_int4(const fh_handle* h, uint8_t* codes, uint16_t* scales) {
+  if (!h || !codes || !scales) return FH_ERR_INVALID_ARG;
+  if (h->quant != FH_QUANT_INT4_G128) return FH_ERR_UNSUPPORTED;
+  const size_t tiles = (size_t)h->ntiles * h->groups;
+  if (hipMemcpy(codes, h->q4, tiles * 1024, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(scales, h->q4s, tiles * 16 * 2, hipMemcpyDeviceToHost) != hipSuccess)
+    return FH_ERR_HIP;
+  return FH_OK;
+}
+
+int flashhead_profile_begin(fh_handle* h, int32_t max_calls) {
+  if (!h || max_calls < 1 || max_calls > (1 << 20)) return FH_ERR_INVALID_ARG;
+  drop_profile(h);
+  h->prof_ev.resize((size_t)max_calls * 6, nullptr);
+  for (auto& e : h->prof_ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      drop_profile(h);
+      return FH_ERR_HIP;
+    }
+  }
+  h->prof_cap = max_calls;
+  h->prof_calls = 0;
+  return FH_OK;
+}
+
+int flashhead_profile_end(fh_handle* h, double* stage_ms, int32_t* calls) {
+  if (!h || !stage_ms || !calls) return FH_ERR_INVALID_ARG;
+  double acc[3] = {0.0, 0.0, 0.0};
+  const int n = h->prof_calls;
+  int st = FH_OK;
+  for (int i = 0; i < n && st == FH_OK; ++i) {
+    for (int k = 0; k < 3; ++k) {
+      hipEvent_t a = h->prof_ev[(size_t)i * 6 + 2 * k], b = h->prof_ev[(size_t)i * 6 + 2 * k + 1];
+      float ms = 0.0f;
+      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+        st = FH_ERR_HIP;
+        break;
+      }
+      acc[k] += ms;
+    }
+  }
+  for (int k = 0; k < 3; ++k) stage_ms[k] = n ? acc[k] / n : 0.0;
+  *calls = n;
+  drop_profile(h);
+  return st;
+}
+
+int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
+  if (!h || !value) return FH_ERR_INVALID_ARG;
+  switch (what) {
+    case 0: *value = h->v; break;
+    case 1: *value = h->d; break;
+    case 2: *value = h->c; break;
+    case 3: *value = h->b; break;
+    case 4: *value = h->dtype; break;
+    case 5: *value = h->quant; break;
+    case 6: *value = h->max_batch; break;
+    case 7: *value = h->max_p; break;
+    case 8: *value = h->bytes; break;
+    case 9: {  // selection error flag (synchronous read and clear)
+      uint32_t e = 0;
+      if (hipMemcpy(&e, h->error, 4, hipMemcpyDeviceToHost) != hipSuccess) return FH_ERR_HIP;
+      if (e && hipMemset(h->error, 0, 4) != hipSuccess) return FH_ERR_HIP;
+      *value = e;
+      break;
+    }
+    default: return FH_ERR_INVALID_ARG;
+  }
+  return FH_OK;
+}
+
+}  // extern "C"

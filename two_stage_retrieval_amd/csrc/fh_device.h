@@ -1,0 +1,166 @@
+// Device helpers shared by the FlashHead kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fh {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Dot product of one 16-byte chunk with the matching h values.
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+  static constexpr int kElems = 4;
+  __device__ __forceinline__ static void unpack(const uint4& w, float* out) {
+    out[0] = __uint_as_float(w.x); out[1] = __uint_as_float(w.y);
+    out[2] = __uint_as_float(w.z); out[3] = __uint_as_float(w.w);
+  }
+  __device__ __forceinline__ static float dot(const uint4& w, const float* h, float acc) {
+    acc = fmaf(__uint_as_float(w.x), h[0], acc);
+    acc = fmaf(__uint_as_float(w.y), h[1], acc);
+    acc = fmaf(__uint_as_float(w.z), h[2], acc);
+    acc = fmaf(__uint_as_float(w.w), h[3], acc);
+    return acc;
+  }
+};
+struct bf16_t {};  // storage tag: 16-bit brain float
+template <> struct Chunk<bf16_t> {
+  static constexpr int kElems = 8;
+  __device__ __forceinline__ static void unpack(const uint4& w, float* out) {
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+  }
+  // bf16 x bf16 products are exact in fp32; fmaf adds them with one rounding.
+  __device__ __forceinline__ static float dot(const uint4& w, const float* h, float acc) {
+    acc = fmaf(bf16_lo(w.x), h[0], acc); acc = fmaf(bf16_hi(w.x), h[1], acc);
+    acc = fmaf(bf16_lo(w.y), h[2], acc); acc = fmaf(bf16_hi(w.y), h[3], acc);
+    acc = fmaf(bf16_lo(w.z), h[4], acc); acc = fmaf(bf16_hi(w.z), h[5], acc);
+    acc = fmaf(bf16_lo(w.w), h[6], acc); acc = fmaf(bf16_hi(w.w), h[7], acc);
+    return acc;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// order-preserving keys.  Larger float -> larger uint32; -0 and +0 collapse.
+// The 64-bit decode key puts the ordered value above (0xFFFFFFFF - id), so an
+// unsigned max picks the largest value and, among equal values, the lowest
+// id.  Zero is below every key of a finite value (the "empty" state).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ordered_u32(float f) {
+  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t decode_key(float f, uint32_t id) {
+  return ((uint64_t)ordered_u32(f) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) {
+  return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11) and the Gumbel transform.
+// key = (lo32(seed), hi32(seed)); counter = (idx >> 2, stream, 0, 0);
+// the draw for idx is output word idx & 3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint32_t lo0 = 0xD2511F53u * x.x, hi0 = __umulhi(0xD2511F53u, x.x);
+    const uint32_t lo1 = 0xCD9E8D57u * x.z, hi1 = __umulhi(0xCD9E8D57u, x.z);
+    x = make_uint4(hi1 ^ x.y ^ k0, lo1, hi0 ^ x.w ^ k1, lo0);
+  }
+  return x;
+}
+__device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint32_t stream, uint32_t idx) {
+  const uint4 o = philox4x32_10(make_uint4(idx >> 2, stream, 0u, 0u), (uint32_t)seed,
+                                (uint32_t)(seed >> 32));
+  const uint32_t w = idx & 3u;
+  return w == 0 ? o.x : (w == 1 ? o.y : (w == 2 ? o.z : o.w));
+}
+// u = (2*(x >> 9) + 1) * 2^-24 lies in (0,1) and is exact in fp32.
+__device__ __forceinline__ float gumbel_of_word(uint32_t x) {
+  const float u = (float)(2u * (x >> 9) + 1u) * 5.9604644775390625e-08f;
+  return -logf(-logf(u));
+}
+__device__ __forceinline__ float gumbel(uint64_t seed, uint32_t stream, uint32_t idx) {
+  return gumbel_of_word(philox_word(seed, stream, idx));
+}
+constexpr uint32_t kStreamCluster = 0;
+constexpr uint32_t kStreamToken = 1;
+
+// ---------------------------------------------------------------------------
+// wave reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t y = __shfl_xor(x, o, kWave);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+// inclusive prefix sum across the wave (lane order)
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Online log-sum-exp state (max m, scaled sum s = sum exp(x - m)).
+struct Lse {
+  float m, s;
+};
+__device__ __forceinline__ Lse lse_empty() { return Lse{-INFINITY, 0.0f}; }
+__device__ __forceinline__ Lse lse_add(Lse a, float x) {
+  if (x > a.m) { a.s = a.s * __expf(a.m - x) + 1.0f; a.m = x; }
+  else a.s += __expf(x - a.m);
+  return a;
+}
+__device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
+  if (b.m == -INFINITY) return a;
+  if (a.m == -INFINITY) return b;
+  if (a.m >= b.m) return Lse{a.m, a.s + b.s * __expf(b.m - a.m)};
+  return Lse{b.m, b.s + a.s * __expf(a.m - b.m)};
+}
+__device__ __forceinline__ Lse wave_lse(Lse a) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    Lse b{__shfl_xor(a.m, o, kWave), __shfl_xor(a.s, o, kWave)};
+    a = lse_merge(a, b);
+  }
+  return a;
+}
+
+}  // namespace fh

@@ -1,0 +1,87 @@
+// Prepare-time device work (not on the decode path).
+//  * centroid means (notes, Module 1 / Formula 5): c_k = unit(sum of the
+//    cluster's rows), bf16 by round-to-nearest-even for bf16 heads;
+//  * the cluster-major copy of E: row k*b + j holds E[C2T[k, j]], so that the
+//    candidate rows of one cluster form one contiguous block.
+#include "fh_device.h"
+#include "fh_internal.h"
+
+namespace fh {
+
+constexpr int kPrepThreads = 256;
+
+template <typename TE>
+__device__ __forceinline__ float load_elem(const uint8_t* row, int col);
+template <>
+__device__ __forceinline__ float load_elem<float>(const uint8_t* row, int col) {
+  return reinterpret_cast<const float*>(row)[col];
+}
+template <>
+__device__ __forceinline__ float load_elem<bf16_t>(const uint8_t* row, int col) {
+  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[col] << 16);
+}
+
+template <typename TE>
+__global__ __launch_bounds__(kPrepThreads) void centroid_means_kernel(
+    const uint8_t* E, int64_t row_bytes, int d, const int32_t* c2t, int b, void* C) {
+  extern __shared__ float s_sum[];
+  __shared__ float s_red[kPrepThreads / kWave];
+  const int k = blockIdx.x;
+  float ss = 0.0f;
+  for (int col = threadIdx.x; col < d; col += kPrepThreads) {
+    float acc = 0.0f;
+    for (int j = 0; j < b; ++j)
+      acc += load_elem<TE>(E + (int64_t)c2t[(int64_t)k * b + j] * row_bytes, col);
+    s_sum[col] = acc;
+    ss = fmaf(acc, acc, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+  for (int w = 0; w < kPrepThreads / kWave; ++w) tot += s_red[w];
+  const float inv = tot > 0.0f ? 1.0f / sqrtf(tot) : 0.0f;
+  for (int col = threadIdx.x; col < d; col += kPrepThreads) {
+    const float x = s_sum[col] * inv;
+    if constexpr (sizeof(TE) == sizeof(float))
+      reinterpret_cast<float*>(C)[(int64_t)k * d + col] = x;
+    else
+      reinterpret_cast<uint16_t*>(C)[(int64_t)k * d + col] = f32_to_bf16_rne(x);
+  }
+}
+
+hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
+                                 const int32_t* c2t, int c, int b, void* C, hipStream_t s) {
+  const size_t shm = (size_t)d * sizeof(float);
+  if (dtype == FH_DTYPE_BF16)
+    hipLaunchKernelGGL(centroid_means_kernel<bf16_t>, dim3(c), dim3(kPrepThreads), shm, s, E,
+                       row_bytes, d, c2t, b, C);
+  else
+    hipLaunchKernelGGL(centroid_means_kernel<float>, dim3(c), dim3(kPrepThreads), shm, s, E,
+                       row_bytes, d, c2t, b, C);
+  return hipGetLastError();
+}
+
+// one wave per destination row, 16-byte chunks
+__global__ __launch_bounds__(kPrepThreads) void cluster_major_copy_kernel(
+    const uint8_t* E, int64_t lde_bytes, const int32_t* c2t, int64_t v, int nchunk,
+    uint8_t* Ec, int64_t row_bytes) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (kPrepThreads / kWave);
+  for (int64_t dst = (int64_t)blockIdx.x * (kPrepThreads / kWave) + (threadIdx.x >> 6); dst < v;
+       dst += waves) {
+    const uint8_t* src = E + (int64_t)c2t[dst] * lde_bytes;
+    uint8_t* out = Ec + dst * row_bytes;
+    for (int ch = lane; ch < nchunk; ch += kWave)
+      reinterpret_cast<uint4*>(out)[ch] = reinterpret_cast<const uint4*>(src)[ch];
+  }
+}
+
+hipError_t launch_cluster_major_copy(const uint8_t* E, int64_t lde_bytes, const int32_t* c2t,
+                                     int64_t v, int64_t row_bytes, uint8_t* Ec, hipStream_t s) {
+  hipLaunchKernelGGL(cluster_major_copy_kernel, dim3(4096), dim3(kPrepThreads), 0, s, E,
+                     lde_bytes, c2t, v, (int)(row_bytes / 16), Ec, row_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace fh
