@@ -309,6 +309,48 @@ def test_gemma_int4_greedy_parity(fh, B):
 
 
 # --------------------------------------------------------------------------
+# the single-launch batch-1 kernel against the multi-kernel path
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wid,mode", [(0, "greedy"), (0, "sample"), (1, "greedy"),
+                                      (1, "sample"), (4, "greedy")])
+def test_single_launch_matches_multi_kernel(fh, wid, mode):
+    cs = case(wid)
+    p = cs.wl.p
+    one = cs.prepare(fh, max_batch=1, max_p=p)
+    multi = cs.prepare(fh, max_batch=1, max_p=p)
+    fh.flashhead_set_path(multi.handle, 1)
+    assert fh.flashhead_query(one.handle, 10) == 1
+    H, H64 = cs.hidden(12, offset=3)
+    tau = 0.7
+    st = Stats()
+    for i in range(12):
+        seeds = synth.make_seeds(40 + i, 1)
+        sd = torch.from_numpy(seeds.view(np.int64)).cuda()
+        ra = run_debug(fh, one, dev_tensor(H[i:i + 1]), 1, p, mode, tau, sd)
+        rb = run_debug(fh, multi, dev_tensor(H[i:i + 1]), 1, p, mode, tau, sd)
+        for k in ("scores", "clusters", "cand_ids", "cand_logits", "tokens"):
+            assert np.array_equal(ra[k], rb[k]), k
+        if mode == "sample":
+            assert ra["lse"][0] == pytest.approx(rb["lse"][0], abs=1e-4, rel=1e-6)
+        check_batch(cs, ra, H64[i:i + 1], p, mode, tau, seeds, stats=st)
+    assert fh.flashhead_query(one.handle, 9) == 0
+    assert fh.flashhead_query(multi.handle, 9) == 0
+    print(st)
+
+
+@pytest.mark.parametrize("p", [1, 2, 64])
+def test_single_launch_tiny_all_p(fh, p):
+    cs = case(0)
+    head = cs.prepare(fh, max_batch=1, max_p=64)
+    H, H64 = cs.hidden(32, offset=50)
+    for i in range(32):
+        res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, p, "greedy")
+        check_batch(cs, res, H64[i:i + 1], p)
+    assert fh.flashhead_query(head.handle, 9) == 0
+
+
+# --------------------------------------------------------------------------
 # edge cases
 # --------------------------------------------------------------------------
 
@@ -372,14 +414,18 @@ def test_call_errors_return_status(fh):
 # sampling distribution on the tiny workload (1e5 draws)
 # --------------------------------------------------------------------------
 
-def _pooled_chisq(obs, exp):
+def _pooled_chisq(obs, prob):
+    """Chi-square p-value of counts against probabilities; cells with an
+    expected count below 5 are pooled into one."""
     from scipy import stats
+    exp = np.asarray(prob, dtype=np.float64) * obs.sum()
     keep = exp >= 5
     o = np.append(obs[keep], obs[~keep].sum())
     e = np.append(exp[keep], exp[~keep].sum())
     if e[-1] == 0:
         o, e = o[:-1], e[:-1]
     return stats.chisquare(o, e * o.sum() / e.sum()).pvalue
+
 
 
 def test_tiny_sampling_chisquare_p_equals_c(fh):

@@ -53,6 +53,27 @@ template <> struct Chunk<bf16_t> {
   }
 };
 
+// INT4 codes: eight signed 4-bit values per 32-bit word, low nibble first.
+__device__ __forceinline__ float int4_at(uint32_t w, int i) {
+  return (float)(((int32_t)(w << (28 - 4 * i))) >> 28);
+}
+// sum_i code_i * h[i] over one word (products of small integers and bf16
+// values are exact in fp32)
+__device__ __forceinline__ float int4_dot_word(uint32_t w, const float* h) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = fmaf(int4_at(w, i), h[i], s);
+  return s;
+}
+// one lane's 32 codes of a group against the matching 32 h values
+__device__ __forceinline__ float int4_dot_chunk(const uint4& w, const float* h) {
+  float part = int4_dot_word(w.x, h);
+  part += int4_dot_word(w.y, h + 8);
+  part += int4_dot_word(w.z, h + 16);
+  part += int4_dot_word(w.w, h + 24);
+  return part;
+}
+
 // ---------------------------------------------------------------------------
 // order-preserving keys.  Larger float -> larger uint32; -0 and +0 collapse.
 // The 64-bit decode key puts the ordered value above (0xFFFFFFFF - id), so an

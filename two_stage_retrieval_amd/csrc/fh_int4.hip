@@ -17,17 +17,6 @@ namespace fh {
 constexpr int kI4Threads = 256;
 constexpr int kI4Waves = kI4Threads / kWave;
 
-__device__ __forceinline__ float nib(uint32_t w, int i) {
-  return (float)(((int32_t)(w << (28 - 4 * i))) >> 28);
-}
-
-__device__ __forceinline__ float dot_word(uint32_t w, const float* h) {
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = fmaf(nib(w, i), h[i], s);
-  return s;
-}
-
 __global__ __launch_bounds__(kI4Threads) void int4_gemv_kernel(Int4Args a) {
   extern __shared__ float s_h[];
   const int r = blockIdx.y;
@@ -47,12 +36,7 @@ __global__ __launch_bounds__(kI4Threads) void int4_gemv_kernel(Int4Args a) {
     for (int g = 0; g < G; ++g) {
       const uint4 w = codes[(int64_t)g * kWave];
       const float s = __uint_as_float((uint32_t)sc[g * 16] << 16);
-      const float* hp = s_h + g * 128 + q * 32;
-      float part = dot_word(w.x, hp);
-      part += dot_word(w.y, hp + 8);
-      part += dot_word(w.z, hp + 16);
-      part += dot_word(w.w, hp + 24);
-      acc = fmaf(s, part, acc);
+      acc = fmaf(s, int4_dot_chunk(w, s_h + g * 128 + q * 32), acc);
     }
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);

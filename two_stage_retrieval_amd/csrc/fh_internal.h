@@ -72,6 +72,38 @@ struct Int4Args {
   const uint64_t* seeds;
 };
 
+struct FusedArgs {
+  const uint8_t* C;       // c x d centroids (bf16 / fp32)
+  int64_t row_bytes;      // d * element size (rows of C and of Ec)
+  int nchunk;             // 16-byte chunks per row
+  int c, b, p, d;
+  const uint8_t* q4;      // INT4 tiles (when quantized)
+  const uint16_t* q4s;
+  int ntiles, groups;
+  const uint8_t* H;       // one hidden vector
+  const uint8_t* Ec;      // cluster-major copy of E
+  const int32_t* c2t;
+  float cmax;             // upper bound of the centroid norms
+  int64_t rows_per_block; // stage-2 rows per workgroup (multiple of 4)
+  float* keys;            // c selection keys
+  uint32_t* hist;         // 2 x 4096 bins, alternating by epoch
+  uint32_t* arrive;       // grid arrival counter (reset by the last block)
+  uint32_t* done;         // finished-block counter (reset by the last block)
+  uint32_t* epoch;        // call counter (selects the histogram buffer)
+  uint32_t* error;        // bit 0: selection count, bit 1: barrier timeout
+  uint64_t* best;         // running max decode key (reset by the last block)
+  float2* lse_part;       // one per workgroup
+  int32_t* out_tokens;
+  float* out_lse;
+  float* dbg_scores;
+  int32_t* dbg_clusters;
+  int32_t* dbg_ids;
+  float* dbg_logits;
+  int sample;
+  float inv_tau;
+  const uint64_t* seeds;
+};
+
 // Optional events recorded exactly around one kernel (hipExtLaunchKernel).
 struct Timing {
   hipEvent_t start = nullptr, stop = nullptr;
@@ -84,6 +116,11 @@ hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing
 hipError_t launch_int4_gemv(const Int4Args& a, int B, hipStream_t s, const Timing* tm = nullptr);
 hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
                                  const int32_t* c2t, int c, int b, void* C, hipStream_t s);
+int fused_grid();
+int64_t fused_rows_per_block(int p, int b);
+bool fused_supported(int dtype, int nchunk, int c, int quant, int p, int b);
+hipError_t launch_fused(const FusedArgs& a, int dtype, int quant, hipStream_t s,
+                        const Timing* tm);
 hipError_t launch_cluster_major_copy(const uint8_t* E, int64_t lde_bytes, const int32_t* c2t,
                                      int64_t v, int64_t row_bytes, uint8_t* Ec, hipStream_t s);
 

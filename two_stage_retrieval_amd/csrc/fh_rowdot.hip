@@ -123,6 +123,10 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
   if constexpr (MODE == kRowScores) return;
 
   // ---- block reduction, then the last block of this batch row finalizes ----
+  // Blocks publish their results only through device-scope atomics (coherent
+  // across the XCDs), wait for those to complete, and only then count
+  // themselves done; the last block reads everything back with atomics.  No
+  // L2 write-back or invalidate is needed on this path.
   __shared__ uint64_t s_best[kRowdotWaves];
   __shared__ float2 s_lse[kRowdotThreads];
   __shared__ int s_last;
@@ -133,6 +137,9 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
     s_lse[wave] = make_float2(lse.m, lse.s);
   }
   __syncthreads();
+  unsigned long long* gbest = reinterpret_cast<unsigned long long*>(a.best + r);
+  unsigned long long* glse =
+      reinterpret_cast<unsigned long long*>(a.lse_part + (int64_t)r * gridDim.x);
   if (threadIdx.x == 0) {
     uint64_t bb = s_best[0];
     Lse ll{s_lse[0].x, s_lse[0].y};
@@ -140,21 +147,28 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
       bb = s_best[w] > bb ? s_best[w] : bb;
       ll = lse_merge(ll, Lse{s_lse[w].x, s_lse[w].y});
     }
-    if (bb) atomicMax(reinterpret_cast<unsigned long long*>(a.best + r), (unsigned long long)bb);
-    if (a.out_lse) a.lse_part[(int64_t)r * gridDim.x + blockIdx.x] = make_float2(ll.m, ll.s);
-    __threadfence();
-    const uint32_t prev = atomicAdd(a.counters + r, 1u);
+    if (bb) __hip_atomic_fetch_max(gbest, (unsigned long long)bb, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (a.out_lse) {
+      const unsigned long long packed =
+          ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
+      __hip_atomic_exchange(glse + blockIdx.x, packed, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the atomics above have been performed
+    const uint32_t prev = __hip_atomic_fetch_add(a.counters + r, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == gridDim.x - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   if (a.out_lse) {
     // deterministic merge: fixed strided order, fixed tree
     Lse ll = lse_empty();
     for (int j = threadIdx.x; j < (int)gridDim.x; j += kRowdotThreads) {
-      const float2 pr = a.lse_part[(int64_t)r * gridDim.x + j];
-      ll = lse_merge(ll, Lse{pr.x, pr.y});
+      const unsigned long long pr =
+          __hip_atomic_fetch_add(glse + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ll = lse_merge(ll, Lse{__uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32))});
     }
     s_lse[threadIdx.x] = make_float2(ll.m, ll.s);
     __syncthreads();
@@ -169,10 +183,11 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
     if (threadIdx.x == 0) a.out_lse[r] = s_lse[0].x + logf(s_lse[0].y);
   }
   if (threadIdx.x == 0) {
-    const uint64_t k = atomicAdd(reinterpret_cast<unsigned long long*>(a.best + r), 0ull);
+    const uint64_t k =
+        __hip_atomic_fetch_add(gbest, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.out_tokens[r] = (int32_t)key_id(k);
-    atomicExch(reinterpret_cast<unsigned long long*>(a.best + r), 0ull);
-    atomicExch(a.counters + r, 0u);
+    __hip_atomic_exchange(gbest, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_exchange(a.counters + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
