@@ -66,8 +66,6 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--multi-kernel", action="store_true",
-                    help="force the three-kernel path at batch 1")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -106,8 +104,6 @@ def main():
     fh = fhb.FlashHead(E_dev, head.c2t, C_init,
                        quant=fhb.FH_QUANT_INT4_G128 if int4 else fhb.FH_QUANT_NONE,
                        max_batch=B, max_p=wl.p)
-    if args.multi_kernel:
-        fhb.flashhead_set_path(fh.handle, 1)
     nb = nvec // B
     batches = [H_dev[i * B:(i + 1) * B] for i in range(nb)]
     out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -201,14 +197,11 @@ def main():
     cold_p50 = statistics.median(cold)
     cold_p90 = float(np.percentile(cold, 90))
     gbs = total_b / (cold_p50 * 1e-6) / 1e9
-    # dominant kernel: the single-launch kernel, else the longer stage
-    fused = kern_us[1] < 0.05 and kern_us[2] < 0.05
-    if fused:
-        dom, dom_bytes, dom_name = 0, total_b, "fused_step"
-    elif kern_us[2] >= kern_us[0]:
+    # dominant kernel: the longer of the two streaming stages
+    if kern_us[2] >= kern_us[0]:
         dom, dom_bytes, dom_name = 2, s2_b, "stage2_gather"
     else:
-        dom, dom_bytes, dom_name = 0, s1_b, "stage1_scores"
+        dom, dom_bytes, dom_name = 0, s1_b, "stage1_select"
     dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom_name,
                 "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -245,9 +238,8 @@ def main():
         "union_clusters": U,
         "cold_p90_us": round(cold_p90, 3),
         "warm_us": round(warm, 3),
-        "kernels_us": ({"fused_step": round(kern_us[0], 3)} if fused else
-                       {"stage1": round(kern_us[0], 3), "select": round(kern_us[1], 3),
-                        "stage2": round(kern_us[2], 3)}),
+        "kernels_us": {"stage1_select": round(kern_us[0], 3), "select": round(kern_us[1], 3),
+                       "stage2": round(kern_us[2], 3)},
         "dense_us_cold": round(dense_p50, 3) if dense_p50 else None,
         "dense_us_warm": round(dense_warm, 3) if dense_warm else None,
         "speedup_vs_dense": round(dense_p50 / cold_p50, 3) if dense_p50 else None,

@@ -203,25 +203,17 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
 
 /* Sizes of a prepared head: what = 0 v, 1 d, 2 c, 3 b, 4 dtype, 5 quant,
  * 6 max_batch, 7 max_p, 8 device bytes owned by the handle, 9 the
- * self-check flags (bit 0: a selection produced a count other than p;
- * bit 1: the single-launch path's grid barrier timed out; reading
- * synchronises with the device and clears them), 10 whether batch-1 calls
- * can use the single-launch path (one workgroup per CU, all resident). */
+ * selection self-check flag (non-zero if a selection produced a count other
+ * than p; reading it synchronises with the device and clears it). */
 int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
-
-/* Execution path for later calls: 0 = automatic (batch-1 calls use the
- * single-launch kernel when supported), 1 = always the multi-kernel path
- * (stage-1 kernel, select kernel, stage-2 kernel).  Both compute the same
- * results; the switch exists for testing and measurement. */
-int flashhead_set_path(fh_handle* h, int32_t path);
 
 /*
  * Per-kernel timing for measurement (not for the decode loop).
  * flashhead_profile_begin creates 6 HIP events per call for the next
  * max_calls decode calls on this handle; each of those calls records them
  * exactly around its stage-1, select and stage-2 kernels (on the call's
- * stream; a single-launch call reports its one kernel as stage 1 and zero
- * for the others).  flashhead_profile_end waits for the recorded events, writes the
+ * stream; when the selection runs inside the stage-1 kernel, as it does for
+ * c <= 16384, stage 1 includes it and the select time is reported as zero).  flashhead_profile_end waits for the recorded events, writes the
  * average duration in milliseconds of each of the three kernels per call to
  * stage_ms[0..2] and the number of recorded calls to *calls, and releases
  * the events.

@@ -309,38 +309,11 @@ def test_gemma_int4_greedy_parity(fh, B):
 
 
 # --------------------------------------------------------------------------
-# the single-launch batch-1 kernel against the multi-kernel path
+# batch 1 across p (the selection inside stage 1)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("wid,mode", [(0, "greedy"), (0, "sample"), (1, "greedy"),
-                                      (1, "sample"), (4, "greedy")])
-def test_single_launch_matches_multi_kernel(fh, wid, mode):
-    cs = case(wid)
-    p = cs.wl.p
-    one = cs.prepare(fh, max_batch=1, max_p=p)
-    multi = cs.prepare(fh, max_batch=1, max_p=p)
-    fh.flashhead_set_path(multi.handle, 1)
-    assert fh.flashhead_query(one.handle, 10) == 1
-    H, H64 = cs.hidden(12, offset=3)
-    tau = 0.7
-    st = Stats()
-    for i in range(12):
-        seeds = synth.make_seeds(40 + i, 1)
-        sd = torch.from_numpy(seeds.view(np.int64)).cuda()
-        ra = run_debug(fh, one, dev_tensor(H[i:i + 1]), 1, p, mode, tau, sd)
-        rb = run_debug(fh, multi, dev_tensor(H[i:i + 1]), 1, p, mode, tau, sd)
-        for k in ("scores", "clusters", "cand_ids", "cand_logits", "tokens"):
-            assert np.array_equal(ra[k], rb[k]), k
-        if mode == "sample":
-            assert ra["lse"][0] == pytest.approx(rb["lse"][0], abs=1e-4, rel=1e-6)
-        check_batch(cs, ra, H64[i:i + 1], p, mode, tau, seeds, stats=st)
-    assert fh.flashhead_query(one.handle, 9) == 0
-    assert fh.flashhead_query(multi.handle, 9) == 0
-    print(st)
-
-
 @pytest.mark.parametrize("p", [1, 2, 64])
-def test_single_launch_tiny_all_p(fh, p):
+def test_batch1_tiny_all_p(fh, p):
     cs = case(0)
     head = cs.prepare(fh, max_batch=1, max_p=64)
     H, H64 = cs.hidden(32, offset=50)
@@ -363,6 +336,18 @@ def test_ragged_small_head(fh, p):
     for lo in range(0, 9, 3):
         res = run_debug(fh, head, dev_tensor(H[lo:lo + 3]), 3, p, "greedy")
         check_batch(cs, res, H64[lo:lo + 3], p)
+
+
+@pytest.mark.parametrize("p", [1, 300])
+def test_many_clusters_separate_select_kernel(fh, p):
+    """c = 20000 > 16384: selection runs in its own kernel (b = 2, d = 128)."""
+    cs = case(1, c=20000, b=2, d=128, seed=91)
+    head = cs.prepare(fh, max_batch=2, max_p=300)
+    H, H64 = cs.hidden(4)
+    for lo in range(0, 4, 2):
+        res = run_debug(fh, head, dev_tensor(H[lo:lo + 2]), 2, p, "greedy")
+        check_batch(cs, res, H64[lo:lo + 2], p)
+    assert fh.flashhead_query(head.handle, 9) == 0
 
 
 @pytest.mark.parametrize("wid", [0, 1])

@@ -34,7 +34,7 @@ EXPORTED = [
     "flashhead_sample", "dense_head_workspace_bytes", "dense_head",
     "flashhead_status_string", "flashhead_export_centroids",
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
-    "flashhead_profile_end", "flashhead_set_path",
+    "flashhead_profile_end",
 ]
 
 
@@ -92,8 +92,6 @@ def _load() -> C.CDLL:
     lib.flashhead_profile_end.argtypes = [vp, C.POINTER(C.c_double),
                                           C.POINTER(i32)]
     lib.flashhead_profile_end.restype = C.c_int
-    lib.flashhead_set_path.argtypes = [vp, i32]
-    lib.flashhead_set_path.restype = C.c_int
     return lib
 
 
@@ -222,11 +220,6 @@ def flashhead_query(handle: int, what: int) -> int:
     v = C.c_int64()
     _check(lib.flashhead_query(handle, what, C.byref(v)), "flashhead_query")
     return v.value
-
-
-def flashhead_set_path(handle: int, path: int) -> None:
-    """0 = automatic, 1 = always the multi-kernel path."""
-    _check(lib.flashhead_set_path(handle, path), "flashhead_set_path")
 
 
 def flashhead_profile_begin(handle: int, max_calls: int) -> None:

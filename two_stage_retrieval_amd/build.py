@@ -16,8 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflashhead.so")
 
-SOURCES = ["fh_api.hip", "fh_rowdot.hip", "fh_select.hip", "fh_int4.hip",
-           "fh_prepare.hip", "fh_fused.hip", "fh_batched.hip"]
+SOURCES = ["fh_api.hip", "fh_stage1.hip", "fh_rowdot.hip", "fh_select.hip",
+           "fh_prepare.hip", "fh_batched.hip"]
 
 # Packed-fp32 instructions are disabled for all device code.
 HIPCC_FLAGS = [

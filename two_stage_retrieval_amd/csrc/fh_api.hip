@@ -30,16 +30,13 @@ struct fh_handle {
   float2* lse_part = nullptr; // max_batch x kMaxGrid
   uint64_t* masks = nullptr;  // c
   uint32_t* error = nullptr;  // 1
-  // single-launch path (batch 1)
-  uint32_t* fused_state = nullptr;  // [0] arrive, [1] done, [2] epoch, then 2 x 4096 bins
-  float cmax = 0.0f;                // bound of the stage-1 centroid norms
-  bool fused_ok = false;
+
+
   int64_t bytes = 0;
   std::vector<void*> allocs;
   // per-kernel timing (flashhead_profile_begin / _end)
   std::vector<hipEvent_t> prof_ev;  // 6 per recorded call
   int prof_cap = 0, prof_calls = 0;
-  bool force_multi = false;  // testing: always use the multi-kernel path
 };
 
 namespace {
@@ -184,58 +181,6 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(hipMemsetAsync(h->counters, 0, (size_t)mb * 4, s));
   FH_TRY(hipMemsetAsync(h->masks, 0, (size_t)c * 8, s));
   FH_TRY(hipMemsetAsync(h->error, 0, 4, s));
-  // bound of the centroid norms used by the single-launch path's key binning
-  {
-    std::vector<uint8_t> hostC((size_t)c * h->row_bytes);
-    FH_TRY(hipMemcpyAsync(hostC.data(), h->C, hostC.size(), hipMemcpyDeviceToHost, s));
-    FH_TRY(hipStreamSynchronize(s));
-    double cm = 0.0;
-    for (int k = 0; k < c; ++k) {
-      double ss = 0.0;
-      for (int j = 0; j < d; ++j) {
-        double x;
-        if (h->dtype == FH_DTYPE_F32) {
-          float f;
-          memcpy(&f, hostC.data() + ((size_t)k * d + j) * 4, 4);
-          x = f;
-        } else {
-          uint16_t b16;
-          memcpy(&b16, hostC.data() + ((size_t)k * d + j) * 2, 2);
-          x = bf16_value(b16);
-        }
-        ss += x * x;
-      }
-      cm = fmax(cm, sqrt(ss));
-    }
-    if (h->quant == FH_QUANT_INT4_G128) {  // norms of the dequantized rows
-      std::vector<uint8_t> codes((size_t)h->ntiles * h->groups * 1024);
-      std::vector<uint16_t> scales((size_t)h->ntiles * h->groups * 16);
-      FH_TRY(hipMemcpy(codes.data(), h->q4, codes.size(), hipMemcpyDeviceToHost));
-      FH_TRY(hipMemcpy(scales.data(), h->q4s, scales.size() * 2, hipMemcpyDeviceToHost));
-      std::vector<double> ss((size_t)h->ntiles * 16, 0.0);
-      for (int t = 0; t < h->ntiles; ++t)
-        for (int g = 0; g < h->groups; ++g)
-          for (int lane = 0; lane < 64; ++lane) {
-            const double sc = bf16_value(scales[((size_t)t * h->groups + g) * 16 + (lane & 15)]);
-            const uint8_t* by = codes.data() + (((size_t)t * h->groups + g) * 64 + lane) * 16;
-            for (int j = 0; j < 16; ++j)
-              for (int nib = 0; nib < 2; ++nib) {
-                int q = (by[j] >> (4 * nib)) & 0xF;
-                q = q > 7 ? q - 16 : q;
-                ss[(size_t)t * 16 + (lane & 15)] += (q * sc) * (q * sc);
-              }
-          }
-      cm = 0.0;
-      for (double x : ss) cm = fmax(cm, sqrt(x));
-    }
-    h->cmax = (float)(cm * (1.0 + 1e-6)) + 1e-30f;
-  }
-  const int nchunk = (int)(h->row_bytes / 16);
-  h->fused_ok = fused_grid() > 0 &&
-                fused_supported(h->dtype, nchunk, c, h->quant, h->max_p, b) &&
-                fused_supported(h->dtype, nchunk, c, h->quant, 1, b);
-  FH_TRY(alloc(h, &h->fused_state, (3 + 2 * 4096) * 4));
-  FH_TRY(hipMemsetAsync(h->fused_state, 0, (3 + 2 * 4096) * 4, s));
   FH_TRY(hipStreamSynchronize(s));
   return FH_OK;
 }
@@ -270,88 +215,37 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   const float inv_tau = sample ? 1.0f / tau : 1.0f;
   const int nchunk = (int)(h->row_bytes / 16);
 
-  if (B == 1 && h->fused_ok && !h->force_multi &&
-      fused_supported(h->dtype, nchunk, h->c, h->quant, p, h->b)) {
-    FusedArgs a{};
-    a.C = static_cast<const uint8_t*>(h->C);
-    a.row_bytes = h->row_bytes;
-    a.nchunk = nchunk;
-    a.c = h->c;
-    a.b = h->b;
-    a.p = p;
-    a.d = h->d;
-    a.q4 = h->q4;
-    a.q4s = h->q4s;
-    a.ntiles = h->ntiles;
-    a.groups = h->groups;
-    a.H = static_cast<const uint8_t*>(H);
-    a.Ec = h->Ec;
-    a.c2t = h->c2t;
-    a.cmax = h->cmax;
-    a.rows_per_block = fused_rows_per_block(p, h->b);
-    a.keys = h->keys;
-    a.arrive = h->fused_state;
-    a.done = h->fused_state + 1;
-    a.epoch = h->fused_state + 2;
-    a.hist = h->fused_state + 3;
-    a.error = h->error;
-    a.best = h->best;
-    a.lse_part = h->lse_part;
-    a.out_tokens = out;
-    a.out_lse = out_lse;
-    a.dbg_scores = dbg ? dbg->scores : nullptr;
-    a.dbg_clusters = dbg ? dbg->clusters : nullptr;
-    a.dbg_ids = dbg ? dbg->cand_ids : nullptr;
-    a.dbg_logits = dbg ? dbg->cand_logits : nullptr;
-    a.sample = sample;
-    a.inv_tau = inv_tau;
-    a.seeds = seeds;
-    if (t1) {  // the single kernel's time is reported as stage 1
-      (void)hipEventRecord(t2->start, s);
-      (void)hipEventRecord(t2->stop, s);
-      (void)hipEventRecord(t3->start, s);
-      (void)hipEventRecord(t3->stop, s);
-    }
-    return launch_fused(a, h->dtype, h->quant, s, t1) == hipSuccess ? FH_OK : FH_ERR_HIP;
-  }
 
-  // stage 1: selection keys per (row, cluster)
-  if (h->quant == FH_QUANT_INT4_G128) {
-    Int4Args a{};
-    a.codes = h->q4;
-    a.scales = h->q4s;
-    a.ntiles = h->ntiles;
-    a.groups = h->groups;
-    a.c = h->c;
-    a.d = h->d;
-    a.H = static_cast<const uint16_t*>(H);
-    a.keys_out = h->keys;
-    a.key_stride = h->c;
-    a.dbg_scores = dbg ? dbg->scores : nullptr;
-    a.sample = sample;
-    a.inv_tau = inv_tau;
-    a.seeds = seeds;
-    if (launch_int4_gemv(a, B, s, t1) != hipSuccess) return FH_ERR_HIP;
-  } else {
-    RowdotArgs a{};
-    a.base = static_cast<const uint8_t*>(h->C);
-    a.row_bytes = h->row_bytes;
-    a.nchunk = nchunk;
-    a.H = static_cast<const uint8_t*>(H);
-    a.h_bytes = h->row_bytes;
-    a.nrows = h->c;
-    a.keys_out = h->keys;
-    a.key_stride = h->c;
-    a.dbg_scores = dbg ? dbg->scores : nullptr;
-    a.sample = sample;
-    a.inv_tau = inv_tau;
-    a.seeds = seeds;
-    if (launch_rowdot(a, kRowScores, h->dtype, B, rowdot_grid(h->c, nchunk, kRowScores), s,
-                      t1) != hipSuccess)
-      return FH_ERR_HIP;
-  }
-  // select p clusters per row
-  {
+  // stage 1 (+ selection by each batch row's last block)
+  Stage1Args s1{};
+  s1.C = static_cast<const uint8_t*>(h->C);
+  s1.row_bytes = h->row_bytes;
+  s1.nchunk = nchunk;
+  s1.c = h->c;
+  s1.d = h->d;
+  s1.q4 = h->q4;
+  s1.q4s = h->q4s;
+  s1.ntiles = h->ntiles;
+  s1.groups = h->groups;
+  s1.H = static_cast<const uint8_t*>(H);
+  s1.h_bytes = h->row_bytes;
+  s1.keys = h->keys;
+  s1.key_stride = h->c;
+  s1.dbg_scores = dbg ? dbg->scores : nullptr;
+  s1.sample = sample;
+  s1.inv_tau = inv_tau;
+  s1.seeds = seeds;
+  s1.select = stage1_selects(h->c) ? 1 : 0;
+  s1.p = p;
+  s1.counters = h->counters;
+  s1.sel = h->sel;
+  s1.sel_stride = h->max_p;
+  s1.masks = nullptr;
+  s1.error = h->error;
+
+  if (launch_stage1(s1, h->dtype, h->quant == FH_QUANT_INT4_G128, B, s, t1) != hipSuccess)
+    return FH_ERR_HIP;
+  if (!s1.select) {
     SelectArgs a{};
     a.keys = h->keys;
     a.key_stride = h->c;
@@ -362,6 +256,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.masks = nullptr;
     a.error = h->error;
     if (launch_select(a, B, s, t2) != hipSuccess) return FH_ERR_HIP;
+  } else if (t2) {  // selection ran inside stage 1
+    (void)hipEventRecord(t2->start, s);
+    (void)hipEventRecord(t2->stop, s);
   }
   if (dbg && dbg->clusters) {
     if (hipMemcpy2DAsync(dbg->clusters, (size_t)p * 4, h->sel, (size_t)h->max_p * 4,
@@ -579,12 +476,6 @@ int flashhead_profile_end(fh_handle* h, double* stage_ms, int32_t* calls) {
   return st;
 }
 
-int flashhead_set_path(fh_handle* h, int32_t path) {
-  if (!h || path < 0 || path > 1) return FH_ERR_INVALID_ARG;
-  h->force_multi = path == 1;
-  return FH_OK;
-}
-
 int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
   if (!h || !value) return FH_ERR_INVALID_ARG;
   switch (what) {
@@ -597,7 +488,6 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
     case 6: *value = h->max_batch; break;
     case 7: *value = h->max_p; break;
     case 8: *value = h->bytes; break;
-    case 10: *value = h->fused_ok ? 1 : 0; break;
     case 9: {  // selection error flag (synchronous read and clear)
       uint32_t e = 0;
       if (hipMemcpy(&e, h->error, 4, hipMemcpyDeviceToHost) != hipSuccess) return FH_ERR_HIP;

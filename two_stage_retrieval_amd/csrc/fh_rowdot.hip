@@ -1,8 +1,6 @@
 // Row-dot kernels: one wave computes full dot products of R rows of a
 // row-major matrix with one hidden vector h (GEMV family, batch rows on
-// grid.y).  Three epilogues:
-//   scores  stage-1 centroid scores s = C h (notes, Figure 1), written as
-//           selection keys (s, or s / tau + Gumbel for sampling mode);
+// grid.y).  Two epilogues:
 //   gather  stage-2 exact logits of the candidate rows of the selected
 //           clusters (notes, Overall architecture and Module 1), fused with
 //           the decode (Formula 2 argmax or Formula 3 Gumbel-max sample);
@@ -99,14 +97,7 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
       if (lane == rr) mine = acc[rr];
     const int64_t myrow = row0 + lane;
     const bool valid = lane < R && myrow < a.nrows;
-    if constexpr (MODE == kRowScores) {
-      if (valid) {
-        float key = mine;
-        if (a.sample) key = mine * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)myrow);
-        a.keys_out[(int64_t)r * a.key_stride + myrow] = key;
-        if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.key_stride + myrow] = mine;
-      }
-    } else {
+    {
       if (valid) {
         const float x = mine * a.inv_tau;
         const float kx = a.sample ? x + gumbel(seed, kStreamToken, mytok) : mine;
@@ -120,8 +111,6 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
       }
     }
   }
-  if constexpr (MODE == kRowScores) return;
-
   // ---- block reduction, then the last block of this batch row finalizes ----
   // Blocks publish their results only through device-scope atomics (coherent
   // across the XCDs), wait for those to complete, and only then count
@@ -236,11 +225,9 @@ int rowdot_grid(int64_t nrows, int nchunk, int mode) {
 hipError_t launch_rowdot(const RowdotArgs& a, int mode, int dtype, int B, int grid_x,
                          hipStream_t s, const Timing* tm) {
   if (dtype == FH_DTYPE_BF16) {
-    if (mode == kRowScores) return launch_t<bf16_t, kRowScores>(a, B, grid_x, s, tm);
     if (mode == kRowGather) return launch_t<bf16_t, kRowGather>(a, B, grid_x, s, tm);
     return launch_t<bf16_t, kRowDense>(a, B, grid_x, s, tm);
   }
-  if (mode == kRowScores) return launch_t<float, kRowScores>(a, B, grid_x, s, tm);
   if (mode == kRowGather) return launch_t<float, kRowGather>(a, B, grid_x, s, tm);
   return launch_t<float, kRowDense>(a, B, grid_x, s, tm);
 }
