@@ -30,6 +30,12 @@ struct fh_handle {
   float2* lse_part = nullptr; // max_batch x kMaxGrid
   uint64_t* masks = nullptr;  // c
   uint32_t* error = nullptr;  // 1
+  // batched path
+  uint32_t* sel_counter = nullptr;  // select kernel's finished-block counter
+  int32_t* ulist = nullptr;         // union of the selected clusters (c)
+  int32_t* ucount = nullptr;
+  uint64_t* part_best = nullptr;    // stage-2 partials, grid x max_batch
+  float2* part_lse = nullptr;
 
 
   int64_t bytes = 0;
@@ -181,6 +187,13 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(hipMemsetAsync(h->counters, 0, (size_t)mb * 4, s));
   FH_TRY(hipMemsetAsync(h->masks, 0, (size_t)c * 8, s));
   FH_TRY(hipMemsetAsync(h->error, 0, 4, s));
+  FH_TRY(alloc(h, &h->sel_counter, 4));
+  FH_TRY(alloc(h, &h->ulist, (size_t)c * 4));
+  FH_TRY(alloc(h, &h->ucount, 4));
+  FH_TRY(alloc(h, &h->part_best, (size_t)stage2_mfma_grid() * mb * 8));
+  FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
+  FH_TRY(hipMemsetAsync(h->sel_counter, 0, 4, s));
+  FH_TRY(hipMemsetAsync(h->ucount, 0, 4, s));
   FH_TRY(hipStreamSynchronize(s));
   return FH_OK;
 }
@@ -216,7 +229,10 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   const int nchunk = (int)(h->row_bytes / 16);
 
 
-  // stage 1 (+ selection by each batch row's last block)
+  const bool int4 = h->quant == FH_QUANT_INT4_G128;
+  const bool batched = B >= 2 && h->b % 16 == 0 && batched_supported(h->dtype, h->d, B, int4);
+
+  // stage 1 (+ selection by each batch row's last block on the GEMV path)
   Stage1Args s1{};
   s1.C = static_cast<const uint8_t*>(h->C);
   s1.row_bytes = h->row_bytes;
@@ -235,7 +251,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.sample = sample;
   s1.inv_tau = inv_tau;
   s1.seeds = seeds;
-  s1.select = stage1_selects(h->c) ? 1 : 0;
+  s1.select = (!batched && stage1_selects(h->c)) ? 1 : 0;
   s1.p = p;
   s1.counters = h->counters;
   s1.sel = h->sel;
@@ -243,8 +259,11 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.masks = nullptr;
   s1.error = h->error;
 
-  if (launch_stage1(s1, h->dtype, h->quant == FH_QUANT_INT4_G128, B, s, t1) != hipSuccess)
+  if (batched) {
+    if (launch_stage1_mfma(s1, int4, B, s, t1) != hipSuccess) return FH_ERR_HIP;
+  } else if (launch_stage1(s1, h->dtype, int4, B, s, t1) != hipSuccess) {
     return FH_ERR_HIP;
+  }
   if (!s1.select) {
     SelectArgs a{};
     a.keys = h->keys;
@@ -253,8 +272,13 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.p = p;
     a.sel = h->sel;
     a.sel_stride = h->max_p;
-    a.masks = nullptr;
+    a.masks = batched ? h->masks : nullptr;
     a.error = h->error;
+    if (batched) {
+      a.counter = h->sel_counter;
+      a.ulist = h->ulist;
+      a.ucount = h->ucount;
+    }
     if (launch_select(a, B, s, t2) != hipSuccess) return FH_ERR_HIP;
   } else if (t2) {  // selection ran inside stage 1
     (void)hipEventRecord(t2->start, s);
@@ -266,6 +290,36 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
       return FH_ERR_HIP;
   }
   // stage 2: candidate logits + decode
+  if (batched) {
+    Stage2mArgs a{};
+    a.base = h->Ec;
+    a.row_bytes = h->row_bytes;
+    a.v = h->v;
+    a.b = h->b;
+    a.d = h->d;
+    a.B = B;
+    a.p = p;
+    a.H = static_cast<const uint8_t*>(H);
+    a.h_bytes = h->row_bytes;
+    a.ulist = h->ulist;
+    a.ucount = h->ucount;
+    a.masks = h->masks;
+    a.c2t = h->c2t;
+    a.sel = h->sel;
+    a.sel_stride = h->max_p;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    a.with_lse = out_lse != nullptr;
+    a.part_best = h->part_best;
+    a.part_lse = h->part_lse;
+    a.out_tokens = out;
+    a.out_lse = out_lse;
+    a.dbg_ids = dbg ? dbg->cand_ids : nullptr;
+    a.dbg_logits = dbg ? dbg->cand_logits : nullptr;
+    a.dbg_stride = (int64_t)p * h->b;
+    return launch_stage2_mfma(a, false, s, t3) == hipSuccess ? FH_OK : FH_ERR_HIP;
+  }
   {
     RowdotArgs a{};
     a.base = h->Ec;
@@ -399,6 +453,29 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   if (!aligned16(E) || !aligned16(H) || !aligned16(workspace)) return FH_ERR_UNSUPPORTED;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const size_t nb = (size_t)B;
+  uint8_t* ws_part = ws + nb * 8 + ((nb * 4 + 15) / 16) * 16;
+  if (B >= 2 && batched_supported(dtype, d, B, false)) {
+    Stage2mArgs m{};
+    m.base = static_cast<const uint8_t*>(E);
+    m.row_bytes = lde * es;
+    m.v = v;
+    m.b = 16;
+    m.d = d;
+    m.B = B;
+    m.H = static_cast<const uint8_t*>(H);
+    m.h_bytes = row_bytes;
+    m.sample = mode == FH_MODE_SAMPLE;
+    m.inv_tau = m.sample ? 1.0f / tau : 1.0f;
+    m.seeds = seeds;
+    m.with_lse = out_lse != nullptr;
+    m.part_best = reinterpret_cast<uint64_t*>(ws_part);
+    m.part_lse = reinterpret_cast<float2*>(ws_part + (size_t)stage2_mfma_grid() * nb * 8);
+    m.out_tokens = out_tokens;
+    m.out_lse = out_lse;
+    return launch_stage2_mfma(m, true, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? FH_OK
+               : FH_ERR_HIP;
+  }
   RowdotArgs a{};
   a.base = static_cast<const uint8_t*>(E);
   a.row_bytes = lde * es;
@@ -408,7 +485,7 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   a.nrows = v;
   a.best = reinterpret_cast<uint64_t*>(ws);
   a.counters = reinterpret_cast<uint32_t*>(ws + nb * 8);
-  a.lse_part = reinterpret_cast<float2*>(ws + nb * 8 + ((nb * 4 + 15) / 16) * 16);
+  a.lse_part = reinterpret_cast<float2*>(ws_part);
   a.out_tokens = out_tokens;
   a.out_lse = out_lse;
   a.sample = mode == FH_MODE_SAMPLE;

@@ -50,6 +50,36 @@ struct SelectArgs {
   int sel_stride;
   uint64_t* masks;       // optional: per-cluster bitmask of selecting rows
   uint32_t* error;       // optional: set non-zero if a row selected != p
+  // optional union compaction by the last block (needs masks)
+  uint32_t* counter;     // finished-block counter (zero between calls)
+  int32_t* ulist;        // clusters with a non-zero mask, ascending
+  int32_t* ucount;
+};
+
+struct Stage2mArgs {
+  const uint8_t* base;   // cluster-major copy of E (flash) or E (dense)
+  int64_t row_bytes;
+  int64_t v;             // rows of E (dense)
+  int b, d, B, p;
+  const uint8_t* H;      // B x d bf16
+  int64_t h_bytes;
+  const int32_t* ulist;  // flash: union of the selected clusters, ascending
+  const int32_t* ucount;
+  uint64_t* masks;       // flash: rows that selected each cluster
+  const int32_t* c2t;
+  const int32_t* sel;    // flash debug: B x sel_stride ascending selections
+  int sel_stride;
+  int sample;
+  float inv_tau;
+  const uint64_t* seeds;
+  int with_lse;
+  uint64_t* part_best;   // per block x B
+  float2* part_lse;
+  int32_t* out_tokens;
+  float* out_lse;
+  int32_t* dbg_ids;
+  float* dbg_logits;
+  int64_t dbg_stride;
 };
 
 struct Stage1Args {
@@ -93,6 +123,12 @@ hipError_t launch_stage1(const Stage1Args& a, int dtype, bool int4, int B, hipSt
 bool stage1_selects(int c);
 hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
                                  const int32_t* c2t, int c, int b, void* C, hipStream_t s);
+bool batched_supported(int dtype, int d, int B, bool int4);
+hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t s,
+                              const Timing* tm = nullptr);
+int stage2_mfma_grid();
+hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s,
+                              const Timing* tm = nullptr);
 hipError_t launch_cluster_major_copy(const uint8_t* E, int64_t lde_bytes, const int32_t* c2t,
                                      int64_t v, int64_t row_bytes, uint8_t* Ec, hipStream_t s);
 

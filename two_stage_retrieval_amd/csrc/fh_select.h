@@ -312,4 +312,50 @@ __device__ void select_block(const float* keys, int c, int p, int32_t* out, uint
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);
 }
 
+// The clusters whose row mask is non-zero, ascending, into ulist / ucount.
+// Masks are read coherently (they were set by atomics of other workgroups).
+template <int NT, int IPT>
+__device__ void compact_masks_block(const uint64_t* masks, int c, int32_t* ulist, int32_t* ucount,
+                                    SelSmem& sm) {
+  constexpr int WPT = (FH_MAX_C / 32 + NT - 1) / NT;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  int parity = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int k = t + j * NT;
+    const bool nz = k < c && __hip_atomic_load(masks + k, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) != 0ull;
+    const uint64_t bal = __ballot(nz);
+    const int k0 = j * NT + wave * kWave;
+    if (lane == 0 && k0 < c) {
+      sm.sel[k0 >> 5] = (uint32_t)bal;
+      if ((k0 >> 5) + 1 < FH_MAX_C / 32) sm.sel[(k0 >> 5) + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  __syncthreads();
+  const int words = (c + 31) >> 5;
+  uint32_t mw[WPT];
+  int wc = 0;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    const int w = t * WPT + q;
+    mw[q] = w < words ? sm.sel[w] : 0u;
+    wc += __popc(mw[q]);
+  }
+  const int incl = sel_scan<NT>(wc, sm, parity, lane, wave);
+  int pos = incl - wc;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    uint32_t bw = mw[q];
+    while (bw) {
+      ulist[pos++] = ((t * WPT + q) << 5) + __ffs(bw) - 1;
+      bw &= bw - 1u;
+    }
+  }
+  if (t == NT - 1) *ucount = incl;
+}
+
 }  // namespace fh

@@ -10,10 +10,24 @@ constexpr int kSelThreads = 1024;
 template <int IPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelSmem sm;
+  __shared__ int s_last;
   const int r = blockIdx.x;
   select_block<kSelThreads, IPT, false>(a.keys + (int64_t)r * a.key_stride, a.c, a.p,
                                         a.sel + (int64_t)r * a.sel_stride, a.masks, r, a.error,
                                         sm);
+  if (!a.counter) return;
+  // the last row to finish compacts the union of the selected clusters
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's mask updates have been performed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_exchange(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  compact_masks_block<kSelThreads, IPT>(a.masks, a.c, a.ulist, a.ucount, sm);
 }
 
 hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing* tm) {
