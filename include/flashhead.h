@@ -186,6 +186,11 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype,
 /* Static text for a status code. */
 const char* flashhead_status_string(int status);
 
+/* Name of the HIP error (hipGetErrorName) behind the most recent
+ * FH_ERR_HIP or FH_ERR_OOM returned to the calling thread; "hipSuccess" if
+ * there was none.  The string is static. */
+const char* flashhead_last_hip_error(void);
+
 /*
  * Prepare-time data, copied to host memory (synchronous):
  *   flashhead_export_centroids  c x d in the handle's dtype

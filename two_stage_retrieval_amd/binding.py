@@ -34,7 +34,7 @@ EXPORTED = [
     "flashhead_sample", "dense_head_workspace_bytes", "dense_head",
     "flashhead_status_string", "flashhead_export_centroids",
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
-    "flashhead_profile_end",
+    "flashhead_profile_end", "flashhead_last_hip_error",
 ]
 
 
@@ -53,7 +53,10 @@ class fh_debug(C.Structure):
 
 class FlashHeadError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {status_string(status)} ({status})")
+        msg = f"{what}: {status_string(status)} ({status})"
+        if status in (FH_ERR_HIP, FH_ERR_OOM):
+            msg += f" [{flashhead_last_hip_error()}]"
+        super().__init__(msg)
         self.status = status
 
 
@@ -81,6 +84,8 @@ def _load() -> C.CDLL:
     lib.dense_head.restype = C.c_int
     lib.flashhead_status_string.argtypes = [C.c_int]
     lib.flashhead_status_string.restype = C.c_char_p
+    lib.flashhead_last_hip_error.argtypes = []
+    lib.flashhead_last_hip_error.restype = C.c_char_p
     lib.flashhead_export_centroids.argtypes = [vp, vp]
     lib.flashhead_export_centroids.restype = C.c_int
     lib.flashhead_export_int4.argtypes = [vp, vp, vp]
@@ -100,6 +105,10 @@ lib = _load()
 
 def status_string(status: int) -> str:
     return lib.flashhead_status_string(status).decode()
+
+
+def flashhead_last_hip_error() -> str:
+    return lib.flashhead_last_hip_error().decode()
 
 
 def _check(status: int, what: str) -> None:

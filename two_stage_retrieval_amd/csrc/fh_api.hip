@@ -48,7 +48,7 @@ struct fh_handle {
 namespace {
 
 constexpr int kMaxGrid = 8192;       // largest grid.x of a decode launch
-constexpr int kDenseMaxGrid = 2048;  // dense launches loop inside
+constexpr int kDenseMaxGrid = 8192;  // dense: partial slots of the batched kernel (2 x 4096)
 
 int esize_of(int dtype) { return dtype == FH_DTYPE_F32 ? 4 : dtype == FH_DTYPE_BF16 ? 2 : 0; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -133,16 +133,25 @@ void quantize_int4(const uint16_t* C, int c, int d, std::vector<uint8_t>& codes,
   *groups_out = G;
 }
 
+// the HIP error behind the last FH_ERR_HIP / FH_ERR_OOM of this thread
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = e;
+  return e == hipErrorOutOfMemory ? FH_ERR_OOM : FH_ERR_HIP;
+}
+
 int check_device(const fh_handle* h) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return FH_ERR_HIP;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
   return dev == h->device ? FH_OK : FH_ERR_INVALID_ARG;
 }
 
 #define FH_TRY(expr)                                              \
   do {                                                            \
     const hipError_t e_ = (expr);                                 \
-    if (e_ != hipSuccess) return e_ == hipErrorOutOfMemory ? FH_ERR_OOM : FH_ERR_HIP; \
+    if (e_ != hipSuccess) return hip_fail(e_);                   \
   } while (0)
 
 int prepare_impl(const fh_desc* ds, fh_handle* h) {
@@ -260,9 +269,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.error = h->error;
 
   if (batched) {
-    if (launch_stage1_mfma(s1, int4, B, s, t1) != hipSuccess) return FH_ERR_HIP;
-  } else if (launch_stage1(s1, h->dtype, int4, B, s, t1) != hipSuccess) {
-    return FH_ERR_HIP;
+    FH_TRY(launch_stage1_mfma(s1, int4, B, s, t1));
+  } else {
+    FH_TRY(launch_stage1(s1, h->dtype, int4, B, s, t1));
   }
   if (!s1.select) {
     SelectArgs a{};
@@ -279,15 +288,14 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
       a.ulist = h->ulist;
       a.ucount = h->ucount;
     }
-    if (launch_select(a, B, s, t2) != hipSuccess) return FH_ERR_HIP;
+    FH_TRY(launch_select(a, B, s, t2));
   } else if (t2) {  // selection ran inside stage 1
     (void)hipEventRecord(t2->start, s);
     (void)hipEventRecord(t2->stop, s);
   }
   if (dbg && dbg->clusters) {
-    if (hipMemcpy2DAsync(dbg->clusters, (size_t)p * 4, h->sel, (size_t)h->max_p * 4,
-                         (size_t)p * 4, B, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return FH_ERR_HIP;
+    FH_TRY(hipMemcpy2DAsync(dbg->clusters, (size_t)p * 4, h->sel, (size_t)h->max_p * 4,
+                            (size_t)p * 4, B, hipMemcpyDeviceToDevice, s));
   }
   // stage 2: candidate logits + decode
   if (batched) {
@@ -295,6 +303,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.base = h->Ec;
     a.row_bytes = h->row_bytes;
     a.v = h->v;
+    a.c = h->c;
     a.b = h->b;
     a.d = h->d;
     a.B = B;
@@ -318,7 +327,8 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.dbg_ids = dbg ? dbg->cand_ids : nullptr;
     a.dbg_logits = dbg ? dbg->cand_logits : nullptr;
     a.dbg_stride = (int64_t)p * h->b;
-    return launch_stage2_mfma(a, false, s, t3) == hipSuccess ? FH_OK : FH_ERR_HIP;
+    FH_TRY(launch_stage2_mfma(a, false, s, t3));
+    return FH_OK;
   }
   {
     RowdotArgs a{};
@@ -346,7 +356,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.seeds = seeds;
     const int gx = rowdot_grid(a.nrows, nchunk, kRowGather);
     if (gx > kMaxGrid) return FH_ERR_UNSUPPORTED;
-    if (launch_rowdot(a, kRowGather, h->dtype, B, gx, s, t3) != hipSuccess) return FH_ERR_HIP;
+    FH_TRY(launch_rowdot(a, kRowGather, h->dtype, B, gx, s, t3));
   }
   return FH_OK;
 }
@@ -354,6 +364,8 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
 }  // namespace
 
 extern "C" {
+
+const char* flashhead_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
 const char* flashhead_status_string(int status) {
   switch (status) {
@@ -472,9 +484,8 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
     m.part_lse = reinterpret_cast<float2*>(ws_part + (size_t)stage2_mfma_grid() * nb * 8);
     m.out_tokens = out_tokens;
     m.out_lse = out_lse;
-    return launch_stage2_mfma(m, true, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? FH_OK
-               : FH_ERR_HIP;
+    FH_TRY(launch_stage2_mfma(m, true, static_cast<hipStream_t>(stream)));
+    return FH_OK;
   }
   RowdotArgs a{};
   a.base = static_cast<const uint8_t*>(E);
@@ -493,15 +504,13 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   a.seeds = seeds;
   const int gx = rowdot_grid(v, a.nchunk, kRowDense);
   if (gx > kDenseMaxGrid) return FH_ERR_UNSUPPORTED;
-  if (launch_rowdot(a, kRowDense, dtype, B, gx, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return FH_ERR_HIP;
+  FH_TRY(launch_rowdot(a, kRowDense, dtype, B, gx, static_cast<hipStream_t>(stream)));
   return FH_OK;
 }
 
 int flashhead_export_centroids(const fh_handle* h, void* dst) {
   if (!h || !dst) return FH_ERR_INVALID_ARG;
-  if (hipMemcpy(dst, h->C, (size_t)h->c * h->row_bytes, hipMemcpyDeviceToHost) != hipSuccess)
-    return FH_ERR_HIP;
+  FH_TRY(hipMemcpy(dst, h->C, (size_t)h->c * h->row_bytes, hipMemcpyDeviceToHost));
   return FH_OK;
 }
 
@@ -509,9 +518,8 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes, uint16_t* scales) 
   if (!h || !codes || !scales) return FH_ERR_INVALID_ARG;
   if (h->quant != FH_QUANT_INT4_G128) return FH_ERR_UNSUPPORTED;
   const size_t tiles = (size_t)h->ntiles * h->groups;
-  if (hipMemcpy(codes, h->q4, tiles * 1024, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemcpy(scales, h->q4s, tiles * 16 * 2, hipMemcpyDeviceToHost) != hipSuccess)
-    return FH_ERR_HIP;
+  FH_TRY(hipMemcpy(codes, h->q4, tiles * 1024, hipMemcpyDeviceToHost));
+  FH_TRY(hipMemcpy(scales, h->q4s, tiles * 16 * 2, hipMemcpyDeviceToHost));
   return FH_OK;
 }
 
@@ -520,10 +528,11 @@ int flashhead_profile_begin(fh_handle* h, int32_t max_calls) {
   drop_profile(h);
   h->prof_ev.resize((size_t)max_calls * 6, nullptr);
   for (auto& e : h->prof_ev) {
-    if (hipEventCreate(&e) != hipSuccess) {
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
       e = nullptr;
       drop_profile(h);
-      return FH_ERR_HIP;
+      return hip_fail(err);
     }
   }
   h->prof_cap = max_calls;
@@ -540,8 +549,10 @@ int flashhead_profile_end(fh_handle* h, double* stage_ms, int32_t* calls) {
     for (int k = 0; k < 3; ++k) {
       hipEvent_t a = h->prof_ev[(size_t)i * 6 + 2 * k], b = h->prof_ev[(size_t)i * 6 + 2 * k + 1];
       float ms = 0.0f;
-      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
-        st = FH_ERR_HIP;
+      hipError_t err = hipEventSynchronize(b);
+      if (err == hipSuccess) err = hipEventElapsedTime(&ms, a, b);
+      if (err != hipSuccess) {
+        st = hip_fail(err);
         break;
       }
       acc[k] += ms;
@@ -567,8 +578,8 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
     case 8: *value = h->bytes; break;
     case 9: {  // selection error flag (synchronous read and clear)
       uint32_t e = 0;
-      if (hipMemcpy(&e, h->error, 4, hipMemcpyDeviceToHost) != hipSuccess) return FH_ERR_HIP;
-      if (e && hipMemset(h->error, 0, 4) != hipSuccess) return FH_ERR_HIP;
+      FH_TRY(hipMemcpy(&e, h->error, 4, hipMemcpyDeviceToHost));
+      if (e) FH_TRY(hipMemset(h->error, 0, 4));
       *value = e;
       break;
     }

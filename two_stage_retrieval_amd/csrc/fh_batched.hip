@@ -29,71 +29,6 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
 }
 
 // ---------------------------------------------------------------------------
-// stage 1, bf16 centroids.  Block: 32 centroid rows x all batch columns.
-// 8 waves = 2 row tiles x 4 quarters of K; each wave issues all its A loads
-// first (16 rows x d/4 columns), then walks K with B fragments from H.  The
-// four K-partials are summed through LDS in fixed order.
-// ---------------------------------------------------------------------------
-constexpr int kS1mThreads = 512;
-constexpr int kS1mRows = 32;
-constexpr int kS1mSteps = 16;  // k-steps of 32 per load round
-
-template <int NT>
-__global__ __launch_bounds__(kS1mThreads) void stage1_mfma_kernel(Stage1Args a, int B) {
-  __shared__ float red[4][NT * 16][kS1mRows + 1];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mt = wave >> 2, kq = wave & 3;
-  const int qd = a.d / 4;            // columns per K-quarter (multiple of 32)
-  const int ksteps = qd / 32;
-  const int slice = lane >> 4, lr = lane & 15;
-  int arow = blockIdx.x * kS1mRows + mt * 16 + lr;
-  arow = arow < a.c ? arow : a.c - 1;
-  const uint8_t* ap = a.C + (int64_t)arow * a.row_bytes + (int64_t)(kq * qd + 8 * slice) * 2;
-  const uint8_t* hp[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int j = nt * 16 + lr;
-    j = j < B ? j : B - 1;
-    hp[nt] = a.H + (int64_t)j * a.h_bytes + (int64_t)(kq * qd + 8 * slice) * 2;
-  }
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ksteps; s0 += kS1mSteps) {
-    uint4 av[kS1mSteps];
-#pragma unroll
-    for (int u = 0; u < kS1mSteps; ++u)
-      av[u] = s0 + u < ksteps ? *reinterpret_cast<const uint4*>(ap + (int64_t)(s0 + u) * 64)
-                              : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int u = 0; u < kS1mSteps; ++u) {
-      if (s0 + u >= ksteps) break;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(hp[nt] + (int64_t)(s0 + u) * 64);
-        acc[nt] = mfma_bf16(av[u], bv, acc[nt]);
-      }
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) red[kq][nt * 16 + lr][mt * 16 + 4 * slice + q] = acc[nt][q];
-  __syncthreads();
-  // outputs (batch row r, centroid k): consecutive threads take consecutive k
-  for (int o = threadIdx.x; o < NT * 16 * kS1mRows; o += kS1mThreads) {
-    const int r = o / kS1mRows, kk = o % kS1mRows;
-    const int k = blockIdx.x * kS1mRows + kk;
-    if (r >= B || k >= a.c) continue;
-    const float s = ((red[0][r][kk] + red[1][r][kk]) + red[2][r][kk]) + red[3][r][kk];
-    const float key = a.sample ? s * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : s;
-    a.keys[(int64_t)r * a.key_stride + k] = key;
-    if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.key_stride + k] = s;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // stage 1, INT4 centroids (notes, Module 3).  One 16-row group tile per wave;
 // per 128-column group the wave runs 4 MFMA steps on the codes (small
 // integers are exact in bf16) into a fresh accumulator, then adds
@@ -171,100 +106,193 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 }
 
 // ---------------------------------------------------------------------------
-// stage 2 (and the batched dense head).  Work item = 16 consecutive rows:
-// FLASH mode, 16 rows of a selected cluster in the cluster-major copy of E
-// (cluster ulist[i / (b/16)]); DENSE mode, rows 16 i .. 16 i + 15 of E.  A
-// wave computes the 16 x B logits of an item and folds, per batch row, the
-// candidates the row selected (its bit in the cluster's mask) into a running
-// best decode key and log-sum-exp; the block writes one partial per row.
+// Skinny GEMM engine: rows of a bf16 matrix (16-row items) times H^T (B
+// columns), K = d in chunks of 128.  A workgroup of 4 waves owns 4 * IT
+// consecutive items (each wave IT of them) and walks K chunk by chunk: the
+// chunk of H (B x 128) is staged once in LDS for all four waves (padded rows
+// against bank conflicts, double-buffered), while each wave streams its
+// items' rows with the next chunk's loads issued before the current chunk's
+// matrix products.  Epilogues:
+//   SCORES  stage-1 keys: item rows are centroids; key = score (or score /
+//           tau + Gumbel noise) for every (batch row, centroid);
+//   FLASH   stage 2: item rows are the candidate rows of a selected cluster
+//           (cluster ulist[i / (b/16)] of the cluster-major copy of E); per
+//           batch row, candidates of clusters the row selected (its bit in
+//           the cluster's mask) are folded into a running best decode key
+//           and log-sum-exp;
+//   DENSE   the batched dense head: item rows are rows of E, every token a
+//           candidate for every batch row.
+// FLASH and DENSE write one partial per (workgroup, batch row).
 // ---------------------------------------------------------------------------
-constexpr int kS2mThreads = 256;
-constexpr int kS2mWaves = kS2mThreads / kWave;
-constexpr int kS2mSteps = 16;
+constexpr int kGmThreads = 256;
+constexpr int kGmWaves = kGmThreads / kWave;
+constexpr int kGmKC = 128;                 // K per chunk (4 MFMA steps)
+constexpr int kGmHRow = kGmKC + 8;         // LDS row pitch in bf16 (16-byte pad)
+enum GmMode : int { kGmScores = 0, kGmFlash = 1, kGmDense = 2 };
 
-template <int NT, bool DENSE>
-__global__ __launch_bounds__(kS2mThreads) void stage2_mfma_kernel(Stage2mArgs a) {
-  __shared__ uint64_t s_best[kS2mWaves][NT * 16];
-  __shared__ float2 s_lse[kS2mWaves][NT * 16];
+template <int NT, int IT, int MODE>
+__global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) {
+  __shared__ uint4 s_h[2][NT * 16 * kGmHRow / 8];
+  __shared__ uint64_t s_best[kGmWaves][NT * 16];
+  __shared__ float2 s_lse[kGmWaves][NT * 16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = lane >> 4, lr = lane & 15;
   const int B = a.B;
-  const int sub = a.b / 16;  // items per cluster (FLASH)
-  const int64_t nitems = DENSE ? (a.v + 15) / 16 : (int64_t)(*a.ucount) * sub;
-  const int ksteps = a.d / 32;
-  const uint8_t* hp[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int j = nt * 16 + lr;
-    j = j < B ? j : B - 1;
-    hp[nt] = a.H + (int64_t)j * a.h_bytes + (int64_t)(8 * slice) * 2;
-  }
+  const int sub = a.b / 16;
+  const int64_t nrows_total = MODE == kGmScores ? (int64_t)a.c : a.v;
+  const int64_t nitems = MODE == kGmFlash ? (int64_t)(*a.ucount) * sub : (nrows_total + 15) / 16;
+  const int nchunks = a.d / kGmKC;
   uint64_t best[NT];
   Lse lse[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) { best[nt] = 0ull; lse[nt] = lse_empty(); }
 
-  for (int64_t it = (int64_t)blockIdx.x * kS2mWaves + wave; it < nitems;
-       it += (int64_t)gridDim.x * kS2mWaves) {
-    int64_t row0, k = 0;
-    uint64_t mask;
-    if constexpr (DENSE) {
-      row0 = it * 16;
-      mask = ~0ull;
+  // groups of kGmWaves * IT items, grid-stride (uniform per workgroup)
+  for (int64_t item0 = (int64_t)blockIdx.x * kGmWaves * IT; item0 < nitems;
+       item0 += (int64_t)gridDim.x * kGmWaves * IT) {
+  __syncthreads();  // the previous group's readers of both LDS buffers are done
+
+  // this wave's items
+  int64_t row0[IT], kc[IT];
+  uint64_t mask[IT];
+  const uint8_t* ap[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    int64_t it = item0 + wave * IT + i;
+    const bool live = it < nitems;
+    it = live ? it : nitems - 1;
+    if constexpr (MODE == kGmFlash) {
+      kc[i] = a.ulist[it / sub];
+      row0[i] = kc[i] * a.b + (it % sub) * 16;
+      mask[i] = live ? a.masks[kc[i]] : 0ull;
     } else {
-      k = a.ulist[it / sub];
-      row0 = k * a.b + (it % sub) * 16;
-      mask = a.masks[k];
+      kc[i] = 0;
+      row0[i] = it * 16;
+      mask[i] = live ? ~0ull : 0ull;
     }
-    int64_t arow = row0 + lr;
-    if constexpr (DENSE) arow = arow < a.v ? arow : a.v - 1;
-    const uint8_t* ap = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
-    f32x4_t acc[NT];
+    int64_t arow = row0[i] + lr;
+    if constexpr (MODE != kGmFlash) arow = arow < nrows_total ? arow : nrows_total - 1;
+    ap[i] = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
+  }
+  // H chunk staging: thread t moves NT 16-byte pieces per chunk
+  const uint8_t* hsrc[NT];
+  int hdst[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ksteps; s0 += kS2mSteps) {
-      uint4 av[kS2mSteps];
+  for (int n = 0; n < NT; ++n) {
+    const int piece = threadIdx.x + n * kGmThreads;  // 16 pieces per H row
+    int j = piece >> 4;
+    const int kp = piece & 15;
+    hdst[n] = j * (kGmHRow / 8) + kp;
+    j = j < B ? j : B - 1;
+    hsrc[n] = a.H + (int64_t)j * a.h_bytes + (int64_t)kp * 16;
+  }
+  f32x4_t acc[IT][NT];
 #pragma unroll
-      for (int u = 0; u < kS2mSteps; ++u)
-        av[u] = s0 + u < ksteps ? *reinterpret_cast<const uint4*>(ap + (int64_t)(s0 + u) * 64)
-                                : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < IT; ++i)
 #pragma unroll
-      for (int u = 0; u < kS2mSteps; ++u) {
-        if (s0 + u >= ksteps) break;
+    for (int nt = 0; nt < NT; ++nt) acc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 a0[IT][4], a1[IT][4], hreg[NT];
+  auto load_a = [&](uint4 (&dst)[IT][4], int c) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(hp[nt] + (int64_t)(s0 + u) * 64);
-          acc[nt] = mfma_bf16(av[u], bv, acc[nt]);
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dst[i][u] = *reinterpret_cast<const uint4*>(ap[i] + (int64_t)c * kGmKC * 2 + u * 64);
+  };
+  auto load_h = [&](int c) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      hreg[n] = *reinterpret_cast<const uint4*>(hsrc[n] + (int64_t)c * kGmKC * 2);
+  };
+  auto store_h = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) s_h[buf][hdst[n]] = hreg[n];
+  };
+  auto compute = [&](const uint4 (&av)[IT][4], int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint4 bv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bv[nt] = s_h[buf][(nt * 16 + lr) * (kGmHRow / 8) + u * 4 + slice];
+#pragma unroll
+      for (int i = 0; i < IT; ++i)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[i][nt] = mfma_bf16(av[i][u], bv[nt], acc[i][nt]);
+    }
+  };
+
+  load_h(0);
+  load_a(a0, 0);
+  store_h(0);
+  for (int c = 0; c < nchunks; c += 2) {
+    // chunk c from buffer 0 / registers a0; prefetch chunk c + 1
+    __syncthreads();
+    if (c + 1 < nchunks) { load_h(c + 1); load_a(a1, c + 1); }
+    compute(a0, 0);
+    if (c + 1 >= nchunks) break;
+    store_h(1);
+    // chunk c + 1 from buffer 1 / registers a1; prefetch chunk c + 2
+    __syncthreads();
+    if (c + 2 < nchunks) { load_h(c + 2); load_a(a0, c + 2); }
+    compute(a1, 1);
+    if (c + 2 < nchunks) store_h(0);
+  }
+
+  if constexpr (MODE == kGmScores) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      if (!mask[i]) continue;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = nt * 16 + lr;
+        if (r >= B) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t k = row0[i] + 4 * slice + q;
+          if (k >= a.c) continue;
+          const float sc = acc[i][nt][q];
+          const float key =
+              a.sample ? sc * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : sc;
+          a.keys[(int64_t)r * a.key_stride + k] = key;
+          if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.key_stride + k] = sc;
         }
       }
     }
-    // epilogue: rows 4 slice + q of the item, batch column nt*16 + lr
+    continue;
+  }
+
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    if (!mask[i]) continue;
     uint32_t tok[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t row = row0 + 4 * slice + q;
-      if constexpr (DENSE) tok[q] = (uint32_t)row;
+      const int64_t row = row0[i] + 4 * slice + q;
+      if constexpr (MODE == kGmDense) tok[q] = (uint32_t)row;
       else tok[q] = (uint32_t)a.c2t[row];
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int r = nt * 16 + lr;
-      const bool rowsel = r < B && ((mask >> r) & 1ull);
-      const uint64_t seed = (a.sample && r < B) ? a.seeds[r] : 0ull;
+      const bool rowsel = r < B && ((mask[i] >> r) & 1ull);
+      if (!rowsel) continue;
+      const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = row0 + 4 * slice + q;
-        const bool ok = rowsel && (!DENSE || row < a.v);
-        if (!ok) continue;
-        const float x = acc[nt][q];
+        const int64_t row = row0[i] + 4 * slice + q;
+        if (MODE == kGmDense && row >= a.v) continue;
+        const float x = acc[i][nt][q];
         const float xs = x * a.inv_tau;
         const float kx = a.sample ? xs + gumbel(seed, kStreamToken, tok[q]) : x;
         const uint64_t key = decode_key(kx, tok[q]);
         best[nt] = key > best[nt] ? key : best[nt];
         if (a.with_lse) lse[nt] = lse_add(lse[nt], xs);
-        if (!DENSE && a.dbg_logits) {
+        if (MODE == kGmFlash && a.dbg_logits) {
           // position of cluster k in row r's ascending selection
+          const int64_t k = kc[i];
           const int32_t* sr = a.sel + (int64_t)r * a.sel_stride;
           int lo = 0, hi = a.p - 1;
           while (lo < hi) {
@@ -278,6 +306,8 @@ __global__ __launch_bounds__(kS2mThreads) void stage2_mfma_kernel(Stage2mArgs a)
       }
     }
   }
+  }  // groups
+  if constexpr (MODE == kGmScores) return;
   // combine the 4 lanes that share a batch column, then the waves
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -294,10 +324,10 @@ __global__ __launch_bounds__(kS2mThreads) void stage2_mfma_kernel(Stage2mArgs a)
     }
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < B; r += kS2mThreads) {
+  for (int r = threadIdx.x; r < B; r += kGmThreads) {
     uint64_t bb = s_best[0][r];
     Lse ll{s_lse[0][r].x, s_lse[0][r].y};
-    for (int w = 1; w < kS2mWaves; ++w) {
+    for (int w = 1; w < kGmWaves; ++w) {
       bb = s_best[w][r] > bb ? s_best[w][r] : bb;
       ll = lse_merge(ll, Lse{s_lse[w][r].x, s_lse[w][r].y});
     }
@@ -352,55 +382,85 @@ bool batched_supported(int dtype, int d, int B, bool int4) {
   return d % 128 == 0;
 }
 
+// items per wave: enough reuse of each H fragment, registers for double-buffered rows
+template <int NT> constexpr int gm_items() { return NT <= 2 ? 4 : 2; }
+
+template <int MODE>
+static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1) {
+  const int NT = (a.B + 15) / 16;
+  const dim3 block(kGmThreads);
+#define FH_GM(N)                                                                               \
+  case N:                                                                                      \
+    hipExtLaunchKernelGGL((gemm_engine_kernel<N, gm_items<N>(), MODE>), dim3(grid), block, 0, s, \
+                          e0, e1, 0, a);                                                       \
+    break;
+  switch (NT) {
+    FH_GM(1)
+    FH_GM(2)
+    FH_GM(3)
+    FH_GM(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef FH_GM
+  return hipGetLastError();
+}
+
+static int engine_grid(int64_t nrows16, int B) {
+  const int NT = (B + 15) / 16;
+  const int it = NT <= 2 ? 4 : 2;
+  const int64_t per = (int64_t)kGmWaves * it;
+  const int64_t g = (nrows16 + per - 1) / per;
+  return g < 1 ? 1 : (int)g;
+}
+
 hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t s,
                               const Timing* tm) {
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   const int NT = (B + 15) / 16;
   if (int4) {
     const dim3 grid((a.ntiles + kS1qThreads / kWave - 1) / (kS1qThreads / kWave));
-    const uint32_t shm = 0;
     switch (NT) {
-      case 1: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<1>, grid, dim3(kS1qThreads), shm, s, e0, e1, 0, a, B); break;
-      case 2: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<2>, grid, dim3(kS1qThreads), shm, s, e0, e1, 0, a, B); break;
-      case 3: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<3>, grid, dim3(kS1qThreads), shm, s, e0, e1, 0, a, B); break;
-      case 4: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<4>, grid, dim3(kS1qThreads), shm, s, e0, e1, 0, a, B); break;
+      case 1: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<1>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
+      case 2: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<2>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
+      case 3: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<3>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
+      case 4: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<4>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
-  const dim3 grid((a.c + kS1mRows - 1) / kS1mRows);
-  switch (NT) {
-    case 1: hipExtLaunchKernelGGL(stage1_mfma_kernel<1>, grid, dim3(kS1mThreads), 0, s, e0, e1, 0, a, B); break;
-    case 2: hipExtLaunchKernelGGL(stage1_mfma_kernel<2>, grid, dim3(kS1mThreads), 0, s, e0, e1, 0, a, B); break;
-    case 3: hipExtLaunchKernelGGL(stage1_mfma_kernel<3>, grid, dim3(kS1mThreads), 0, s, e0, e1, 0, a, B); break;
-    case 4: hipExtLaunchKernelGGL(stage1_mfma_kernel<4>, grid, dim3(kS1mThreads), 0, s, e0, e1, 0, a, B); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  Stage2mArgs m{};
+  m.base = a.C;
+  m.row_bytes = a.row_bytes;
+  m.c = a.c;
+  m.b = 16;
+  m.d = a.d;
+  m.B = B;
+  m.H = a.H;
+  m.h_bytes = a.h_bytes;
+  m.sample = a.sample;
+  m.inv_tau = a.inv_tau;
+  m.seeds = a.seeds;
+  m.keys = a.keys;
+  m.key_stride = a.key_stride;
+  m.dbg_scores = a.dbg_scores;
+  int grid = engine_grid((a.c + 15) / 16, B);
+  grid = grid < stage2_mfma_grid() ? grid : stage2_mfma_grid();
+  return launch_engine<kGmScores>(m, grid, s, e0, e1);
 }
 
-int stage2_mfma_grid() { return 1024; }
+int stage2_mfma_grid() { return 4096; }
 
 hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s, const Timing* tm) {
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
-  const int NT = (a.B + 15) / 16;
-  const dim3 grid(stage2_mfma_grid()), block(kS2mThreads);
-#define FH_S2M(N)                                                                             \
-  case N:                                                                                     \
-    if (dense) hipExtLaunchKernelGGL((stage2_mfma_kernel<N, true>), grid, block, 0, s, e0, e1, 0, a); \
-    else hipExtLaunchKernelGGL((stage2_mfma_kernel<N, false>), grid, block, 0, s, e0, e1, 0, a); \
-    break;
-  switch (NT) {
-    FH_S2M(1)
-    FH_S2M(2)
-    FH_S2M(3)
-    FH_S2M(4)
-    default: return hipErrorInvalidValue;
-  }
-#undef FH_S2M
-  hipError_t e = hipGetLastError();
+  // flash: the union is known on the device only; launch for every cluster
+  const int64_t items = dense ? (a.v + 15) / 16 : (int64_t)a.c * (a.b / 16);
+  int grid = engine_grid(items, a.B);
+  grid = grid < stage2_mfma_grid() ? grid : stage2_mfma_grid();
+  hipError_t e = dense ? launch_engine<kGmDense>(a, grid, s, e0, e1)
+                       : launch_engine<kGmFlash>(a, grid, s, e0, e1);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(256), 0, s, a, stage2_mfma_grid());
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(256), 0, s, a, grid);
   return hipGetLastError();
 }
 

@@ -57,9 +57,10 @@ struct SelectArgs {
 };
 
 struct Stage2mArgs {
-  const uint8_t* base;   // cluster-major copy of E (flash) or E (dense)
+  const uint8_t* base;   // C (scores), cluster-major copy of E (flash) or E (dense)
   int64_t row_bytes;
   int64_t v;             // rows of E (dense)
+  int c;                 // rows of C (scores)
   int b, d, B, p;
   const uint8_t* H;      // B x d bf16
   int64_t h_bytes;
@@ -80,6 +81,10 @@ struct Stage2mArgs {
   int32_t* dbg_ids;
   float* dbg_logits;
   int64_t dbg_stride;
+  // scores epilogue (stage 1)
+  float* keys;
+  int64_t key_stride;
+  float* dbg_scores;
 };
 
 struct Stage1Args {
