@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/flashhead.h declares, and rejects bad arguments on the host before
+any device work (these paths never reach the HIP runtime)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashhead.h")
+LIB = os.path.join(ROOT, "two_stage_retrieval_amd", "libflashhead.so")
+
+# an aligned address that is never dereferenced: every call below fails its
+# host-side checks before touching device memory
+FAKE_DEV = 0x10000
+
+
+def declared_functions() -> set[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return {n for n in names if not n.startswith("FH_")}
+
+
+@pytest.fixture(scope="module")
+def fh():
+    if not os.path.exists(LIB):
+        pytest.fail("libflashhead.so is not built (run __graft_entry__.build())")
+    from two_stage_retrieval_amd import binding
+    return binding
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("flashhead_prepare", "flashhead_destroy", "flashhead_greedy",
+              "flashhead_sample", "dense_head", "flashhead_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(fh):
+    names = declared_functions()
+    lib = C.CDLL(LIB)
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    # the same set with the dynamic symbol table, independent of ctypes
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert names <= exported
+    # the Python binding wraps exactly the declared set
+    assert set(fh.EXPORTED) == names
+
+
+def test_status_strings(fh):
+    for code in (fh.FH_OK, fh.FH_ERR_INVALID_ARG, fh.FH_ERR_NOT_PERMUTATION,
+                 fh.FH_ERR_UNSUPPORTED, fh.FH_ERR_HIP, fh.FH_ERR_OOM):
+        s = fh.status_string(code)
+        assert s and s != "unknown status"
+    assert fh.status_string(12345) == "unknown status"
+    assert fh.flashhead_last_hip_error() == "hipSuccess"
+
+
+def _desc(fh, c2t, *, v=None, d=256, dtype=None, lde=None, E=FAKE_DEV, C_init=None,
+          quant=0, max_batch=1, max_p=1):
+    c, b = c2t.shape
+    dtype = fh.FH_DTYPE_F32 if dtype is None else dtype
+    return fh.fh_desc(c * b if v is None else v, d, c, b, dtype, d if lde is None else lde,
+                      E, c2t.ctypes.data, C_init, quant, max_batch, max_p, None)
+
+
+def _prepare(fh, desc) -> int:
+    h = C.c_void_p()
+    st = fh.lib.flashhead_prepare(C.byref(desc), C.byref(h))
+    assert h.value is None
+    return st
+
+
+def test_prepare_rejects_bad_descriptors(fh):
+    c2t = np.arange(64, dtype=np.int32).reshape(8, 8)
+    inv, uns = fh.FH_ERR_INVALID_ARG, fh.FH_ERR_UNSUPPORTED
+    assert fh.lib.flashhead_prepare(None, None) == inv
+    h = C.c_void_p()
+    assert fh.lib.flashhead_prepare(None, C.byref(h)) == inv
+    assert _prepare(fh, _desc(fh, c2t, E=None)) == inv
+    assert _prepare(fh, _desc(fh, c2t, v=65)) == inv             # v != c * b
+    assert _prepare(fh, _desc(fh, c2t, max_batch=0)) == inv
+    assert _prepare(fh, _desc(fh, c2t, max_batch=65)) == inv
+    assert _prepare(fh, _desc(fh, c2t, max_p=9)) == inv          # p > c
+    assert _prepare(fh, _desc(fh, c2t, lde=255)) == inv          # lde < d
+    assert _prepare(fh, _desc(fh, c2t, dtype=7)) == uns
+    assert _prepare(fh, _desc(fh, c2t, d=250)) == uns            # rows not 16-byte multiples
+    assert _prepare(fh, _desc(fh, c2t, E=FAKE_DEV + 4)) == uns   # misaligned E
+    assert _prepare(fh, _desc(fh, c2t, quant=5)) == uns
+    assert _prepare(fh, _desc(fh, c2t, quant=fh.FH_QUANT_INT4_G128)) == uns  # INT4 needs bf16
+    assert _prepare(fh, _desc(fh, c2t, dtype=fh.FH_DTYPE_BF16, d=200,
+                              quant=fh.FH_QUANT_INT4_G128)) == uns            # d % 128
+
+
+@pytest.mark.parametrize("kind", ["repeat", "out_of_range", "negative"])
+def test_prepare_rejects_c2t_that_is_not_a_permutation(fh, kind):
+    c2t = np.random.default_rng(3).permutation(64).astype(np.int32).reshape(8, 8)
+    if kind == "repeat":
+        c2t[5, 2] = c2t[1, 1]
+    elif kind == "out_of_range":
+        c2t[0, 0] = 64
+    else:
+        c2t[7, 7] = -1
+    assert _prepare(fh, _desc(fh, c2t)) == fh.FH_ERR_NOT_PERMUTATION
+
+
+def test_step_calls_reject_null_handle_and_arguments(fh):
+    lib = fh.lib
+    inv = fh.FH_ERR_INVALID_ARG
+    out = C.c_void_p(FAKE_DEV)
+    assert lib.flashhead_greedy(None, FAKE_DEV, 1, 1, out, None, None) == inv
+    assert lib.flashhead_sample(None, FAKE_DEV, 1, 1, C.c_float(1.0), FAKE_DEV, out, None,
+                                None, None) == inv
+    lib.flashhead_destroy(None)  # a no-op
+    v = C.c_int64()
+    assert lib.flashhead_query(None, 0, C.byref(v)) == inv
+    calls = C.c_int32()
+    stage = (C.c_double * 3)()
+    assert lib.flashhead_profile_end(None, stage, C.byref(calls)) == inv
+    assert lib.flashhead_profile_begin(None, 4) == inv
+
+
+def test_dense_head_host_checks(fh):
+    lib = fh.lib
+    inv, uns = fh.FH_ERR_INVALID_ARG, fh.FH_ERR_UNSUPPORTED
+    ws = FAKE_DEV
+    args = dict(E=FAKE_DEV, v=4096, d=256, dtype=fh.FH_DTYPE_F32, lde=256, H=FAKE_DEV, B=1,
+                mode=fh.FH_MODE_GREEDY, tau=1.0, seeds=None, out=FAKE_DEV, lse=None, ws=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.dense_head(a["E"], a["v"], a["d"], a["dtype"], a["lde"], a["H"], a["B"],
+                              a["mode"], C.c_float(a["tau"]), a["seeds"], a["out"], a["lse"],
+                              a["ws"], None)
+
+    assert call(E=None) == inv
+    assert call(ws=None) == inv
+    assert call(B=0) == inv
+    assert call(B=65) == inv
+    assert call(lde=100) == inv
+    assert call(mode=3) == inv
+    assert call(mode=fh.FH_MODE_SAMPLE) == inv                  # no seeds
+    assert call(mode=fh.FH_MODE_SAMPLE, seeds=FAKE_DEV, tau=0.0) == inv
+    assert call(mode=fh.FH_MODE_SAMPLE, seeds=FAKE_DEV, tau=float("inf")) == inv
+    assert call(dtype=9) == uns
+    assert call(H=FAKE_DEV + 8) == uns
+
+
+def test_dense_workspace_size(fh):
+    assert fh.dense_head_workspace_bytes(0) == 0
+    for B in (1, 4, 64):
+        n = fh.dense_head_workspace_bytes(B)
+        # best keys, counters (16-byte padded) and per-block partials
+        assert n >= B * 8 + B * 4 + B * 8 and n % 8 == 0
+        assert fh.dense_head_workspace_bytes(B + 1) > n
