@@ -24,6 +24,8 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -43,6 +45,39 @@ PAGES_TPOT_H_US = 400.0   # the paper page's Table 3 FlashHead TPOT^H (0.40 ms)
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def sources_digest() -> str:
+    """Digest of the library's kernel sources: counters taken on other
+    sources no longer describe the kernels that run."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "two_stage_retrieval_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "flashhead.h"))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fp:
+            h.update(fp.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, B: int):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs recorded in profiles/, or None when there is no record
+    for these sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = sources_digest()
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("traffic "):
+            continue
+        kv = dict(item.split("=", 1) for item in line.split()[1:])
+        if (kv.get("kernel") == kernel and kv.get("workload") == workload
+                and int(kv.get("batch", -1)) == B and kv.get("sources") == digest):
+            return int(kv["bytes"])
+    return None
 
 
 def algorithmic_bytes(wl, B, U, int4):
@@ -66,6 +101,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time back-to-back (cache-warm) calls")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run --steps cold calls and a 256 MiB copy-like kernel, then exit "
+                         "(for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -156,16 +196,47 @@ def main():
         return a.elapsed_time(b) * 1e3 / K
 
     K, W = args.steps, args.warmup
-    for i in range(W):
-        call(i)
-        if dense:
-            call_dense(i)
+    if args.pmc_probe:
+        # counters per dispatch: the head's kernels on cold calls, then a
+        # copy-like kernel of known size (reads and writes 256 MiB) whose
+        # FETCH_SIZE / WRITE_SIZE calibrate the counters' units
+        time_cold(call, K)
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        evict()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_probe": wl.name, "batch": B, "calls": K,
+                          "copy_kernel_bytes_each_way": src.numel() * 4}), flush=True)
+        fh.close()
+        return
+
+    # every call below, warm-up included, follows a flush, so that each
+    # dispatch of the head's kernels in this process is a cold one
+    time_cold(call, W)
+    if dense:
+        time_cold(call_dense, W)
     torch.cuda.synchronize()
     log("[bench] warmup done")
 
     cold = time_cold(call, K)
-    warm = time_warm(call, K)
-    log(f"[bench] flashhead cold p50 {statistics.median(cold):.2f} us, warm {warm:.2f} us")
+    warm = time_warm(call, K) if args.warm else None
+    log(f"[bench] flashhead cold p50 {statistics.median(cold):.2f} us"
+        + (f", warm {warm:.2f} us" if warm else ""))
+
+    # the flush itself is a plain streaming read of 1 GiB: the read
+    # bandwidth this GPU achieves, measured in the same process
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(10)]
+    for a, b in ev:
+        a.record()
+        evict()
+        b.record()
+    torch.cuda.synchronize()
+    stream_us = statistics.median([a.elapsed_time(b) * 1e3 for a, b in ev])
+    stream_gbs = flush.numel() * 4 / (stream_us * 1e-6) / 1e9
+    log(f"[bench] streaming read of 1 GiB: {stream_us:.1f} us = {stream_gbs:.0f} GB/s")
 
     # per-kernel durations (events around each kernel), cold
     fhb.flashhead_profile_begin(fh.handle, K)
@@ -178,8 +249,9 @@ def main():
     dense_cold = dense_warm = None
     if dense:
         dense_cold = time_cold(call_dense, K)
-        dense_warm = time_warm(call_dense, K)
-        log(f"[bench] dense cold p50 {statistics.median(dense_cold):.2f} us, warm {dense_warm:.2f} us")
+        dense_warm = time_warm(call_dense, K) if args.warm else None
+        log(f"[bench] dense cold p50 {statistics.median(dense_cold):.2f} us"
+            + (f", warm {dense_warm:.2f} us" if dense_warm else ""))
 
     # union of selected clusters per batch (U = p at batch 1)
     U = wl.p
@@ -187,6 +259,7 @@ def main():
         us = []
         for i in range(min(nb, 8)):
             dbg = {"clusters": torch.empty(B, wl.p, dtype=torch.int32, device=dev)}
+            evict()
             if sample:
                 fh.sample(batches[i], wl.p, tau, seeds[i], out=out, debug=dbg)
             else:
@@ -197,16 +270,20 @@ def main():
     cold_p50 = statistics.median(cold)
     cold_p90 = float(np.percentile(cold, 90))
     gbs = total_b / (cold_p50 * 1e-6) / 1e9
-    # dominant kernel: the longer of the two streaming stages
+    # dominant kernel: the longer of the two streaming stages (at batch 1
+    # stage 1 includes the selection, run by its last workgroup)
     if kern_us[2] >= kern_us[0]:
-        dom, dom_bytes, dom_name = 2, s2_b, "stage2_gather"
+        dom, dom_bytes, dom_name = 2, s2_b, "stage2"
     else:
-        dom, dom_bytes, dom_name = 0, s1_b, "stage1_select"
+        dom, dom_bytes, dom_name = 0, s1_b, "stage1"
     dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+    traffic = measured_traffic(dom_name, wl.name, B)
     roofline = {"bound": "hbm", "kernel": dom_name,
                 "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "bytes_per_launch": dom_bytes, "avg_launch_us": round(kern_us[dom], 3)}
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_us": round(kern_us[dom], 3),
+                "frac_of_streaming_read": round(dom_gbs / stream_gbs, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -237,7 +314,8 @@ def main():
         "algorithmic_bytes": total_b,
         "union_clusters": U,
         "cold_p90_us": round(cold_p90, 3),
-        "warm_us": round(warm, 3),
+        "warm_us": round(warm, 3) if warm else None,
+        "streaming_read_gbs": round(stream_gbs, 1),
         "kernels_us": {"stage1_select": round(kern_us[0], 3), "select": round(kern_us[1], 3),
                        "stage2": round(kern_us[2], 3)},
         "dense_us_cold": round(dense_p50, 3) if dense_p50 else None,
@@ -250,14 +328,27 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(head, H, wl, B, int4, sample, tau, seconds):
-    """The oracle as it stands, on the host cores, over a bounded sample."""
+    """The oracle as it stands, on the host cores, over a bounded sample:
+    median time of one head call (B rows), with the BLAS thread pool at its
+    default size and again limited to one thread."""
     from oracle import flashhead_ref as ref
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:
+        threadpool_info = threadpool_limits = None
+    cores = (max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+             if threadpool_info else int(os.environ.get("OMP_NUM_THREADS", "1")))
     t0 = time.time()
     rows = ref.rows_accessor(head.E, wl.dtype)
     if head.C_given is not None:
@@ -267,21 +358,38 @@ def cpu_baseline(head, H, wl, B, int4, sample, tau, seconds):
     q4 = ref.int4_quantize(C64) if int4 else None
     log(f"[bench] oracle prepare {time.time() - t0:.1f}s")
     H64 = ref.as_f64(H, wl.dtype)
-    times = []
-    start = time.time()
-    n = 0
-    while time.time() - start < seconds and n < len(H64):
-        t = time.perf_counter()
-        for r in range(B):
-            ref.flashhead_step(rows, head.c2t, H64[(n * B + r) % len(H64)], wl.p,
-                               C_f64=C64, int4=q4, mode="sample" if sample else "greedy",
-                               tau=tau, seed=r)
-        times.append((time.perf_counter() - t) * 1e6)
-        n += 1
-    return {"value": round(statistics.median(times), 1), "unit": "us/call", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{n} calls of batch {B} on the same workload (float64 numpy oracle), "
-                      f"median per call"}
+
+    def run(budget):
+        times = []
+        start = time.time()
+        n = 0
+        while time.time() - start < budget and n < len(H64):
+            t = time.perf_counter()
+            for r in range(B):
+                ref.flashhead_step(rows, head.c2t, H64[(n * B + r) % len(H64)], wl.p,
+                                   C_f64=C64, int4=q4, mode="sample" if sample else "greedy",
+                                   tau=tau, seed=r)
+            times.append((time.perf_counter() - t) * 1e6)
+            n += 1
+        return statistics.median(times), n
+
+    med, n = run(seconds)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one, n1 = run(seconds / 3)
+    log(f"[bench] oracle {med:.0f} us/call on {cores} threads ({n} calls)"
+        + (f", {one:.0f} us/call on 1 thread ({n1} calls)" if one else ""))
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"value": round(med, 1), "unit": "us/call", "cores": cores, "kind": "oracle",
+            "sample": f"{n} calls of batch {B} on the same workload (float64 numpy oracle, "
+                      f"{seconds:.0f} s budget), median per call",
+            "value_1_thread": round(one, 1) if one else None,
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": affinity}
 
 
 if __name__ == "__main__":
