@@ -173,8 +173,11 @@ int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p,
  * in-library comparison: z = E h_r over all v tokens, then argmax or the
  * Gumbel-max sample with stream-1 noise keyed by token id (so that
  * flashhead_sample with p = c returns the same ids).
- *   workspace  device memory of dense_head_workspace_bytes(B) bytes, zero
- *              filled before its first use; every call leaves it zeroed
+ *   workspace  device memory of dense_head_workspace_bytes(B) bytes, 16-byte
+ *              aligned.  Its first 4096 * B bytes (completion counters) must
+ *              be zero before the first use; every call leaves them zero.
+ *              The rest holds per-workgroup partials, rewritten each call.
+ *              One call in flight per workspace.
  *   out_lse    optional, as for flashhead_sample (over all v tokens)
  */
 size_t dense_head_workspace_bytes(int32_t B);

@@ -25,7 +25,7 @@ struct fh_handle {
   // workspace (left zeroed / consistent by every call)
   float* keys = nullptr;      // max_batch x c
   int32_t* sel = nullptr;     // max_batch x max_p
-  uint64_t* best = nullptr;   // max_batch
+  uint64_t* row_best = nullptr;  // max_batch x kMaxGrid partial best keys (GEMV stage 2)
   uint32_t* counters = nullptr;
   float2* lse_part = nullptr; // max_batch x kMaxGrid
   uint64_t* masks = nullptr;  // c
@@ -49,6 +49,9 @@ namespace {
 
 constexpr int kMaxGrid = 8192;       // largest grid.x of a decode launch
 constexpr int kDenseMaxGrid = 8192;  // dense: partial slots of the batched kernel (2 x 4096)
+
+// selection keys of a batch row: c floats padded to a 16-byte multiple
+int64_t key_stride(int c) { return ((int64_t)c + 3) & ~(int64_t)3; }
 
 int esize_of(int dtype) { return dtype == FH_DTYPE_F32 ? 4 : dtype == FH_DTYPE_BF16 ? 2 : 0; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -184,24 +187,23 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
     FH_TRY(hipStreamSynchronize(s));  // host vectors die at scope end
   }
   const int mb = h->max_batch;
-  FH_TRY(alloc(h, &h->keys, (size_t)mb * c * 4));
+  FH_TRY(alloc(h, &h->keys, (size_t)mb * key_stride(c) * 4));
   FH_TRY(alloc(h, &h->sel, (size_t)mb * h->max_p * 4));
-  FH_TRY(alloc(h, &h->best, (size_t)mb * 8));
-  FH_TRY(alloc(h, &h->counters, (size_t)mb * 4));
+  FH_TRY(alloc(h, &h->row_best, (size_t)mb * kMaxGrid * 8));
+  FH_TRY(alloc(h, &h->counters, (size_t)mb * kArriveWords * 4));
   FH_TRY(alloc(h, &h->lse_part, (size_t)mb * kMaxGrid * 8));
-  FH_TRY(alloc(h, &h->masks, (size_t)c * 8));
+  FH_TRY(alloc(h, &h->masks, (size_t)(c + 1) * 8));  // the select reads pairs
   FH_TRY(alloc(h, &h->error, 4));
   FH_TRY(hipMemsetAsync(h->sel, 0, (size_t)mb * h->max_p * 4, s));
-  FH_TRY(hipMemsetAsync(h->best, 0, (size_t)mb * 8, s));
-  FH_TRY(hipMemsetAsync(h->counters, 0, (size_t)mb * 4, s));
-  FH_TRY(hipMemsetAsync(h->masks, 0, (size_t)c * 8, s));
+  FH_TRY(hipMemsetAsync(h->counters, 0, (size_t)mb * kArriveWords * 4, s));
+  FH_TRY(hipMemsetAsync(h->masks, 0, (size_t)(c + 1) * 8, s));
   FH_TRY(hipMemsetAsync(h->error, 0, 4, s));
-  FH_TRY(alloc(h, &h->sel_counter, 4));
+  FH_TRY(alloc(h, &h->sel_counter, (size_t)kArriveWords * 4));
   FH_TRY(alloc(h, &h->ulist, (size_t)c * 4));
   FH_TRY(alloc(h, &h->ucount, 4));
   FH_TRY(alloc(h, &h->part_best, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
-  FH_TRY(hipMemsetAsync(h->sel_counter, 0, 4, s));
+  FH_TRY(hipMemsetAsync(h->sel_counter, 0, (size_t)kArriveWords * 4, s));
   FH_TRY(hipMemsetAsync(h->ucount, 0, 4, s));
   FH_TRY(hipStreamSynchronize(s));
   return FH_OK;
@@ -255,7 +257,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.H = static_cast<const uint8_t*>(H);
   s1.h_bytes = h->row_bytes;
   s1.keys = h->keys;
-  s1.key_stride = h->c;
+  s1.key_stride = key_stride(h->c);
   s1.dbg_scores = dbg ? dbg->scores : nullptr;
   s1.sample = sample;
   s1.inv_tau = inv_tau;
@@ -276,7 +278,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   if (!s1.select) {
     SelectArgs a{};
     a.keys = h->keys;
-    a.key_stride = h->c;
+    a.key_stride = key_stride(h->c);
     a.c = h->c;
     a.p = p;
     a.sel = h->sel;
@@ -343,7 +345,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.c2t = h->c2t;
     a.b = h->b;
     a.nclusters = h->c;
-    a.best = h->best;
+    a.part_best = h->row_best;
     a.counters = h->counters;
     a.lse_part = h->lse_part;
     a.out_tokens = out;
@@ -446,7 +448,7 @@ int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p, float ta
 size_t dense_head_workspace_bytes(int32_t B) {
   if (B < 1) return 0;
   const size_t nb = (size_t)B;
-  return nb * 8 + ((nb * 4 + 15) / 16) * 16 + nb * kDenseMaxGrid * 8;
+  return nb * kArriveWords * 4 + nb * kDenseMaxGrid * 16;
 }
 
 int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, const void* H,
@@ -465,7 +467,10 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   if (!aligned16(E) || !aligned16(H) || !aligned16(workspace)) return FH_ERR_UNSUPPORTED;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const size_t nb = (size_t)B;
-  uint8_t* ws_part = ws + nb * 8 + ((nb * 4 + 15) / 16) * 16;
+  // workspace: arrival counters | partial best keys | partial lse pairs
+  uint32_t* ws_ctr = reinterpret_cast<uint32_t*>(ws);
+  uint64_t* ws_best = reinterpret_cast<uint64_t*>(ws + nb * kArriveWords * 4);
+  float2* ws_lse = reinterpret_cast<float2*>(ws + nb * kArriveWords * 4 + nb * kDenseMaxGrid * 8);
   if (B >= 2 && batched_supported(dtype, d, B, false)) {
     Stage2mArgs m{};
     m.base = static_cast<const uint8_t*>(E);
@@ -480,8 +485,8 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
     m.inv_tau = m.sample ? 1.0f / tau : 1.0f;
     m.seeds = seeds;
     m.with_lse = out_lse != nullptr;
-    m.part_best = reinterpret_cast<uint64_t*>(ws_part);
-    m.part_lse = reinterpret_cast<float2*>(ws_part + (size_t)stage2_mfma_grid() * nb * 8);
+    m.part_best = ws_best;
+    m.part_lse = ws_lse;
     m.out_tokens = out_tokens;
     m.out_lse = out_lse;
     FH_TRY(launch_stage2_mfma(m, true, static_cast<hipStream_t>(stream)));
@@ -494,9 +499,9 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   a.H = static_cast<const uint8_t*>(H);
   a.h_bytes = row_bytes;
   a.nrows = v;
-  a.best = reinterpret_cast<uint64_t*>(ws);
-  a.counters = reinterpret_cast<uint32_t*>(ws + nb * 8);
-  a.lse_part = reinterpret_cast<float2*>(ws_part);
+  a.part_best = ws_best;
+  a.counters = ws_ctr;
+  a.lse_part = ws_lse;
   a.out_tokens = out_tokens;
   a.out_lse = out_lse;
   a.sample = mode == FH_MODE_SAMPLE;

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
       const float key =
           a.sample ? s * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : s;
       a.keys[(int64_t)r * a.key_stride + k] = key;
-      if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.key_stride + k] = s;
+      if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = s;
     }
   }
 }
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
           const float key =
               a.sample ? sc * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : sc;
           a.keys[(int64_t)r * a.key_stride + k] = key;
-          if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.key_stride + k] = sc;
+          if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = sc;
         }
       }
     }

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fh_internal.h"
+
 namespace fh {
 
 constexpr int kWave = 64;
@@ -223,6 +225,51 @@ __device__ __forceinline__ Lse wave_lse(Lse a) {
     a = lse_merge(a, b);
   }
   return a;
+}
+
+// ---------------------------------------------------------------------------
+// Completion of the other workgroups of a grid without same-address
+// serialisation.  A workgroup that has made its results visible device-wide
+// (device-scope stores, then s_waitcnt) adds 1 to one of kArriveCounters
+// counters, each in its own 128-byte line; one designated workgroup polls
+// all of them with a single wave until the expected number of arrivals is
+// counted, then clears them for the next launch.  Same-address device
+// atomics serialise at the memory side (tens of ns each), so spreading the
+// arrivals keeps the wait close to one memory round trip.
+// ---------------------------------------------------------------------------
+constexpr int kArriveSpinLimit = 1 << 22;  // polls before giving up (seconds)
+
+__device__ __forceinline__ void arrive(uint32_t* ctr, int w) {
+  __hip_atomic_fetch_add(ctr + (w % kArriveCounters) * kArriveStride, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Called by all 64 lanes of one wave.  Returns false if the spin limit was
+// reached before `expected` arrivals (the caller reports an error).
+__device__ __forceinline__ bool wait_arrivals(uint32_t* ctr, uint32_t expected, int lane) {
+  uint32_t* mine = ctr + (lane % kArriveCounters) * kArriveStride;
+  bool ok = expected == 0;
+  for (int it = 0; !ok && it < kArriveSpinLimit; ++it) {
+    const uint32_t v =
+        lane < kArriveCounters
+            ? __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+            : 0u;
+    const uint32_t tot = wave_sum_u32(v);
+    if (tot >= expected) {
+      ok = tot == expected;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (lane < kArriveCounters)
+    __hip_atomic_store(mine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return ok;
 }
 
 }  // namespace fh

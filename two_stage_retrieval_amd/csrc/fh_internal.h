@@ -8,6 +8,11 @@
 
 namespace fh {
 
+// Arrival counters of one batch row (see wait_arrivals in fh_device.h).
+constexpr int kArriveCounters = 32;
+constexpr int kArriveStride = 32;  // uint32 per counter: one 128-byte line each
+constexpr int kArriveWords = kArriveCounters * kArriveStride;
+
 // Which rows a row-dot launch visits and what it does with each dot product.
 enum RowdotMode : int {
   kRowGather = 1,  // candidate rows C2T[sel[i / b], i % b]; decode epilogue
@@ -28,8 +33,8 @@ struct RowdotArgs {
   int b;
   int nclusters;         // c (selected ids are clamped to [0, c))
   // decode epilogue
-  uint64_t* best;        // B: running max decode key (zero between calls)
-  uint32_t* counters;    // B: finished-block counters (zero between calls)
+  uint64_t* part_best;   // B x gridDim.x partial best decode keys
+  uint32_t* counters;    // B x kArriveWords arrival counters (zero between calls)
   float2* lse_part;      // B x gridDim.x partial (max, sum)
   int32_t* out_tokens;
   float* out_lse;
@@ -51,7 +56,7 @@ struct SelectArgs {
   uint64_t* masks;       // optional: per-cluster bitmask of selecting rows
   uint32_t* error;       // optional: set non-zero if a row selected != p
   // optional union compaction by the last block (needs masks)
-  uint32_t* counter;     // finished-block counter (zero between calls)
+  uint32_t* counter;     // kArriveWords arrival counters (zero between calls)
   int32_t* ulist;        // clusters with a non-zero mask, ascending
   int32_t* ucount;
 };
@@ -97,16 +102,16 @@ struct Stage1Args {
   int ntiles, groups;     // ceil(c / 16), d / 128
   const uint8_t* H;       // B x d
   int64_t h_bytes;
-  float* keys;            // B x key_stride selection keys
+  float* keys;            // B x key_stride selection keys (stride: c rounded up to 4)
   int64_t key_stride;
-  float* dbg_scores;      // optional raw scores, B x key_stride
+  float* dbg_scores;      // optional raw scores, B x c
   int sample;
   float inv_tau;
   const uint64_t* seeds;
   // selection by the last block of each batch row (when select != 0)
   int select;
   int p;
-  uint32_t* counters;     // B finished-block counters (zero between calls)
+  uint32_t* counters;     // B x kArriveWords arrival counters (zero between calls)
   int32_t* sel;           // B x sel_stride, written ascending
   int sel_stride;
   uint64_t* masks;        // optional per-cluster row bitmask

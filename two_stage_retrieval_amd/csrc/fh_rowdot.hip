@@ -16,6 +16,11 @@
 #include "fh_device.h"
 #include "fh_internal.h"
 
+// Optional timeline hook for measurement builds (empty in the library).
+#ifndef FH_S2_TRACE
+#define FH_S2_TRACE(slot)
+#endif
+
 namespace fh {
 
 constexpr int kRowdotThreads = 256;
@@ -28,6 +33,7 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = blockIdx.y;
+  FH_S2_TRACE(0);
 
   float hreg[NCH][EPC];
   {
@@ -111,14 +117,15 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
       }
     }
   }
-  // ---- block reduction, then the last block of this batch row finalizes ----
-  // Blocks publish their results only through device-scope atomics (coherent
-  // across the XCDs), wait for those to complete, and only then count
-  // themselves done; the last block reads everything back with atomics.  No
-  // L2 write-back or invalidate is needed on this path.
-  __shared__ uint64_t s_best[kRowdotWaves];
+  // ---- block reduction; workgroup 0 of this batch row finishes -----------
+  // Every workgroup stores its partial (best key, lse pair) into its own slot
+  // with device-scope stores, waits for them to complete and counts itself
+  // arrived (spread counters, fh_device.h); workgroup 0, after its own share,
+  // waits for all arrivals and folds the partials in a fixed order.  No
+  // same-address atomics, no L2 write-back or invalidate on this path.
+  __shared__ uint64_t s_best[kRowdotThreads];
   __shared__ float2 s_lse[kRowdotThreads];
-  __shared__ int s_last;
+  FH_S2_TRACE(1);
   best = wave_max_u64(best);
   if (a.out_lse) lse = wave_lse(lse);
   if (lane == 0) {
@@ -126,9 +133,10 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
     s_lse[wave] = make_float2(lse.m, lse.s);
   }
   __syncthreads();
-  unsigned long long* gbest = reinterpret_cast<unsigned long long*>(a.best + r);
-  unsigned long long* glse =
+  uint64_t* pbest = a.part_best + (int64_t)r * gridDim.x;
+  unsigned long long* plse =
       reinterpret_cast<unsigned long long*>(a.lse_part + (int64_t)r * gridDim.x);
+  uint32_t* ctr = a.counters + (int64_t)r * kArriveWords;
   if (threadIdx.x == 0) {
     uint64_t bb = s_best[0];
     Lse ll{s_lse[0].x, s_lse[0].y};
@@ -136,48 +144,59 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
       bb = s_best[w] > bb ? s_best[w] : bb;
       ll = lse_merge(ll, Lse{s_lse[w].x, s_lse[w].y});
     }
-    if (bb) __hip_atomic_fetch_max(gbest, (unsigned long long)bb, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    if (a.out_lse) {
-      const unsigned long long packed =
-          ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
-      __hip_atomic_exchange(glse + blockIdx.x, packed, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x != 0) {
+      __hip_atomic_store(pbest + blockIdx.x, bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.out_lse) {
+        const unsigned long long packed =
+            ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
+        __hip_atomic_store(plse + blockIdx.x, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the partial is visible device-wide
+      arrive(ctr, blockIdx.x);
+    } else {
+      s_best[kRowdotThreads - 1] = bb;  // workgroup 0's own partial
+      s_lse[kRowdotThreads - 1] = make_float2(ll.m, ll.s);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the atomics above have been performed
-    const uint32_t prev = __hip_atomic_fetch_add(a.counters + r, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == gridDim.x - 1);
   }
+  if (blockIdx.x != 0) return;
   __syncthreads();
-  if (!s_last) return;
-  if (a.out_lse) {
-    // deterministic merge: fixed strided order, fixed tree
-    Lse ll = lse_empty();
-    for (int j = threadIdx.x; j < (int)gridDim.x; j += kRowdotThreads) {
+  const uint64_t own_best = s_best[kRowdotThreads - 1];
+  const float2 own_lse = s_lse[kRowdotThreads - 1];
+  if (wave == 0) wait_arrivals(ctr, gridDim.x - 1, lane);
+  __syncthreads();
+  FH_S2_TRACE(2);
+  // deterministic fold: fixed strided order, fixed tree
+  uint64_t bb = threadIdx.x == 0 ? own_best : 0ull;
+  Lse ll = threadIdx.x == 0 ? Lse{own_lse.x, own_lse.y} : lse_empty();
+  for (int j = 1 + threadIdx.x; j < (int)gridDim.x; j += kRowdotThreads) {
+    const uint64_t x = __hip_atomic_load(pbest + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bb = x > bb ? x : bb;
+    if (a.out_lse) {
       const unsigned long long pr =
-          __hip_atomic_fetch_add(glse + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_load(plse + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ll = lse_merge(ll, Lse{__uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32))});
     }
-    s_lse[threadIdx.x] = make_float2(ll.m, ll.s);
-    __syncthreads();
-    for (int w = kRowdotThreads / 2; w >= 1; w >>= 1) {
-      if (threadIdx.x < w) {
+  }
+  __syncthreads();
+  s_best[threadIdx.x] = bb;
+  s_lse[threadIdx.x] = make_float2(ll.m, ll.s);
+  __syncthreads();
+  for (int w = kRowdotThreads / 2; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      if (s_best[threadIdx.x + w] > s_best[threadIdx.x]) s_best[threadIdx.x] = s_best[threadIdx.x + w];
+      if (a.out_lse) {
         const Lse x = lse_merge(Lse{s_lse[threadIdx.x].x, s_lse[threadIdx.x].y},
                                 Lse{s_lse[threadIdx.x + w].x, s_lse[threadIdx.x + w].y});
         s_lse[threadIdx.x] = make_float2(x.m, x.s);
       }
-      __syncthreads();
     }
-    if (threadIdx.x == 0) a.out_lse[r] = s_lse[0].x + logf(s_lse[0].y);
+    __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const uint64_t k =
-        __hip_atomic_fetch_add(gbest, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.out_tokens[r] = (int32_t)key_id(k);
-    __hip_atomic_exchange(gbest, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_exchange(a.counters + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.out_tokens[r] = (int32_t)key_id(s_best[0]);
+    if (a.out_lse) a.out_lse[r] = s_lse[0].x + logf(s_lse[0].y);
   }
+  FH_S2_TRACE(3);
 }
 
 // Rows per wave per step: enough bytes in flight per wave without spilling.

@@ -4,17 +4,21 @@
 // p draws without replacement from softmax(scores / tau)); the noise is added
 // where the scores are produced, so this code only selects.
 //
-// Item j of thread t is cluster t + j*NT (coalesced loads).
+// Thread t owns the IPT consecutive ids [t*IPT, t*IPT + IPT), read with
+// 16-byte loads, so that a scan of per-thread counts is already in id order.
 //  1. block min / max of the keys (DPP wave reductions, one barrier);
 //  2. LDS histogram of 2048 equal-width value bins over [min, max] (a
-//     monotone function of the key, so bin order is key order); a block scan
-//     from the top finds the boundary bin holding the p-th largest key;
-//  3. the boundary bin is resolved exactly: all-pairs rank when it holds at
-//     most 1024 keys, else (heavily tied keys) an 8-bit radix select on the
-//     order-preserving key bits plus the lowest ids among exact ties;
-//  4. the selection becomes a bitmap in cluster-id order (one ballot per 64
-//     consecutive ids); a block scan of per-word popcounts gives every
-//     selected cluster its rank, and the ids are written ascending.
+//     monotone function of the key, so bin order is key order); each item's
+//     bin is computed once and kept; a block scan from the top finds the
+//     boundary bin holding the p-th largest key;
+//  3. the boundary bin is resolved exactly.  Up to 64 keys (the usual case:
+//     a handful) are gathered and wave 0 picks the ones needed with ballots,
+//     bit by bit over (key descending, id ascending).  Larger bins (heavily
+//     tied or skewed keys) first go through 8-bit radix passes on the
+//     order-preserving key bits; keys that stay exactly equal are taken
+//     lowest id first through a block scan;
+//  4. each thread counts its selected ids; one block scan gives every thread
+//     its output offset and the ids are written ascending.
 // Block scans use DPP inside the wave and one barrier each.
 #pragma once
 #include "fh_device.h"
@@ -28,16 +32,16 @@
 namespace fh {
 
 constexpr int kSelBins = 2048;
-constexpr int kSelCandMax = 1024;
+constexpr int kSelWaveMax = 64;           // boundary bins up to this size go to one wave
+constexpr int32_t kCachePolicySc1 = 16;   // buffer-load cache policy: device-coherent read
 
 struct SelSmem {
   int hist[kSelBins];
-  uint32_t cu[kSelCandMax];
-  int ck[kSelCandMax];
-  uint32_t bits[FH_MAX_C / 32];  // chosen keys of the boundary bin / exact ties
-  uint32_t sel[FH_MAX_C / 32];   // selection bitmap, cluster-id order
+  uint32_t cu[kSelWaveMax];        // gathered boundary keys (order-preserving bits)
+  int ck[kSelWaveMax];             // and their ids
+  uint32_t chosen[FH_MAX_C / 32];  // ids picked inside the boundary bin (id bitmap)
   float fmin[16], fmax[16];
-  int w[2][16];                   // block-scan wave totals, alternating buffers
+  int w[2][16];                    // block-scan wave totals, alternating buffers
   int misc[8];
 };
 
@@ -62,64 +66,100 @@ __device__ __forceinline__ int sel_scan(int x, SelSmem& sm, int& parity, int lan
   return incl + off;
 }
 
-template <bool COHERENT>
-__device__ __forceinline__ float sel_load(const float* p) {
-  if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
+// Buffer resource over `bytes` bytes at `base`: loads past the end read as
+// zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sel_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-// Selects p of the c keys; writes the ids ascending to out[0..p).  With
-// `masks`, also sets bit `row` of masks[k] for every selected k.  Sets bit 0
-// of *error if the selection did not produce exactly p ids.  COHERENT reads
-// keys written by other workgroups of the running kernel.
+// One 16-byte load.  COHERENT reads data that other workgroups of the
+// running kernel wrote with device-scope stores.
+template <bool COHERENT>
+__device__ __forceinline__ uint4 sel_load4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  const auto v =
+      __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, COHERENT ? kCachePolicySc1 : 0);
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Selects p of the c keys; writes the ids ascending to out[0..p).  `keys`
+// is 16-byte aligned with room for `stride` floats (stride >= c, a multiple
+// of 4).  With `masks`, also sets bit `row` of masks[k] for every selected
+// k.  Sets bit 0 of *error if the selection did not produce exactly p ids.
+// Needs NT * IPT >= c.
 template <int NT, int IPT, bool COHERENT>
-__device__ void select_block(const float* keys, int c, int p, int32_t* out, uint64_t* masks,
-                             int row, uint32_t* error, SelSmem& sm) {
+__device__ void select_block(const float* keys, int c, int stride, int p, int32_t* out,
+                             uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
+  static_assert(IPT % 4 == 0 && IPT <= 32, "items per thread");
   constexpr int NW = NT / kWave;
-  constexpr int BPT = kSelBins / NT;                  // bins per thread
-  constexpr int WPT = (FH_MAX_C / 32 + NT - 1) / NT;  // bitmap words per thread
+  constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t >> 6;
+  const int k0 = t * IPT;
   int parity = 0;
 
-  // ---- keys, block min / max --------------------------------------------------
+  // ---- keys, block min / max ------------------------------------------------
   FH_SEL_TRACE(0);
   uint32_t u[IPT];
+  {
+    const __amdgpu_buffer_rsrc_t rs = sel_rsrc(keys, (uint32_t)stride * 4u);
+#pragma unroll
+    for (int q = 0; q < IPT / 4; ++q) {
+      const uint4 v = sel_load4<COHERENT>(rs, (uint32_t)(k0 + 4 * q) * 4u);
+      u[4 * q] = v.x;
+      u[4 * q + 1] = v.y;
+      u[4 * q + 2] = v.z;
+      u[4 * q + 3] = v.w;
+    }
+  }
+  for (int i = t; i < kSelBins; i += NT) sm.hist[i] = 0;
+  for (int i = t; i < FH_MAX_C / 32; i += NT) sm.chosen[i] = 0u;
+  if (t < 8) sm.misc[t] = 0;
+  const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
   float lmax = -INFINITY, lmin = INFINITY;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    const int k = t + j * NT;
-    const float f = k < c ? sel_load<COHERENT>(keys + k) : -INFINITY;
+    const float f = __uint_as_float(u[j]);
     u[j] = ordered_u32(f);
-    if (k < c) { lmax = fmaxf(lmax, f); lmin = fminf(lmin, f); }
+    if (j < nvalid) {
+      lmax = fmaxf(lmax, f);
+      lmin = fminf(lmin, f);
+    }
   }
-  for (int i = t; i < kSelBins; i += NT) sm.hist[i] = 0;
-  for (int i = t; i < FH_MAX_C / 32; i += NT) { sm.bits[i] = 0u; sm.sel[i] = 0u; }
-  if (t < 8) sm.misc[t] = 0;
   FH_SEL_TRACE(1);
   lmax = wave_max_dpp(lmax);
   lmin = wave_min_dpp(lmin);
-  if (lane == 0) { sm.fmax[wave] = lmax; sm.fmin[wave] = lmin; }
+  if (lane == 0) {
+    sm.fmax[wave] = lmax;
+    sm.fmin[wave] = lmin;
+  }
   __syncthreads();
   FH_SEL_TRACE(2);
   float fmax = sm.fmax[0], fmin = sm.fmin[0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) { fmax = fmaxf(fmax, sm.fmax[w]); fmin = fminf(fmin, sm.fmin[w]); }
+  for (int w = 1; w < NW; ++w) {
+    fmax = fmaxf(fmax, sm.fmax[w]);
+    fmin = fminf(fmin, sm.fmin[w]);
+  }
   const float range = fmax - fmin;
   const float scale = (float)kSelBins / range;
   const bool flat = !(range > 0.0f) || !(scale < INFINITY);
-  auto bin_of = [&](uint32_t uu) -> int {
-    const int b = (int)((sel_from_ordered(uu) - fmin) * scale);
-    return b < 0 ? 0 : (b < kSelBins - 1 ? b : kSelBins - 1);
-  };
 
   // ---- histogram and the boundary bin -----------------------------------------
-  int beta = 0, ngt = 0;
+  uint32_t bins[IPT / 2];  // this thread's item bins, two 16-bit bins per word
+  int beta = 0, ngt = 0, nb = 0;
   if (!flat) {
 #pragma unroll
-    for (int j = 0; j < IPT; ++j)
-      if (t + j * NT < c) atomicAdd(&sm.hist[bin_of(u[j])], 1);
+    for (int j = 0; j < IPT; j += 2) {
+      int b0 = (int)((sel_from_ordered(u[j]) - fmin) * scale);
+      int b1 = (int)((sel_from_ordered(u[j + 1]) - fmin) * scale);
+      b0 = b0 < 0 ? 0 : (b0 < kSelBins - 1 ? b0 : kSelBins - 1);
+      b1 = b1 < 0 ? 0 : (b1 < kSelBins - 1 ? b1 : kSelBins - 1);
+      bins[j / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      if (j < nvalid) atomicAdd(&sm.hist[b0], 1);
+      if (j + 1 < nvalid) atomicAdd(&sm.hist[b1], 1);
+    }
     __syncthreads();
     FH_SEL_TRACE(3);
     int hb[BPT];
@@ -134,227 +174,202 @@ __device__ void select_block(const float* keys, int c, int p, int32_t* out, uint
     if (acc < p && p <= incl) {
 #pragma unroll
       for (int q = 0; q < BPT; ++q) {
-        if (acc + hb[q] >= p) { sm.misc[0] = kSelBins - 1 - t * BPT - q; sm.misc[1] = acc; break; }
+        if (acc + hb[q] >= p) {
+          sm.misc[0] = kSelBins - 1 - t * BPT - q;
+          sm.misc[1] = acc;
+          sm.misc[2] = hb[q];
+          break;
+        }
         acc += hb[q];
       }
     }
     __syncthreads();
     beta = sm.misc[0];
     ngt = sm.misc[1];
+    nb = sm.misc[2];
+  } else {
+#pragma unroll
+    for (int j = 0; j < IPT / 2; ++j) bins[j] = 0u;
+    nb = c;
   }
   FH_SEL_TRACE(4);
-  const int need = p - ngt;
-  const int m = flat ? c : sm.hist[beta];
+  int need = p - ngt;  // ids still to take from the boundary bin
 
-  uint32_t candmask = 0u, abovemask = 0u, chosenmask = 0u;
+  uint32_t above = 0u, cand = 0u;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    if (t + j * NT >= c) continue;
-    if (flat) { candmask |= 1u << j; continue; }
-    const int b = bin_of(u[j]);
-    if (b > beta) abovemask |= 1u << j;
-    else if (b == beta) candmask |= 1u << j;
+    if (j >= nvalid) continue;
+    const int b = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+    if (b > beta) above |= 1u << j;
+    else if (b == beta) cand |= 1u << j;
   }
 
-  // ---- exact resolution of the boundary bin -----------------------------------
-  if (need == m) {
-    chosenmask = candmask;
-  } else if (m <= kSelCandMax) {
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      if (candmask & (1u << j)) {
-        const int pos = atomicAdd(&sm.misc[2], 1);
-        sm.cu[pos] = u[j];
-        sm.ck[pos] = t + j * NT;
-      }
-    }
+  // ---- large boundary bin: 8-bit radix passes on the key bits -----------------
+  // (block-uniform control flow: need and nb are the same in every thread)
+  for (int shift = 24; need < nb && nb > kSelWaveMax && shift >= 0; shift -= 8) {
     __syncthreads();
-    for (int i = t; i < m; i += NT) {
-      const uint32_t uu = sm.cu[i];
-      const int kk = sm.ck[i];
-      int rank = 0;
-      for (int q = 0; q < m; ++q) {
-        const uint32_t uq = sm.cu[q];
-        rank += (uq > uu) || (uq == uu && sm.ck[q] < kk);
-      }
-      if (rank < need) atomicOr(&sm.bits[kk >> 5], 1u << (kk & 31));
-    }
+    if (t < 256) sm.hist[t] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const int k = t + j * NT;
-      if ((candmask & (1u << j)) && ((sm.bits[k >> 5] >> (k & 31)) & 1u)) chosenmask |= 1u << j;
-    }
-  } else {
-    // heavily tied keys: 8-bit radix select on the order-preserving bits
-    uint32_t prefix = 0u, pmask = 0u;
-    int rem = need;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();
-      if (t < 256) sm.hist[t] = 0;
-      __syncthreads();
+    for (int j = 0; j < IPT; ++j)
+      if ((cand >> j) & 1u) atomicAdd(&sm.hist[(u[j] >> shift) & 255u], 1);
+    __syncthreads();
+    if (wave == 0) {
+      int dq[4];
 #pragma unroll
-      for (int j = 0; j < IPT; ++j)
-        if ((candmask & (1u << j)) && (u[j] & pmask) == prefix)
-          atomicAdd(&sm.hist[(u[j] >> shift) & 255u], 1);
-      __syncthreads();
-      if (wave == 0) {
-        int dq[4];
+      for (int q = 0; q < 4; ++q) dq[q] = sm.hist[255 - 4 * lane - q];
+      const int cnt = dq[0] + dq[1] + dq[2] + dq[3];
+      const int incl = wave_incl_scan_dpp(cnt);
+      int acc = incl - cnt;
+      if (acc < need && need <= incl) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dq[q] = sm.hist[255 - 4 * lane - q];
-        const int cnt = dq[0] + dq[1] + dq[2] + dq[3];
-        const int incl = wave_incl_scan_dpp(cnt);
-        int acc = incl - cnt;
-        if (acc < rem && rem <= incl) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (acc + dq[q] >= rem) { sm.misc[3] = 255 - 4 * lane - q; sm.misc[4] = acc; break; }
-            acc += dq[q];
+        for (int q = 0; q < 4; ++q) {
+          if (acc + dq[q] >= need) {
+            sm.misc[3] = 255 - 4 * lane - q;
+            sm.misc[4] = acc;
+            sm.misc[5] = dq[q];
+            break;
           }
+          acc += dq[q];
         }
       }
-      __syncthreads();
-      rem -= sm.misc[4];
-      prefix |= (uint32_t)sm.misc[3] << shift;
-      pmask |= 0xFFu << shift;
-    }
-    // exact ties at the threshold as a bitmap in id order
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const bool tie = ((candmask >> j) & 1u) && u[j] == prefix;
-      const uint64_t bal = __ballot(tie);
-      const int k = j * NT + wave * kWave;  // first id of this wave's 64
-      if (lane == 0 && k < c) {
-        sm.bits[k >> 5] = (uint32_t)bal;
-        if ((k >> 5) + 1 < FH_MAX_C / 32) sm.bits[(k >> 5) + 1] = (uint32_t)(bal >> 32);
-      }
-      if ((candmask & (1u << j)) && u[j] > prefix) chosenmask |= 1u << j;
     }
     __syncthreads();
-    // keep the `rem` lowest tie ids
-    const int words = (c + 31) >> 5;
-    int wc = 0;
+    const uint32_t digit = (uint32_t)sm.misc[3];
+    need -= sm.misc[4];
+    nb = sm.misc[5];
 #pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int w = t * WPT + q;
-      if (w < words) wc += __popc(sm.bits[w]);
+    for (int j = 0; j < IPT; ++j) {
+      if (!((cand >> j) & 1u)) continue;
+      const uint32_t dj = (u[j] >> shift) & 255u;
+      if (dj > digit) {
+        above |= 1u << j;
+        cand &= ~(1u << j);
+      } else if (dj < digit) {
+        cand &= ~(1u << j);
+      }
     }
-    int below = sel_scan<NT>(wc, sm, parity, lane, wave) - wc;
-    uint32_t keep[WPT];
+  }
+
+  if (need >= nb) {
+    above |= cand;  // the whole boundary set is taken
+  } else if (nb <= kSelWaveMax) {
+    // ---- gather the boundary keys; wave 0 picks `need` of them ---------------
+    const int cc = __popc(cand);
+    const int wincl = wave_incl_scan_dpp(cc);
+    int base = 0;
+    if (lane == kWave - 1 && wincl > 0) base = atomicAdd(&sm.misc[6], wincl);
+    base = __shfl(base, kWave - 1, kWave) + wincl - cc;
 #pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int w = t * WPT + q;
-      keep[q] = 0u;
-      if (w >= words) continue;
-      uint32_t bw = sm.bits[w];
-      while (bw) {
-        const int bit = __ffs(bw) - 1;
-        if (below < rem) keep[q] |= 1u << bit;
-        ++below;
-        bw &= bw - 1u;
+    for (int j = 0; j < IPT; ++j) {
+      if ((cand >> j) & 1u) {
+        sm.cu[base] = u[j];
+        sm.ck[base] = k0 + j;
+        ++base;
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int w = t * WPT + q;
-      if (w < words) sm.bits[w] = keep[q];
+    if (wave == 0) {
+      const bool live = lane < nb;
+      const uint32_t uu = live ? sm.cu[lane] : 0u;
+      const uint32_t kk = live ? (uint32_t)sm.ck[lane] : 0u;
+      uint64_t L = __ballot(live);
+      uint64_t pick = 0ull;
+      int rem = need;
+      // keys descending: a set bit ranks higher
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint64_t ones = __ballot((uu >> bit) & 1u) & L;
+        const int n1 = __popcll(ones);
+        if (n1 == 0 || ones == L) continue;
+        if (n1 >= rem) {
+          L = ones;
+        } else {
+          pick |= ones;
+          rem -= n1;
+          L &= ~ones;
+        }
+      }
+      // equal keys: ids ascending, a clear bit ranks higher
+      for (int bit = 15; bit >= 0; --bit) {
+        const uint64_t zeros = __ballot(((kk >> bit) & 1u) == 0u) & L;
+        const int n0 = __popcll(zeros);
+        if (n0 == 0 || zeros == L) continue;
+        if (n0 >= rem) {
+          L = zeros;
+        } else {
+          pick |= zeros;
+          rem -= n0;
+          L &= ~zeros;
+        }
+      }
+      pick |= L;  // one id is left, the last one needed
+      if ((pick >> lane) & 1ull) atomicOr(&sm.chosen[kk >> 5], 1u << (kk & 31));
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      const int k = t + j * NT;
-      if ((candmask & (1u << j)) && u[j] == prefix && ((sm.bits[k >> 5] >> (k & 31)) & 1u))
-        chosenmask |= 1u << j;
+      const int k = k0 + j;
+      if (((cand >> j) & 1u) && ((sm.chosen[k >> 5] >> (k & 31)) & 1u)) above |= 1u << j;
+    }
+  } else {
+    // ---- more than kSelWaveMax exactly equal keys: lowest ids first ----------
+    const int cc = __popc(cand);
+    int r = sel_scan<NT>(cc, sm, parity, lane, wave) - cc;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      if ((cand >> j) & 1u) {
+        if (r < need) above |= 1u << j;
+        ++r;
+      }
     }
   }
   FH_SEL_TRACE(5);
 
-  // ---- selection bitmap in id order, ranks, ascending ids -----------------------
+  // ---- ascending ids -------------------------------------------------------------
+  const int cnt = __popc(above);
+  const int incl = sel_scan<NT>(cnt, sm, parity, lane, wave);
+  FH_SEL_TRACE(6);
+  int rank = incl - cnt;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    const bool sj = ((abovemask | chosenmask) >> j) & 1u;
-    const uint64_t bal = __ballot(sj);
-    const int k = j * NT + wave * kWave;
-    if (lane == 0 && k < c) {
-      sm.sel[k >> 5] = (uint32_t)bal;
-      if ((k >> 5) + 1 < FH_MAX_C / 32) sm.sel[(k >> 5) + 1] = (uint32_t)(bal >> 32);
-    }
-  }
-  __syncthreads();
-  FH_SEL_TRACE(6);
-  const int words = (c + 31) >> 5;
-  uint32_t mw[WPT];
-  int wc = 0;
-#pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    const int w = t * WPT + q;
-    mw[q] = w < words ? sm.sel[w] : 0u;
-    wc += __popc(mw[q]);
-  }
-  const int incl = sel_scan<NT>(wc, sm, parity, lane, wave);
-  FH_SEL_TRACE(7);
-  int rank = incl - wc;
-#pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    uint32_t bw = mw[q];
-    while (bw) {
-      const int k = ((t * WPT + q) << 5) + __ffs(bw) - 1;
+    if ((above >> j) & 1u) {
       if (rank < p) {
-        out[rank] = k;
-        if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k), 1ull << row);
+        out[rank] = k0 + j;
+        if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k0 + j), 1ull << row);
       }
       ++rank;
-      bw &= bw - 1u;
     }
   }
-  FH_SEL_TRACE(8);
+  FH_SEL_TRACE(7);
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);
 }
 
 // The clusters whose row mask is non-zero, ascending, into ulist / ucount.
-// Masks are read coherently (they were set by atomics of other workgroups).
+// Masks are read coherently (they were set by atomics of other workgroups);
+// thread t owns the IPT consecutive clusters [t*IPT, t*IPT + IPT).  `masks`
+// is 16-byte aligned with room for c rounded up to even entries.
 template <int NT, int IPT>
 __device__ void compact_masks_block(const uint64_t* masks, int c, int32_t* ulist, int32_t* ucount,
                                     SelSmem& sm) {
-  constexpr int WPT = (FH_MAX_C / 32 + NT - 1) / NT;
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t >> 6;
+  const int k0 = t * IPT;
   int parity = 0;
-  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs = sel_rsrc(masks, (uint32_t)((c + 1) & ~1) * 8u);
+  uint32_t nz = 0u;
 #pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    const int k = t + j * NT;
-    const bool nz = k < c && __hip_atomic_load(masks + k, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT) != 0ull;
-    const uint64_t bal = __ballot(nz);
-    const int k0 = j * NT + wave * kWave;
-    if (lane == 0 && k0 < c) {
-      sm.sel[k0 >> 5] = (uint32_t)bal;
-      if ((k0 >> 5) + 1 < FH_MAX_C / 32) sm.sel[(k0 >> 5) + 1] = (uint32_t)(bal >> 32);
-    }
+  for (int q = 0; q < IPT / 2; ++q) {
+    const uint4 v = sel_load4<true>(rs, (uint32_t)(k0 + 2 * q) * 8u);
+    if ((v.x | v.y) && k0 + 2 * q < c) nz |= 1u << (2 * q);
+    if ((v.z | v.w) && k0 + 2 * q + 1 < c) nz |= 1u << (2 * q + 1);
   }
-  __syncthreads();
-  const int words = (c + 31) >> 5;
-  uint32_t mw[WPT];
-  int wc = 0;
+  const int cnt = __popc(nz);
+  const int incl = sel_scan<NT>(cnt, sm, parity, lane, wave);
+  int pos = incl - cnt;
 #pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    const int w = t * WPT + q;
-    mw[q] = w < words ? sm.sel[w] : 0u;
-    wc += __popc(mw[q]);
-  }
-  const int incl = sel_scan<NT>(wc, sm, parity, lane, wave);
-  int pos = incl - wc;
-#pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    uint32_t bw = mw[q];
-    while (bw) {
-      ulist[pos++] = ((t * WPT + q) << 5) + __ffs(bw) - 1;
-      bw &= bw - 1u;
-    }
-  }
+  for (int j = 0; j < IPT; ++j)
+    if ((nz >> j) & 1u) ulist[pos++] = k0 + j;
   if (t == NT - 1) *ucount = incl;
 }
 

@@ -10,23 +10,24 @@ constexpr int kSelThreads = 1024;
 template <int IPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelSmem sm;
-  __shared__ int s_last;
   const int r = blockIdx.x;
-  select_block<kSelThreads, IPT, false>(a.keys + (int64_t)r * a.key_stride, a.c, a.p,
-                                        a.sel + (int64_t)r * a.sel_stride, a.masks, r, a.error,
-                                        sm);
+  select_block<kSelThreads, IPT, false>(a.keys + (int64_t)r * a.key_stride, a.c,
+                                        (int)a.key_stride, a.p, a.sel + (int64_t)r * a.sel_stride,
+                                        a.masks, r, a.error, sm);
   if (!a.counter) return;
-  // the last row to finish compacts the union of the selected clusters
+  // row 0's workgroup compacts the union of the selected clusters once every
+  // other row has set its mask bits
   __builtin_amdgcn_s_waitcnt(0);  // this wave's mask updates have been performed
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == gridDim.x - 1;
+  if (r != 0) {
+    if (threadIdx.x == 0) arrive(a.counter, r);
+    return;
+  }
+  if (threadIdx.x < kWave) {
+    const bool ok = wait_arrivals(a.counter, gridDim.x - 1, threadIdx.x);
+    if (!ok && threadIdx.x == 0 && a.error) atomicOr(a.error, 2u);
   }
   __syncthreads();
-  if (!s_last) return;
-  if (threadIdx.x == 0) __hip_atomic_exchange(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   compact_masks_block<kSelThreads, IPT>(a.masks, a.c, a.ulist, a.ucount, sm);
 }
 
@@ -34,9 +35,7 @@ hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   const int ipt = (a.c + kSelThreads - 1) / kSelThreads;
   const dim3 grid(B), block(kSelThreads);
-  if (ipt <= 1) hipExtLaunchKernelGGL(select_kernel<1>, grid, block, 0, s, e0, e1, 0, a);
-  else if (ipt <= 2) hipExtLaunchKernelGGL(select_kernel<2>, grid, block, 0, s, e0, e1, 0, a);
-  else if (ipt <= 4) hipExtLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, e0, e1, 0, a);
+  if (ipt <= 4) hipExtLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, e0, e1, 0, a);
   else if (ipt <= 8) hipExtLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, e0, e1, 0, a);
   else if (ipt <= 16) hipExtLaunchKernelGGL(select_kernel<16>, grid, block, 0, s, e0, e1, 0, a);
   else if (ipt <= 32) hipExtLaunchKernelGGL(select_kernel<32>, grid, block, 0, s, e0, e1, 0, a);

@@ -12,11 +12,17 @@
 // combine their sums.  Each key (the score, or score / tau + Gumbel noise in
 // sampling mode) is stored with a coherent store.
 //
-// The last block of a batch row to finish (one device-scope counter per
-// row; no block ever waits for another) reads the row's c keys and runs the
+// Workgroup 0 of a batch row waits, after its own share, until every other
+// workgroup of the row has stored its keys (arrival counters spread over
+// separate lines, see fh_device.h), then reads the row's c keys and runs the
 // block-level selection, writing the p selected cluster ids in ascending
-// order for stage 2.  The counter is reset by that block.
+// order for stage 2.
 #include "fh_select.h"
+
+// Optional timeline hook for measurement builds (empty in the library).
+#ifndef FH_S1_TRACE
+#define FH_S1_TRACE(slot)
+#endif
 
 namespace fh {
 
@@ -30,15 +36,15 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   constexpr int EPC = CK::kElems;
   __shared__ SelSmem sm;
   __shared__ float s_h[INT4 ? FH_MAX_ROW_BYTES / 2 : 1];
-  __shared__ int s_last;
   const int r = blockIdx.y;
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint8_t* hrow = a.H + (int64_t)r * a.h_bytes;
+  FH_S1_TRACE(0);
   const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
   float* keys = a.keys + (int64_t)r * a.key_stride;
-  float* dbg = a.dbg_scores ? a.dbg_scores + (int64_t)r * a.key_stride : nullptr;
+  float* dbg = a.dbg_scores ? a.dbg_scores + (int64_t)r * a.c : nullptr;
 
   auto publish = [&](int row, float score) {
     const float key =
@@ -113,21 +119,27 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
       if (q == 0 && row < a.c) publish(row, acc);
     }
   }
+  FH_S1_TRACE(1);
   if constexpr (!SELECT) return;
 
-  // ---- the last block of this batch row selects --------------------------
+  // ---- workgroup 0 of this batch row selects, once every other workgroup
+  // of the row has stored its keys -----------------------------------------
+  uint32_t* ctr = a.counters + (int64_t)r * kArriveWords;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's key stores have been performed
   __syncthreads();
-  if (t == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(a.counters + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == gridDim.x - 1;
+  if (blockIdx.x != 0) {
+    if (t == 0) arrive(ctr, blockIdx.x);
+    return;
+  }
+  if (wave == 0) {
+    const bool ok = wait_arrivals(ctr, gridDim.x - 1, lane);
+    if (!ok && lane == 0 && a.error) atomicOr(a.error, 2u);
   }
   __syncthreads();
-  if (!s_last) return;
-  if (t == 0) __hip_atomic_exchange(a.counters + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  select_block<kS1Threads, IPT, true>(keys, a.c, a.p, a.sel + (int64_t)r * a.sel_stride, a.masks,
-                                      r, a.error, sm);
+  FH_S1_TRACE(2);
+  select_block<kS1Threads, IPT, true>(keys, a.c, (int)a.key_stride, a.p,
+                                      a.sel + (int64_t)r * a.sel_stride, a.masks, r, a.error, sm);
+  FH_S1_TRACE(3);
 }
 
 int stage1_blocks(const Stage1Args& a, bool int4) {
@@ -143,7 +155,7 @@ static hipError_t launch_nch(const Stage1Args& a, int B, hipStream_t s, const Ti
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   const dim3 grid(stage1_blocks(a, INT4), B), block(kS1Threads);
   if (!a.select) {
-    hipExtLaunchKernelGGL((stage1_kernel<TE, NCH, 1, INT4, false>), grid, block, 0, s, e0, e1, 0,
+    hipExtLaunchKernelGGL((stage1_kernel<TE, NCH, 4, INT4, false>), grid, block, 0, s, e0, e1, 0,
                           a);
     return hipGetLastError();
   }
@@ -154,8 +166,6 @@ static hipError_t launch_nch(const Stage1Args& a, int B, hipStream_t s, const Ti
                           0, a);                                                              \
     return hipGetLastError();                                                                 \
   }
-  FH_S1_IPT(1)
-  FH_S1_IPT(2)
   FH_S1_IPT(4)
   FH_S1_IPT(8)
   FH_S1_IPT(16)
