@@ -36,6 +36,14 @@ struct fh_handle {
   int32_t* ucount = nullptr;
   uint64_t* part_best = nullptr;    // stage-2 partials, grid x max_batch
   float2* part_lse = nullptr;
+  // single-launch batch-1 decode
+  int num_cu = 0;
+  float* b1_keys = nullptr;         // 2 x key_stride(c), all bits set between launches
+  uint64_t* b1_slots = nullptr;     // 2 x kMaxGrid, zero between launches
+  float2* b1_lse = nullptr;         // kMaxGrid
+  int32_t* b1_sel = nullptr;        // 2 x kDecodeB1MaxP, -1 between launches
+  uint64_t b1_launches = 0;         // host copy of the device epoch
+  uint32_t* b1_epoch = nullptr;     // launch counter (picks the buffer set)
 
 
   int64_t bytes = 0;
@@ -160,6 +168,7 @@ int check_device(const fh_handle* h) {
 int prepare_impl(const fh_desc* ds, fh_handle* h) {
   hipStream_t s = static_cast<hipStream_t>(ds->stream);
   FH_TRY(hipGetDevice(&h->device));
+  FH_TRY(hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device));
   const int64_t v = ds->v;
   const int c = ds->c, b = ds->b, d = ds->d;
   FH_TRY(alloc(h, &h->c2t, (size_t)v * 4));
@@ -204,6 +213,15 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(alloc(h, &h->part_best, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(hipMemsetAsync(h->sel_counter, 0, (size_t)kArriveWords * 4, s));
+  FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * key_stride(c) * 4));
+  FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * key_stride(c) * 4, s));
+  FH_TRY(alloc(h, &h->b1_slots, (size_t)2 * kMaxGrid * 8));
+  FH_TRY(hipMemsetAsync(h->b1_slots, 0, (size_t)2 * kMaxGrid * 8, s));
+  FH_TRY(alloc(h, &h->b1_lse, (size_t)kMaxGrid * 8));
+  FH_TRY(alloc(h, &h->b1_sel, (size_t)2 * kDecodeB1MaxP * 4));
+  FH_TRY(hipMemsetAsync(h->b1_sel, 0xFF, (size_t)2 * kDecodeB1MaxP * 4, s));
+  FH_TRY(alloc(h, &h->b1_epoch, 4));
+  FH_TRY(hipMemsetAsync(h->b1_epoch, 0, 4, s));
   FH_TRY(hipMemsetAsync(h->ucount, 0, 4, s));
   FH_TRY(hipStreamSynchronize(s));
   return FH_OK;
@@ -270,6 +288,66 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.masks = nullptr;
   s1.error = h->error;
 
+  // stage-2 gather over the cluster-major copy (GEMV paths)
+  auto gather_args = [&]() {
+    RowdotArgs a{};
+    a.base = h->Ec;
+    a.row_bytes = h->row_bytes;
+    a.nchunk = nchunk;
+    a.H = static_cast<const uint8_t*>(H);
+    a.h_bytes = h->row_bytes;
+    a.nrows = (int64_t)p * h->b;
+    a.sel = h->sel;
+    a.sel_stride = h->max_p;
+    a.c2t = h->c2t;
+    a.b = h->b;
+    a.nclusters = h->c;
+    a.part_best = h->row_best;
+    a.counters = h->counters;
+    a.lse_part = h->lse_part;
+    a.out_tokens = out;
+    a.out_lse = out_lse;
+    a.dbg_ids = dbg ? dbg->cand_ids : nullptr;
+    a.dbg_logits = dbg ? dbg->cand_logits : nullptr;
+    a.dbg_stride = (int64_t)p * h->b;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    return a;
+  };
+
+  // batch 1: the whole step in one launch when the shape allows it
+  if (B == 1 && !batched && s1.select) {
+    DecodeB1Args f{};
+    f.s1 = s1;
+    f.s2 = gather_args();
+    f.s1.keys = h->b1_keys;
+    f.s2.part_best = h->b1_slots;
+    f.s2.lse_part = h->b1_lse;
+    f.sel = h->b1_sel;
+    f.epoch = h->b1_epoch;
+    f.slot_stride = kMaxGrid;
+    const int grid = decode_b1_grid(f, int4, h->num_cu);
+    if (grid > 0 && grid <= kMaxGrid) {
+      FH_TRY(launch_decode_b1(f, h->dtype, int4, grid, s, t1));
+      if (t2) {  // selection and stage 2 ran inside the one launch
+        (void)hipEventRecord(t2->start, s);
+        (void)hipEventRecord(t2->stop, s);
+        (void)hipEventRecord(t3->start, s);
+        (void)hipEventRecord(t3->stop, s);
+      }
+      if (dbg && dbg->clusters) {
+        // the selection of this launch sits in the set picked by the epoch
+        // before it; both sets are read back and the host-side epoch says
+        // which (one launch in flight per handle)
+        const int32_t* src = h->b1_sel + (size_t)(h->b1_launches & 1) * kDecodeB1MaxP;
+        FH_TRY(hipMemcpyAsync(dbg->clusters, src, (size_t)p * 4, hipMemcpyDeviceToDevice, s));
+      }
+      ++h->b1_launches;
+      return FH_OK;
+    }
+  }
+
   if (batched) {
     FH_TRY(launch_stage1_mfma(s1, int4, B, s, t1));
   } else {
@@ -333,29 +411,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     return FH_OK;
   }
   {
-    RowdotArgs a{};
-    a.base = h->Ec;
-    a.row_bytes = h->row_bytes;
-    a.nchunk = nchunk;
-    a.H = static_cast<const uint8_t*>(H);
-    a.h_bytes = h->row_bytes;
-    a.nrows = (int64_t)p * h->b;
-    a.sel = h->sel;
-    a.sel_stride = h->max_p;
-    a.c2t = h->c2t;
-    a.b = h->b;
-    a.nclusters = h->c;
-    a.part_best = h->row_best;
-    a.counters = h->counters;
-    a.lse_part = h->lse_part;
-    a.out_tokens = out;
-    a.out_lse = out_lse;
-    a.dbg_ids = dbg ? dbg->cand_ids : nullptr;
-    a.dbg_logits = dbg ? dbg->cand_logits : nullptr;
-    a.dbg_stride = (int64_t)p * h->b;
-    a.sample = sample;
-    a.inv_tau = inv_tau;
-    a.seeds = seeds;
+    RowdotArgs a = gather_args();
     const int gx = rowdot_grid(a.nrows, nchunk, kRowGather);
     if (gx > kMaxGrid) return FH_ERR_UNSUPPORTED;
     FH_TRY(launch_rowdot(a, kRowGather, h->dtype, B, gx, s, t3));

@@ -118,6 +118,24 @@ struct Stage1Args {
   uint32_t* error;
 };
 
+// The single-launch batch-1 decode: stage 1 + selection (s1) and stage 2
+// gather + decode (s2, kRowGather).  Two buffer sets, picked by the parity
+// of the device word *epoch (advanced by every launch):
+//   s1.keys       2 x key_stride floats, every key pending (all bits set)
+//                 before the first launch;
+//   sel           2 x kDecodeB1MaxP int32, all -1 before the first launch;
+//   s2.part_best  2 x slot_stride u64 slots, zero before the first launch;
+//   s2.lse_part   slot_stride lse partials.
+// Launches keep them consistent.  The selection of the launch is copied to
+// s1.sel (plain) only for the debug output.
+constexpr int kDecodeB1MaxP = 2048;
+struct DecodeB1Args {
+  Stage1Args s1;
+  RowdotArgs s2;
+  int32_t* sel;
+  uint32_t* epoch;
+  int64_t slot_stride;
+};
 
 // Optional events recorded exactly around one kernel (hipExtLaunchKernel).
 struct Timing {
@@ -131,6 +149,10 @@ hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing
 hipError_t launch_stage1(const Stage1Args& a, int dtype, bool int4, int B, hipStream_t s,
                          const Timing* tm = nullptr);
 bool stage1_selects(int c);
+// grid of the single-launch batch-1 decode (0: not available for this shape)
+int decode_b1_grid(const DecodeB1Args& a, bool int4, int num_cu);
+hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid,
+                            hipStream_t s, const Timing* tm = nullptr);
 hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
                                  const int32_t* c2t, int c, int b, void* C, hipStream_t s);
 bool batched_supported(int dtype, int d, int B, bool int4);

@@ -13,8 +13,7 @@
 // candidate rows of a cluster are one contiguous block, and C2T is read only
 // for the token ids (in parallel with the row loads, not in their address
 // chain).
-#include "fh_device.h"
-#include "fh_internal.h"
+#include "fh_rows.h"
 
 // Optional timeline hook for measurement builds (empty in the library).
 #ifndef FH_S2_TRACE
@@ -28,175 +27,24 @@ constexpr int kRowdotWaves = kRowdotThreads / kWave;
 
 template <typename TE, int NCH, int R, int MODE>
 __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
-  using CK = Chunk<TE>;
-  constexpr int EPC = CK::kElems;
+  __shared__ MergeSmem<kRowdotThreads> ms;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = blockIdx.y;
   FH_S2_TRACE(0);
-
-  float hreg[NCH][EPC];
-  {
-    const uint8_t* hrow = a.H + (int64_t)r * a.h_bytes;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = lane + kWave * i;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (ch < a.nchunk) w = *reinterpret_cast<const uint4*>(hrow + (int64_t)ch * 16);
-      CK::unpack(w, hreg[i]);
-    }
-  }
+  float hreg[NCH][Chunk<TE>::kElems];
+  load_h<TE, NCH>(a.H + (int64_t)r * a.h_bytes, a.nchunk, lane, hreg);
   const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
-  const int64_t ngroups = (a.nrows + R - 1) / R;
-  const int64_t wstride = (int64_t)gridDim.x * kRowdotWaves;
   uint64_t best = 0;
   Lse lse = lse_empty();
-
-  for (int64_t g = (int64_t)blockIdx.x * kRowdotWaves + wave; g < ngroups; g += wstride) {
-    const int64_t row0 = g * R;
-    int64_t phys[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      int64_t i = row0 + rr;
-      if (i >= a.nrows) i = a.nrows - 1;  // tail: reread the last row, result dropped
-      if constexpr (MODE == kRowGather) {
-        const int64_t j = i / a.b;
-        int64_t k = a.sel[(int64_t)r * a.sel_stride + j];
-        k = k < 0 ? 0 : (k >= a.nclusters ? a.nclusters - 1 : k);  // never leave the table
-        phys[rr] = k * a.b + (i - j * a.b);  // row of the cluster-major copy
-      } else {
-        phys[rr] = i;
-      }
-    }
-    uint4 data[R][NCH];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      const uint8_t* rowp = a.base + phys[rr] * a.row_bytes;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int ch = lane + kWave * i;
-        data[rr][i] = (ch < a.nchunk)
-                          ? *reinterpret_cast<const uint4*>(rowp + (int64_t)ch * 16)
-                          : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    // token ids of the gathered rows (lane rr fetches row rr's id)
-    int64_t myphys = phys[0];
-#pragma unroll
-    for (int rr = 1; rr < R; ++rr)
-      if (lane == rr) myphys = phys[rr];
-    uint32_t mytok = (uint32_t)myphys;
-    if constexpr (MODE == kRowGather) {
-      if (lane < R) mytok = (uint32_t)a.c2t[myphys];
-    }
-    float acc[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      float s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) s = CK::dot(data[rr][i], hreg[i], s);
-      acc[rr] = wave_sum(s);
-    }
-    float mine = acc[0];
-#pragma unroll
-    for (int rr = 1; rr < R; ++rr)
-      if (lane == rr) mine = acc[rr];
-    const int64_t myrow = row0 + lane;
-    const bool valid = lane < R && myrow < a.nrows;
-    {
-      if (valid) {
-        const float x = mine * a.inv_tau;
-        const float kx = a.sample ? x + gumbel(seed, kStreamToken, mytok) : mine;
-        const uint64_t key = decode_key(kx, mytok);
-        best = key > best ? key : best;
-        if (a.out_lse) lse = lse_add(lse, x);
-        if (a.dbg_logits) {
-          a.dbg_ids[(int64_t)r * a.dbg_stride + myrow] = (int32_t)mytok;
-          a.dbg_logits[(int64_t)r * a.dbg_stride + myrow] = mine;
-        }
-      }
-    }
-  }
-  // ---- block reduction; workgroup 0 of this batch row finishes -----------
-  // Every workgroup stores its partial (best key, lse pair) into its own slot
-  // with device-scope stores, waits for them to complete and counts itself
-  // arrived (spread counters, fh_device.h); workgroup 0, after its own share,
-  // waits for all arrivals and folds the partials in a fixed order.  No
-  // same-address atomics, no L2 write-back or invalidate on this path.
-  __shared__ uint64_t s_best[kRowdotThreads];
-  __shared__ float2 s_lse[kRowdotThreads];
+  dot_rows<TE, NCH, R, MODE>(a, r, a.sel + (int64_t)r * a.sel_stride, hreg, seed, lane,
+                                    (int64_t)blockIdx.x * kRowdotWaves + wave,
+                                    (int64_t)gridDim.x * kRowdotWaves, best, lse);
   FH_S2_TRACE(1);
-  best = wave_max_u64(best);
-  if (a.out_lse) lse = wave_lse(lse);
-  if (lane == 0) {
-    s_best[wave] = best;
-    s_lse[wave] = make_float2(lse.m, lse.s);
+  // workgroup 0 of the batch row folds every workgroup's partial
+  if (merge_decode<kRowdotThreads>(a, r, gridDim.x, blockIdx.x, 0, best, lse, ms)) {
+    FH_S2_TRACE(3);
   }
-  __syncthreads();
-  uint64_t* pbest = a.part_best + (int64_t)r * gridDim.x;
-  unsigned long long* plse =
-      reinterpret_cast<unsigned long long*>(a.lse_part + (int64_t)r * gridDim.x);
-  uint32_t* ctr = a.counters + (int64_t)r * kArriveWords;
-  if (threadIdx.x == 0) {
-    uint64_t bb = s_best[0];
-    Lse ll{s_lse[0].x, s_lse[0].y};
-    for (int w = 1; w < kRowdotWaves; ++w) {
-      bb = s_best[w] > bb ? s_best[w] : bb;
-      ll = lse_merge(ll, Lse{s_lse[w].x, s_lse[w].y});
-    }
-    if (blockIdx.x != 0) {
-      __hip_atomic_store(pbest + blockIdx.x, bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.out_lse) {
-        const unsigned long long packed =
-            ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
-        __hip_atomic_store(plse + blockIdx.x, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // the partial is visible device-wide
-      arrive(ctr, blockIdx.x);
-    } else {
-      s_best[kRowdotThreads - 1] = bb;  // workgroup 0's own partial
-      s_lse[kRowdotThreads - 1] = make_float2(ll.m, ll.s);
-    }
-  }
-  if (blockIdx.x != 0) return;
-  __syncthreads();
-  const uint64_t own_best = s_best[kRowdotThreads - 1];
-  const float2 own_lse = s_lse[kRowdotThreads - 1];
-  if (wave == 0) wait_arrivals(ctr, gridDim.x - 1, lane);
-  __syncthreads();
-  FH_S2_TRACE(2);
-  // deterministic fold: fixed strided order, fixed tree
-  uint64_t bb = threadIdx.x == 0 ? own_best : 0ull;
-  Lse ll = threadIdx.x == 0 ? Lse{own_lse.x, own_lse.y} : lse_empty();
-  for (int j = 1 + threadIdx.x; j < (int)gridDim.x; j += kRowdotThreads) {
-    const uint64_t x = __hip_atomic_load(pbest + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bb = x > bb ? x : bb;
-    if (a.out_lse) {
-      const unsigned long long pr =
-          __hip_atomic_load(plse + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ll = lse_merge(ll, Lse{__uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32))});
-    }
-  }
-  __syncthreads();
-  s_best[threadIdx.x] = bb;
-  s_lse[threadIdx.x] = make_float2(ll.m, ll.s);
-  __syncthreads();
-  for (int w = kRowdotThreads / 2; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
-      if (s_best[threadIdx.x + w] > s_best[threadIdx.x]) s_best[threadIdx.x] = s_best[threadIdx.x + w];
-      if (a.out_lse) {
-        const Lse x = lse_merge(Lse{s_lse[threadIdx.x].x, s_lse[threadIdx.x].y},
-                                Lse{s_lse[threadIdx.x + w].x, s_lse[threadIdx.x + w].y});
-        s_lse[threadIdx.x] = make_float2(x.m, x.s);
-      }
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    a.out_tokens[r] = (int32_t)key_id(s_best[0]);
-    if (a.out_lse) a.out_lse[r] = s_lse[0].x + logf(s_lse[0].y);
-  }
-  FH_S2_TRACE(3);
 }
 
 // Rows per wave per step: enough bytes in flight per wave without spilling.

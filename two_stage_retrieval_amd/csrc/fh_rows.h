@@ -1,0 +1,394 @@
+// Row-dot building blocks shared by the GEMV kernels (stage 1 at small
+// batch, stage 2 gather, the dense head, and the single-launch batch-1
+// decode).  A wave computes full dot products of whole rows with one hidden
+// vector: lane l owns the 16-byte chunks l, l+64, ... of a row, so a wave
+// reads each row as one contiguous, fully coalesced span, and keeps its
+// slice of h in registers for every row it visits.
+#pragma once
+#include "fh_device.h"
+#include "fh_internal.h"
+
+namespace fh {
+
+// h (one row of H) into registers: chunk lane + 64 i of the row.
+template <typename TE, int NCH>
+__device__ __forceinline__ void load_h(const uint8_t* hrow, int nchunk, int lane,
+                                       float (&hreg)[NCH][Chunk<TE>::kElems]) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int ch = lane + kWave * i;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (ch < nchunk) w = *reinterpret_cast<const uint4*>(hrow + (int64_t)ch * 16);
+    Chunk<TE>::unpack(w, hreg[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1 (notes, Overall architecture and Figure 1: inner products of h with
+// the c centroids).  Key = score, or score / tau + Gumbel noise of stream 0
+// keyed by the cluster id in sampling mode (Gumbel-top-p).  COHERENT stores
+// the keys device-coherently for a reader in the same launch.
+// ---------------------------------------------------------------------------
+// The raw bits of an unwritten key for readers that poll (a NaN that no
+// finite score produces).
+constexpr uint32_t kKeyPending = 0xFFFFFFFFu;
+
+// With `keys_next`, also marks the row pending in the key buffer of the next
+// launch (single-launch batch-1 decode).
+template <bool COHERENT>
+__device__ __forceinline__ void publish_key(const Stage1Args& a, float* keys, float* keys_next,
+                                            float* dbg, uint64_t seed, int row, float score) {
+  const float key =
+      a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
+  if constexpr (COHERENT) {
+    __hip_atomic_store(keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    keys[row] = key;
+  }
+  if (keys_next) keys_next[row] = __uint_as_float(kKeyPending);
+  if (dbg) dbg[row] = score;
+}
+
+constexpr int kS1Rows = 4;  // centroid rows per wave step (bf16 / fp32)
+
+// bf16 / fp32 centroid rows: wave w0, w0 + wstride, ... take groups of 4 rows.
+template <typename TE, int NCH, bool COHERENT>
+__device__ __forceinline__ void score_rows(const Stage1Args& a, float* keys, float* keys_next,
+                                           float* dbg, uint64_t seed,
+                                           const float (&hreg)[NCH][Chunk<TE>::kElems],
+                                           int lane, int w0, int wstride) {
+  using CK = Chunk<TE>;
+  const int ngroups = (a.c + kS1Rows - 1) / kS1Rows;
+  for (int g = w0; g < ngroups; g += wstride) {
+    const int row0 = g * kS1Rows;
+    uint4 data[kS1Rows][NCH];
+#pragma unroll
+    for (int rr = 0; rr < kS1Rows; ++rr) {
+      const int row = row0 + rr < a.c ? row0 + rr : a.c - 1;
+      const uint8_t* rowp = a.C + (int64_t)row * a.row_bytes;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ch = lane + kWave * i;
+        data[rr][i] = ch < a.nchunk ? *reinterpret_cast<const uint4*>(rowp + (int64_t)ch * 16)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float acc[kS1Rows];
+#pragma unroll
+    for (int rr = 0; rr < kS1Rows; ++rr) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) s = CK::dot(data[rr][i], hreg[i], s);
+      acc[rr] = wave_sum(s);
+    }
+    float mine = acc[0];
+#pragma unroll
+    for (int rr = 1; rr < kS1Rows; ++rr)
+      if (lane == rr) mine = acc[rr];
+    if (lane < kS1Rows && row0 + lane < a.c)
+      publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine);
+  }
+}
+
+// INT4 centroids (notes, Module 3): one 16-row group tile per wave step,
+// one coalesced 1 KB load per 128-column group; lane l owns row l mod 16 and
+// 32 of the group's columns; h comes from LDS (s_h, d floats).
+template <bool COHERENT>
+__device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* keys,
+                                                 float* keys_next, float* dbg, uint64_t seed,
+                                                 const float* s_h, int lane, int w0,
+                                                 int wstride) {
+  const int q = lane >> 4, rin = lane & 15;
+  const int G = a.groups;
+  for (int tile = w0; tile < a.ntiles; tile += wstride) {
+    const uint4* codes = reinterpret_cast<const uint4*>(a.q4) + (int64_t)tile * G * kWave + lane;
+    const uint16_t* sc = a.q4s + (int64_t)tile * G * 16 + rin;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int g = 0; g < G; ++g) {
+      const uint4 w = codes[(int64_t)g * kWave];
+      const float s = __uint_as_float((uint32_t)sc[g * 16] << 16);
+      acc = fmaf(s, int4_dot_chunk(w, s_h + g * 128 + q * 32), acc);
+    }
+    acc += __shfl_xor(acc, 16, kWave);
+    acc += __shfl_xor(acc, 32, kWave);
+    const int row = tile * 16 + rin;
+    if (q == 0 && row < a.c) publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row dots with the decode epilogue (notes, Formulas 2 and 3): stage 2 over
+// the candidate rows of the selected clusters, or the dense head over all
+// rows.  Each candidate's decode key is (ordered z or z / tau + G1(t)) << 32
+// | ~t; the running maximum and the online log-sum-exp of z / tau stay in
+// the lane that owns the row.
+// ---------------------------------------------------------------------------
+// `sel_row`: the batch row's selected clusters.  POLL: they are being
+// published by another workgroup of the running kernel; an entry reads -1
+// until it is written (bounded wait; on timeout bit 2 of *error is set).
+template <bool POLL>
+__device__ __forceinline__ int64_t selected_cluster(const int32_t* sel_row, int64_t j,
+                                                    uint32_t* error) {
+  if constexpr (!POLL) {
+    return sel_row[j];
+  } else {
+    int32_t k = -1;
+    for (int it = 0; it < kArriveSpinLimit; ++it) {
+      k = __hip_atomic_load(sel_row + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (k >= 0) return k;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (error) atomicOr(error, 4u);
+    return 0;
+  }
+}
+
+template <typename TE, int NCH, int R, int MODE, bool POLL = false>
+__device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32_t* sel_row,
+                                         const float (&hreg)[NCH][Chunk<TE>::kElems],
+                                         uint64_t seed, int lane, int64_t w0, int64_t wstride,
+                                         uint64_t& best, Lse& lse, uint32_t* error = nullptr) {
+  using CK = Chunk<TE>;
+  const int64_t ngroups = (a.nrows + R - 1) / R;
+  for (int64_t g = w0; g < ngroups; g += wstride) {
+    const int64_t row0 = g * R;
+    int64_t phys[R];
+    if constexpr (MODE == kRowGather) {
+      // one selection entry per cluster the group touches (usually one)
+      const int64_t jfirst = row0 / a.b;
+      int64_t jprev = jfirst;
+      int64_t k = selected_cluster<POLL>(sel_row, jfirst, error);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        int64_t i = row0 + rr;
+        if (i >= a.nrows) i = a.nrows - 1;  // tail: reread the last row, result dropped
+        const int64_t j = i / a.b;
+        if (j != jprev) {
+          k = selected_cluster<POLL>(sel_row, j, error);
+          jprev = j;
+        }
+        const int64_t kc = k < 0 ? 0 : (k >= a.nclusters ? a.nclusters - 1 : k);  // stay in the table
+        phys[rr] = kc * a.b + (i - j * a.b);  // row of the cluster-major copy
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int64_t i = row0 + rr;
+        phys[rr] = i < a.nrows ? i : a.nrows - 1;  // tail: reread the last row, result dropped
+      }
+    }
+    uint4 data[R][NCH];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const uint8_t* rowp = a.base + phys[rr] * a.row_bytes;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ch = lane + kWave * i;
+        data[rr][i] = (ch < a.nchunk) ? *reinterpret_cast<const uint4*>(rowp + (int64_t)ch * 16)
+                                      : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    // token ids of the rows (lane rr fetches row rr's id)
+    int64_t myphys = phys[0];
+#pragma unroll
+    for (int rr = 1; rr < R; ++rr)
+      if (lane == rr) myphys = phys[rr];
+    uint32_t mytok = (uint32_t)myphys;
+    if constexpr (MODE == kRowGather) {
+      if (lane < R) mytok = (uint32_t)a.c2t[myphys];
+    }
+    float acc[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) s = CK::dot(data[rr][i], hreg[i], s);
+      acc[rr] = wave_sum(s);
+    }
+    float mine = acc[0];
+#pragma unroll
+    for (int rr = 1; rr < R; ++rr)
+      if (lane == rr) mine = acc[rr];
+    const int64_t myrow = row0 + lane;
+    if (lane < R && myrow < a.nrows) {
+      const float x = mine * a.inv_tau;
+      const float kx = a.sample ? x + gumbel(seed, kStreamToken, mytok) : mine;
+      const uint64_t key = decode_key(kx, mytok);
+      best = key > best ? key : best;
+      if (a.out_lse) lse = lse_add(lse, x);
+      if (a.dbg_logits) {
+        a.dbg_ids[(int64_t)r * a.dbg_stride + myrow] = (int32_t)mytok;
+        a.dbg_logits[(int64_t)r * a.dbg_stride + myrow] = mine;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup decode merge.  Every workgroup folds its waves' (best, lse)
+// in LDS; workgroups other than `finisher` store theirs into their own slot
+// with device-scope stores, wait for them to complete and count themselves
+// arrived (spread counters); the finisher, after its own share, waits for
+// every arrival and folds all partials in a fixed order (deterministic),
+// then writes the token and the lse.  No same-address atomics, no L2
+// write-back or invalidate.  Returns true in the finisher.
+// ---------------------------------------------------------------------------
+template <int NT>
+struct MergeSmem {
+  uint64_t best[NT];
+  float2 lse[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ bool merge_decode(const RowdotArgs& a, int r, int nblocks, int block,
+                                             int finisher, uint64_t best, Lse lse,
+                                             MergeSmem<NT>& ms) {
+  constexpr int NW = NT / kWave;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  best = wave_max_u64(best);
+  if (a.out_lse) lse = wave_lse(lse);
+  if (lane == 0) {
+    ms.best[wave] = best;
+    ms.lse[wave] = make_float2(lse.m, lse.s);
+  }
+  __syncthreads();
+  uint64_t* pbest = a.part_best + (int64_t)r * nblocks;
+  unsigned long long* plse = reinterpret_cast<unsigned long long*>(a.lse_part + (int64_t)r * nblocks);
+  uint32_t* ctr = a.counters + (int64_t)r * kArriveWords;
+  uint64_t bb = ms.best[0];
+  Lse ll{ms.lse[0].x, ms.lse[0].y};
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    bb = ms.best[w] > bb ? ms.best[w] : bb;
+    ll = lse_merge(ll, Lse{ms.lse[w].x, ms.lse[w].y});
+  }
+  if (block != finisher) {
+    if (t == 0) {
+      __hip_atomic_store(pbest + block, bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.out_lse) {
+        const unsigned long long packed =
+            ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
+        __hip_atomic_store(plse + block, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the partial is visible device-wide
+      arrive(ctr, block);
+    }
+    return false;
+  }
+  // finisher: wave 0 waits for the others, then folds every partial
+  if (wave != 0) return true;
+  wait_arrivals(ctr, nblocks - 1, lane);
+  if (lane != 0) {
+    bb = 0ull;
+    ll = lse_empty();
+  }
+  for (int j = lane; j < nblocks; j += kWave) {
+    if (j == finisher) continue;
+    const uint64_t x = __hip_atomic_load(pbest + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bb = x > bb ? x : bb;
+    if (a.out_lse) {
+      const unsigned long long pr =
+          __hip_atomic_load(plse + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ll = lse_merge(ll, Lse{__uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32))});
+    }
+  }
+  bb = wave_max_u64(bb);
+  if (a.out_lse) ll = wave_lse(ll);
+  if (lane == 0) {
+    a.out_tokens[r] = (int32_t)key_id(bb);
+    if (a.out_lse) a.out_lse[r] = ll.m + logf(ll.s);
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// The same merge with the data as its own flag (single-launch batch-1
+// decode): workgroups other than 0 store their partial key into their slot
+// of `slot` (zero = not yet written; a published key is never zero) after
+// their lse partial, if any, has been performed; workgroup 0's wave 0 polls
+// the slots until every one is written and folds them.  Every workgroup also
+// clears its slot of `slot_next`, the set the next launch uses.  Returns
+// true in workgroup 0.
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblocks,
+                                                   uint64_t* slot, uint64_t* slot_next,
+                                                   unsigned long long* lse_slot, uint64_t best,
+                                                   Lse lse, uint32_t* error, MergeSmem<NT>& ms) {
+  constexpr int NW = NT / kWave;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  const int block = blockIdx.x;
+  best = wave_max_u64(best);
+  if (a.out_lse) lse = wave_lse(lse);
+  if (lane == 0) {
+    ms.best[wave] = best;
+    ms.lse[wave] = make_float2(lse.m, lse.s);
+  }
+  __syncthreads();
+  uint64_t bb = ms.best[0];
+  Lse ll{ms.lse[0].x, ms.lse[0].y};
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    bb = ms.best[w] > bb ? ms.best[w] : bb;
+    ll = lse_merge(ll, Lse{ms.lse[w].x, ms.lse[w].y});
+  }
+  if (t == 0) slot_next[block] = 0ull;
+  if (block != 0) {
+    if (t == 0) {
+      if (a.out_lse) {
+        const unsigned long long packed =
+            ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
+        __hip_atomic_store(lse_slot + block, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);  // the lse partial is performed before the key
+      }
+      __hip_atomic_store(slot + block, bb ? bb : 1ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return false;
+  }
+  if (wave != 0) return true;
+  // workgroup 0, wave 0: poll every other slot until all are written
+  if (lane != 0) {
+    bb = 0ull;
+    ll = lse_empty();
+  }
+  uint64_t got = 0ull;
+  for (int it = 0;; ++it) {
+    bool missing = false;
+    got = bb;
+    for (int j = lane; j < nblocks; j += kWave) {
+      if (j == 0) continue;
+      const uint64_t x = __hip_atomic_load(slot + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (x == 0ull) missing = true;
+      got = x > got ? x : got;
+    }
+    if (!__any(missing)) break;
+    if (it == kArriveSpinLimit) {
+      if (lane == 0 && error) atomicOr(error, 8u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  bb = wave_max_u64(got);
+  if (a.out_lse) {
+    for (int j = lane; j < nblocks; j += kWave) {
+      if (j == 0) continue;
+      const unsigned long long pr =
+          __hip_atomic_load(lse_slot + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ll = lse_merge(ll, Lse{__uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32))});
+    }
+    ll = wave_lse(ll);
+  }
+  if (lane == 0) {
+    a.out_tokens[0] = (int32_t)key_id(bb);
+    if (a.out_lse) a.out_lse[0] = ll.m + logf(ll.s);
+  }
+  return true;
+}
+
+}  // namespace fh

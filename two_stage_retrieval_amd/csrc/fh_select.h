@@ -82,14 +82,34 @@ __device__ __forceinline__ uint4 sel_load4(__amdgpu_buffer_rsrc_t rs, uint32_t b
   return __builtin_bit_cast(uint4, v);
 }
 
-// Selects p of the c keys; writes the ids ascending to out[0..p).  `keys`
-// is 16-byte aligned with room for `stride` floats (stride >= c, a multiple
-// of 4).  With `masks`, also sets bit `row` of masks[k] for every selected
-// k.  Sets bit 0 of *error if the selection did not produce exactly p ids.
-// Needs NT * IPT >= c.
-template <int NT, int IPT, bool COHERENT>
-__device__ void select_block(const float* keys, int c, int stride, int p, int32_t* out,
-                             uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
+// Loads this thread's IPT keys (thread t owns [t*IPT, t*IPT + IPT)) as raw
+// fp32 bits.  `keys` is 16-byte aligned with room for `stride` floats
+// (stride >= c, a multiple of 4); words past `stride` read as zero.
+// COHERENT: the keys were written by other workgroups of the running kernel.
+template <int IPT, bool COHERENT>
+__device__ __forceinline__ void select_load_keys(const float* keys, int stride,
+                                                 uint32_t (&u)[IPT]) {
+  const int k0 = threadIdx.x * IPT;
+  const __amdgpu_buffer_rsrc_t rs = sel_rsrc(keys, (uint32_t)stride * 4u);
+#pragma unroll
+  for (int q = 0; q < IPT / 4; ++q) {
+    const uint4 v = sel_load4<COHERENT>(rs, (uint32_t)(k0 + 4 * q) * 4u);
+    u[4 * q] = v.x;
+    u[4 * q + 1] = v.y;
+    u[4 * q + 2] = v.z;
+    u[4 * q + 3] = v.w;
+  }
+}
+
+// Selects p of the c keys held by the workgroup (raw fp32 bits in u, from
+// select_load_keys); writes the ids ascending to out[0..p) (global or LDS
+// memory).  COHERENT_OUT stores the ids device-coherently for readers in
+// the running kernel.  With `masks`, also sets bit `row` of masks[k] for
+// every selected k.  Sets bit 0 of *error (if given) when the selection did
+// not produce exactly p ids.  Needs NT * IPT >= c.
+template <int NT, int IPT, bool COHERENT_OUT>
+__device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
+                                 uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
   static_assert(IPT % 4 == 0 && IPT <= 32, "items per thread");
   constexpr int NW = NT / kWave;
   constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
@@ -99,20 +119,8 @@ __device__ void select_block(const float* keys, int c, int stride, int p, int32_
   const int k0 = t * IPT;
   int parity = 0;
 
-  // ---- keys, block min / max ------------------------------------------------
+  // ---- block min / max ----------------------------------------------------------
   FH_SEL_TRACE(0);
-  uint32_t u[IPT];
-  {
-    const __amdgpu_buffer_rsrc_t rs = sel_rsrc(keys, (uint32_t)stride * 4u);
-#pragma unroll
-    for (int q = 0; q < IPT / 4; ++q) {
-      const uint4 v = sel_load4<COHERENT>(rs, (uint32_t)(k0 + 4 * q) * 4u);
-      u[4 * q] = v.x;
-      u[4 * q + 1] = v.y;
-      u[4 * q + 2] = v.z;
-      u[4 * q + 3] = v.w;
-    }
-  }
   for (int i = t; i < kSelBins; i += NT) sm.hist[i] = 0;
   for (int i = t; i < FH_MAX_C / 32; i += NT) sm.chosen[i] = 0u;
   if (t < 8) sm.misc[t] = 0;
@@ -334,7 +342,11 @@ __device__ void select_block(const float* keys, int c, int stride, int p, int32_
   for (int j = 0; j < IPT; ++j) {
     if ((above >> j) & 1u) {
       if (rank < p) {
-        out[rank] = k0 + j;
+        if constexpr (COHERENT_OUT) {
+          __hip_atomic_store(out + rank, k0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          out[rank] = k0 + j;
+        }
         if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k0 + j), 1ull << row);
       }
       ++rank;
@@ -342,6 +354,16 @@ __device__ void select_block(const float* keys, int c, int stride, int p, int32_
   }
   FH_SEL_TRACE(7);
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);
+}
+
+// Loads the keys and selects (see select_load_keys / select_from_keys).
+template <int NT, int IPT, bool COHERENT>
+__device__ __forceinline__ void select_block(const float* keys, int c, int stride, int p,
+                                             int32_t* out, uint64_t* masks, int row,
+                                             uint32_t* error, SelSmem& sm) {
+  uint32_t u[IPT];
+  select_load_keys<IPT, COHERENT>(keys, stride, u);
+  select_from_keys<NT, IPT, COHERENT>(u, c, p, out, masks, row, error, sm);
 }
 
 // The clusters whose row mask is non-zero, ascending, into ulist / ucount.

@@ -17,6 +17,7 @@
 // separate lines, see fh_device.h), then reads the row's c keys and runs the
 // block-level selection, writing the p selected cluster ids in ascending
 // order for stage 2.
+#include "fh_rows.h"
 #include "fh_select.h"
 
 // Optional timeline hook for measurement builds (empty in the library).
@@ -28,12 +29,9 @@ namespace fh {
 
 constexpr int kS1Threads = 512;
 constexpr int kS1Waves = kS1Threads / kWave;
-constexpr int kS1R = 4;
 
 template <typename TE, int NCH, int IPT, bool INT4, bool SELECT>
 __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
-  using CK = Chunk<TE>;
-  constexpr int EPC = CK::kElems;
   __shared__ SelSmem sm;
   __shared__ float s_h[INT4 ? FH_MAX_ROW_BYTES / 2 : 1];
   const int r = blockIdx.y;
@@ -45,79 +43,17 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
   float* keys = a.keys + (int64_t)r * a.key_stride;
   float* dbg = a.dbg_scores ? a.dbg_scores + (int64_t)r * a.c : nullptr;
-
-  auto publish = [&](int row, float score) {
-    const float key =
-        a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
-    if constexpr (SELECT) {
-      __hip_atomic_store(keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      keys[row] = key;
-    }
-    if (dbg) dbg[row] = score;
-  };
+  const int w0 = blockIdx.x * kS1Waves + wave, wstride = gridDim.x * kS1Waves;
 
   if constexpr (!INT4) {
-    float hreg[NCH][EPC];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = lane + kWave * i;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (ch < a.nchunk) w = *reinterpret_cast<const uint4*>(hrow + (int64_t)ch * 16);
-      CK::unpack(w, hreg[i]);
-    }
-    const int ngroups = (a.c + kS1R - 1) / kS1R;
-    for (int g = blockIdx.x * kS1Waves + wave; g < ngroups; g += gridDim.x * kS1Waves) {
-      const int row0 = g * kS1R;
-      uint4 data[kS1R][NCH];
-#pragma unroll
-      for (int rr = 0; rr < kS1R; ++rr) {
-        const int row = row0 + rr < a.c ? row0 + rr : a.c - 1;
-        const uint8_t* rowp = a.C + (int64_t)row * a.row_bytes;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int ch = lane + kWave * i;
-          data[rr][i] = ch < a.nchunk ? *reinterpret_cast<const uint4*>(rowp + (int64_t)ch * 16)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-      float acc[kS1R];
-#pragma unroll
-      for (int rr = 0; rr < kS1R; ++rr) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) s = CK::dot(data[rr][i], hreg[i], s);
-        acc[rr] = wave_sum(s);
-      }
-      float mine = acc[0];
-#pragma unroll
-      for (int rr = 1; rr < kS1R; ++rr)
-        if (lane == rr) mine = acc[rr];
-      if (lane < kS1R && row0 + lane < a.c) publish(row0 + lane, mine);
-    }
+    float hreg[NCH][Chunk<TE>::kElems];
+    load_h<TE, NCH>(hrow, a.nchunk, lane, hreg);
+    score_rows<TE, NCH, SELECT>(a, keys, nullptr, dbg, seed, hreg, lane, w0, wstride);
   } else {
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(hrow);
     for (int i = t; i < a.d; i += kS1Threads) s_h[i] = __uint_as_float((uint32_t)hb[i] << 16);
     __syncthreads();
-    const int q = lane >> 4, rin = lane & 15;
-    const int G = a.groups;
-    for (int tile = blockIdx.x * kS1Waves + wave; tile < a.ntiles;
-         tile += gridDim.x * kS1Waves) {
-      const uint4* codes =
-          reinterpret_cast<const uint4*>(a.q4) + (int64_t)tile * G * kWave + lane;
-      const uint16_t* sc = a.q4s + (int64_t)tile * G * 16 + rin;
-      float acc = 0.0f;
-#pragma unroll 4
-      for (int g = 0; g < G; ++g) {
-        const uint4 w = codes[(int64_t)g * kWave];
-        const float s = __uint_as_float((uint32_t)sc[g * 16] << 16);
-        acc = fmaf(s, int4_dot_chunk(w, s_h + g * 128 + q * 32), acc);
-      }
-      acc += __shfl_xor(acc, 16, kWave);
-      acc += __shfl_xor(acc, 32, kWave);
-      const int row = tile * 16 + rin;
-      if (q == 0 && row < a.c) publish(row, acc);
-    }
+    score_int4_tiles<SELECT>(a, keys, nullptr, dbg, seed, s_h, lane, w0, wstride);
   }
   FH_S1_TRACE(1);
   if constexpr (!SELECT) return;
@@ -142,8 +78,122 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   FH_S1_TRACE(3);
 }
 
+// ---------------------------------------------------------------------------
+// The whole batch-1 decode step in one launch (notes, Overall architecture
+// and Figure 1): one workgroup per compute unit, all resident at once.  No
+// counters and no flags: the data are their own flags.
+//  A  every workgroup scores its share of the centroids and stores the keys
+//     device-coherently into this launch's key buffer (and marks the same
+//     rows pending in the other buffer, which the next launch uses);
+//  B  workgroup 0 polls the key buffer until no key is pending, runs the
+//     block-level selection and publishes the p cluster ids, device-
+//     coherently, into this launch's selection buffer, whose entries read -1
+//     until written (it also clears the other buffer for the next launch);
+//  C  every workgroup computes the exact logits of its share of the p*b
+//     candidate rows, with the hidden vector still in registers, waiting
+//     only for the selection entries its rows need;
+//  D  partials meet in zero-initialised slots polled by workgroup 0
+//     (merge_decode_slots), which finally advances the launch epoch that
+//     picks the buffer sets.
+// Every wait is bounded; running out of patience sets a bit of the error
+// word instead of hanging.
+// ---------------------------------------------------------------------------
+template <typename TE, int NCH, int R, int IPT, bool INT4>
+__global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args) {
+  __shared__ SelSmem sm;
+  __shared__ float s_h[INT4 ? FH_MAX_ROW_BYTES / 2 : 1];
+  __shared__ MergeSmem<kS1Threads> ms;
+  const Stage1Args& a = args.s1;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint32_t epoch = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const int cur = (int)(epoch & 1u);
+  float* keys = a.keys + (int64_t)cur * a.key_stride;
+  float* keys_next = a.keys + (int64_t)(1 - cur) * a.key_stride;
+  int32_t* sel = args.sel + (int64_t)cur * kDecodeB1MaxP;
+  int32_t* sel_next = args.sel + (int64_t)(1 - cur) * kDecodeB1MaxP;
+  FH_S1_TRACE(0);
+  const uint64_t seed = a.sample ? a.seeds[0] : 0ull;
+  const int w0 = blockIdx.x * kS1Waves + wave, wstride = gridDim.x * kS1Waves;
+
+  // ---- A: stage-1 share ----------------------------------------------------------
+  float hreg[NCH][Chunk<TE>::kElems];
+  load_h<TE, NCH>(a.H, args.s2.nchunk, lane, hreg);
+  if constexpr (!INT4) {
+    score_rows<TE, NCH, true>(a, keys, keys_next, a.dbg_scores, seed, hreg, lane, w0, wstride);
+  } else {
+    const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.H);
+    for (int i = t; i < a.d; i += kS1Threads) s_h[i] = __uint_as_float((uint32_t)hb[i] << 16);
+    __syncthreads();
+    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride);
+  }
+  FH_S1_TRACE(1);
+
+
+  // ---- B: workgroup 0 waits for all keys, selects and publishes ------------------
+  if (blockIdx.x == 0) {
+    for (int i = t; i < kDecodeB1MaxP; i += kS1Threads) sel_next[i] = -1;
+    uint32_t u[IPT];
+    const int k0 = t * IPT;
+    const int nvalid = a.c - k0 < 0 ? 0 : (a.c - k0 < IPT ? a.c - k0 : IPT);
+    for (int it = 0;; ++it) {
+      select_load_keys<IPT, true>(keys, (int)a.key_stride, u);
+      int pending = 0;
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) pending |= (j < nvalid && u[j] == kKeyPending) ? 1 : 0;
+      if (!__syncthreads_or(pending)) break;
+      if (it == kArriveSpinLimit) {
+        if (t == 0 && a.error) atomicOr(a.error, 2u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    FH_S1_TRACE(2);
+    select_from_keys<kS1Threads, IPT, true>(u, a.c, a.p, sel, nullptr, 0, a.error, sm);
+    FH_S1_TRACE(3);
+  }
+
+  // ---- C: stage-2 share ---------------------------------------------------------
+  // one lane per workgroup waits for the entries of the workgroup's first rows
+  // (the whole selection is published at once), instead of every wave
+  // polling the same lines
+  if (blockIdx.x != 0) {
+    if (t == 0) {
+      const int64_t ngroups = (args.s2.nrows + R - 1) / R;
+      const int64_t g0 = (int64_t)blockIdx.x * kS1Waves;
+      if (g0 < ngroups) {
+        const int64_t g1 = g0 + kS1Waves - 1 < ngroups ? g0 + kS1Waves - 1 : ngroups - 1;
+        (void)selected_cluster<true>(sel, g0 * R / args.s2.b, a.error);
+        (void)selected_cluster<true>(sel, (g1 * R + R - 1 < args.s2.nrows ? g1 * R + R - 1
+                                                                        : args.s2.nrows - 1) /
+                                              args.s2.b,
+                                     a.error);
+      }
+    }
+    __syncthreads();
+  }
+  uint64_t best = 0;
+  Lse lse = lse_empty();
+  dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, sel, hreg, seed, lane, w0, wstride, best,
+                                         lse, a.error);
+  FH_S1_TRACE(5);
+
+  // ---- D: the decode merge; workgroup 0 then advances the epoch --------------------
+  uint64_t* slots = args.s2.part_best + (int64_t)cur * args.slot_stride;
+  uint64_t* slots_next = args.s2.part_best + (int64_t)(1 - cur) * args.slot_stride;
+  if (merge_decode_slots<kS1Threads>(args.s2, gridDim.x, slots, slots_next,
+                                     reinterpret_cast<unsigned long long*>(args.s2.lse_part),
+                                     best, lse, a.error, ms) &&
+      t == 0) {
+    __hip_atomic_store(args.epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    FH_S1_TRACE(6);
+  }
+}
+
 int stage1_blocks(const Stage1Args& a, bool int4) {
-  const int64_t units = int4 ? a.ntiles : (a.c + kS1R - 1) / kS1R;
+  const int64_t units = int4 ? a.ntiles : (a.c + kS1Rows - 1) / kS1Rows;
   int64_t blocks = (units + kS1Waves - 1) / kS1Waves;
   return (int)(blocks < 1 ? 1 : blocks);
 }
@@ -202,6 +252,64 @@ hipError_t launch_stage1(const Stage1Args& a, int dtype, bool int4, int B, hipSt
     case 8: return launch_nch<float, 8, false>(a, B, s, tm);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------------------------
+// single-launch batch-1 decode
+// ---------------------------------------------------------------------------
+int decode_b1_grid(const DecodeB1Args& a, bool int4, int num_cu) {
+  if (!stage1_selects(a.s1.c) || num_cu < 1 || a.s1.p > kDecodeB1MaxP) return 0;
+  const int nch = (a.s2.nchunk + kWave - 1) / kWave;
+  if (nch < 1 || nch > 8) return 0;
+  const int R = nch <= 2 ? 8 : 4;
+  const int64_t units1 = int4 ? a.s1.ntiles : (a.s1.c + kS1Rows - 1) / kS1Rows;
+  const int64_t units2 = (a.s2.nrows + R - 1) / R;
+  const int64_t units = units1 > units2 ? units1 : units2;
+  int64_t g = (units + kS1Waves - 1) / kS1Waves;
+  if (g > num_cu) g = num_cu;  // one resident workgroup per compute unit
+  return (int)(g < 1 ? 1 : g);
+}
+
+template <typename TE, int NCH, bool INT4>
+static hipError_t launch_b1_nch(const DecodeB1Args& a, int grid, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1) {
+  constexpr int R = NCH <= 2 ? 8 : 4;
+  const int c = a.s1.c;
+  const dim3 g(grid), block(kS1Threads);
+  if (c <= kS1Threads * 4) {
+    hipExtLaunchKernelGGL((decode_b1_kernel<TE, NCH, R, 4, INT4>), g, block, 0, s, e0, e1, 0, a);
+  } else if (c <= kS1Threads * 16) {
+    hipExtLaunchKernelGGL((decode_b1_kernel<TE, NCH, R, 16, INT4>), g, block, 0, s, e0, e1, 0, a);
+  } else if (c <= kS1Threads * 32) {
+    hipExtLaunchKernelGGL((decode_b1_kernel<TE, NCH, R, 32, INT4>), g, block, 0, s, e0, e1, 0, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename TE, bool INT4>
+static hipError_t launch_b1_t(const DecodeB1Args& a, int grid, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
+  switch ((a.s2.nchunk + kWave - 1) / kWave) {
+    case 1: return launch_b1_nch<TE, 1, INT4>(a, grid, s, e0, e1);
+    case 2: return launch_b1_nch<TE, 2, INT4>(a, grid, s, e0, e1);
+    case 3: return launch_b1_nch<TE, 3, INT4>(a, grid, s, e0, e1);
+    case 4: return launch_b1_nch<TE, 4, INT4>(a, grid, s, e0, e1);
+    case 5: return launch_b1_nch<TE, 5, INT4>(a, grid, s, e0, e1);
+    case 6: return launch_b1_nch<TE, 6, INT4>(a, grid, s, e0, e1);
+    case 7: return launch_b1_nch<TE, 7, INT4>(a, grid, s, e0, e1);
+    case 8: return launch_b1_nch<TE, 8, INT4>(a, grid, s, e0, e1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid,
+                            hipStream_t s, const Timing* tm) {
+  hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
+  if (int4) return launch_b1_t<bf16_t, true>(a, grid, s, e0, e1);
+  if (dtype == FH_DTYPE_BF16) return launch_b1_t<bf16_t, false>(a, grid, s, e0, e1);
+  return launch_b1_t<float, false>(a, grid, s, e0, e1);
 }
 
 }  // namespace fh
