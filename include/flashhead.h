@@ -211,9 +211,21 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
 
 /* Sizes of a prepared head: what = 0 v, 1 d, 2 c, 3 b, 4 dtype, 5 quant,
  * 6 max_batch, 7 max_p, 8 device bytes owned by the handle, 9 the
- * selection self-check flag (non-zero if a selection produced a count other
- * than p; reading it synchronises with the device and clears it). */
+ * self-check word (reading it synchronises with the device and clears it;
+ * bit 0: a selection produced a count other than p; bits 1-3: a bounded
+ * wait between workgroups of one launch gave up), 10 the kernels the last
+ * step ran (0 none yet, 1 the single-launch batch-1 decode, 2 stage 1 and
+ * stage 2 as separate row-dot launches, 3 the batched matrix-core path). */
 int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
+
+/*
+ * Measurement reference, not part of the method: reads `bytes` (a multiple
+ * of 16, 16-byte aligned device memory) once with a plain streaming kernel
+ * on the stream and may write one word to `sink` (device).  Timed by the
+ * caller, it gives the read bandwidth this GPU achieves; it also evicts the
+ * caches without leaving dirty lines.
+ */
+int flashhead_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /*
  * Per-kernel timing for measurement (not for the decode loop).

@@ -34,7 +34,7 @@ EXPORTED = [
     "flashhead_sample", "dense_head_workspace_bytes", "dense_head",
     "flashhead_status_string", "flashhead_export_centroids",
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
-    "flashhead_profile_end", "flashhead_last_hip_error",
+    "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
 ]
 
 
@@ -84,6 +84,8 @@ def _load() -> C.CDLL:
     lib.dense_head.restype = C.c_int
     lib.flashhead_status_string.argtypes = [C.c_int]
     lib.flashhead_status_string.restype = C.c_char_p
+    lib.flashhead_stream_read.argtypes = [vp, i64, vp, vp]
+    lib.flashhead_stream_read.restype = C.c_int
     lib.flashhead_last_hip_error.argtypes = []
     lib.flashhead_last_hip_error.restype = C.c_char_p
     lib.flashhead_export_centroids.argtypes = [vp, vp]
@@ -105,6 +107,12 @@ lib = _load()
 
 def status_string(status: int) -> str:
     return lib.flashhead_status_string(status).decode()
+
+
+def flashhead_stream_read(buf, sink, stream=None) -> None:
+    """Streaming read of a whole device tensor (measurement reference)."""
+    _check(lib.flashhead_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                     _ptr(sink), _stream(stream)), "flashhead_stream_read")
 
 
 def flashhead_last_hip_error() -> str:

@@ -43,6 +43,7 @@ struct fh_handle {
   float2* b1_lse = nullptr;         // kMaxGrid
   int32_t* b1_sel = nullptr;        // 2 x kDecodeB1MaxP, -1 between launches
   uint64_t b1_launches = 0;         // host copy of the device epoch
+  int last_path = 0;                // kernels of the last step (flashhead_query 10)
   uint32_t* b1_epoch = nullptr;     // launch counter (picks the buffer set)
 
 
@@ -344,10 +345,12 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
         FH_TRY(hipMemcpyAsync(dbg->clusters, src, (size_t)p * 4, hipMemcpyDeviceToDevice, s));
       }
       ++h->b1_launches;
+      h->last_path = 1;
       return FH_OK;
     }
   }
 
+  h->last_path = batched ? 3 : 2;
   if (batched) {
     FH_TRY(launch_stage1_mfma(s1, int4, B, s, t1));
   } else {
@@ -424,6 +427,15 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
 extern "C" {
 
 const char* flashhead_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
+int flashhead_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 || !aligned16(buf)) return FH_ERR_INVALID_ARG;
+  int dev = 0, ncu = 0;
+  FH_TRY(hipGetDevice(&dev));
+  FH_TRY(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  FH_TRY(launch_stream_read(buf, bytes, sink, ncu, static_cast<hipStream_t>(stream)));
+  return FH_OK;
+}
 
 const char* flashhead_status_string(int status) {
   switch (status) {
@@ -637,6 +649,7 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
     case 6: *value = h->max_batch; break;
     case 7: *value = h->max_p; break;
     case 8: *value = h->bytes; break;
+    case 10: *value = h->last_path; break;
     case 9: {  // selection error flag (synchronous read and clear)
       uint32_t e = 0;
       FH_TRY(hipMemcpy(&e, h->error, 4, hipMemcpyDeviceToHost));

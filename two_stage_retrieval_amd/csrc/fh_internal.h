@@ -161,6 +161,8 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
 int stage2_mfma_grid();
 hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s,
                               const Timing* tm = nullptr);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int num_cu,
+                              hipStream_t s);
 hipError_t launch_cluster_major_copy(const uint8_t* E, int64_t lde_bytes, const int32_t* c2t,
                                      int64_t v, int64_t row_bytes, uint8_t* Ec, hipStream_t s);
 
