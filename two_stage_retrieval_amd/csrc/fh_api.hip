@@ -39,8 +39,8 @@ struct fh_handle {
   // single-launch batch-1 decode
   int num_cu = 0;
   float* b1_keys = nullptr;         // 2 x key_stride(c), all bits set between launches
-  uint64_t* b1_slots = nullptr;     // 2 x kMaxGrid, zero between launches
-  float2* b1_lse = nullptr;         // kMaxGrid
+  uint64_t* b1_slots = nullptr;     // 2 x kDecodeB1SlotStride words, zero between launches
+  float2* b1_lse = nullptr;         // kDecodeB1SlotStride words
   int32_t* b1_sel = nullptr;        // 2 x kDecodeB1MaxP, -1 between launches
   uint64_t b1_launches = 0;         // host copy of the device epoch
   int last_path = 0;                // kernels of the last step (flashhead_query 10)
@@ -216,9 +216,9 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(hipMemsetAsync(h->sel_counter, 0, (size_t)kArriveWords * 4, s));
   FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * key_stride(c) * 4));
   FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * key_stride(c) * 4, s));
-  FH_TRY(alloc(h, &h->b1_slots, (size_t)2 * kMaxGrid * 8));
-  FH_TRY(hipMemsetAsync(h->b1_slots, 0, (size_t)2 * kMaxGrid * 8, s));
-  FH_TRY(alloc(h, &h->b1_lse, (size_t)kMaxGrid * 8));
+  FH_TRY(alloc(h, &h->b1_slots, (size_t)2 * kDecodeB1SlotStride * 8));
+  FH_TRY(hipMemsetAsync(h->b1_slots, 0, (size_t)2 * kDecodeB1SlotStride * 8, s));
+  FH_TRY(alloc(h, &h->b1_lse, (size_t)kDecodeB1SlotStride * 8));
   FH_TRY(alloc(h, &h->b1_sel, (size_t)2 * kDecodeB1MaxP * 4));
   FH_TRY(hipMemsetAsync(h->b1_sel, 0xFF, (size_t)2 * kDecodeB1MaxP * 4, s));
   FH_TRY(alloc(h, &h->b1_epoch, 4));
@@ -327,7 +327,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     f.s2.lse_part = h->b1_lse;
     f.sel = h->b1_sel;
     f.epoch = h->b1_epoch;
-    f.slot_stride = kMaxGrid;
+    f.slot_stride = kDecodeB1SlotStride;
     const int grid = decode_b1_grid(f, int4, h->num_cu);
     if (grid > 0 && grid <= kMaxGrid) {
       FH_TRY(launch_decode_b1(f, h->dtype, int4, grid, s, t1));

@@ -124,11 +124,14 @@ struct Stage1Args {
 //   s1.keys       2 x key_stride floats, every key pending (all bits set)
 //                 before the first launch;
 //   sel           2 x kDecodeB1MaxP int32, all -1 before the first launch;
-//   s2.part_best  2 x slot_stride u64 slots, zero before the first launch;
-//   s2.lse_part   slot_stride lse partials.
+//   s2.part_best  2 x slot_stride u64 words of slots (slot j at word 16 j),
+//                 zero before the first launch;
+//   s2.lse_part   slot_stride u64 words of lse partials (same spacing).
 // Launches keep them consistent.  The selection of the launch is copied to
 // s1.sel (plain) only for the debug output.
 constexpr int kDecodeB1MaxP = 2048;
+constexpr int kDecodeB1MaxGrid = 512;
+constexpr int64_t kDecodeB1SlotStride = (int64_t)kDecodeB1MaxGrid * 16;  // u64 words
 struct DecodeB1Args {
   Stage1Args s1;
   RowdotArgs s2;

@@ -236,8 +236,8 @@ __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32
 // ---------------------------------------------------------------------------
 template <int NT>
 struct MergeSmem {
-  uint64_t best[NT];
-  float2 lse[NT];
+  uint64_t best[NT / kWave];
+  float2 lse[NT / kWave];
 };
 
 template <int NT>
@@ -310,9 +310,11 @@ __device__ __forceinline__ bool merge_decode(const RowdotArgs& a, int r, int nbl
 // of `slot` (zero = not yet written; a published key is never zero) after
 // their lse partial, if any, has been performed; workgroup 0's wave 0 polls
 // the slots until every one is written and folds them.  Every workgroup also
-// clears its slot of `slot_next`, the set the next launch uses.  Returns
-// true in workgroup 0.
+// clears its slot of `slot_next`, the set the next launch uses.  Slot j is
+// word j * kSlotWords: one 128-byte line per writer.  Returns true in
+// workgroup 0.
 // ---------------------------------------------------------------------------
+constexpr int kSlotWords = 16;  // u64 words per slot
 template <int NT>
 __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblocks,
                                                    uint64_t* slot, uint64_t* slot_next,
@@ -337,16 +339,17 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
     bb = ms.best[w] > bb ? ms.best[w] : bb;
     ll = lse_merge(ll, Lse{ms.lse[w].x, ms.lse[w].y});
   }
-  if (t == 0) slot_next[block] = 0ull;
+  if (t == 0) slot_next[block * kSlotWords] = 0ull;
   if (block != 0) {
     if (t == 0) {
       if (a.out_lse) {
         const unsigned long long packed =
             ((unsigned long long)__float_as_uint(ll.s) << 32) | __float_as_uint(ll.m);
-        __hip_atomic_store(lse_slot + block, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(lse_slot + block * kSlotWords, packed, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);  // the lse partial is performed before the key
       }
-      __hip_atomic_store(slot + block, bb ? bb : 1ull, __ATOMIC_RELAXED,
+      __hip_atomic_store(slot + block * kSlotWords, bb ? bb : 1ull, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
     return false;
@@ -357,29 +360,42 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
     bb = 0ull;
     ll = lse_empty();
   }
-  uint64_t got = 0ull;
+  // a round issues all of a lane's pending loads before looking at any (one
+  // memory round trip per round); a lane rereads only slots not yet written
+  constexpr int kQ = kDecodeB1MaxGrid / kWave;
+  uint64_t got = bb;
+  uint32_t todo = 0u;
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int j = lane + kWave * q;
+    if (j != 0 && j < nblocks) todo |= 1u << q;
+  }
   for (int it = 0;; ++it) {
-    bool missing = false;
-    got = bb;
-    for (int j = lane; j < nblocks; j += kWave) {
-      if (j == 0) continue;
-      const uint64_t x = __hip_atomic_load(slot + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (x == 0ull) missing = true;
-      got = x > got ? x : got;
+    uint64_t xs[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      xs[q] = ((todo >> q) & 1u) ? __hip_atomic_load(slot + (lane + kWave * q) * kSlotWords,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0ull;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      if (((todo >> q) & 1u) && xs[q] != 0ull) {
+        todo &= ~(1u << q);
+        got = xs[q] > got ? xs[q] : got;
+      }
     }
-    if (!__any(missing)) break;
+    if (!__any(todo != 0u)) break;
     if (it == kArriveSpinLimit) {
       if (lane == 0 && error) atomicOr(error, 8u);
       break;
     }
-    __builtin_amdgcn_s_sleep(1);
   }
   bb = wave_max_u64(got);
   if (a.out_lse) {
     for (int j = lane; j < nblocks; j += kWave) {
       if (j == 0) continue;
-      const unsigned long long pr =
-          __hip_atomic_load(lse_slot + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long pr = __hip_atomic_load(lse_slot + j * kSlotWords, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
       ll = lse_merge(ll, Lse{__uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32))});
     }
     ll = wave_lse(ll);

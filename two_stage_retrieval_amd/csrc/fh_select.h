@@ -125,11 +125,12 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
   for (int i = t; i < FH_MAX_C / 32; i += NT) sm.chosen[i] = 0u;
   if (t < 8) sm.misc[t] = 0;
   const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
+  // u keeps the raw fp32 bits; the order-preserving form is made where the
+  // bits themselves are compared (boundary candidates, radix passes)
   float lmax = -INFINITY, lmin = INFINITY;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     const float f = __uint_as_float(u[j]);
-    u[j] = ordered_u32(f);
     if (j < nvalid) {
       lmax = fmaxf(lmax, f);
       lmin = fminf(lmin, f);
@@ -152,7 +153,8 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
   }
   const float range = fmax - fmin;
   const float scale = (float)kSelBins / range;
-  const bool flat = !(range > 0.0f) || !(scale < INFINITY);
+  const float offset = -fmin * scale;
+  const bool flat = !(range > 0.0f) || !(scale < INFINITY) || !(offset > -INFINITY && offset < INFINITY);
 
   // ---- histogram and the boundary bin -----------------------------------------
   uint32_t bins[IPT / 2];  // this thread's item bins, two 16-bit bins per word
@@ -160,10 +162,11 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
   if (!flat) {
 #pragma unroll
     for (int j = 0; j < IPT; j += 2) {
-      int b0 = (int)((sel_from_ordered(u[j]) - fmin) * scale);
-      int b1 = (int)((sel_from_ordered(u[j + 1]) - fmin) * scale);
-      b0 = b0 < 0 ? 0 : (b0 < kSelBins - 1 ? b0 : kSelBins - 1);
-      b1 = b1 < 0 ? 0 : (b1 < kSelBins - 1 ? b1 : kSelBins - 1);
+      // (f - min) * scale as one fma; a monotone map of f, clamped to the bins
+      int b0 = (int)fmaf(__uint_as_float(u[j]), scale, offset);
+      int b1 = (int)fmaf(__uint_as_float(u[j + 1]), scale, offset);
+      b0 = min(max(b0, 0), kSelBins - 1);
+      b1 = min(max(b1, 0), kSelBins - 1);
       bins[j / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
       if (j < nvalid) atomicAdd(&sm.hist[b0], 1);
       if (j + 1 < nvalid) atomicAdd(&sm.hist[b1], 1);
@@ -220,7 +223,8 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      if ((cand >> j) & 1u) atomicAdd(&sm.hist[(u[j] >> shift) & 255u], 1);
+      if ((cand >> j) & 1u)
+        atomicAdd(&sm.hist[(ordered_u32(__uint_as_float(u[j])) >> shift) & 255u], 1);
     __syncthreads();
     if (wave == 0) {
       int dq[4];
@@ -249,7 +253,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       if (!((cand >> j) & 1u)) continue;
-      const uint32_t dj = (u[j] >> shift) & 255u;
+      const uint32_t dj = (ordered_u32(__uint_as_float(u[j])) >> shift) & 255u;
       if (dj > digit) {
         above |= 1u << j;
         cand &= ~(1u << j);
@@ -271,7 +275,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       if ((cand >> j) & 1u) {
-        sm.cu[base] = u[j];
+        sm.cu[base] = ordered_u32(__uint_as_float(u[j]));
         sm.ck[base] = k0 + j;
         ++base;
       }

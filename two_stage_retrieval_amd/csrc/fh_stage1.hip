@@ -103,6 +103,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   __shared__ SelSmem sm;
   __shared__ float s_h[INT4 ? FH_MAX_ROW_BYTES / 2 : 1];
   __shared__ MergeSmem<kS1Threads> ms;
+  __shared__ int32_t s_sel[kDecodeB1MaxP];
   const Stage1Args& a = args.s1;
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -138,8 +139,8 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     uint32_t u[IPT];
     const int k0 = t * IPT;
     const int nvalid = a.c - k0 < 0 ? 0 : (a.c - k0 < IPT ? a.c - k0 : IPT);
+    select_load_keys<IPT, true>(keys, (int)a.key_stride, u);
     for (int it = 0;; ++it) {
-      select_load_keys<IPT, true>(keys, (int)a.key_stride, u);
       int pending = 0;
 #pragma unroll
       for (int j = 0; j < IPT; ++j) pending |= (j < nvalid && u[j] == kKeyPending) ? 1 : 0;
@@ -148,10 +149,14 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
         if (t == 0 && a.error) atomicOr(a.error, 2u);
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      if (pending) select_load_keys<IPT, true>(keys, (int)a.key_stride, u);  // only if needed
     }
     FH_S1_TRACE(2);
-    select_from_keys<kS1Threads, IPT, true>(u, a.c, a.p, sel, nullptr, 0, a.error, sm);
+    // the selection goes to LDS, then out in one coalesced device-coherent pass
+    select_from_keys<kS1Threads, IPT, false>(u, a.c, a.p, s_sel, nullptr, 0, a.error, sm);
+    __syncthreads();
+    for (int i = t; i < a.p; i += kS1Threads)
+      __hip_atomic_store(sel + i, s_sel[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     FH_S1_TRACE(3);
   }
 
@@ -176,8 +181,9 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   }
   uint64_t best = 0;
   Lse lse = lse_empty();
-  dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, sel, hreg, seed, lane, w0, wstride, best,
-                                         lse, a.error);
+  // workgroup 0 reads its own copy in LDS
+  dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, blockIdx.x == 0 ? s_sel : sel, hreg, seed,
+                                         lane, w0, wstride, best, lse, a.error);
   FH_S1_TRACE(5);
 
   // ---- D: the decode merge; workgroup 0 then advances the epoch --------------------
@@ -267,6 +273,7 @@ int decode_b1_grid(const DecodeB1Args& a, bool int4, int num_cu) {
   const int64_t units = units1 > units2 ? units1 : units2;
   int64_t g = (units + kS1Waves - 1) / kS1Waves;
   if (g > num_cu) g = num_cu;  // one resident workgroup per compute unit
+  if (g > kDecodeB1MaxGrid) g = kDecodeB1MaxGrid;  // slots the merge's polling wave tracks
   return (int)(g < 1 ? 1 : g);
 }
 
