@@ -1,0 +1,126 @@
+"""Parity of each kernel path the library picks, at the shapes that select
+it, and of its edge cases (through the C ABI, against the CPU oracle):
+
+* path 1: the single-launch batch-1 decode (B = 1, c <= 16384, p <= 2048);
+* path 2: stage 1 and stage 2 as separate row-dot launches (B = 1 with a
+  larger p, or shapes the matrix-core path does not take);
+* path 3: the batched matrix-core path (bf16, B >= 2, b a multiple of 16,
+  d a multiple of 128), at ragged batch sizes.
+"""
+import numpy as np
+import pytest
+
+from oracle import flashhead_ref as ref
+from two_stage_retrieval_amd import synth
+
+from .parity import Stats
+from .test_gpu_parity import case, check_batch, dev_tensor, fh, run_debug  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+PATH_SINGLE_LAUNCH, PATH_ROWDOT, PATH_BATCHED = 1, 2, 3
+
+
+def path_of(fhmod, head):
+    return fhmod.flashhead_query(head.handle, 10)
+
+
+def seeds_dev(seeds):
+    return torch.from_numpy(seeds.view(np.int64)).cuda()
+
+
+@pytest.mark.parametrize("B", [3, 17, 33, 50])
+def test_batched_path_ragged_batches(fh, B):
+    # 16-row MFMA tiles over B columns: 1, 2, 3 and 4 column tiles, each
+    # with a partial last tile; c = 50 leaves a partial 16-row stage-1 tile
+    cs = case(1, c=50, b=16, d=256, seed=55)
+    head = cs.prepare(fh, max_batch=B, max_p=20)
+    H, H64 = cs.hidden(B, offset=B)
+    st = Stats()
+    res = run_debug(fh, head, dev_tensor(H), B, 20, "greedy")
+    assert path_of(fh, head) == PATH_BATCHED
+    check_batch(cs, res, H64, 20, stats=st)
+    seeds = synth.make_seeds(5, B)
+    res = run_debug(fh, head, dev_tensor(H), B, 20, "sample", 0.8, seeds_dev(seeds))
+    check_batch(cs, res, H64, 20, "sample", 0.8, seeds, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
+def test_single_launch_p_equals_c_matches_dense(fh):
+    # every cluster probed: the head is the dense argmax, id for id
+    cs = case(1, c=50, b=16, d=256, seed=56)
+    head = cs.prepare(fh, max_batch=1, max_p=50)
+    dense = fh.DenseHead(cs.E_dev, max_batch=1)
+    H, H64 = cs.hidden(8)
+    for i in range(8):
+        x = dev_tensor(H[i:i + 1])
+        t_head = int(head.greedy(x, 50).cpu().numpy()[0])
+        assert path_of(fh, head) == PATH_SINGLE_LAUNCH
+        t_dense = int(dense(x).cpu().numpy()[0])
+        assert t_head == t_dense
+        z = ref.dense_logits(cs.rows, cs.wl.v, H64[i])
+        tok, m2, _, keys = ref.decode_tokens(np.arange(cs.wl.v), z, "greedy", 1.0, 0)
+        if m2 > 1e-3:
+            assert t_head == tok
+        else:
+            assert keys[t_head] >= keys.max() - 1e-3
+
+
+def test_single_launch_alternating_p(fh):
+    # consecutive launches alternate buffer sets; p changes between them
+    cs = case(1)
+    head = cs.prepare(fh, max_batch=1, max_p=512)
+    H, H64 = cs.hidden(6, offset=300)
+    st = Stats()
+    for i, p in enumerate([512, 37, 512, 1, 200, 512]):
+        res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, p, "greedy")
+        assert path_of(fh, head) == PATH_SINGLE_LAUNCH
+        check_batch(cs, res, H64[i:i + 1], p, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
+def test_large_p_takes_the_two_launch_path(fh):
+    # p above what the single launch keeps in LDS
+    cs = case(1, c=4096, b=16, d=128, seed=57)
+    head = cs.prepare(fh, max_batch=1, max_p=3000)
+    H, H64 = cs.hidden(2)
+    st = Stats()
+    for i in range(2):
+        res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, 3000, "greedy")
+        assert path_of(fh, head) == PATH_ROWDOT
+        check_batch(cs, res, H64[i:i + 1], 3000, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_debug_outputs_do_not_change_results(fh, B):
+    cs = case(3)
+    head = cs.prepare(fh, max_batch=B, max_p=512)
+    H, _ = cs.hidden(B, offset=900)
+    x = dev_tensor(H)
+    seeds = seeds_dev(synth.make_seeds(3, B))
+    plain = head.greedy(x, 512).cpu().numpy()
+    dbg = run_debug(fh, head, x, B, 512, "greedy")["tokens"]
+    assert np.array_equal(plain, dbg)
+    lse = torch.empty(B, dtype=torch.float32, device="cuda")
+    s_plain = head.sample(x, 512, 0.7, seeds).cpu().numpy()
+    s_lse = head.sample(x, 512, 0.7, seeds, out_lse=lse).cpu().numpy()
+    s_dbg = run_debug(fh, head, x, B, 512, "sample", 0.7, seeds)
+    assert np.array_equal(s_plain, s_lse)
+    assert np.array_equal(s_plain, s_dbg["tokens"])
+    assert np.array_equal(lse.cpu().numpy(), s_dbg["lse"])
+
+
+def test_stream_read_reference(fh):
+    buf = torch.ones(1 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    fh.flashhead_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    # the data-dependent write does not happen for this content
+    assert sink.cpu().numpy().tolist() == [0, 0, 0, 0]
+    with pytest.raises(fh.FlashHeadError):
+        fh.flashhead_stream_read(buf[1:], sink)  # misaligned, not a multiple of 16 bytes
