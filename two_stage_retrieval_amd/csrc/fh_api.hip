@@ -197,7 +197,7 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
     FH_TRY(hipStreamSynchronize(s));  // host vectors die at scope end
   }
   const int mb = h->max_batch;
-  FH_TRY(alloc(h, &h->keys, (size_t)mb * key_stride(c) * 4));
+  FH_TRY(alloc(h, &h->keys, (size_t)kMaxKSplit * mb * key_stride(c) * 4));  // K-slice partials
   FH_TRY(alloc(h, &h->sel, (size_t)mb * h->max_p * 4));
   FH_TRY(alloc(h, &h->row_best, (size_t)mb * kMaxGrid * 8));
   FH_TRY(alloc(h, &h->counters, (size_t)mb * kArriveWords * 4));
@@ -277,6 +277,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.h_bytes = h->row_bytes;
   s1.keys = h->keys;
   s1.key_stride = key_stride(h->c);
+  s1.part_stride = (int64_t)h->max_batch * key_stride(h->c);
   s1.dbg_scores = dbg ? dbg->scores : nullptr;
   s1.sample = sample;
   s1.inv_tau = inv_tau;
@@ -351,8 +352,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   }
 
   h->last_path = batched ? 3 : 2;
+  int ksplit = 1;
   if (batched) {
-    FH_TRY(launch_stage1_mfma(s1, int4, B, s, t1));
+    FH_TRY(launch_stage1_mfma(s1, int4, B, s, t1, &ksplit));
   } else {
     FH_TRY(launch_stage1(s1, h->dtype, int4, B, s, t1));
   }
@@ -366,6 +368,12 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.sel_stride = h->max_p;
     a.masks = batched ? h->masks : nullptr;
     a.error = h->error;
+    a.nparts = ksplit;
+    a.part_stride = s1.part_stride;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    a.dbg_scores = ksplit > 1 && dbg ? dbg->scores : nullptr;
     if (batched) {
       a.counter = h->sel_counter;
       a.ulist = h->ulist;

@@ -148,10 +148,16 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) { best[nt] = 0ull; lse[nt] = lse_empty(); }
 
-  // groups of kGmWaves * IT items, grid-stride (uniform per workgroup)
-  for (int64_t item0 = (int64_t)blockIdx.x * kGmWaves * IT; item0 < nitems;
-       item0 += (int64_t)gridDim.x * kGmWaves * IT) {
+  // work units: groups of kGmWaves * IT items times ksplit slices of K (the
+  // waves of a workgroup share the slice, so the staged H chunk is shared),
+  // grid-stride (uniform per workgroup)
+  const int S = MODE == kGmScores ? a.ksplit : 1;
+  const int64_t nunits = ((nitems + kGmWaves * IT - 1) / (kGmWaves * IT)) * S;
+  for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
   __syncthreads();  // the previous group's readers of both LDS buffers are done
+  const int64_t item0 = (unit / S) * kGmWaves * IT;
+  const int sp = (int)(unit % S);
+  const int cbeg = sp * nchunks / S, cend = (sp + 1) * nchunks / S;
 
   // this wave's items
   int64_t row0[IT], kc[IT];
@@ -224,21 +230,21 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
     }
   };
 
-  load_h(0);
-  load_a(a0, 0);
+  load_h(cbeg);
+  load_a(a0, cbeg);
   store_h(0);
-  for (int c = 0; c < nchunks; c += 2) {
+  for (int c = cbeg; c < cend; c += 2) {
     // chunk c from buffer 0 / registers a0; prefetch chunk c + 1
     __syncthreads();
-    if (c + 1 < nchunks) { load_h(c + 1); load_a(a1, c + 1); }
+    if (c + 1 < cend) { load_h(c + 1); load_a(a1, c + 1); }
     compute(a0, 0);
-    if (c + 1 >= nchunks) break;
+    if (c + 1 >= cend) break;
     store_h(1);
     // chunk c + 1 from buffer 1 / registers a1; prefetch chunk c + 2
     __syncthreads();
-    if (c + 2 < nchunks) { load_h(c + 2); load_a(a0, c + 2); }
+    if (c + 2 < cend) { load_h(c + 2); load_a(a0, c + 2); }
     compute(a1, 1);
-    if (c + 2 < nchunks) store_h(0);
+    if (c + 2 < cend) store_h(0);
   }
 
   if constexpr (MODE == kGmScores) {
@@ -254,6 +260,10 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
           const int64_t k = row0[i] + 4 * slice + q;
           if (k >= a.c) continue;
           const float sc = acc[i][nt][q];
+          if (S > 1) {  // partial score over this K slice; the select sums the slices
+            a.keys[sp * a.part_stride + (int64_t)r * a.key_stride + k] = sc;
+            continue;
+          }
           const float key =
               a.sample ? sc * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : sc;
           a.keys[(int64_t)r * a.key_stride + k] = key;
@@ -383,7 +393,9 @@ bool batched_supported(int dtype, int d, int B, bool int4) {
 }
 
 // items per wave: enough reuse of each H fragment, registers for double-buffered rows
-template <int NT> constexpr int gm_items() { return NT <= 2 ? 4 : 2; }
+// items per wave (measured): one column tile streams best with one item and
+// more waves per SIMD; wider batches reuse each H fragment over two items
+template <int NT> constexpr int gm_items() { return NT == 1 ? 1 : 2; }
 
 template <int MODE>
 static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
@@ -408,16 +420,17 @@ static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, h
 
 static int engine_grid(int64_t nrows16, int B) {
   const int NT = (B + 15) / 16;
-  const int it = NT <= 2 ? 4 : 2;
+  const int it = NT == 1 ? 1 : 2;
   const int64_t per = (int64_t)kGmWaves * it;
   const int64_t g = (nrows16 + per - 1) / per;
   return g < 1 ? 1 : (int)g;
 }
 
 hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t s,
-                              const Timing* tm) {
+                              const Timing* tm, int* ksplit) {
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   const int NT = (B + 15) / 16;
+  *ksplit = 1;
   if (int4) {
     const dim3 grid((a.ntiles + kS1qThreads / kWave - 1) / (kS1qThreads / kWave));
     switch (NT) {
@@ -444,9 +457,33 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   m.keys = a.keys;
   m.key_stride = a.key_stride;
   m.dbg_scores = a.dbg_scores;
-  int grid = engine_grid((a.c + 15) / 16, B);
-  grid = grid < stage2_mfma_grid() ? grid : stage2_mfma_grid();
-  return launch_engine<kGmScores>(m, grid, s, e0, e1);
+  // one 16-row item per wave and enough K slices to give the chip ~2 x 256
+  // workgroups
+  const int nchunks = a.d / 128;
+  const int64_t groups = ((int64_t)(a.c + 15) / 16 + kGmWaves - 1) / kGmWaves;
+  int S = (int)((512 + groups - 1) / groups);
+  S = S < 1 ? 1 : (S > kMaxKSplit ? kMaxKSplit : S);
+  S = S > nchunks ? nchunks : S;
+  m.ksplit = S;
+  m.part_stride = a.part_stride;
+  *ksplit = S;
+  const int64_t units = groups * S;
+  const int grid = (int)(units < 4096 ? units : 4096);
+  const dim3 block(kGmThreads);
+#define FH_GMS(N)                                                                            \
+  case N:                                                                                    \
+    hipExtLaunchKernelGGL((gemm_engine_kernel<N, 1, kGmScores>), dim3(grid), block, 0, s, e0, \
+                          e1, 0, m);                                                          \
+    break;
+  switch (NT) {
+    FH_GMS(1)
+    FH_GMS(2)
+    FH_GMS(3)
+    FH_GMS(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef FH_GMS
+  return hipGetLastError();
 }
 
 int stage2_mfma_grid() { return 4096; }

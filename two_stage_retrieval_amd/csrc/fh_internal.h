@@ -50,6 +50,15 @@ struct RowdotArgs {
 struct SelectArgs {
   const float* keys;     // B x key_stride
   int64_t key_stride;
+  // nparts > 1: keys holds nparts partial-score blocks part_stride floats
+  // apart; the select sums them in slice order and forms the keys (score, or
+  // score / tau + Gumbel noise), writing the scores to dbg_scores if given
+  int nparts;
+  int64_t part_stride;
+  int sample;
+  float inv_tau;
+  const uint64_t* seeds;
+  float* dbg_scores;     // B x c
   int c, p;
   int32_t* sel;          // B x sel_stride, written ascending
   int sel_stride;
@@ -90,7 +99,10 @@ struct Stage2mArgs {
   float* keys;
   int64_t key_stride;
   float* dbg_scores;
+  int ksplit;            // K slices (scores); > 1: keys holds per-slice partial scores
+  int64_t part_stride;   // floats between the slices' B x key_stride blocks
 };
+constexpr int kMaxKSplit = 4;
 
 struct Stage1Args {
   const uint8_t* C;       // c x d centroids (bf16 / fp32)
@@ -104,6 +116,7 @@ struct Stage1Args {
   int64_t h_bytes;
   float* keys;            // B x key_stride selection keys (stride: c rounded up to 4)
   int64_t key_stride;
+  int64_t part_stride;    // batched stage 1: floats between K-slice partial blocks
   float* dbg_scores;      // optional raw scores, B x c
   int sample;
   float inv_tau;
@@ -159,8 +172,9 @@ hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int gri
 hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
                                  const int32_t* c2t, int c, int b, void* C, hipStream_t s);
 bool batched_supported(int dtype, int d, int B, bool int4);
+// returns the K slices used (the select sums them) in *ksplit
 hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t s,
-                              const Timing* tm = nullptr);
+                              const Timing* tm, int* ksplit);
 int stage2_mfma_grid();
 hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s,
                               const Timing* tm = nullptr);

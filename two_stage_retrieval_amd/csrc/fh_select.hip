@@ -11,9 +11,33 @@ template <int IPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelSmem sm;
   const int r = blockIdx.x;
-  select_block<kSelThreads, IPT, false>(a.keys + (int64_t)r * a.key_stride, a.c,
-                                        (int)a.key_stride, a.p, a.sel + (int64_t)r * a.sel_stride,
-                                        a.masks, r, a.error, sm);
+  uint32_t u[IPT];
+  select_load_keys<IPT, false>(a.keys + (int64_t)r * a.key_stride, (int)a.key_stride, u);
+  if (a.nparts > 1) {
+    // the scores arrive as K-slice partials: sum them in slice order, then
+    // form the keys (sampling: score / tau + Gumbel noise of stream 0)
+    const int k0 = threadIdx.x * IPT;
+    for (int sp = 1; sp < a.nparts; ++sp) {
+      uint32_t v[IPT];
+      select_load_keys<IPT, false>(a.keys + sp * a.part_stride + (int64_t)r * a.key_stride,
+                                   (int)a.key_stride, v);
+#pragma unroll
+      for (int j = 0; j < IPT; ++j)
+        u[j] = __float_as_uint(__uint_as_float(u[j]) + __uint_as_float(v[j]));
+    }
+    const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int k = k0 + j;
+      if (k >= a.c) continue;
+      const float sc = __uint_as_float(u[j]);
+      if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = sc;
+      if (a.sample)
+        u[j] = __float_as_uint(sc * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)k));
+    }
+  }
+  select_from_keys<kSelThreads, IPT, false>(u, a.c, a.p, a.sel + (int64_t)r * a.sel_stride,
+                                            a.masks, r, a.error, sm);
   if (!a.counter) return;
   // row 0's workgroup compacts the union of the selected clusters once every
   // other row has set its mask bits
