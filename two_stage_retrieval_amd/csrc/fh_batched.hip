@@ -92,13 +92,17 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + lr;
     if (r >= B) continue;
+    // the lane's 4 consecutive clusters share one Philox block
+    const int kq0 = tile * 16 + 4 * slice;
+    const float4 g4 = a.sample ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k = tile * 16 + 4 * slice + q;
+      const int k = kq0 + q;
       if (k >= a.c) continue;
       const float s = tot[nt][q];
-      const float key =
-          a.sample ? s * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : s;
+      const float key = a.sample ? s * a.inv_tau + gq[q] : s;
       a.keys[(int64_t)r * a.key_stride + k] = key;
       if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = s;
     }
@@ -126,13 +130,17 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 // ---------------------------------------------------------------------------
 constexpr int kGmThreads = 256;
 constexpr int kGmWaves = kGmThreads / kWave;
-constexpr int kGmKC = 128;                 // K per chunk (4 MFMA steps)
-constexpr int kGmHRow = kGmKC + 8;         // LDS row pitch in bf16 (16-byte pad)
 enum GmMode : int { kGmScores = 0, kGmFlash = 1, kGmDense = 2 };
 
-template <int NT, int IT, int MODE>
+// KC: K per chunk (KC / 32 MFMA steps); a wave requests KC * 2 contiguous
+// bytes of each of its rows per chunk
+template <int NT, int IT, int MODE, int KC>
 __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) {
-  __shared__ uint4 s_h[2][NT * 16 * kGmHRow / 8];
+  constexpr int kSteps = KC / 32;
+  constexpr int kHRow = KC + 8;  // LDS row pitch in bf16 (16-byte pad)
+  constexpr int kHP = NT * 16 * (KC / 8) / kGmThreads;  // H pieces per thread per chunk
+  static_assert(kHP * kGmThreads == NT * 16 * (KC / 8), "H staging");
+  __shared__ uint4 s_h[2][NT * 16 * kHRow / 8];
   __shared__ uint64_t s_best[kGmWaves][NT * 16];
   __shared__ float2 s_lse[kGmWaves][NT * 16];
   const int lane = threadIdx.x & (kWave - 1);
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
   const int sub = a.b / 16;
   const int64_t nrows_total = MODE == kGmScores ? (int64_t)a.c : a.v;
   const int64_t nitems = MODE == kGmFlash ? (int64_t)(*a.ucount) * sub : (nrows_total + 15) / 16;
-  const int nchunks = a.d / kGmKC;
+  const int nchunks = a.d / KC;
   uint64_t best[NT];
   Lse lse[NT];
 #pragma unroll
@@ -181,15 +189,15 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
     if constexpr (MODE != kGmFlash) arow = arow < nrows_total ? arow : nrows_total - 1;
     ap[i] = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
   }
-  // H chunk staging: thread t moves NT 16-byte pieces per chunk
-  const uint8_t* hsrc[NT];
-  int hdst[NT];
+  // H chunk staging: thread t moves kHP 16-byte pieces per chunk
+  const uint8_t* hsrc[kHP];
+  int hdst[kHP];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int piece = threadIdx.x + n * kGmThreads;  // 16 pieces per H row
-    int j = piece >> 4;
-    const int kp = piece & 15;
-    hdst[n] = j * (kGmHRow / 8) + kp;
+  for (int n = 0; n < kHP; ++n) {
+    const int piece = threadIdx.x + n * kGmThreads;  // KC / 8 pieces per H row
+    int j = piece / (KC / 8);
+    const int kp = piece % (KC / 8);
+    hdst[n] = j * (kHRow / 8) + kp;
     j = j < B ? j : B - 1;
     hsrc[n] = a.H + (int64_t)j * a.h_bytes + (int64_t)kp * 16;
   }
@@ -199,30 +207,30 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 a0[IT][4], a1[IT][4], hreg[NT];
-  auto load_a = [&](uint4 (&dst)[IT][4], int c) {
+  uint4 a0[IT][kSteps], a1[IT][kSteps], hreg[kHP];
+  auto load_a = [&](uint4 (&dst)[IT][kSteps], int c) {
 #pragma unroll
     for (int i = 0; i < IT; ++i)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dst[i][u] = *reinterpret_cast<const uint4*>(ap[i] + (int64_t)c * kGmKC * 2 + u * 64);
+      for (int u = 0; u < kSteps; ++u)
+        dst[i][u] = *reinterpret_cast<const uint4*>(ap[i] + (int64_t)c * KC * 2 + u * 64);
   };
   auto load_h = [&](int c) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      hreg[n] = *reinterpret_cast<const uint4*>(hsrc[n] + (int64_t)c * kGmKC * 2);
+    for (int n = 0; n < kHP; ++n)
+      hreg[n] = *reinterpret_cast<const uint4*>(hsrc[n] + (int64_t)c * KC * 2);
   };
   auto store_h = [&](int buf) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) s_h[buf][hdst[n]] = hreg[n];
+    for (int n = 0; n < kHP; ++n) s_h[buf][hdst[n]] = hreg[n];
   };
-  auto compute = [&](const uint4 (&av)[IT][4], int buf) {
+  auto compute = [&](const uint4 (&av)[IT][kSteps], int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kSteps; ++u) {
       uint4 bv[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bv[nt] = s_h[buf][(nt * 16 + lr) * (kGmHRow / 8) + u * 4 + slice];
+        bv[nt] = s_h[buf][(nt * 16 + lr) * (kHRow / 8) + u * 4 + slice];
 #pragma unroll
       for (int i = 0; i < IT; ++i)
 #pragma unroll
@@ -255,17 +263,22 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
       for (int nt = 0; nt < NT; ++nt) {
         const int r = nt * 16 + lr;
         if (r >= B) continue;
+        // the lane's 4 consecutive clusters share one Philox block
+        const int64_t kq0 = row0[i] + 4 * slice;
+        const float4 g4 = (a.sample && S == 1)
+                              ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t k = row0[i] + 4 * slice + q;
+          const int64_t k = kq0 + q;
           if (k >= a.c) continue;
           const float sc = acc[i][nt][q];
           if (S > 1) {  // partial score over this K slice; the select sums the slices
             a.keys[sp * a.part_stride + (int64_t)r * a.key_stride + k] = sc;
             continue;
           }
-          const float key =
-              a.sample ? sc * a.inv_tau + gumbel(a.seeds[r], kStreamCluster, (uint32_t)k) : sc;
+          const float key = a.sample ? sc * a.inv_tau + gq[q] : sc;
           a.keys[(int64_t)r * a.key_stride + k] = key;
           if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = sc;
         }
@@ -397,24 +410,28 @@ bool batched_supported(int dtype, int d, int B, bool int4) {
 // more waves per SIMD; wider batches reuse each H fragment over two items
 template <int NT> constexpr int gm_items() { return NT == 1 ? 1 : 2; }
 
+// K per chunk: 128 (4 MFMA steps).  Longer chunks (256, 512) request
+// longer contiguous runs per row but cost registers and waves per SIMD; on
+// these shapes they measured slower (one column tile) or the same (wider).
+constexpr int kGmKC = 128;
+
+template <int NT, int IT, int MODE>
+static void launch_engine_kc(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                             hipEvent_t e1) {
+  hipExtLaunchKernelGGL((gemm_engine_kernel<NT, IT, MODE, kGmKC>), dim3(grid), dim3(kGmThreads), 0,
+                        s, e0, e1, 0, a);
+}
+
 template <int MODE>
 static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                                 hipEvent_t e1) {
-  const int NT = (a.B + 15) / 16;
-  const dim3 block(kGmThreads);
-#define FH_GM(N)                                                                               \
-  case N:                                                                                      \
-    hipExtLaunchKernelGGL((gemm_engine_kernel<N, gm_items<N>(), MODE>), dim3(grid), block, 0, s, \
-                          e0, e1, 0, a);                                                       \
-    break;
-  switch (NT) {
-    FH_GM(1)
-    FH_GM(2)
-    FH_GM(3)
-    FH_GM(4)
+  switch ((a.B + 15) / 16) {
+    case 1: launch_engine_kc<1, gm_items<1>(), MODE>(a, grid, s, e0, e1); break;
+    case 2: launch_engine_kc<2, gm_items<2>(), MODE>(a, grid, s, e0, e1); break;
+    case 3: launch_engine_kc<3, gm_items<3>(), MODE>(a, grid, s, e0, e1); break;
+    case 4: launch_engine_kc<4, gm_items<4>(), MODE>(a, grid, s, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
-#undef FH_GM
   return hipGetLastError();
 }
 
@@ -458,8 +475,8 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   m.key_stride = a.key_stride;
   m.dbg_scores = a.dbg_scores;
   // one 16-row item per wave and enough K slices to give the chip ~2 x 256
-  // workgroups
-  const int nchunks = a.d / 128;
+  // workgroups (slices are whole K chunks)
+  const int nchunks = a.d / kGmKC;
   const int64_t groups = ((int64_t)(a.c + 15) / 16 + kGmWaves - 1) / kGmWaves;
   int S = (int)((512 + groups - 1) / groups);
   S = S < 1 ? 1 : (S > kMaxKSplit ? kMaxKSplit : S);
@@ -469,20 +486,13 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   *ksplit = S;
   const int64_t units = groups * S;
   const int grid = (int)(units < 4096 ? units : 4096);
-  const dim3 block(kGmThreads);
-#define FH_GMS(N)                                                                            \
-  case N:                                                                                    \
-    hipExtLaunchKernelGGL((gemm_engine_kernel<N, 1, kGmScores>), dim3(grid), block, 0, s, e0, \
-                          e1, 0, m);                                                          \
-    break;
   switch (NT) {
-    FH_GMS(1)
-    FH_GMS(2)
-    FH_GMS(3)
-    FH_GMS(4)
+    case 1: launch_engine_kc<1, 1, kGmScores>(m, grid, s, e0, e1); break;
+    case 2: launch_engine_kc<2, 1, kGmScores>(m, grid, s, e0, e1); break;
+    case 3: launch_engine_kc<3, 1, kGmScores>(m, grid, s, e0, e1); break;
+    case 4: launch_engine_kc<4, 1, kGmScores>(m, grid, s, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
-#undef FH_GMS
   return hipGetLastError();
 }
 

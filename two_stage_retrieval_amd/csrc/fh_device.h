@@ -122,6 +122,14 @@ __device__ __forceinline__ float gumbel_of_word(uint32_t x) {
 __device__ __forceinline__ float gumbel(uint64_t seed, uint32_t stream, uint32_t idx) {
   return gumbel_of_word(philox_word(seed, stream, idx));
 }
+// the noise of ids 4 m .. 4 m + 3 from one Philox block (the same values as
+// gumbel() for each id)
+__device__ __forceinline__ float4 gumbel4(uint64_t seed, uint32_t stream, uint32_t m) {
+  const uint4 o = philox4x32_10(make_uint4(m, stream, 0u, 0u), (uint32_t)seed,
+                                (uint32_t)(seed >> 32));
+  return make_float4(gumbel_of_word(o.x), gumbel_of_word(o.y), gumbel_of_word(o.z),
+                     gumbel_of_word(o.w));
+}
 constexpr uint32_t kStreamCluster = 0;
 constexpr uint32_t kStreamToken = 1;
 

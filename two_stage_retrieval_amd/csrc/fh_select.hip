@@ -14,26 +14,37 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   uint32_t u[IPT];
   select_load_keys<IPT, false>(a.keys + (int64_t)r * a.key_stride, (int)a.key_stride, u);
   if (a.nparts > 1) {
-    // the scores arrive as K-slice partials: sum them in slice order, then
-    // form the keys (sampling: score / tau + Gumbel noise of stream 0)
+    // the scores arrive as K-slice partials: all slices are loaded before
+    // any is added, then summed in slice order; then the keys are formed
+    // (sampling: score / tau + Gumbel noise of stream 0, one Philox block per
+    // four consecutive ids)
     const int k0 = threadIdx.x * IPT;
-    for (int sp = 1; sp < a.nparts; ++sp) {
-      uint32_t v[IPT];
-      select_load_keys<IPT, false>(a.keys + sp * a.part_stride + (int64_t)r * a.key_stride,
-                                   (int)a.key_stride, v);
+    uint32_t v[kMaxKSplit - 1][IPT];
 #pragma unroll
-      for (int j = 0; j < IPT; ++j)
-        u[j] = __float_as_uint(__uint_as_float(u[j]) + __uint_as_float(v[j]));
-    }
+    for (int sp = 1; sp < kMaxKSplit; ++sp)
+      if (sp < a.nparts)
+        select_load_keys<IPT, false>(a.keys + sp * a.part_stride + (int64_t)r * a.key_stride,
+                                     (int)a.key_stride, v[sp - 1]);
+#pragma unroll
+    for (int sp = 1; sp < kMaxKSplit; ++sp)
+      if (sp < a.nparts)
+#pragma unroll
+        for (int j = 0; j < IPT; ++j)
+          u[j] = __float_as_uint(__uint_as_float(u[j]) + __uint_as_float(v[sp - 1][j]));
     const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const int k = k0 + j;
-      if (k >= a.c) continue;
-      const float sc = __uint_as_float(u[j]);
-      if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = sc;
-      if (a.sample)
-        u[j] = __float_as_uint(sc * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)k));
+    for (int j4 = 0; j4 < IPT; j4 += 4) {
+      float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.sample && k0 + j4 < a.c) g = gumbel4(seed, kStreamCluster, (uint32_t)(k0 + j4) >> 2);
+      const float gj[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = k0 + j4 + q;
+        if (k >= a.c) continue;
+        const float sc = __uint_as_float(u[j4 + q]);
+        if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = sc;
+        if (a.sample) u[j4 + q] = __float_as_uint(sc * a.inv_tau + gj[q]);
+      }
     }
   }
   select_from_keys<kSelThreads, IPT, false>(u, a.c, a.p, a.sel + (int64_t)r * a.sel_stride,
