@@ -8,19 +8,41 @@
 #include "fh_device.h"
 #include "fh_internal.h"
 
+// Optional timeline hooks for measurement builds (empty in the library).
+#ifndef FH_PUB_TRACE
+#define FH_PUB_TRACE()
+#endif
+#ifndef FH_MERGE_POLL_TRACE
+#define FH_MERGE_POLL_TRACE(round)
+#endif
+
 namespace fh {
 
-// h (one row of H) into registers: chunk lane + 64 i of the row.
-template <typename TE, int NCH>
-__device__ __forceinline__ void load_h(const uint8_t* hrow, int nchunk, int lane,
-                                       float (&hreg)[NCH][Chunk<TE>::kElems]) {
+// h (one row of H): chunk lane + 64 i of the row, raw, then unpacked.
+template <int NCH>
+__device__ __forceinline__ void load_h_raw(const uint8_t* hrow, int nchunk, int lane,
+                                           uint4 (&hraw)[NCH]) {
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int ch = lane + kWave * i;
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (ch < nchunk) w = *reinterpret_cast<const uint4*>(hrow + (int64_t)ch * 16);
-    Chunk<TE>::unpack(w, hreg[i]);
+    hraw[i] = ch < nchunk ? *reinterpret_cast<const uint4*>(hrow + (int64_t)ch * 16)
+                          : make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+template <typename TE, int NCH>
+__device__ __forceinline__ void unpack_h(const uint4 (&hraw)[NCH],
+                                         float (&hreg)[NCH][Chunk<TE>::kElems]) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) Chunk<TE>::unpack(hraw[i], hreg[i]);
+}
+
+template <typename TE, int NCH>
+__device__ __forceinline__ void load_h(const uint8_t* hrow, int nchunk, int lane,
+                                       float (&hreg)[NCH][Chunk<TE>::kElems]) {
+  uint4 hraw[NCH];
+  load_h_raw<NCH>(hrow, nchunk, lane, hraw);
+  unpack_h<TE, NCH>(hraw, hreg);
 }
 
 // ---------------------------------------------------------------------------
@@ -36,8 +58,8 @@ constexpr uint32_t kKeyPending = 0xFFFFFFFFu;
 // With `keys_next`, also marks the row pending in the key buffer of the next
 // launch (single-launch batch-1 decode).
 template <bool COHERENT>
-__device__ __forceinline__ void publish_key(const Stage1Args& a, float* keys, float* keys_next,
-                                            float* dbg, uint64_t seed, int row, float score) {
+__device__ __forceinline__ float publish_key(const Stage1Args& a, float* keys, float* keys_next,
+                                             float* dbg, uint64_t seed, int row, float score) {
   const float key =
       a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
   if constexpr (COHERENT) {
@@ -47,32 +69,52 @@ __device__ __forceinline__ void publish_key(const Stage1Args& a, float* keys, fl
   }
   if (keys_next) keys_next[row] = __uint_as_float(kKeyPending);
   if (dbg) dbg[row] = score;
+  return key;
+}
+
+// Running best (key, row) of a lane as one orderable word: larger key,
+// then lower row (0 = none).
+__device__ __forceinline__ uint64_t key_row_word(float key, int row) {
+  return ((uint64_t)ordered_u32(key) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
 }
 
 constexpr int kS1Rows = 4;  // centroid rows per wave step (bf16 / fp32)
 
 // bf16 / fp32 centroid rows: wave w0, w0 + wstride, ... take groups of 4 rows.
+// h arrives raw (its loads issued by the caller) and is unpacked into hreg
+// only after the first group's rows have been requested, so that neither
+// waits for the other.
+template <typename TE, int NCH>
+__device__ __forceinline__ void load_centroid_group(const Stage1Args& a, int g, int lane,
+                                                    uint4 (&data)[kS1Rows][NCH]) {
+  const int row0 = g * kS1Rows;
+#pragma unroll
+  for (int rr = 0; rr < kS1Rows; ++rr) {
+    const int row = row0 + rr < a.c ? row0 + rr : a.c - 1;
+    const uint8_t* rowp = a.C + (int64_t)row * a.row_bytes;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = lane + kWave * i;
+      data[rr][i] = ch < a.nchunk ? *reinterpret_cast<const uint4*>(rowp + (int64_t)ch * 16)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// Groups g, g + wstride, ...; the rows of group g are already in `data` (if
+// g < number of groups).
 template <typename TE, int NCH, bool COHERENT>
-__device__ __forceinline__ void score_rows(const Stage1Args& a, float* keys, float* keys_next,
-                                           float* dbg, uint64_t seed,
-                                           const float (&hreg)[NCH][Chunk<TE>::kElems],
-                                           int lane, int w0, int wstride) {
+__device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys,
+                                                float* keys_next, float* dbg, uint64_t seed,
+                                                const uint4 (&hraw)[NCH],
+                                                float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
+                                                int g, int wstride, uint64_t& kbest,
+                                                uint4 (&data)[kS1Rows][NCH]) {
   using CK = Chunk<TE>;
   const int ngroups = (a.c + kS1Rows - 1) / kS1Rows;
-  for (int g = w0; g < ngroups; g += wstride) {
+  unpack_h<TE, NCH>(hraw, hreg);
+  while (g < ngroups) {
     const int row0 = g * kS1Rows;
-    uint4 data[kS1Rows][NCH];
-#pragma unroll
-    for (int rr = 0; rr < kS1Rows; ++rr) {
-      const int row = row0 + rr < a.c ? row0 + rr : a.c - 1;
-      const uint8_t* rowp = a.C + (int64_t)row * a.row_bytes;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int ch = lane + kWave * i;
-        data[rr][i] = ch < a.nchunk ? *reinterpret_cast<const uint4*>(rowp + (int64_t)ch * 16)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
     float acc[kS1Rows];
 #pragma unroll
     for (int rr = 0; rr < kS1Rows; ++rr) {
@@ -85,9 +127,25 @@ __device__ __forceinline__ void score_rows(const Stage1Args& a, float* keys, flo
 #pragma unroll
     for (int rr = 1; rr < kS1Rows; ++rr)
       if (lane == rr) mine = acc[rr];
-    if (lane < kS1Rows && row0 + lane < a.c)
-      publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine);
+    if (lane < kS1Rows && row0 + lane < a.c) {
+      const float key = publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine);
+      const uint64_t w = key_row_word(key, row0 + lane);
+      kbest = w > kbest ? w : kbest;
+    }
+    g += wstride;
+    if (g < ngroups) load_centroid_group<TE, NCH>(a, g, lane, data);
   }
+}
+
+template <typename TE, int NCH, bool COHERENT>
+__device__ __forceinline__ void score_rows(const Stage1Args& a, float* keys, float* keys_next,
+                                           float* dbg, uint64_t seed, const uint4 (&hraw)[NCH],
+                                           float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
+                                           int w0, int wstride, uint64_t& kbest) {
+  uint4 data[kS1Rows][NCH];
+  if (w0 < (a.c + kS1Rows - 1) / kS1Rows) load_centroid_group<TE, NCH>(a, w0, lane, data);
+  score_rows_from<TE, NCH, COHERENT>(a, keys, keys_next, dbg, seed, hraw, hreg, lane, w0,
+                                     wstride, kbest, data);
 }
 
 // INT4 centroids (notes, Module 3): one 16-row group tile per wave step,
@@ -97,7 +155,7 @@ template <bool COHERENT>
 __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* keys,
                                                  float* keys_next, float* dbg, uint64_t seed,
                                                  const float* s_h, int lane, int w0,
-                                                 int wstride) {
+                                                 int wstride, uint64_t& kbest) {
   const int q = lane >> 4, rin = lane & 15;
   const int G = a.groups;
   for (int tile = w0; tile < a.ntiles; tile += wstride) {
@@ -113,7 +171,11 @@ __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* key
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
     const int row = tile * 16 + rin;
-    if (q == 0 && row < a.c) publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc);
+    if (q == 0 && row < a.c) {
+      const float key = publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc);
+      const uint64_t w = key_row_word(key, row);
+      kbest = w > kbest ? w : kbest;
+    }
   }
 }
 
@@ -144,32 +206,45 @@ __device__ __forceinline__ int64_t selected_cluster(const int32_t* sel_row, int6
   }
 }
 
+// `win` (optional): entries [wlo, wlo + wn) of the selection already in
+// LDS; other entries are read from sel_row.
 template <typename TE, int NCH, int R, int MODE, bool POLL = false>
 __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32_t* sel_row,
                                          const float (&hreg)[NCH][Chunk<TE>::kElems],
                                          uint64_t seed, int lane, int64_t w0, int64_t wstride,
-                                         uint64_t& best, Lse& lse, uint32_t* error = nullptr) {
+                                         uint64_t& best, Lse& lse, uint32_t* error = nullptr,
+                                         const int32_t* win = nullptr, int64_t wlo = 0,
+                                         int64_t wn = 0) {
   using CK = Chunk<TE>;
   const int64_t ngroups = (a.nrows + R - 1) / R;
+  auto entry = [&](int64_t j) -> int64_t {
+    const int64_t q = j - wlo;
+    if (win && q >= 0 && q < wn) return win[q];
+    return selected_cluster<POLL>(sel_row, j, error);
+  };
   for (int64_t g = w0; g < ngroups; g += wstride) {
     const int64_t row0 = g * R;
     int64_t phys[R];
     if constexpr (MODE == kRowGather) {
-      // one selection entry per cluster the group touches (usually one)
-      const int64_t jfirst = row0 / a.b;
-      int64_t jprev = jfirst;
-      int64_t k = selected_cluster<POLL>(sel_row, jfirst, error);
+      // candidate i is slot i mod b of selection entry i / b (candidate
+      // indices fit 32 bits: there are at most v of them); one division per
+      // group, and one selection entry per cluster the group touches
+      const uint32_t b = (uint32_t)a.b;
+      uint32_t j = (uint32_t)row0 / b;
+      uint32_t slot = (uint32_t)row0 - j * b;
+      int64_t k = entry(j);
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        int64_t i = row0 + rr;
-        if (i >= a.nrows) i = a.nrows - 1;  // tail: reread the last row, result dropped
-        const int64_t j = i / a.b;
-        if (j != jprev) {
-          k = selected_cluster<POLL>(sel_row, j, error);
-          jprev = j;
+        if (rr > 0 && row0 + rr >= a.nrows) {
+          phys[rr] = phys[rr - 1];  // tail: reread a row, result dropped
+          continue;
+        }
+        if (rr > 0 && ++slot == b) {
+          slot = 0;
+          k = entry(++j);
         }
         const int64_t kc = k < 0 ? 0 : (k >= a.nclusters ? a.nclusters - 1 : k);  // stay in the table
-        phys[rr] = kc * a.b + (i - j * a.b);  // row of the cluster-major copy
+        phys[rr] = kc * (int64_t)b + slot;  // row of the cluster-major copy
       }
     } else {
 #pragma unroll
@@ -351,6 +426,7 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
       }
       __hip_atomic_store(slot + block * kSlotWords, bb ? bb : 1ull, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+      FH_PUB_TRACE();
     }
     return false;
   }
@@ -371,6 +447,7 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
     if (j != 0 && j < nblocks) todo |= 1u << q;
   }
   for (int it = 0;; ++it) {
+    FH_MERGE_POLL_TRACE(it);
     uint64_t xs[kQ];
 #pragma unroll
     for (int q = 0; q < kQ; ++q)

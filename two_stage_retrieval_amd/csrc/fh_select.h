@@ -74,13 +74,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sel_rsrc(const void* base, uin
 }
 
 // One 16-byte load.  COHERENT reads data that other workgroups of the
-// running kernel wrote with device-scope stores.
+// running kernel wrote with device-scope stores.  The compiler treats these
+// loads as plain reads: a loop that polls with them needs poll_barrier()
+// in every round, or the reloads are merged with the first load.
 template <bool COHERENT>
 __device__ __forceinline__ uint4 sel_load4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
   const auto v =
       __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, COHERENT ? kCachePolicySc1 : 0);
   return __builtin_bit_cast(uint4, v);
 }
+
+// Compiler-only memory barrier (no instruction): memory may have changed,
+// so loads after it are not merged with loads before it.
+__device__ __forceinline__ void poll_barrier() { asm volatile("" ::: "memory"); }
 
 // Loads this thread's IPT keys (thread t owns [t*IPT, t*IPT + IPT)) as raw
 // fp32 bits.  `keys` is 16-byte aligned with room for `stride` floats
@@ -101,32 +107,24 @@ __device__ __forceinline__ void select_load_keys(const float* keys, int stride,
   }
 }
 
-// Selects p of the c keys held by the workgroup (raw fp32 bits in u, from
-// select_load_keys); writes the ids ascending to out[0..p) (global or LDS
-// memory).  COHERENT_OUT stores the ids device-coherently for readers in
-// the running kernel.  With `masks`, also sets bit `row` of masks[k] for
-// every selected k.  Sets bit 0 of *error (if given) when the selection did
-// not produce exactly p ids.  Needs NT * IPT >= c.
-template <int NT, int IPT, bool COHERENT_OUT>
-__device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
-                                 uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
-  static_assert(IPT % 4 == 0 && IPT <= 32, "items per thread");
-  constexpr int NW = NT / kWave;
-  constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
+// Clears what the selection accumulates into (histogram, boundary id bitmap
+// words of [0, c), counters).  Needs no key, so a caller that waits for the
+// keys can do it beforehand.
+template <int NT>
+__device__ __forceinline__ void select_clear(int c, SelSmem& sm) {
   const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const int wave = t >> 6;
-  const int k0 = t * IPT;
-  int parity = 0;
-
-  // ---- block min / max ----------------------------------------------------------
-  FH_SEL_TRACE(0);
   for (int i = t; i < kSelBins; i += NT) sm.hist[i] = 0;
-  for (int i = t; i < FH_MAX_C / 32; i += NT) sm.chosen[i] = 0u;
+  for (int i = t; i < (c + 31) / 32; i += NT) sm.chosen[i] = 0u;
   if (t < 8) sm.misc[t] = 0;
+}
+
+// The wave's min / max of the keys its threads own (raw fp32 bits; items
+// past c are skipped) into sm.fmin / sm.fmax[wave].
+template <int IPT>
+__device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int c, SelSmem& sm) {
+  const int t = threadIdx.x;
+  const int k0 = t * IPT;
   const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
-  // u keeps the raw fp32 bits; the order-preserving form is made where the
-  // bits themselves are compared (boundary candidates, radix passes)
   float lmax = -INFINITY, lmin = INFINITY;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
@@ -136,14 +134,44 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
       lmin = fminf(lmin, f);
     }
   }
-  FH_SEL_TRACE(1);
   lmax = wave_max_dpp(lmax);
   lmin = wave_min_dpp(lmin);
-  if (lane == 0) {
-    sm.fmax[wave] = lmax;
-    sm.fmin[wave] = lmin;
+  if ((t & (kWave - 1)) == 0) {
+    sm.fmax[t >> 6] = lmax;
+    sm.fmin[t >> 6] = lmin;
   }
-  __syncthreads();
+}
+
+// Selects p of the c keys held by the workgroup (raw fp32 bits in u, from
+// select_load_keys); writes the ids ascending to out[0..p) (global or LDS
+// memory).  COHERENT_OUT stores the ids device-coherently for readers in
+// the running kernel.  With `masks`, also sets bit `row` of masks[k] for
+// every selected k.  Sets bit 0 of *error (if given) when the selection did
+// not produce exactly p ids.  Needs NT * IPT >= c.  PREPARED: the caller has
+// run select_clear and select_wave_range on these keys, followed by a
+// barrier.
+template <int NT, int IPT, bool COHERENT_OUT, bool PREPARED = false>
+__device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
+                                 uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
+  static_assert(IPT % 4 == 0 && IPT <= 32, "items per thread");
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  const int k0 = t * IPT;
+  const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
+  int parity = 0;
+
+  // ---- block min / max ----------------------------------------------------------
+  // u keeps the raw fp32 bits; the order-preserving form is made where the
+  // bits themselves are compared (boundary candidates, radix passes)
+  FH_SEL_TRACE(0);
+  if constexpr (!PREPARED) {
+    select_clear<NT>(c, sm);
+    select_wave_range<IPT>(u, c, sm);
+    __syncthreads();
+  }
   FH_SEL_TRACE(2);
   float fmax = sm.fmax[0], fmin = sm.fmin[0];
 #pragma unroll

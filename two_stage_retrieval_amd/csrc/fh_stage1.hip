@@ -24,11 +24,27 @@
 #ifndef FH_S1_TRACE
 #define FH_S1_TRACE(slot)
 #endif
+#ifndef FH_B1_PREFETCH
+#define FH_B1_PREFETCH 0
+#endif
+#ifndef FH_S1_WAVE_TRACE
+#define FH_S1_WAVE_TRACE(wave)
+#endif
+#ifndef FH_S2_WAVE_TRACE
+#define FH_S2_WAVE_TRACE(wave)
+#endif
+#ifndef FH_S1_POLL_TRACE
+#define FH_S1_POLL_TRACE(round)
+#endif
 
 namespace fh {
 
 constexpr int kS1Threads = 512;
 constexpr int kS1Waves = kS1Threads / kWave;
+// selection entries the rows of one workgroup's first groups can touch
+// (kS1Waves groups of at most 8 rows, at least one row per entry)
+constexpr int kB1Window = 2 * kWave;
+static_assert(kS1Waves * 8 + 1 <= kB1Window, "stage-2 entry window");
 
 template <typename TE, int NCH, int IPT, bool INT4, bool SELECT>
 __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
@@ -46,14 +62,18 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   const int w0 = blockIdx.x * kS1Waves + wave, wstride = gridDim.x * kS1Waves;
 
   if constexpr (!INT4) {
+    uint4 hraw[NCH];
     float hreg[NCH][Chunk<TE>::kElems];
-    load_h<TE, NCH>(hrow, a.nchunk, lane, hreg);
-    score_rows<TE, NCH, SELECT>(a, keys, nullptr, dbg, seed, hreg, lane, w0, wstride);
+    load_h_raw<NCH>(hrow, a.nchunk, lane, hraw);
+    uint64_t kbest = 0;
+    score_rows<TE, NCH, SELECT>(a, keys, nullptr, dbg, seed, hraw, hreg, lane, w0, wstride,
+                                kbest);
   } else {
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(hrow);
     for (int i = t; i < a.d; i += kS1Threads) s_h[i] = __uint_as_float((uint32_t)hb[i] << 16);
     __syncthreads();
-    score_int4_tiles<SELECT>(a, keys, nullptr, dbg, seed, s_h, lane, w0, wstride);
+    uint64_t kbest = 0;
+    score_int4_tiles<SELECT>(a, keys, nullptr, dbg, seed, s_h, lane, w0, wstride, kbest);
   }
   FH_S1_TRACE(1);
   if constexpr (!SELECT) return;
@@ -108,6 +128,44 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int w0 = blockIdx.x * kS1Waves + wave, wstride = gridDim.x * kS1Waves;
+
+  // ---- A: stage-1 share ----------------------------------------------------------
+  // h and the wave's first centroid rows are requested before anything else
+  // is waited for (the buffer set and the seed are needed only when keys
+  // are stored)
+  FH_S1_TRACE(0);
+  // Straight-line prologue: bounds-checked buffer loads (a chunk past the
+  // row, or a group past the last, reads as zero without a memory access),
+  // so that the requests go out after one wait for the few arguments they
+  // need, ahead of everything the rest of the kernel loads.
+  float hreg[NCH][Chunk<TE>::kElems];
+  uint4 hraw[NCH];
+  uint4 data[kS1Rows][NCH];
+  {
+    const int nch2 = args.s2.nchunk;
+    const __amdgpu_buffer_rsrc_t hrs = sel_rsrc(a.H, (uint32_t)nch2 * 16u);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      hraw[i] = sel_load4<false>(hrs, (uint32_t)(lane + kWave * i) * 16u);
+    if constexpr (!INT4) {
+      const __amdgpu_buffer_rsrc_t crs = sel_rsrc(a.C, (uint32_t)(a.c * a.row_bytes));
+      const bool have = w0 < (a.c + kS1Rows - 1) / kS1Rows;
+#pragma unroll
+      for (int rr = 0; rr < kS1Rows; ++rr) {
+        const int row = w0 * kS1Rows + rr < a.c ? w0 * kS1Rows + rr : a.c - 1;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int ch = lane + kWave * i;
+          const uint32_t off = (have && ch < a.nchunk)
+                                   ? (uint32_t)(row * a.row_bytes) + (uint32_t)ch * 16u
+                                   : 0xFFFFFFF0u;
+          data[rr][i] = sel_load4<false>(crs, off);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const uint32_t epoch = __builtin_amdgcn_readfirstlane(
       __hip_atomic_load(args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   const int cur = (int)(epoch & 1u);
@@ -115,45 +173,104 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   float* keys_next = a.keys + (int64_t)(1 - cur) * a.key_stride;
   int32_t* sel = args.sel + (int64_t)cur * kDecodeB1MaxP;
   int32_t* sel_next = args.sel + (int64_t)(1 - cur) * kDecodeB1MaxP;
-  FH_S1_TRACE(0);
   const uint64_t seed = a.sample ? a.seeds[0] : 0ull;
-  const int w0 = blockIdx.x * kS1Waves + wave, wstride = gridDim.x * kS1Waves;
-
-  // ---- A: stage-1 share ----------------------------------------------------------
-  float hreg[NCH][Chunk<TE>::kElems];
-  load_h<TE, NCH>(a.H, args.s2.nchunk, lane, hreg);
+  uint64_t kbest = 0;
   if constexpr (!INT4) {
-    score_rows<TE, NCH, true>(a, keys, keys_next, a.dbg_scores, seed, hreg, lane, w0, wstride);
+    score_rows_from<TE, NCH, true>(a, keys, keys_next, a.dbg_scores, seed, hraw, hreg, lane, w0,
+                                   wstride, kbest, data);
   } else {
-    const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.H);
-    for (int i = t; i < a.d; i += kS1Threads) s_h[i] = __uint_as_float((uint32_t)hb[i] << 16);
+    // h in LDS for the INT4 tiles, written by wave 0 from its registers
+    // (lane l holds elements 8 (l + 64 i) .. 8 (l + 64 i) + 7)
+    unpack_h<TE, NCH>(hraw, hreg);
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ch = lane + kWave * i;
+        if (ch < args.s2.nchunk) {
+#pragma unroll
+          for (int e = 0; e < Chunk<TE>::kElems; ++e) s_h[ch * Chunk<TE>::kElems + e] = hreg[i][e];
+        }
+      }
+    }
     __syncthreads();
-    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride);
+    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride,
+                           kbest);
   }
   FH_S1_TRACE(1);
+  FH_S1_WAVE_TRACE(wave);
+#if FH_B1_PREFETCH
+  // The cluster with the workgroup's best key is very likely selected: its
+  // rows of the cluster-major copy are requested now, while workgroup 0
+  // selects, so that stage 2 finds them in the memory-side cache.  The data
+  // land in an LDS scratch area nobody reads (direct loads to LDS leave no
+  // register to wait on).
+  __shared__ uint64_t s_kb[kS1Waves];
+  __shared__ uint4 s_pf[kS1Waves][kWave];
+  if (blockIdx.x != 0) {
+    kbest = wave_max_u64(kbest);
+    if (lane == 0) s_kb[wave] = kbest;
+    __syncthreads();
+    if (wave >= 1) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int w = 0; w < kS1Waves; ++w) m = s_kb[w] > m ? s_kb[w] : m;
+      if (m != 0) {
+        const int64_t k = (int64_t)(0xFFFFFFFFu - (uint32_t)m);
+        const int64_t bytes = (int64_t)args.s2.b * args.s2.row_bytes;
+        const uint8_t* src = args.s2.base + k * bytes;
+        constexpr int kPfWaves = kS1Waves - 1;
+        const int64_t per = ((bytes + kPfWaves - 1) / kPfWaves + 1023) & ~(int64_t)1023;
+        const int64_t lo = (int64_t)(wave - 1) * per;
+        const int64_t hi = lo + per < bytes ? lo + per : bytes;
+        for (int64_t off = lo; off + 1024 <= hi; off += 1024)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(src + off + lane * 16),
+              (void __attribute__((address_space(3)))*)&s_pf[wave][0], 16, 0, 0);
+      }
+    }
+  }
+#endif
 
 
   // ---- B: workgroup 0 waits for all keys, selects and publishes ------------------
   if (blockIdx.x == 0) {
     for (int i = t; i < kDecodeB1MaxP; i += kS1Threads) sel_next[i] = -1;
+    select_clear<kS1Threads>(a.c, sm);  // ordered before the selection by the polls' barriers
     uint32_t u[IPT];
     const int k0 = t * IPT;
     const int nvalid = a.c - k0 < 0 ? 0 : (a.c - k0 < IPT ? a.c - k0 : IPT);
+    // each wave polls its own keys (no block barrier per round); a thread
+    // rereads only the 16-byte chunks that still hold a pending key
+    const __amdgpu_buffer_rsrc_t krs = sel_rsrc(keys, (uint32_t)a.key_stride * 4u);
     select_load_keys<IPT, true>(keys, (int)a.key_stride, u);
     for (int it = 0;; ++it) {
-      int pending = 0;
+      uint32_t pend = 0u;  // chunks with a pending key
 #pragma unroll
-      for (int j = 0; j < IPT; ++j) pending |= (j < nvalid && u[j] == kKeyPending) ? 1 : 0;
-      if (!__syncthreads_or(pending)) break;
+      for (int j = 0; j < IPT; ++j)
+        if (j < nvalid && u[j] == kKeyPending) pend |= 1u << (j / 4);
+      FH_S1_POLL_TRACE(it);
+      if (!__any(pend != 0u)) break;
       if (it == kArriveSpinLimit) {
-        if (t == 0 && a.error) atomicOr(a.error, 2u);
+        if (lane == 0 && a.error) atomicOr(a.error, 2u);
         break;
       }
-      if (pending) select_load_keys<IPT, true>(keys, (int)a.key_stride, u);  // only if needed
+      poll_barrier();
+#pragma unroll
+      for (int q = 0; q < IPT / 4; ++q) {
+        if ((pend >> q) & 1u) {
+          const uint4 v = sel_load4<true>(krs, (uint32_t)(k0 + 4 * q) * 4u);
+          u[4 * q] = v.x;
+          u[4 * q + 1] = v.y;
+          u[4 * q + 2] = v.z;
+          u[4 * q + 3] = v.w;
+        }
+      }
     }
+    select_wave_range<IPT>(u, a.c, sm);
+    __syncthreads();
     FH_S1_TRACE(2);
     // the selection goes to LDS, then out in one coalesced device-coherent pass
-    select_from_keys<kS1Threads, IPT, false>(u, a.c, a.p, s_sel, nullptr, 0, a.error, sm);
+    select_from_keys<kS1Threads, IPT, false, true>(u, a.c, a.p, s_sel, nullptr, 0, a.error, sm);
     __syncthreads();
     for (int i = t; i < a.p; i += kS1Threads)
       __hip_atomic_store(sel + i, s_sel[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -161,29 +278,56 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   }
 
   // ---- C: stage-2 share ---------------------------------------------------------
-  // one lane per workgroup waits for the entries of the workgroup's first rows
-  // (the whole selection is published at once), instead of every wave
-  // polling the same lines
+  // The entries of the workgroup's first groups (one group per wave when the
+  // grid covers the rows) are fetched once, by wave 0, into LDS: one
+  // coherent round trip per workgroup instead of one per wave.  Workgroup 0
+  // has the whole selection in LDS already.
+  __shared__ int32_t s_win[kB1Window];
+  int64_t wlo = 0, wn = 0;
   if (blockIdx.x != 0) {
-    if (t == 0) {
-      const int64_t ngroups = (args.s2.nrows + R - 1) / R;
-      const int64_t g0 = (int64_t)blockIdx.x * kS1Waves;
-      if (g0 < ngroups) {
-        const int64_t g1 = g0 + kS1Waves - 1 < ngroups ? g0 + kS1Waves - 1 : ngroups - 1;
-        (void)selected_cluster<true>(sel, g0 * R / args.s2.b, a.error);
-        (void)selected_cluster<true>(sel, (g1 * R + R - 1 < args.s2.nrows ? g1 * R + R - 1
-                                                                        : args.s2.nrows - 1) /
-                                              args.s2.b,
-                                     a.error);
+    const int64_t ngroups = (args.s2.nrows + R - 1) / R;
+    const int64_t g0 = (int64_t)blockIdx.x * kS1Waves;
+    if (g0 < ngroups) {
+      const int64_t g1 = g0 + kS1Waves < ngroups ? g0 + kS1Waves : ngroups;
+      const int64_t rend = g1 * R < args.s2.nrows ? g1 * R : args.s2.nrows;
+      wlo = g0 * R / args.s2.b;
+      wn = (rend - 1) / args.s2.b - wlo + 1;
+    }
+    if (wave == 0 && wn > 0) {
+      const bool n0 = lane < wn, n1 = lane + kWave < wn;
+      int32_t e0 = -1, e1 = -1;
+      for (int it = 0;; ++it) {
+        if (n0 && e0 < 0)
+          e0 = __hip_atomic_load(sel + wlo + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n1 && e1 < 0)
+          e1 = __hip_atomic_load(sel + wlo + lane + kWave, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (!__any((n0 && e0 < 0) || (n1 && e1 < 0))) break;
+        if (it == kArriveSpinLimit) {
+          if (lane == 0 && a.error) atomicOr(a.error, 4u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
+      if (n0) s_win[lane] = e0;
+      if (n1) s_win[lane + kWave] = e1;
     }
     __syncthreads();
+    FH_S1_TRACE(7);
   }
   uint64_t best = 0;
   Lse lse = lse_empty();
-  // workgroup 0 reads its own copy in LDS
-  dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, blockIdx.x == 0 ? s_sel : sel, hreg, seed,
-                                         lane, w0, wstride, best, lse, a.error);
+  if (blockIdx.x == 0) {
+    dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, sel, hreg, seed, lane, w0, wstride, best,
+                                           lse, a.error, s_sel, 0, a.p);
+  } else {
+    dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, sel, hreg, seed, lane, w0, wstride, best,
+                                           lse, a.error, s_win, wlo, wn);
+  }
+#if FH_B1_PREFETCH
+  __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS load outlives the workgroup
+#endif
+  FH_S2_WAVE_TRACE(wave);
   FH_S1_TRACE(5);
 
   // ---- D: the decode merge; workgroup 0 then advances the epoch --------------------
