@@ -124,3 +124,45 @@ def test_stream_read_reference(fh):
     assert sink.cpu().numpy().tolist() == [0, 0, 0, 0]
     with pytest.raises(fh.FlashHeadError):
         fh.flashhead_stream_read(buf[1:], sink)  # misaligned, not a multiple of 16 bytes
+
+
+def with_outlier_centroids(cs, frac=0.01, factor=32.0, seed=91):
+    """A copy of the case whose centroid rows include a few scaled by a
+    power of two (exact in bf16): their scores spread far beyond the
+    others', which inflates the spread of all keys while leaving only a
+    handful far above the mean."""
+    import copy
+    rng = np.random.default_rng(seed)
+    out = copy.copy(cs)
+    C64 = cs.C64.copy()
+    rows = rng.choice(C64.shape[0], size=max(1, int(frac * C64.shape[0])), replace=False)
+    C64[rows] *= factor
+    out.C64 = C64
+    out.C_store = ref.bf16_bits_of(C64) if cs.dtype == "bf16" else C64.astype(np.float32)
+    out.C_dev = dev_tensor(out.C_store)
+    return out
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_selection_with_outlier_keys(fh, B):
+    # few keys far above the rest: the histogram range the key moments
+    # suggest holds fewer than p keys, and the selection redoes it over the
+    # full range (both the single-launch and the batched selection)
+    cs = with_outlier_centroids(case(1))
+    head = cs.prepare(fh, max_batch=B, max_p=64)
+    H, H64 = cs.hidden(B, offset=700)
+    # the case does take the second pass: fewer than p scores lie above
+    # mean + z sd, z the normal quantile with upper tail 4 p / c
+    from scipy.stats import norm
+    z = norm.isf(4 * 64 / cs.wl.c)
+    for r in range(B):
+        sc = cs.oracle_scores(H64[r])
+        assert np.count_nonzero(sc >= sc.mean() + z * sc.std()) < 64
+    st = Stats()
+    res = run_debug(fh, head, dev_tensor(H), B, 64, "greedy")
+    check_batch(cs, res, H64, 64, stats=st)
+    seeds = synth.make_seeds(9, B)
+    res = run_debug(fh, head, dev_tensor(H), B, 64, "sample", 0.7, seeds_dev(seeds))
+    check_batch(cs, res, H64, 64, "sample", 0.7, seeds, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)

@@ -284,6 +284,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.seeds = seeds;
   s1.select = (!batched && stage1_selects(h->c)) ? 1 : 0;
   s1.p = p;
+  s1.zcut = select_zcut(h->c, p);
   s1.counters = h->counters;
   s1.sel = h->sel;
   s1.sel_stride = h->max_p;
@@ -364,6 +365,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.key_stride = key_stride(h->c);
     a.c = h->c;
     a.p = p;
+    a.zcut = s1.zcut;
     a.sel = h->sel;
     a.sel_stride = h->max_p;
     a.masks = batched ? h->masks : nullptr;

@@ -39,18 +39,26 @@ template <> struct Chunk<float> {
   }
 };
 struct bf16_t {};  // storage tag: 16-bit brain float
+// h is kept as its raw bf16 pairs (one 32-bit word per pair, bit-cast to
+// float storage); each word of a row chunk meets the matching word of h in
+// one two-way dot-product instruction: both bf16 x bf16 products are exact
+// in fp32 and are added to the fp32 accumulator by the instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t w, float h, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, h), acc, false);
+}
 template <> struct Chunk<bf16_t> {
-  static constexpr int kElems = 8;
+  static constexpr int kElems = 4;
   __device__ __forceinline__ static void unpack(const uint4& w, float* out) {
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+    out[0] = __uint_as_float(w.x); out[1] = __uint_as_float(w.y);
+    out[2] = __uint_as_float(w.z); out[3] = __uint_as_float(w.w);
   }
-  // bf16 x bf16 products are exact in fp32; fmaf adds them with one rounding.
   __device__ __forceinline__ static float dot(const uint4& w, const float* h, float acc) {
-    acc = fmaf(bf16_lo(w.x), h[0], acc); acc = fmaf(bf16_hi(w.x), h[1], acc);
-    acc = fmaf(bf16_lo(w.y), h[2], acc); acc = fmaf(bf16_hi(w.y), h[3], acc);
-    acc = fmaf(bf16_lo(w.z), h[4], acc); acc = fmaf(bf16_hi(w.z), h[5], acc);
-    acc = fmaf(bf16_lo(w.w), h[6], acc); acc = fmaf(bf16_hi(w.w), h[7], acc);
+    acc = dot2_bf16(w.x, h[0], acc);
+    acc = dot2_bf16(w.y, h[1], acc);
+    acc = dot2_bf16(w.z, h[2], acc);
+    acc = dot2_bf16(w.w, h[3], acc);
     return acc;
   }
 };
@@ -196,6 +204,16 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x118, 0xf, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x142, 0xa, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_add_dpp(float x) {
+  float v = x;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_min_dpp(float x) {

@@ -60,6 +60,7 @@ struct SelectArgs {
   const uint64_t* seeds;
   float* dbg_scores;     // B x c
   int c, p;
+  float zcut;            // histogram range hint (select_zcut; 0: none)
   int32_t* sel;          // B x sel_stride, written ascending
   int sel_stride;
   uint64_t* masks;       // optional: per-cluster bitmask of selecting rows
@@ -124,6 +125,7 @@ struct Stage1Args {
   // selection by the last block of each batch row (when select != 0)
   int select;
   int p;
+  float zcut;             // histogram range hint (select_zcut; 0: none)
   uint32_t* counters;     // B x kArriveWords arrival counters (zero between calls)
   int32_t* sel;           // B x sel_stride, written ascending
   int sel_stride;
@@ -162,6 +164,10 @@ hipError_t launch_rowdot(const RowdotArgs& a, int mode, int dtype, int B, int gr
                          hipStream_t s, const Timing* tm = nullptr);
 int rowdot_grid(int64_t nrows, int nchunk, int mode);
 hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing* tm = nullptr);
+// The selection's histogram range hint for p of c keys: z with an upper
+// normal tail of min(1, 4 p / c), or 0 (no hint) when that tail is half or
+// more, or c is small.
+float select_zcut(int c, int p);
 hipError_t launch_stage1(const Stage1Args& a, int dtype, bool int4, int B, hipStream_t s,
                          const Timing* tm = nullptr);
 bool stage1_selects(int c);

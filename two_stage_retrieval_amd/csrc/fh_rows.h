@@ -58,8 +58,8 @@ constexpr uint32_t kKeyPending = 0xFFFFFFFFu;
 // With `keys_next`, also marks the row pending in the key buffer of the next
 // launch (single-launch batch-1 decode).
 template <bool COHERENT>
-__device__ __forceinline__ float publish_key(const Stage1Args& a, float* keys, float* keys_next,
-                                             float* dbg, uint64_t seed, int row, float score) {
+__device__ __forceinline__ void publish_key(const Stage1Args& a, float* keys, float* keys_next,
+                                            float* dbg, uint64_t seed, int row, float score) {
   const float key =
       a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
   if constexpr (COHERENT) {
@@ -69,14 +69,8 @@ __device__ __forceinline__ float publish_key(const Stage1Args& a, float* keys, f
   }
   if (keys_next) keys_next[row] = __uint_as_float(kKeyPending);
   if (dbg) dbg[row] = score;
-  return key;
 }
 
-// Running best (key, row) of a lane as one orderable word: larger key,
-// then lower row (0 = none).
-__device__ __forceinline__ uint64_t key_row_word(float key, int row) {
-  return ((uint64_t)ordered_u32(key) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
-}
 
 constexpr int kS1Rows = 4;  // centroid rows per wave step (bf16 / fp32)
 
@@ -108,7 +102,7 @@ __device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys
                                                 float* keys_next, float* dbg, uint64_t seed,
                                                 const uint4 (&hraw)[NCH],
                                                 float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
-                                                int g, int wstride, uint64_t& kbest,
+                                                int g, int wstride,
                                                 uint4 (&data)[kS1Rows][NCH]) {
   using CK = Chunk<TE>;
   const int ngroups = (a.c + kS1Rows - 1) / kS1Rows;
@@ -127,11 +121,8 @@ __device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys
 #pragma unroll
     for (int rr = 1; rr < kS1Rows; ++rr)
       if (lane == rr) mine = acc[rr];
-    if (lane < kS1Rows && row0 + lane < a.c) {
-      const float key = publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine);
-      const uint64_t w = key_row_word(key, row0 + lane);
-      kbest = w > kbest ? w : kbest;
-    }
+    if (lane < kS1Rows && row0 + lane < a.c)
+      publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine);
     g += wstride;
     if (g < ngroups) load_centroid_group<TE, NCH>(a, g, lane, data);
   }
@@ -141,11 +132,11 @@ template <typename TE, int NCH, bool COHERENT>
 __device__ __forceinline__ void score_rows(const Stage1Args& a, float* keys, float* keys_next,
                                            float* dbg, uint64_t seed, const uint4 (&hraw)[NCH],
                                            float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
-                                           int w0, int wstride, uint64_t& kbest) {
+                                           int w0, int wstride) {
   uint4 data[kS1Rows][NCH];
   if (w0 < (a.c + kS1Rows - 1) / kS1Rows) load_centroid_group<TE, NCH>(a, w0, lane, data);
   score_rows_from<TE, NCH, COHERENT>(a, keys, keys_next, dbg, seed, hraw, hreg, lane, w0,
-                                     wstride, kbest, data);
+                                     wstride, data);
 }
 
 // INT4 centroids (notes, Module 3): one 16-row group tile per wave step,
@@ -155,7 +146,7 @@ template <bool COHERENT>
 __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* keys,
                                                  float* keys_next, float* dbg, uint64_t seed,
                                                  const float* s_h, int lane, int w0,
-                                                 int wstride, uint64_t& kbest) {
+                                                 int wstride) {
   const int q = lane >> 4, rin = lane & 15;
   const int G = a.groups;
   for (int tile = w0; tile < a.ntiles; tile += wstride) {
@@ -171,11 +162,7 @@ __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* key
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
     const int row = tile * 16 + rin;
-    if (q == 0 && row < a.c) {
-      const float key = publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc);
-      const uint64_t w = key_row_word(key, row);
-      kbest = w > kbest ? w : kbest;
-    }
+    if (q == 0 && row < a.c) publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc);
   }
 }
 

@@ -6,17 +6,21 @@
 //
 // Thread t owns the IPT consecutive ids [t*IPT, t*IPT + IPT), read with
 // 16-byte loads, so that a scan of per-thread counts is already in id order.
-//  1. block min / max of the keys (DPP wave reductions, one barrier);
-//  2. LDS histogram of 2048 equal-width value bins over [min, max] (a
-//     monotone function of the key, so bin order is key order); each item's
-//     bin is computed once and kept; a block scan from the top finds the
-//     boundary bin holding the p-th largest key;
+//  1. block min / max (and sum / sum of squares) of the keys (DPP wave
+//     reductions, one barrier);
+//  2. LDS histogram of 2048 equal-width value bins over [lo, max] (a
+//     monotone function of the key, so bin order is key order), lo = min,
+//     or a point the moments place below the p-th largest key (then the
+//     keys under it skip the histogram; if it turns out to leave fewer than
+//     p keys, the pass is redone with lo = min); each item's bin is
+//     computed once and kept; a block scan from the top finds the boundary
+//     bin holding the p-th largest key;
 //  3. the boundary bin is resolved exactly.  Up to 64 keys (the usual case:
-//     a handful) are gathered and wave 0 picks the ones needed with ballots,
-//     bit by bit over (key descending, id ascending).  Larger bins (heavily
-//     tied or skewed keys) first go through 8-bit radix passes on the
-//     order-preserving key bits; keys that stay exactly equal are taken
-//     lowest id first through a block scan;
+//     a handful) are gathered and wave 0 ranks each against the others in
+//     (key descending, id ascending) order, taking the ones needed.  Larger
+//     bins (heavily tied or skewed keys) first go through 8-bit radix passes
+//     on the order-preserving key bits; keys that stay exactly equal are
+//     taken lowest id first through a block scan;
 //  4. each thread counts its selected ids; one block scan gives every thread
 //     its output offset and the ids are written ascending.
 // Block scans use DPP inside the wave and one barrier each.
@@ -27,6 +31,9 @@
 // Optional phase hook for measurement builds (empty in the library).
 #ifndef FH_SEL_TRACE
 #define FH_SEL_TRACE(i)
+#endif
+#ifndef FH_SEL_STATE
+#define FH_SEL_STATE(lo, fmin, fmax, total, nb, ngt)
 #endif
 
 namespace fh {
@@ -40,7 +47,7 @@ struct SelSmem {
   uint32_t cu[kSelWaveMax];        // gathered boundary keys (order-preserving bits)
   int ck[kSelWaveMax];             // and their ids
   uint32_t chosen[FH_MAX_C / 32];  // ids picked inside the boundary bin (id bitmap)
-  float fmin[16], fmax[16];
+  float fmin[16], fmax[16], fsum[16], fsq[16];
   int w[2][16];                    // block-scan wave totals, alternating buffers
   int misc[8];
 };
@@ -118,27 +125,34 @@ __device__ __forceinline__ void select_clear(int c, SelSmem& sm) {
   if (t < 8) sm.misc[t] = 0;
 }
 
-// The wave's min / max of the keys its threads own (raw fp32 bits; items
-// past c are skipped) into sm.fmin / sm.fmax[wave].
+// The wave's min, max, sum and sum of squares of the keys its threads own
+// (raw fp32 bits; items past c are skipped) into sm.fmin / fmax / fsum /
+// fsq[wave].  The sums only steer the histogram range (see below).
 template <int IPT>
 __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int c, SelSmem& sm) {
   const int t = threadIdx.x;
   const int k0 = t * IPT;
   const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
-  float lmax = -INFINITY, lmin = INFINITY;
+  float lmax = -INFINITY, lmin = INFINITY, lsum = 0.0f, lsq = 0.0f;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     const float f = __uint_as_float(u[j]);
     if (j < nvalid) {
       lmax = fmaxf(lmax, f);
       lmin = fminf(lmin, f);
+      lsum += f;
+      lsq = fmaf(f, f, lsq);
     }
   }
   lmax = wave_max_dpp(lmax);
   lmin = wave_min_dpp(lmin);
+  lsum = wave_add_dpp(lsum);
+  lsq = wave_add_dpp(lsq);
   if ((t & (kWave - 1)) == 0) {
     sm.fmax[t >> 6] = lmax;
     sm.fmin[t >> 6] = lmin;
+    sm.fsum[t >> 6] = lsum;
+    sm.fsq[t >> 6] = lsq;
   }
 }
 
@@ -150,8 +164,15 @@ __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int 
 // not produce exactly p ids.  Needs NT * IPT >= c.  PREPARED: the caller has
 // run select_clear and select_wave_range on these keys, followed by a
 // barrier.
+//
+// zcut > 0 narrows the histogram to [mean + zcut * sd, max] of the keys
+// (keys below are not counted): with zcut chosen so that a normal sample
+// would leave a few times p keys in that range, most keys skip the
+// histogram and the bins are finer.  If fewer than p keys fall in the
+// range, the histogram is redone over [min, max]; the result never depends
+// on zcut.
 template <int NT, int IPT, bool COHERENT_OUT, bool PREPARED = false>
-__device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
+__device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, int32_t* out,
                                  uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
   static_assert(IPT % 4 == 0 && IPT <= 32, "items per thread");
   constexpr int NW = NT / kWave;
@@ -163,7 +184,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
   const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
   int parity = 0;
 
-  // ---- block min / max ----------------------------------------------------------
+  // ---- block min / max / moments --------------------------------------------------
   // u keeps the raw fp32 bits; the order-preserving form is made where the
   // bits themselves are compared (boundary candidates, radix passes)
   FH_SEL_TRACE(0);
@@ -173,31 +194,53 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
     __syncthreads();
   }
   FH_SEL_TRACE(2);
-  float fmax = sm.fmax[0], fmin = sm.fmin[0];
+  float fmax = sm.fmax[0], fmin = sm.fmin[0], fsum = sm.fsum[0], fsq = sm.fsq[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
     fmax = fmaxf(fmax, sm.fmax[w]);
     fmin = fminf(fmin, sm.fmin[w]);
+    fsum += sm.fsum[w];
+    fsq += sm.fsq[w];
   }
-  const float range = fmax - fmin;
-  const float scale = (float)kSelBins / range;
-  const float offset = -fmin * scale;
-  const bool flat = !(range > 0.0f) || !(scale < INFINITY) || !(offset > -INFINITY && offset < INFINITY);
+  float lo = fmin;
+  if (zcut > 0.0f) {
+    const float mean = fsum / (float)c;
+    const float sd = sqrtf(fmaxf(fsq / (float)c - mean * mean, 0.0f));
+    const float t0 = fmaf(zcut, sd, mean);
+    if (t0 > fmin && t0 < fmax) lo = t0;  // false for NaN or infinite moments
+  }
 
   // ---- histogram and the boundary bin -----------------------------------------
-  uint32_t bins[IPT / 2];  // this thread's item bins, two 16-bit bins per word
+  // bins[j / 2] holds this thread's item bins + 1 in 16 bits each (0: below
+  // the histogram's range)
+  uint32_t bins[IPT / 2];
   int beta = 0, ngt = 0, nb = 0;
-  if (!flat) {
+  for (;;) {  // at most two passes (block-uniform)
+    const float range = fmax - lo;
+    const float scale = (float)kSelBins / range;
+    const float offset = -lo * scale;
+    const bool flat =
+        !(range > 0.0f) || !(scale < INFINITY) || !(offset > -INFINITY && offset < INFINITY);
+    if (flat) {  // all keys equal (lo == fmin here): one bin holds all
 #pragma unroll
-    for (int j = 0; j < IPT; j += 2) {
-      // (f - min) * scale as one fma; a monotone map of f, clamped to the bins
-      int b0 = (int)fmaf(__uint_as_float(u[j]), scale, offset);
-      int b1 = (int)fmaf(__uint_as_float(u[j + 1]), scale, offset);
-      b0 = min(max(b0, 0), kSelBins - 1);
-      b1 = min(max(b1, 0), kSelBins - 1);
-      bins[j / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-      if (j < nvalid) atomicAdd(&sm.hist[b0], 1);
-      if (j + 1 < nvalid) atomicAdd(&sm.hist[b1], 1);
+      for (int j = 0; j < IPT / 2; ++j) bins[j] = 0x00010001u;
+      beta = 0;
+      ngt = 0;
+      nb = c;
+      break;
+    }
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      // (f - lo) * scale as one fma: a monotone map of f, clamped to the bins
+      const float f = __uint_as_float(u[j]);
+      uint32_t bp = 0u;
+      if (j < nvalid && f >= lo) {
+        const int b = min(max((int)fmaf(f, scale, offset), 0), kSelBins - 1);
+        atomicAdd(&sm.hist[b], 1);
+        bp = (uint32_t)b + 1u;
+      }
+      if (j & 1) bins[j / 2] |= bp << 16;
+      else bins[j / 2] = bp;
     }
     __syncthreads();
     FH_SEL_TRACE(3);
@@ -210,6 +253,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
     }
     const int incl = sel_scan<NT>(hs, sm, parity, lane, wave);
     int acc = incl - hs;
+    if (t == NT - 1) sm.misc[7] = incl;  // keys in the histogram
     if (acc < p && p <= incl) {
 #pragma unroll
       for (int q = 0; q < BPT; ++q) {
@@ -226,11 +270,13 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
     beta = sm.misc[0];
     ngt = sm.misc[1];
     nb = sm.misc[2];
-  } else {
-#pragma unroll
-    for (int j = 0; j < IPT / 2; ++j) bins[j] = 0u;
-    nb = c;
+    if (sm.misc[7] >= p || lo == fmin) break;
+    // fewer than p keys in the narrowed range: again over [min, max]
+    lo = fmin;
+    for (int i = t; i < kSelBins; i += NT) sm.hist[i] = 0;
+    __syncthreads();
   }
+  FH_SEL_STATE(lo, fmin, fmax, sm.misc[7], nb, ngt);
   FH_SEL_TRACE(4);
   int need = p - ngt;  // ids still to take from the boundary bin
 
@@ -238,7 +284,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     if (j >= nvalid) continue;
-    const int b = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+    const int b = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xFFFFu) - 1;  // -1: below range
     if (b > beta) above |= 1u << j;
     else if (b == beta) cand |= 1u << j;
   }
@@ -310,40 +356,18 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
     }
     __syncthreads();
     if (wave == 0) {
+      // each candidate's rank in (key descending, id ascending); the `need`
+      // first are taken
       const bool live = lane < nb;
       const uint32_t uu = live ? sm.cu[lane] : 0u;
       const uint32_t kk = live ? (uint32_t)sm.ck[lane] : 0u;
-      uint64_t L = __ballot(live);
-      uint64_t pick = 0ull;
-      int rem = need;
-      // keys descending: a set bit ranks higher
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint64_t ones = __ballot((uu >> bit) & 1u) & L;
-        const int n1 = __popcll(ones);
-        if (n1 == 0 || ones == L) continue;
-        if (n1 >= rem) {
-          L = ones;
-        } else {
-          pick |= ones;
-          rem -= n1;
-          L &= ~ones;
-        }
+      int rank = 0;
+      for (int j = 0; j < nb; ++j) {
+        const uint32_t uj = sm.cu[j];
+        const uint32_t kj = (uint32_t)sm.ck[j];
+        rank += (uj > uu || (uj == uu && kj < kk)) ? 1 : 0;
       }
-      // equal keys: ids ascending, a clear bit ranks higher
-      for (int bit = 15; bit >= 0; --bit) {
-        const uint64_t zeros = __ballot(((kk >> bit) & 1u) == 0u) & L;
-        const int n0 = __popcll(zeros);
-        if (n0 == 0 || zeros == L) continue;
-        if (n0 >= rem) {
-          L = zeros;
-        } else {
-          pick |= zeros;
-          rem -= n0;
-          L &= ~zeros;
-        }
-      }
-      pick |= L;  // one id is left, the last one needed
-      if ((pick >> lane) & 1ull) atomicOr(&sm.chosen[kk >> 5], 1u << (kk & 31));
+      if (live && rank < need) atomicOr(&sm.chosen[kk >> 5], 1u << (kk & 31));
     }
     __syncthreads();
 #pragma unroll
@@ -391,11 +415,11 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, int32_t* out,
 // Loads the keys and selects (see select_load_keys / select_from_keys).
 template <int NT, int IPT, bool COHERENT>
 __device__ __forceinline__ void select_block(const float* keys, int c, int stride, int p,
-                                             int32_t* out, uint64_t* masks, int row,
+                                             float zcut, int32_t* out, uint64_t* masks, int row,
                                              uint32_t* error, SelSmem& sm) {
   uint32_t u[IPT];
   select_load_keys<IPT, COHERENT>(keys, stride, u);
-  select_from_keys<NT, IPT, COHERENT>(u, c, p, out, masks, row, error, sm);
+  select_from_keys<NT, IPT, COHERENT>(u, c, p, zcut, out, masks, row, error, sm);
 }
 
 // The clusters whose row mask is non-zero, ascending, into ulist / ucount.

@@ -1,6 +1,8 @@
 // Standalone selection kernel: one 1024-thread workgroup per batch row,
 // running the block-level selection of fh_select.h on keys produced by an
 // earlier kernel.
+#include <cmath>
+
 #include "fh_select.h"
 
 namespace fh {
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       }
     }
   }
-  select_from_keys<kSelThreads, IPT, false>(u, a.c, a.p, a.sel + (int64_t)r * a.sel_stride,
+  select_from_keys<kSelThreads, IPT, false>(u, a.c, a.p, a.zcut, a.sel + (int64_t)r * a.sel_stride,
                                             a.masks, r, a.error, sm);
   if (!a.counter) return;
   // row 0's workgroup compacts the union of the selected clusters once every
@@ -64,6 +66,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
   __syncthreads();
   compact_masks_block<kSelThreads, IPT>(a.masks, a.c, a.ulist, a.ucount, sm);
+}
+
+// z with upper normal tail probability q, by the rational approximation of
+// Abramowitz and Stegun 26.2.23 (absolute error below 4.5e-4), for
+// 0 < q <= 0.5.  Only a hint: the selection's result does not depend on it.
+static double normal_upper_quantile(double q) {
+  const double t = std::sqrt(-2.0 * std::log(q));
+  const double num = 2.515517 + t * (0.802853 + t * 0.010328);
+  const double den = 1.0 + t * (1.432788 + t * (0.189269 + t * 0.001308));
+  return t - num / den;
+}
+
+float select_zcut(int c, int p) {
+  if (c < 2048 || p < 1) return 0.0f;
+  const double q = 4.0 * (double)p / (double)c;
+  if (q >= 0.5) return 0.0f;
+  return (float)normal_upper_quantile(q);
 }
 
 hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing* tm) {

@@ -24,11 +24,11 @@
 #ifndef FH_S1_TRACE
 #define FH_S1_TRACE(slot)
 #endif
-#ifndef FH_B1_PREFETCH
-#define FH_B1_PREFETCH 0
-#endif
 #ifndef FH_S1_WAVE_TRACE
 #define FH_S1_WAVE_TRACE(wave)
+#endif
+#ifndef FH_S1_ISSUE_TRACE
+#define FH_S1_ISSUE_TRACE(wave)
 #endif
 #ifndef FH_S2_WAVE_TRACE
 #define FH_S2_WAVE_TRACE(wave)
@@ -65,15 +65,12 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
     uint4 hraw[NCH];
     float hreg[NCH][Chunk<TE>::kElems];
     load_h_raw<NCH>(hrow, a.nchunk, lane, hraw);
-    uint64_t kbest = 0;
-    score_rows<TE, NCH, SELECT>(a, keys, nullptr, dbg, seed, hraw, hreg, lane, w0, wstride,
-                                kbest);
+    score_rows<TE, NCH, SELECT>(a, keys, nullptr, dbg, seed, hraw, hreg, lane, w0, wstride);
   } else {
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(hrow);
     for (int i = t; i < a.d; i += kS1Threads) s_h[i] = __uint_as_float((uint32_t)hb[i] << 16);
     __syncthreads();
-    uint64_t kbest = 0;
-    score_int4_tiles<SELECT>(a, keys, nullptr, dbg, seed, s_h, lane, w0, wstride, kbest);
+    score_int4_tiles<SELECT>(a, keys, nullptr, dbg, seed, s_h, lane, w0, wstride);
   }
   FH_S1_TRACE(1);
   if constexpr (!SELECT) return;
@@ -93,7 +90,7 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   }
   __syncthreads();
   FH_S1_TRACE(2);
-  select_block<kS1Threads, IPT, true>(keys, a.c, (int)a.key_stride, a.p,
+  select_block<kS1Threads, IPT, true>(keys, a.c, (int)a.key_stride, a.p, a.zcut,
                                       a.sel + (int64_t)r * a.sel_stride, a.masks, r, a.error, sm);
   FH_S1_TRACE(3);
 }
@@ -165,6 +162,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    FH_S1_ISSUE_TRACE(wave);
   }
   const uint32_t epoch = __builtin_amdgcn_readfirstlane(
       __hip_atomic_load(args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -174,62 +172,32 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   int32_t* sel = args.sel + (int64_t)cur * kDecodeB1MaxP;
   int32_t* sel_next = args.sel + (int64_t)(1 - cur) * kDecodeB1MaxP;
   const uint64_t seed = a.sample ? a.seeds[0] : 0ull;
-  uint64_t kbest = 0;
   if constexpr (!INT4) {
     score_rows_from<TE, NCH, true>(a, keys, keys_next, a.dbg_scores, seed, hraw, hreg, lane, w0,
-                                   wstride, kbest, data);
+                                   wstride, data);
   } else {
-    // h in LDS for the INT4 tiles, written by wave 0 from its registers
-    // (lane l holds elements 8 (l + 64 i) .. 8 (l + 64 i) + 7)
+    // h in LDS as floats for the INT4 tiles, written by wave 0 from its
+    // registers (lane l holds bf16 elements 8 (l + 64 i) .. 8 (l + 64 i) + 7)
     unpack_h<TE, NCH>(hraw, hreg);
     if (wave == 0) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int ch = lane + kWave * i;
         if (ch < args.s2.nchunk) {
+          const uint32_t wv[4] = {hraw[i].x, hraw[i].y, hraw[i].z, hraw[i].w};
 #pragma unroll
-          for (int e = 0; e < Chunk<TE>::kElems; ++e) s_h[ch * Chunk<TE>::kElems + e] = hreg[i][e];
+          for (int e = 0; e < 4; ++e) {
+            s_h[ch * 8 + 2 * e] = bf16_lo(wv[e]);
+            s_h[ch * 8 + 2 * e + 1] = bf16_hi(wv[e]);
+          }
         }
       }
     }
     __syncthreads();
-    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride,
-                           kbest);
+    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride);
   }
   FH_S1_TRACE(1);
   FH_S1_WAVE_TRACE(wave);
-#if FH_B1_PREFETCH
-  // The cluster with the workgroup's best key is very likely selected: its
-  // rows of the cluster-major copy are requested now, while workgroup 0
-  // selects, so that stage 2 finds them in the memory-side cache.  The data
-  // land in an LDS scratch area nobody reads (direct loads to LDS leave no
-  // register to wait on).
-  __shared__ uint64_t s_kb[kS1Waves];
-  __shared__ uint4 s_pf[kS1Waves][kWave];
-  if (blockIdx.x != 0) {
-    kbest = wave_max_u64(kbest);
-    if (lane == 0) s_kb[wave] = kbest;
-    __syncthreads();
-    if (wave >= 1) {
-      uint64_t m = 0;
-#pragma unroll
-      for (int w = 0; w < kS1Waves; ++w) m = s_kb[w] > m ? s_kb[w] : m;
-      if (m != 0) {
-        const int64_t k = (int64_t)(0xFFFFFFFFu - (uint32_t)m);
-        const int64_t bytes = (int64_t)args.s2.b * args.s2.row_bytes;
-        const uint8_t* src = args.s2.base + k * bytes;
-        constexpr int kPfWaves = kS1Waves - 1;
-        const int64_t per = ((bytes + kPfWaves - 1) / kPfWaves + 1023) & ~(int64_t)1023;
-        const int64_t lo = (int64_t)(wave - 1) * per;
-        const int64_t hi = lo + per < bytes ? lo + per : bytes;
-        for (int64_t off = lo; off + 1024 <= hi; off += 1024)
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(src + off + lane * 16),
-              (void __attribute__((address_space(3)))*)&s_pf[wave][0], 16, 0, 0);
-      }
-    }
-  }
-#endif
 
 
   // ---- B: workgroup 0 waits for all keys, selects and publishes ------------------
@@ -270,7 +238,8 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     __syncthreads();
     FH_S1_TRACE(2);
     // the selection goes to LDS, then out in one coalesced device-coherent pass
-    select_from_keys<kS1Threads, IPT, false, true>(u, a.c, a.p, s_sel, nullptr, 0, a.error, sm);
+    select_from_keys<kS1Threads, IPT, false, true>(u, a.c, a.p, a.zcut, s_sel, nullptr, 0, a.error,
+                                                   sm);
     __syncthreads();
     for (int i = t; i < a.p; i += kS1Threads)
       __hip_atomic_store(sel + i, s_sel[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -324,9 +293,6 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, sel, hreg, seed, lane, w0, wstride, best,
                                            lse, a.error, s_win, wlo, wn);
   }
-#if FH_B1_PREFETCH
-  __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS load outlives the workgroup
-#endif
   FH_S2_WAVE_TRACE(wave);
   FH_S1_TRACE(5);
 
