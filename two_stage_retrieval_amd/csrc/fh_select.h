@@ -174,7 +174,7 @@ __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int 
 template <int NT, int IPT, bool COHERENT_OUT, bool PREPARED = false>
 __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, int32_t* out,
                                  uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
-  static_assert(IPT % 4 == 0 && IPT <= 32, "items per thread");
+  static_assert(IPT % 4 == 0 && IPT <= 32 && (IPT & (IPT - 1)) == 0, "items per thread");
   constexpr int NW = NT / kWave;
   constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
   const int t = threadIdx.x;
@@ -341,17 +341,20 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
     above |= cand;  // the whole boundary set is taken
   } else if (nb <= kSelWaveMax) {
     // ---- gather the boundary keys; wave 0 picks `need` of them ---------------
+    // (few threads hold a candidate: the others skip the per-item loop)
     const int cc = __popc(cand);
     const int wincl = wave_incl_scan_dpp(cc);
     int base = 0;
     if (lane == kWave - 1 && wincl > 0) base = atomicAdd(&sm.misc[6], wincl);
     base = __shfl(base, kWave - 1, kWave) + wincl - cc;
+    if (cand) {
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      if ((cand >> j) & 1u) {
-        sm.cu[base] = ordered_u32(__uint_as_float(u[j]));
-        sm.ck[base] = k0 + j;
-        ++base;
+      for (int j = 0; j < IPT; ++j) {
+        if ((cand >> j) & 1u) {
+          sm.cu[base] = ordered_u32(__uint_as_float(u[j]));
+          sm.ck[base] = k0 + j;
+          ++base;
+        }
       }
     }
     __syncthreads();
@@ -370,11 +373,9 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
       if (live && rank < need) atomicOr(&sm.chosen[kk >> 5], 1u << (kk & 31));
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const int k = k0 + j;
-      if (((cand >> j) & 1u) && ((sm.chosen[k >> 5] >> (k & 31)) & 1u)) above |= 1u << j;
-    }
+    // the thread's ids [k0, k0 + IPT) lie in one word of the bitmap (IPT is
+    // a power of two up to 32 and k0 a multiple of it)
+    if (cand) above |= cand & (sm.chosen[k0 >> 5] >> (k0 & 31));
   } else {
     // ---- more than kSelWaveMax exactly equal keys: lowest ids first ----------
     const int cc = __popc(cand);
@@ -393,20 +394,16 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
   const int cnt = __popc(above);
   const int incl = sel_scan<NT>(cnt, sm, parity, lane, wave);
   FH_SEL_TRACE(6);
+  // one step per selected id of the thread, lowest first
   int rank = incl - cnt;
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    if ((above >> j) & 1u) {
-      if (rank < p) {
-        if constexpr (COHERENT_OUT) {
-          __hip_atomic_store(out + rank, k0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          out[rank] = k0 + j;
-        }
-        if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k0 + j), 1ull << row);
-      }
-      ++rank;
+  for (uint32_t m = above; m != 0u && rank < p; m &= m - 1u, ++rank) {
+    const int k = k0 + __ffs(m) - 1;
+    if constexpr (COHERENT_OUT) {
+      __hip_atomic_store(out + rank, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      out[rank] = k;
     }
+    if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k), 1ull << row);
   }
   FH_SEL_TRACE(7);
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);

@@ -33,6 +33,9 @@
 #ifndef FH_S2_WAVE_TRACE
 #define FH_S2_WAVE_TRACE(wave)
 #endif
+#ifndef FH_S1_TRACE_END
+#define FH_S1_TRACE_END()
+#endif
 #ifndef FH_S1_POLL_TRACE
 #define FH_S1_POLL_TRACE(round)
 #endif
@@ -306,6 +309,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     __hip_atomic_store(args.epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     FH_S1_TRACE(6);
   }
+  FH_S1_TRACE_END();
 }
 
 int stage1_blocks(const Stage1Args& a, bool int4) {
