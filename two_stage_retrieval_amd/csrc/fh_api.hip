@@ -45,6 +45,7 @@ struct fh_handle {
   uint64_t b1_launches = 0;         // host copy of the device epoch
   int last_path = 0;                // kernels of the last step (flashhead_query 10)
   uint32_t* b1_epoch = nullptr;     // launch counter (picks the buffer set)
+  uint32_t* b1_go = nullptr;        // 2 words: all keys seen, per buffer set (0 between launches)
 
 
   int64_t bytes = 0;
@@ -223,6 +224,8 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(hipMemsetAsync(h->b1_sel, 0xFF, (size_t)2 * kDecodeB1MaxP * 4, s));
   FH_TRY(alloc(h, &h->b1_epoch, 4));
   FH_TRY(hipMemsetAsync(h->b1_epoch, 0, 4, s));
+  FH_TRY(alloc(h, &h->b1_go, 8));
+  FH_TRY(hipMemsetAsync(h->b1_go, 0, 8, s));
   FH_TRY(hipMemsetAsync(h->ucount, 0, 4, s));
   FH_TRY(hipStreamSynchronize(s));
   return FH_OK;
@@ -329,6 +332,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     f.s2.lse_part = h->b1_lse;
     f.sel = h->b1_sel;
     f.epoch = h->b1_epoch;
+    f.go = h->b1_go;
     f.slot_stride = kDecodeB1SlotStride;
     const int grid = decode_b1_grid(f, int4, h->num_cu);
     if (grid > 0 && grid <= kMaxGrid) {

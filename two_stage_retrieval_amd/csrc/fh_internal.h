@@ -142,6 +142,9 @@ struct Stage1Args {
 //   s2.part_best  2 x slot_stride u64 words of slots (slot j at word 16 j),
 //                 zero before the first launch;
 //   s2.lse_part   slot_stride u64 words of lse partials (same spacing).
+//   go            2 words, zero before the first launch: workgroup 0 sets
+//                 the current set's word once it holds every key (a hint
+//                 that the other workgroups may now prefetch).
 // Launches keep them consistent.  The selection of the launch is copied to
 // s1.sel (plain) only for the debug output.
 constexpr int kDecodeB1MaxP = 2048;
@@ -153,6 +156,7 @@ struct DecodeB1Args {
   int32_t* sel;
   uint32_t* epoch;
   int64_t slot_stride;
+  uint32_t* go;
 };
 
 // Optional events recorded exactly around one kernel (hipExtLaunchKernel).

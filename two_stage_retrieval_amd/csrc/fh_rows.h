@@ -58,8 +58,8 @@ constexpr uint32_t kKeyPending = 0xFFFFFFFFu;
 // With `keys_next`, also marks the row pending in the key buffer of the next
 // launch (single-launch batch-1 decode).
 template <bool COHERENT>
-__device__ __forceinline__ void publish_key(const Stage1Args& a, float* keys, float* keys_next,
-                                            float* dbg, uint64_t seed, int row, float score) {
+__device__ __forceinline__ float publish_key(const Stage1Args& a, float* keys, float* keys_next,
+                                             float* dbg, uint64_t seed, int row, float score) {
   const float key =
       a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
   if constexpr (COHERENT) {
@@ -69,6 +69,15 @@ __device__ __forceinline__ void publish_key(const Stage1Args& a, float* keys, fl
   }
   if (keys_next) keys_next[row] = __uint_as_float(kKeyPending);
   if (dbg) dbg[row] = score;
+  return key;
+}
+
+// A lane's running best (key, row) as one orderable word: larger key, then
+// lower row; 0 means none.
+__device__ __forceinline__ void track_best_key(uint64_t* best, float key, int row) {
+  if (!best) return;
+  const uint64_t w = ((uint64_t)ordered_u32(key) << 32) | (0xFFFFFFFFu - (uint32_t)row);
+  *best = w > *best ? w : *best;
 }
 
 
@@ -103,7 +112,8 @@ __device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys
                                                 const uint4 (&hraw)[NCH],
                                                 float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
                                                 int g, int wstride,
-                                                uint4 (&data)[kS1Rows][NCH]) {
+                                                uint4 (&data)[kS1Rows][NCH],
+                                                uint64_t* best_key = nullptr) {
   using CK = Chunk<TE>;
   const int ngroups = (a.c + kS1Rows - 1) / kS1Rows;
   unpack_h<TE, NCH>(hraw, hreg);
@@ -122,7 +132,9 @@ __device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys
     for (int rr = 1; rr < kS1Rows; ++rr)
       if (lane == rr) mine = acc[rr];
     if (lane < kS1Rows && row0 + lane < a.c)
-      publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine);
+      track_best_key(best_key,
+                     publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine),
+                     row0 + lane);
     g += wstride;
     if (g < ngroups) load_centroid_group<TE, NCH>(a, g, lane, data);
   }
@@ -146,7 +158,7 @@ template <bool COHERENT>
 __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* keys,
                                                  float* keys_next, float* dbg, uint64_t seed,
                                                  const float* s_h, int lane, int w0,
-                                                 int wstride) {
+                                                 int wstride, uint64_t* best_key = nullptr) {
   const int q = lane >> 4, rin = lane & 15;
   const int G = a.groups;
   for (int tile = w0; tile < a.ntiles; tile += wstride) {
@@ -162,7 +174,9 @@ __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* key
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
     const int row = tile * 16 + rin;
-    if (q == 0 && row < a.c) publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc);
+    if (q == 0 && row < a.c)
+      track_best_key(best_key, publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc),
+                     row);
   }
 }
 

@@ -175,9 +175,10 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   int32_t* sel = args.sel + (int64_t)cur * kDecodeB1MaxP;
   int32_t* sel_next = args.sel + (int64_t)(1 - cur) * kDecodeB1MaxP;
   const uint64_t seed = a.sample ? a.seeds[0] : 0ull;
+  uint64_t best_key = 0;  // this lane's best (key, row), for the prefetch below
   if constexpr (!INT4) {
     score_rows_from<TE, NCH, true>(a, keys, keys_next, a.dbg_scores, seed, hraw, hreg, lane, w0,
-                                   wstride, data);
+                                   wstride, data, &best_key);
   } else {
     // h in LDS as floats for the INT4 tiles, written by wave 0 from its
     // registers (lane l holds bf16 elements 8 (l + 64 i) .. 8 (l + 64 i) + 7)
@@ -197,7 +198,8 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       }
     }
     __syncthreads();
-    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride);
+    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride,
+                           &best_key);
   }
   FH_S1_TRACE(1);
   FH_S1_WAVE_TRACE(wave);
@@ -239,6 +241,10 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     }
     select_wave_range<IPT>(u, a.c, sm);
     __syncthreads();
+    if (t == 0) {  // every key is in: the other workgroups may prefetch
+      __hip_atomic_store(args.go + cur, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      args.go[1 - cur] = 0u;
+    }
     FH_S1_TRACE(2);
     // the selection goes to LDS, then out in one coalesced device-coherent pass
     select_from_keys<kS1Threads, IPT, false, true>(u, a.c, a.p, a.zcut, s_sel, nullptr, 0, a.error,
@@ -250,13 +256,56 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   }
 
   // ---- C: stage-2 share ---------------------------------------------------------
+  // While workgroup 0 selects, memory is idle.  Once it holds every key (the
+  // go word), each other workgroup requests the rows of the cluster with its
+  // own best key, which is very likely selected, so that stage 2 finds them
+  // in the memory-side cache.  The requests are direct-to-LDS loads into a
+  // scratch area nobody reads: no register waits on them.  Requesting them
+  // right after stage 1 instead slows workgroup 0's key polls more than it
+  // gains; two clusters per workgroup outlast the selection.
+  //
   // The entries of the workgroup's first groups (one group per wave when the
-  // grid covers the rows) are fetched once, by wave 0, into LDS: one
+  // grid covers the rows) are then fetched once, by wave 0, into LDS: one
   // coherent round trip per workgroup instead of one per wave.  Workgroup 0
   // has the whole selection in LDS already.
   __shared__ int32_t s_win[kB1Window];
+  __shared__ uint64_t s_best[kS1Waves];
+  __shared__ uint4 s_prefetch[kS1Waves][kWave];
   int64_t wlo = 0, wn = 0;
   if (blockIdx.x != 0) {
+    const uint64_t wbest = wave_max_u64(best_key);
+    if (lane == 0) s_best[wave] = wbest;
+    if (wave == 0) {
+      for (int it = 0;; ++it) {
+        if (__hip_atomic_load(args.go + cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+          break;
+        if (it == kArriveSpinLimit) {
+          if (lane == 0 && a.error) atomicOr(a.error, 4u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    if (wave >= 1) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int w = 0; w < kS1Waves; ++w) m = s_best[w] > m ? s_best[w] : m;
+      if (m != 0) {
+        // waves 1 .. kS1Waves - 1 split the cluster's rows in 1 KB requests
+        const int64_t k = (int64_t)(0xFFFFFFFFu - (uint32_t)m);  // < c
+        const int64_t bytes = (int64_t)args.s2.b * args.s2.row_bytes;
+        const uint8_t* src = args.s2.base + k * bytes;
+        constexpr int kParts = kS1Waves - 1;
+        const int64_t per = ((bytes + kParts - 1) / kParts + 1023) & ~(int64_t)1023;
+        const int64_t lo = (int64_t)(wave - 1) * per;
+        const int64_t hi = lo + per < bytes ? lo + per : bytes;
+        for (int64_t off = lo; off + 1024 <= hi; off += 1024)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(src + off + lane * 16),
+              (void __attribute__((address_space(3)))*)&s_prefetch[wave][0], 16, 0, 0);
+      }
+    }
     const int64_t ngroups = (args.s2.nrows + R - 1) / R;
     const int64_t g0 = (int64_t)blockIdx.x * kS1Waves;
     if (g0 < ngroups) {
@@ -296,6 +345,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     dot_rows<TE, NCH, R, kRowGather, true>(args.s2, 0, sel, hreg, seed, lane, w0, wstride, best,
                                            lse, a.error, s_win, wlo, wn);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS load outlives the workgroup
   FH_S2_WAVE_TRACE(wave);
   FH_S1_TRACE(5);
 
