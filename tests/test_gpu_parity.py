@@ -350,18 +350,22 @@ def test_many_clusters_separate_select_kernel(fh, p):
     assert fh.flashhead_query(head.handle, 9) == 0
 
 
-@pytest.mark.parametrize("wid", [0, 1])
-def test_all_equal_scores_pick_lowest_ids(fh, wid):
-    """h = 0: every score and logit is 0; ties go to the lowest ids."""
-    cs = case(wid)
-    p = cs.wl.p
-    head = cs.prepare(fh, max_batch=2, max_p=p)
-    H = np.zeros((2, cs.wl.d), dtype=cs.head.E.dtype)
-    res = run_debug(fh, head, dev_tensor(H), 2, p, "greedy")
-    for r in range(2):
+@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("wid, over, p", [(0, (), None), (1, (), None),
+                                          (1, (("c", 50), ("b", 16), ("d", 256)), 20)])
+def test_all_equal_scores_pick_lowest_ids(fh, wid, over, p, B):
+    """h = 0: every score and logit is 0; ties go to the lowest ids (also
+    with c not a multiple of the keys each selecting thread holds)."""
+    cs = case(wid, **dict(over))
+    p = p or cs.wl.p
+    head = cs.prepare(fh, max_batch=B, max_p=p)
+    H = np.zeros((B, cs.wl.d), dtype=cs.head.E.dtype)
+    res = run_debug(fh, head, dev_tensor(H), B, p, "greedy")
+    for r in range(B):
         assert np.array_equal(res["clusters"][r], np.arange(p))
         T = ref.candidate_tokens(np.arange(p), cs.head.c2t)
         assert res["tokens"][r] == T.min()
+    assert fh.flashhead_query(head.handle, 9) == 0
 
 
 def test_repeated_calls_are_deterministic(fh):

@@ -223,7 +223,8 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
         !(range > 0.0f) || !(scale < INFINITY) || !(offset > -INFINITY && offset < INFINITY);
     if (flat) {  // all keys equal (lo == fmin here): one bin holds all
 #pragma unroll
-      for (int j = 0; j < IPT / 2; ++j) bins[j] = 0x00010001u;
+      for (int j = 0; j < IPT / 2; ++j)
+        bins[j] = (2 * j < nvalid ? 1u : 0u) | (2 * j + 1 < nvalid ? 0x10000u : 0u);
       beta = 0;
       ngt = 0;
       nb = c;
@@ -233,14 +234,11 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
     for (int j = 0; j < IPT; ++j) {
       // (f - lo) * scale as one fma: a monotone map of f, clamped to the bins
       const float f = __uint_as_float(u[j]);
-      uint32_t bp = 0u;
-      if (j < nvalid && f >= lo) {
-        const int b = min(max((int)fmaf(f, scale, offset), 0), kSelBins - 1);
-        atomicAdd(&sm.hist[b], 1);
-        bp = (uint32_t)b + 1u;
-      }
-      if (j & 1) bins[j / 2] |= bp << 16;
-      else bins[j / 2] = bp;
+      const int b = min(max((int)fmaf(f, scale, offset), 0), kSelBins - 1);
+      const bool in = j < nvalid && f >= lo;
+      const uint32_t bp = in ? (uint32_t)b + 1u : 0u;
+      bins[j / 2] = (j & 1) ? (bins[j / 2] | (bp << 16)) : bp;
+      if (in) atomicAdd(&sm.hist[b], 1);
     }
     __syncthreads();
     FH_SEL_TRACE(3);
@@ -280,13 +278,14 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
   FH_SEL_TRACE(4);
   int need = p - ngt;  // ids still to take from the boundary bin
 
+  // (branch-free: items past c carry bin 0, below every key's)
   uint32_t above = 0u, cand = 0u;
+  const uint32_t bb = (uint32_t)beta + 1u;  // the boundary bin in the stored form
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    if (j >= nvalid) continue;
-    const int b = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xFFFFu) - 1;  // -1: below range
-    if (b > beta) above |= 1u << j;
-    else if (b == beta) cand |= 1u << j;
+    const uint32_t b = (bins[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+    above |= (uint32_t)(b > bb) << j;
+    cand |= (uint32_t)(b == bb) << j;
   }
 
   // ---- large boundary bin: 8-bit radix passes on the key bits -----------------
@@ -360,14 +359,14 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
     __syncthreads();
     if (wave == 0) {
       // each candidate's rank in (key descending, id ascending); the `need`
-      // first are taken
+      // first are taken (candidate j is read from lane j's registers)
       const bool live = lane < nb;
       const uint32_t uu = live ? sm.cu[lane] : 0u;
       const uint32_t kk = live ? (uint32_t)sm.ck[lane] : 0u;
       int rank = 0;
       for (int j = 0; j < nb; ++j) {
-        const uint32_t uj = sm.cu[j];
-        const uint32_t kj = (uint32_t)sm.ck[j];
+        const uint32_t uj = (uint32_t)__builtin_amdgcn_readlane((int)uu, j);
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kk, j);
         rank += (uj > uu || (uj == uu && kj < kk)) ? 1 : 0;
       }
       if (live && rank < need) atomicOr(&sm.chosen[kk >> 5], 1u << (kk & 31));
