@@ -365,6 +365,56 @@ def rows_accessor(E, dtype: str) -> Callable[[np.ndarray], np.ndarray]:
 
 
 # --------------------------------------------------------------------------
+# Monte Carlo marginal ([notes] Module 4 and Formula 7): N independent draws
+# S_1..S_N of the probed clusters share one stage-1 scoring; draw i gives the
+# conditional p(v | h, S_i), the softmax of z / tau over S_i's candidates
+# (zero for a token outside them); the estimate of p(v | h) is their mean.
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class MCResult:
+    prob: np.ndarray         # the estimate for each query token
+    per_draw: np.ndarray     # N x Q conditionals p(v | h, S_i)
+    lse: np.ndarray          # N: lse of z / tau over each draw's candidates
+    m1: np.ndarray           # N: gap between the p-th and (p+1)-th key
+    S: list                  # N arrays of selected cluster ids
+
+
+def mc_marginal(rows_f64: Callable, c2t, h_f64, p: int, tau: float, seeds,
+                tokens, *, C_f64=None, int4=None) -> MCResult:
+    """[notes] Formula 7 with the draws of Module 2's sampling mode."""
+    if int4 is not None:
+        scores = stage1_scores_int4(int4[0], int4[1], h_f64)
+    else:
+        scores = stage1_scores(C_f64, h_f64)
+    c2t = np.asarray(c2t)
+    c, b = c2t.shape
+    cluster_of = np.empty(c * b, dtype=np.int64)
+    cluster_of[c2t.reshape(-1)] = np.repeat(np.arange(c), b)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    zq = exact_logits(rows_f64, tokens, h_f64)
+    z_of_cluster = {}        # exact logits of a cluster's rows, computed once
+    seeds = [int(x) for x in seeds]
+    per_draw = np.zeros((len(seeds), len(tokens)))
+    lses = np.zeros(len(seeds))
+    m1s = np.zeros(len(seeds))
+    Ss = []
+    for i, seed in enumerate(seeds):
+        S, _, m1 = select_clusters(scores, p, "sample", tau, seed)
+        for k in S:
+            if k not in z_of_cluster:
+                z_of_cluster[k] = exact_logits(rows_f64, c2t[k], h_f64)
+        z = np.concatenate([z_of_cluster[k] for k in S])
+        lse = logsumexp(z / tau)
+        member = np.isin(cluster_of[tokens], S)
+        per_draw[i] = np.where(member, np.exp(zq / tau - lse), 0.0)
+        lses[i], m1s[i] = lse, m1
+        Ss.append(S)
+    return MCResult(per_draw.mean(axis=0), per_draw, lses, m1s, Ss)
+
+
+# --------------------------------------------------------------------------
 # algorithmic work ([notes] Formula 6, [paper] Table 8 parameter counts)
 # --------------------------------------------------------------------------
 

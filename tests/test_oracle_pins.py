@@ -392,6 +392,65 @@ def test_marginal_over_cluster_draws_matches_exact_enumeration():
 
 
 # --------------------------------------------------------------------------
+# Monte Carlo marginal (Formula 7)
+# --------------------------------------------------------------------------
+
+def test_mc_marginal_p_equals_c_is_the_softmax(tiny_workload):
+    """Every draw probes every cluster: each term, and so the mean, is the
+    closed-form softmax of z / tau over the vocabulary."""
+    head, H = tiny_workload
+    rows = ref.rows_accessor(head.E, "f32")
+    h = ref.as_f64(H[3], "f32")
+    C = head.C_given.astype(np.float64)
+    tau = 0.8
+    toks = np.arange(0, head.wl.v, 37)
+    r = ref.mc_marginal(rows, head.c2t, h, head.wl.c, tau, [5, 6, 7], toks, C_f64=C)
+    z = ref.dense_logits(rows, head.wl.v, h)
+    want = np.exp(z / tau - special.logsumexp(z / tau))[toks]
+    np.testing.assert_allclose(r.prob, want, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r.per_draw, np.tile(want, (3, 1)), rtol=1e-12, atol=1e-15)
+
+
+def test_mc_marginal_single_draw_is_the_candidate_softmax():
+    """N = 1: the estimate is the sampled set's softmax at tau on its
+    candidates and zero elsewhere, so it sums to one over the vocabulary."""
+    E, c2t, C = _tiny_head(5, d=6)
+    h = np.random.default_rng(6).standard_normal(6)
+    tau = 0.6
+    r = ref.mc_marginal(lambda idx: E[idx], c2t, h, 2, tau, [11], np.arange(24), C_f64=C)
+    S = r.S[0]
+    # the draw itself, by the definition: top-2 of s / tau + Gumbel noise
+    g = ref.gumbel(11, ref.STREAM_CLUSTER, np.arange(6))
+    assert sorted(S.tolist()) == sorted(np.argsort(-(C @ h / tau + g))[:2].tolist())
+    T = np.concatenate([c2t[k] for k in S])
+    want = np.zeros(24)
+    want[T] = special.softmax((E @ h)[T] / tau)
+    np.testing.assert_allclose(r.prob, want, rtol=1e-12, atol=1e-15)
+    assert r.prob.sum() == pytest.approx(1.0, abs=1e-12)
+
+
+def test_mc_marginal_converges_to_exact_enumeration():
+    """v=24, c=6, b=4, p=2: the estimate's expectation is
+    sum_S P(S) softmax_{T(S)}(z/tau); 20000 draws land within five standard
+    errors of it for every token, and each draw's terms sum to one."""
+    E, c2t, C = _tiny_head(3, d=6)
+    h = np.random.default_rng(4).standard_normal(6) * 0.8
+    tau = 0.9
+    s = C @ h
+    z = E @ h
+    set_probs = _plackett_luce_set_probs(np.exp(s / tau), 2)
+    exact = np.zeros(24)
+    for S, pS in set_probs.items():
+        T = ref.candidate_tokens(np.array(S), c2t)
+        exact[T] += pS * special.softmax(z[T] / tau)
+    n = 20000
+    r = ref.mc_marginal(lambda idx: E[idx], c2t, h, 2, tau, range(n), np.arange(24), C_f64=C)
+    np.testing.assert_allclose(r.per_draw.sum(axis=1), 1.0, atol=1e-12)
+    se = r.per_draw.std(axis=0) / math.sqrt(n)
+    assert np.all(np.abs(r.prob - exact) <= 5 * se + 1e-12)
+
+
+# --------------------------------------------------------------------------
 # prepare-time data: centroid means and the INT4 quantizer
 # --------------------------------------------------------------------------
 
