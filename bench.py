@@ -103,6 +103,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time back-to-back (cache-warm) calls")
+    ap.add_argument("--mc", type=int, default=0, metavar="N",
+                    help="time the Monte Carlo marginal (Formula 7) with N draws "
+                         "instead of the decode step; prints its own JSON line")
+    ap.add_argument("--mc-tokens", type=int, default=16)
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run --steps cold calls and a 256 MiB copy-like kernel, then exit "
                          "(for rocprofv3 --pmc runs)")
@@ -163,6 +167,11 @@ def main():
             fh.sample(x, wl.p, tau, seeds[i % nb], out=out)
         else:
             fh.greedy(x, wl.p, out=out)
+
+    if args.mc:
+        mc_bench(args, wl, head, H, H_dev, fh, evict, int4)
+        fh.close()
+        return
 
     dense = None if args.no_dense else fhb.DenseHead(E_dev, max_batch=B)
 
@@ -332,6 +341,83 @@ def main():
         "cpu_baseline": cpu,
     }
     fh.close()
+    print(json.dumps(res), flush=True)
+
+
+def mc_bench(args, wl, head, H, H_dev, fh, evict, int4):
+    """Formula 7: one estimate = N draws of the probed clusters for one
+    hidden vector and the mean conditional probability of Q query tokens.
+    Cold timing as for the decode step; the oracle is timed on a bounded
+    number of draws and scaled to N."""
+    import torch
+    N, Q = args.mc, args.mc_tokens
+    dev = H_dev.device
+    tau = args.tau
+    rng = np.random.default_rng(5)
+    nvec = min(len(H), 64)
+    toks = [torch.from_numpy(rng.integers(0, wl.v, size=Q).astype(np.int32)).to(dev)
+            for _ in range(nvec)]
+    seeds = torch.from_numpy((np.arange(N, dtype=np.uint64) + (np.uint64(21) << np.uint64(32)))
+                             .view(np.int64)).to(dev)
+    out = torch.empty(Q, dtype=torch.float32, device=dev)
+    from two_stage_retrieval_amd import binding as fhb
+    nbytes = fhb.flashhead_mc_workspace_bytes(fh.handle, N, wl.p, Q)
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    ws = raw[(-raw.data_ptr()) % 256:][:nbytes]
+
+    def call(i):
+        fh.mc_marginal(H_dev[i % nvec:i % nvec + 1], wl.p, tau, seeds, toks[i % nvec],
+                       out=out, workspace=ws)
+    times = []
+    for i in range(args.warmup + args.steps):
+        evict()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call(i)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(a.elapsed_time(b) * 1e3)
+    us = statistics.median(times)
+    log(f"[bench] mc: {N} draws, {Q} tokens: cold p50 {us:.1f} us")
+    if args.pmc_probe:
+        # the copy-like kernel of known size that calibrates the counters
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        evict()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_probe": wl.name, "mc_draws": N, "calls": len(times),
+                          "copy_kernel_bytes_each_way": src.numel() * 4}), flush=True)
+        return
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import flashhead_ref as ref
+        rows = ref.rows_accessor(head.E, wl.dtype)
+        C64 = (ref.as_f64(head.C_given, wl.dtype) if head.C_given is not None
+               else ref.centroid_means(rows, head.c2t))
+        kw = {"int4": ref.int4_quantize(C64)} if int4 else {"C_f64": C64}
+        h64 = ref.as_f64(H[0], wl.dtype)
+        n_s = max(1, min(N, 64))
+        sd = [int(x) for x in (np.arange(n_s, dtype=np.uint64) + (np.uint64(21) << np.uint64(32)))]
+        t0 = time.perf_counter()
+        ref.mc_marginal(rows, head.c2t, h64, wl.p, tau, sd,
+                        rng.integers(0, wl.v, size=Q), **kw)
+        per_draw = (time.perf_counter() - t0) * 1e6 / n_s
+        cpu = {"value": round(per_draw * N, 1), "unit": "us/estimate", "cores": None,
+               "kind": "oracle",
+               "sample": f"{n_s} draws timed ({per_draw:.0f} us/draw, float64 numpy oracle), "
+                         f"scaled to {N} draws"}
+        log(f"[bench] oracle: {per_draw:.0f} us per draw")
+    res = {"metric": f"Monte Carlo marginal (Formula 7) us/estimate, {N} draws, {Q} tokens",
+           "value": round(us, 3), "unit": "us/estimate", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False,
+           "dtype": wl.dtype if not int4 else "int4+bf16",
+           "data": "synthetic (seeded generator, pages' head shapes)",
+           "config": {"workload": f"{wl.name} mc N={N} Q={Q}", "p": wl.p, "tau": tau,
+                      "timing": "cold (1 GiB read-only flush before each call)"},
+           "us_per_draw": round(us / N, 4), "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
 

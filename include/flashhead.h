@@ -169,6 +169,42 @@ int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p,
                      float* out_lse, const fh_debug* dbg, void* stream);
 
 /*
+ * Monte Carlo marginal (notes, Module 4 and Formula 7): the estimate of
+ * p(v | h) for each query token v as the mean over n_draws independent
+ * draws S_i of
+ *   p(v | h, S_i) = exp(z_v / tau - lse_i)  if v's cluster is in S_i, else 0,
+ * where lse_i = log sum over the candidates t of S_i of exp(z_t / tau).  S_i
+ * is drawn as in flashhead_sample (Gumbel-top-p of the stage-1 scores over
+ * tau with the Philox key seeds[i]), so draw i probes the clusters that
+ * flashhead_sample with that key would, and lse_i is its out_lse.  Stage 1
+ * runs once for all draws, and each cluster that any draw selects has its
+ * candidate logits computed once.
+ *   H          device, 1 x d in E's dtype, 16-byte aligned
+ *   p          1 <= p <= min(c, max_p, 4096)
+ *   tau        finite, > 0
+ *   seeds      device, n_draws uint64 Philox keys; 1 <= n_draws <= 2^20
+ *   tokens     device, n_tokens token ids in [0, v); 1 <= n_tokens <= 2^16.
+ *              An id outside [0, v) is read as token 0 and sets bit 4 of
+ *              the self-check word (flashhead_query 9).
+ *   out_prob   device, n_tokens fp32 estimates
+ *   out_lse    device, n_draws fp32 lse_i, or NULL
+ *   workspace  device memory of at least
+ *              flashhead_mc_workspace_bytes(h, n_draws, p, n_tokens) bytes,
+ *              256-byte aligned, owned by the caller; its contents need no
+ *              initialisation and one call is in flight per workspace (and,
+ *              as for every call, per handle).
+ * Asynchronous on `stream`; argument errors return before anything is
+ * enqueued.  The sum over the draws runs in a fixed order, so a call is
+ * reproducible bit for bit.
+ */
+size_t flashhead_mc_workspace_bytes(const fh_handle* h, int32_t n_draws, int32_t p,
+                                    int32_t n_tokens);
+int flashhead_mc_marginal(fh_handle* h, const void* H, int32_t p, float tau,
+                          const uint64_t* seeds, int32_t n_draws, const int32_t* tokens,
+                          int32_t n_tokens, float* out_prob, float* out_lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * The dense head it replaces (Formula 1 followed by Formula 2 or 3), as the
  * in-library comparison: z = E h_r over all v tokens, then argmax or the
  * Gumbel-max sample with stream-1 noise keyed by token id (so that

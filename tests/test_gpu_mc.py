@@ -1,0 +1,154 @@
+"""Parity of the Monte Carlo marginal (Formula 7) with the CPU oracle,
+through the C ABI: the same Philox keys give the same draws on both sides,
+so the estimates are compared token by token."""
+import numpy as np
+import pytest
+
+from oracle import flashhead_ref as ref
+from two_stage_retrieval_amd import synth
+
+from .test_gpu_parity import case, dev_tensor, fh  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def seeds_dev(seeds):
+    return torch.from_numpy(np.asarray(seeds, dtype=np.uint64).view(np.int64)).cuda()
+
+
+def run_mc(head, x, p, tau, seeds, tokens):
+    lse = torch.empty(len(seeds), dtype=torch.float32, device="cuda")
+    toks = torch.from_numpy(np.asarray(tokens, dtype=np.int32)).cuda()
+    out = head.mc_marginal(x, p, tau, seeds_dev(seeds), toks, out_lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_mc(cs, h64, p, tau, seeds, tokens):
+    kw = {"int4": cs.int4} if cs.int4 is not None else {"C_f64": cs.C64}
+    return ref.mc_marginal(cs.rows, cs.head.c2t, h64, p, tau, seeds, tokens, **kw)
+
+
+def check_mc(cs, prob, lse, o, rtol):
+    """Draws whose p-th and (p+1)-th keys lie within 1e-5 may select
+    differently in fp32 and float64; each such draw may move an estimate by
+    at most 1/N.  Elsewhere the draws' lse and the estimates agree to the
+    arithmetic's tolerance."""
+    n = len(o.lse)
+    tie = o.m1 < 1e-5
+    ok = ~tie
+    np.testing.assert_allclose(lse[ok], o.lse[ok], rtol=rtol, atol=rtol)
+    slack = tie.sum() / n
+    err = np.abs(prob - o.prob)
+    assert np.all(err <= rtol * np.abs(o.prob) + 1e-7 + slack), err.max()
+
+
+def tokens_for(cs, o_first, rng, q):
+    """Candidates of the first draw (non-zero terms) and random tokens."""
+    T = ref.candidate_tokens(o_first.S[0], cs.head.c2t)
+    picks = rng.choice(T, size=q // 2, replace=False)
+    rest = rng.integers(0, cs.wl.v, size=q - q // 2)
+    return np.concatenate([picks, rest]).astype(np.int64)
+
+
+@pytest.mark.parametrize("p,tau", [(8, 0.8), (1, 1.0), (64, 0.7)])
+def test_tiny_mc_marginal_parity(fh, p, tau):
+    cs = case(0)
+    head = cs.prepare(fh, max_batch=1, max_p=64)
+    H, H64 = cs.hidden(3, offset=40)
+    seeds = [(7 << 32) | i for i in range(96)]
+    toks = np.arange(cs.wl.v)
+    for r in range(3):
+        x = dev_tensor(H[r:r + 1])
+        prob, lse = run_mc(head, x, p, tau, seeds, toks)
+        o = oracle_mc(cs, H64[r], p, tau, seeds, toks)
+        check_mc(cs, prob, lse, o, rtol=2e-5)
+        assert prob.sum() == pytest.approx(1.0, abs=1e-4)
+    assert fh.flashhead_query(head.handle, 9) == 0
+
+
+def test_tiny_mc_p_equals_c_is_the_softmax(fh):
+    cs = case(0)
+    head = cs.prepare(fh, max_batch=1, max_p=64)
+    H, H64 = cs.hidden(1, offset=77)
+    tau = 0.9
+    toks = np.arange(cs.wl.v)
+    prob, _ = run_mc(head, dev_tensor(H), 64, tau, [3, 4, 5, 6], toks)
+    z = ref.dense_logits(cs.rows, cs.wl.v, H64[0])
+    want = np.exp(z / tau - ref.logsumexp(z / tau))
+    np.testing.assert_allclose(prob, want, rtol=2e-5, atol=1e-9)
+
+
+def test_llama_mc_marginal_parity(fh):
+    cs = case(1)
+    head = cs.prepare(fh, max_batch=1, max_p=512)
+    H, H64 = cs.hidden(2, offset=1200)
+    rng = np.random.default_rng(8)
+    seeds = [(11 << 32) | i for i in range(24)]
+    for r in range(2):
+        o1 = oracle_mc(cs, H64[r], 512, 1.0, seeds[:1], [0])
+        toks = tokens_for(cs, o1, rng, 64)
+        prob, lse = run_mc(head, dev_tensor(H[r:r + 1]), 512, 1.0, seeds, toks)
+        o = oracle_mc(cs, H64[r], 512, 1.0, seeds, toks)
+        check_mc(cs, prob, lse, o, rtol=1e-4)
+        assert (prob > 0).sum() >= 32
+    assert fh.flashhead_query(head.handle, 9) == 0
+
+
+def test_gemma_int4_mc_marginal_parity(fh):
+    cs = case(4)
+    head = cs.prepare(fh, max_batch=1, max_p=1024)
+    H, H64 = cs.hidden(1, offset=1300)
+    rng = np.random.default_rng(9)
+    seeds = [(12 << 32) | i for i in range(12)]
+    o1 = oracle_mc(cs, H64[0], 1024, 0.8, seeds[:1], [0])
+    toks = tokens_for(cs, o1, rng, 32)
+    prob, lse = run_mc(head, dev_tensor(H), 1024, 0.8, seeds, toks)
+    o = oracle_mc(cs, H64[0], 1024, 0.8, seeds, toks)
+    check_mc(cs, prob, lse, o, rtol=1e-4)
+
+
+def test_mc_draw_lse_matches_the_sampling_step(fh):
+    # draw i probes what flashhead_sample with key seeds[i] probes: its lse
+    # is that step's out_lse (summed in another order)
+    cs = case(1)
+    head = cs.prepare(fh, max_batch=1, max_p=512)
+    H, _ = cs.hidden(1, offset=1400)
+    x = dev_tensor(H)
+    seeds = [(13 << 32) | i for i in range(16)]
+    _, lse = run_mc(head, x, 512, 0.7, seeds, [5, 6])
+    step_lse = torch.empty(1, dtype=torch.float32, device="cuda")
+    for i, s in enumerate(seeds):
+        head.sample(x, 512, 0.7, seeds_dev([s]), out_lse=step_lse)
+        assert float(step_lse.cpu()[0]) == pytest.approx(lse[i], rel=1e-5)
+
+
+def test_mc_repeatable_and_errors(fh):
+    cs = case(0)
+    head = cs.prepare(fh, max_batch=1, max_p=64)
+    H, _ = cs.hidden(1, offset=90)
+    x = dev_tensor(H)
+    seeds = list(range(200, 300))
+    toks = np.arange(0, cs.wl.v, 3)
+    a, la = run_mc(head, x, 8, 0.8, seeds, toks)
+    b, lb = run_mc(head, x, 8, 0.8, seeds, toks)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    sd = seeds_dev(seeds)
+    tk = torch.from_numpy(toks.astype(np.int32)).cuda()
+    out = torch.empty(len(toks), dtype=torch.float32, device="cuda")
+    nbytes = fh.flashhead_mc_workspace_bytes(head.handle, len(seeds), 8, len(toks))
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+    wsv = ws[(-ws.data_ptr()) % 256:]
+    for p, tau, n, nb in ((0, 0.8, 100, nbytes), (8, 0.0, 100, nbytes),
+                          (8, float("nan"), 100, nbytes), (8, 0.8, 0, nbytes),
+                          (65, 0.8, 100, nbytes), (8, 0.8, 100, nbytes - 1)):
+        with pytest.raises(fh.FlashHeadError) as ei:
+            fh.flashhead_mc_marginal(head.handle, x, p, tau, sd, n, tk, len(toks), out,
+                                     None, wsv, nb)
+        assert ei.value.status == fh.FH_ERR_INVALID_ARG
+    # a token id outside the vocabulary is reported, not read out of bounds
+    bad = torch.tensor([5, cs.wl.v, -3], dtype=torch.int32, device="cuda")
+    head.mc_marginal(x, 8, 0.8, sd, bad)
+    torch.cuda.synchronize()
+    assert fh.flashhead_query(head.handle, 9) == 16

@@ -35,6 +35,7 @@ EXPORTED = [
     "flashhead_status_string", "flashhead_export_centroids",
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
     "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
+    "flashhead_mc_workspace_bytes", "flashhead_mc_marginal",
 ]
 
 
@@ -99,6 +100,11 @@ def _load() -> C.CDLL:
     lib.flashhead_profile_end.argtypes = [vp, C.POINTER(C.c_double),
                                           C.POINTER(i32)]
     lib.flashhead_profile_end.restype = C.c_int
+    lib.flashhead_mc_workspace_bytes.argtypes = [vp, i32, i32, i32]
+    lib.flashhead_mc_workspace_bytes.restype = C.c_size_t
+    lib.flashhead_mc_marginal.argtypes = [vp, vp, i32, f32, vp, i32, vp, i32,
+                                          vp, vp, vp, C.c_size_t, vp]
+    lib.flashhead_mc_marginal.restype = C.c_int
     return lib
 
 
@@ -205,6 +211,23 @@ def flashhead_sample(handle: int, H, B: int, p: int, tau: float, seeds,
            "flashhead_sample")
 
 
+def flashhead_mc_workspace_bytes(handle: int, n_draws: int, p: int,
+                                 n_tokens: int) -> int:
+    return int(lib.flashhead_mc_workspace_bytes(handle, n_draws, p, n_tokens))
+
+
+def flashhead_mc_marginal(handle: int, H, p: int, tau: float, seeds,
+                          n_draws: int, tokens, n_tokens: int, out_prob,
+                          out_lse, workspace, workspace_bytes: int,
+                          stream=None) -> None:
+    _check(lib.flashhead_mc_marginal(handle, _ptr(H), p, tau, _ptr(seeds),
+                                     n_draws, _ptr(tokens), n_tokens,
+                                     _ptr(out_prob), _ptr(out_lse),
+                                     _ptr(workspace), workspace_bytes,
+                                     _stream(stream)),
+           "flashhead_mc_marginal")
+
+
 def dense_head_workspace_bytes(B: int) -> int:
     return int(lib.dense_head_workspace_bytes(B))
 
@@ -298,6 +321,24 @@ class FlashHead:
             out = torch.empty(B, dtype=torch.int32, device=H.device)
         flashhead_sample(self.handle, H, B, p, tau, seeds, out, out_lse,
                          debug, stream)
+        return out
+
+    def mc_marginal(self, H, p: int, tau: float, seeds, tokens, out=None,
+                    out_lse=None, workspace=None, stream=None):
+        """Formula 7: the mean over len(seeds) draws of p(v | h, S_i) for
+        each token of `tokens` (H: 1 x d)."""
+        torch = _torch()
+        n, q = seeds.numel(), tokens.numel()
+        if out is None:
+            out = torch.empty(q, dtype=torch.float32, device=H.device)
+        nbytes = flashhead_mc_workspace_bytes(self.handle, n, p, q)
+        if workspace is None:
+            # 256-byte aligned view of a fresh byte buffer
+            raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=H.device)
+            off = (-raw.data_ptr()) % 256
+            workspace = raw[off:off + nbytes]
+        flashhead_mc_marginal(self.handle, H, p, tau, seeds, n, tokens, q, out,
+                              out_lse, workspace, nbytes, stream)
         return out
 
     def centroids(self) -> np.ndarray:

@@ -46,6 +46,7 @@ struct fh_handle {
   int last_path = 0;                // kernels of the last step (flashhead_query 10)
   uint32_t* b1_epoch = nullptr;     // launch counter (picks the buffer set)
   uint32_t* b1_go = nullptr;        // 2 words: all keys seen, per buffer set (0 between launches)
+  int32_t* t2row = nullptr;         // v: row of each token in the cluster-major copy
 
 
   int64_t bytes = 0;
@@ -184,6 +185,15 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
     FH_TRY(launch_centroid_means(E, lde_bytes, h->dtype, d, h->c2t, c, b, h->C, s));
   FH_TRY(alloc(h, &h->Ec, (size_t)v * h->row_bytes));
   FH_TRY(launch_cluster_major_copy(E, lde_bytes, h->c2t, v, h->row_bytes, h->Ec, s));
+  {
+    // token -> row of the cluster-major copy (the inverse of the table)
+    std::vector<int32_t> inv((size_t)v);
+    const int32_t* t = static_cast<const int32_t*>(ds->c2t);
+    for (int64_t r = 0; r < v; ++r) inv[(size_t)t[r]] = (int32_t)r;
+    FH_TRY(alloc(h, &h->t2row, (size_t)v * 4));
+    FH_TRY(hipMemcpyAsync(h->t2row, inv.data(), (size_t)v * 4, hipMemcpyHostToDevice, s));
+    FH_TRY(hipStreamSynchronize(s));  // the host vector dies at scope end
+  }
   if (h->quant == FH_QUANT_INT4_G128) {
     std::vector<uint16_t> hostC((size_t)c * d);
     FH_TRY(hipMemcpyAsync(hostC.data(), h->C, hostC.size() * 2, hipMemcpyDeviceToHost, s));
@@ -438,6 +448,31 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
 
 }  // namespace
 
+// Workspace of flashhead_mc_marginal: byte offsets of its parts, each
+// 256-byte aligned.
+struct McLayout {
+  size_t sel, flags, cl, zq, qcl, contrib, total;
+};
+static McLayout mc_layout(int c, int n, int p, int q) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  McLayout L{};
+  size_t o = 0;
+  L.sel = o;
+  o += up((size_t)n * p * 4);
+  L.flags = o;
+  o += up((size_t)c * 4);
+  L.cl = o;
+  o += up((size_t)c * 8);
+  L.zq = o;
+  o += up((size_t)q * 4);
+  L.qcl = o;
+  o += up((size_t)q * 4);
+  L.contrib = o;
+  o += up((size_t)n * q * 4);
+  L.total = o;
+  return L;
+}
+
 extern "C" {
 
 const char* flashhead_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
@@ -525,6 +560,96 @@ int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p, float ta
                      const uint64_t* seeds, int32_t* out_tokens, float* out_lse,
                      const fh_debug* dbg, void* stream) {
   return step_impl(h, H, B, p, FH_MODE_SAMPLE, tau, seeds, out_tokens, out_lse, dbg, stream);
+}
+
+size_t flashhead_mc_workspace_bytes(const fh_handle* h, int32_t n_draws, int32_t p,
+                                    int32_t n_tokens) {
+  if (!h || n_draws < 1 || p < 1 || n_tokens < 1) return 0;
+  return mc_layout(h->c, n_draws, p, n_tokens).total;
+}
+
+int flashhead_mc_marginal(fh_handle* h, const void* H, int32_t p, float tau,
+                          const uint64_t* seeds, int32_t n_draws, const int32_t* tokens,
+                          int32_t n_tokens, float* out_prob, float* out_lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!h || !H || !seeds || !tokens || !out_prob || !workspace) return FH_ERR_INVALID_ARG;
+  if (p < 1 || p > h->c || p > h->max_p || p > kMcMaxP) return FH_ERR_INVALID_ARG;
+  if (!(tau > 0.0f) || !isfinite(tau)) return FH_ERR_INVALID_ARG;
+  if (n_draws < 1 || n_draws > (1 << 20) || n_tokens < 1 || n_tokens > (1 << 16))
+    return FH_ERR_INVALID_ARG;
+  const McLayout L = mc_layout(h->c, n_draws, p, n_tokens);
+  if (workspace_bytes < L.total) return FH_ERR_INVALID_ARG;
+  if (!aligned16(H) || ((uintptr_t)workspace & 255u) != 0) return FH_ERR_UNSUPPORTED;
+  {
+    const int st = check_device(h);
+    if (st != FH_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool int4 = h->quant == FH_QUANT_INT4_G128;
+  const int nchunk = (int)(h->row_bytes / 16);
+
+  // stage 1 once: the plain scores of h into the handle's first key row
+  Stage1Args s1{};
+  s1.C = static_cast<const uint8_t*>(h->C);
+  s1.row_bytes = h->row_bytes;
+  s1.nchunk = nchunk;
+  s1.c = h->c;
+  s1.d = h->d;
+  s1.q4 = h->q4;
+  s1.q4s = h->q4s;
+  s1.ntiles = h->ntiles;
+  s1.groups = h->groups;
+  s1.H = static_cast<const uint8_t*>(H);
+  s1.h_bytes = h->row_bytes;
+  s1.keys = h->keys;
+  s1.key_stride = key_stride(h->c);
+  s1.inv_tau = 1.0f;
+  s1.error = h->error;
+  FH_TRY(launch_stage1(s1, h->dtype, int4, 1, s));
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  McArgs a{};
+  a.scores = h->keys;
+  a.score_stride = key_stride(h->c);
+  a.c = h->c;
+  a.p = p;
+  a.zcut = select_zcut(h->c, p);
+  a.inv_tau = 1.0f / tau;
+  a.seeds = seeds;
+  a.n = n_draws;
+  a.sel = reinterpret_cast<int32_t*>(ws + L.sel);
+  a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  a.cl = reinterpret_cast<float2*>(ws + L.cl);
+  a.H = static_cast<const uint8_t*>(H);
+  a.nchunk = nchunk;
+  a.Ec = h->Ec;
+  a.row_bytes = h->row_bytes;
+  a.b = h->b;
+  a.t2row = h->t2row;
+  a.v = h->v;
+  a.tokens = tokens;
+  a.q = n_tokens;
+  a.zq = reinterpret_cast<float*>(ws + L.zq);
+  a.qcl = reinterpret_cast<int32_t*>(ws + L.qcl);
+  a.contrib = reinterpret_cast<float*>(ws + L.contrib);
+  a.out_prob = out_prob;
+  a.out_lse = out_lse;
+  a.error = h->error;
+  FH_TRY(hipMemsetAsync(a.flags, 0, (size_t)h->c * 4, s));
+
+  // a cluster's rows in the cluster-major copy, folded into (max, sum)
+  RowdotArgs ra{};
+  ra.base = h->Ec;
+  ra.row_bytes = h->row_bytes;
+  ra.nchunk = nchunk;
+  ra.nrows = h->b;
+  ra.c2t = h->c2t;
+  ra.b = h->b;
+  ra.nclusters = h->c;
+  ra.inv_tau = 1.0f / tau;
+  ra.out_lse = out_prob;  // only marks that the rows' lse is folded; never written here
+  FH_TRY(launch_mc(a, ra, h->dtype, s));
+  return FH_OK;
 }
 
 size_t dense_head_workspace_bytes(int32_t B) {

@@ -159,6 +159,39 @@ struct DecodeB1Args {
   uint32_t* go;
 };
 
+// Monte Carlo marginal (Formula 7): n draws of the probed clusters from one
+// row of stage-1 scores, per-cluster (max, sum) pairs of z / tau over the
+// union of the draws, and the mean conditional probability of q query tokens.
+constexpr int kMcMaxP = 4096;
+struct McArgs {
+  const float* scores;    // c stage-1 scores (one row)
+  int64_t score_stride;   // floats the score row is read over (c rounded up to 4)
+  int c, p;
+  float zcut;             // histogram range hint (select_zcut)
+  float inv_tau;
+  const uint64_t* seeds;  // n Philox keys, one per draw
+  int n;
+  int32_t* sel;           // n x p, each draw's clusters ascending
+  uint32_t* flags;        // c, zero between calls: clusters some draw selected
+  float2* cl;             // c (max, sum of exp(x - max)) of z / tau over a cluster's rows
+  const uint8_t* H;       // the hidden vector (d elements of E's type)
+  int nchunk;             // 16-byte chunks per row
+  const uint8_t* Ec;      // cluster-major copy of E
+  int64_t row_bytes;
+  int b;
+  const int32_t* t2row;   // v: row of each token in the cluster-major copy
+  int64_t v;
+  const int32_t* tokens;  // q query tokens
+  int q;
+  float* zq;              // q exact logits
+  int32_t* qcl;           // q clusters of the query tokens
+  float* contrib;         // q x n conditional probabilities (token-major)
+  float* out_prob;        // q estimates
+  float* out_lse;         // optional: n lse of z / tau over each draw's candidates
+  uint32_t* error;
+};
+hipError_t launch_mc(const McArgs& a, const RowdotArgs& ra, int dtype, hipStream_t s);
+
 // Optional events recorded exactly around one kernel (hipExtLaunchKernel).
 struct Timing {
   hipEvent_t start = nullptr, stop = nullptr;
