@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time back-to-back (cache-warm) calls")
+    ap.add_argument("--c", type=int, default=None, help="cluster count variant (v = c * b)")
+    ap.add_argument("--b", type=int, default=None, help="cluster size variant (v = c * b)")
+    ap.add_argument("--p", type=int, default=None, help="probe count variant")
     ap.add_argument("--mc", type=int, default=0, metavar="N",
                     help="time the Monte Carlo marginal (Formula 7) with N draws "
                          "instead of the decode step; prints its own JSON line")
@@ -123,6 +126,13 @@ def main():
     from two_stage_retrieval_amd import synth
 
     wl = synth.workload(args.workload)
+    if args.c or args.b or args.p:
+        # c / p variants of the same head shape ([paper] Table 7's trade-off)
+        import dataclasses
+        c = args.c or wl.c
+        b = args.b or wl.b
+        p = args.p or wl.p
+        wl = dataclasses.replace(wl, name=f"{wl.name}-c{c}-b{b}-p{p}", c=c, b=b, v=c * b, p=p)
     B = args.batch or wl.batches[0]
     int4 = wl.quant == "int4_g128"
     sample = wl.mode == "sample"

@@ -166,3 +166,28 @@ def test_selection_with_outlier_keys(fh, B):
     check_batch(cs, res, H64, 64, "sample", 0.7, seeds, stats=st)
     assert fh.flashhead_query(head.handle, 9) == 0
     print(st)
+
+
+# --------------------------------------------------------------------------
+# c / p variants of the Llama head shape ([paper] Table 7): same kernels,
+# other cluster sizes and probe counts
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("c,b,p", [(4008, 32, 128), (4008, 32, 256), (4008, 32, 512),
+                                   (8016, 16, 128)])
+def test_cp_variants_parity(fh, c, b, p):
+    cs = case(1, c=c, b=b)
+    head = cs.prepare(fh, max_batch=16, max_p=p)
+    st = Stats()
+    H, H64 = cs.hidden(8, offset=1500)
+    for i in range(8):
+        res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, p, "greedy")
+        assert path_of(fh, head) == PATH_SINGLE_LAUNCH
+        check_batch(cs, res, H64[i:i + 1], p, stats=st)
+    seeds = synth.make_seeds(6, 16)
+    H16, H16_64 = cs.hidden(16, offset=1600)
+    res = run_debug(fh, head, dev_tensor(H16), 16, p, "sample", 0.8, seeds_dev(seeds))
+    assert path_of(fh, head) == PATH_BATCHED
+    check_batch(cs, res, H16_64, p, "sample", 0.8, seeds, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
