@@ -185,15 +185,27 @@ def centroid_means(rows_f64: Callable[[np.ndarray], np.ndarray], c2t
     return round_to_bf16(np.stack(out))
 
 
-def int4_quantize(C_f64, group: int = 128):
+def int4_mean_shift(C_f64) -> np.ndarray:
+    """The shift of the mean-shifted INT4 variant: the column means of C over
+    its c rows, rounded to bf16 (t = 1, the data-free choice)."""
+    return round_to_bf16(np.asarray(C_f64, dtype=np.float64).mean(axis=0))
+
+
+def int4_quantize(C_f64, group: int = 128, shift=None):
     """[notes] Module 3 (INT4 stage-1 centroids), symmetric per-group codes.
 
     For each row k and group g of `group` consecutive columns:
       amax = max |C[k, g]|, s = bf16(amax / 7),
       q = round_half_even(C / s) clipped to [-8, 7]   (q = 0 where s = 0).
+    With `shift` (a d-vector), C - shift is quantized instead: every score
+    then moves by the same shift . h, which changes neither the top p nor a
+    Gumbel-top-p draw, while the codes cover a narrower range when the rows
+    share a common direction.
     Returns (q int8 c x d, s float64 c x G with bf16 values).
     """
     C = np.asarray(C_f64, dtype=np.float64)
+    if shift is not None:
+        C = C - np.asarray(shift, dtype=np.float64)[None, :]
     c, d = C.shape
     if d % group:
         raise ValueError("d must be a multiple of the group size")

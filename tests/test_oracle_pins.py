@@ -517,6 +517,38 @@ def test_int4_quantizer_definition_and_roundtrip_bound():
 # work model ([paper] Table 8 parameter counts)
 # --------------------------------------------------------------------------
 
+def test_int4_mean_shift_definition_and_invariance():
+    """The shift is the bf16 of the column means; the shifted codes follow the
+    quantizer's definition on C - shift (round trip within half a scale);
+    and the shift moves every score by shift . h, so the greedy top p and a
+    Gumbel-top-p draw of the unquantized scores do not change."""
+    rng = np.random.default_rng(21)
+    c, d, p = 300, 256, 20
+    m = rng.standard_normal(d)
+    m /= np.linalg.norm(m)
+    C = rng.standard_normal((c, d)) * 0.05 + 2.0 * m          # a shared direction
+    C = ref.round_to_bf16(C / np.linalg.norm(C, axis=1, keepdims=True))
+    mu = ref.int4_mean_shift(C)
+    assert np.array_equal(mu, ref.round_to_bf16(C.sum(axis=0) / c))
+    q, sc = ref.int4_quantize(C, shift=mu)
+    deq = q.reshape(c, d // 128, 128) * sc[:, :, None]
+    assert np.all(np.abs((C - mu).reshape(c, d // 128, 128) - deq) <= sc[:, :, None] / 2 + 1e-15)
+    q0, sc0 = ref.int4_quantize(C)
+    # the shared direction leaves the shifted rows a narrower range
+    assert np.median(sc) < 0.8 * np.median(sc0)
+    for i in range(10):
+        h = rng.standard_normal(d)
+        s_plain = C @ h
+        s_shift = (C - mu) @ h
+        np.testing.assert_allclose(s_plain - s_shift, mu @ h, rtol=0, atol=1e-12)
+        S1, _, _ = ref.select_clusters(s_plain, p)
+        S2, _, _ = ref.select_clusters(s_shift, p)
+        assert set(S1.tolist()) == set(S2.tolist())
+        G1, _, _ = ref.select_clusters(s_plain, p, "sample", 0.7, seed=i)
+        G2, _, _ = ref.select_clusters(s_shift, p, "sample", 0.7, seed=i)
+        assert set(G1.tolist()) == set(G2.tolist())
+
+
 def test_active_params_match_the_pages():
     vals = {}
     with open(os.path.join(GOLDEN, "active_params_llama32_1b.txt")) as f:
