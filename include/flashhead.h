@@ -68,6 +68,11 @@ extern "C" {
 #define FH_QUANT_NONE 0
 #define FH_QUANT_INT4_G128 1 /* stage-1 centroids as 4-bit codes, groups of
                                 128 columns, one bf16 scale per group        */
+#define FH_QUANT_INT4_G128_MEAN 2 /* the same codes of C minus mu, mu the bf16
+                                of C's column means: every stage-1 score
+                                moves by mu . h, which changes neither the top
+                                p nor a Gumbel-top-p draw; the debug scores
+                                are the shifted ones                         */
 
 #define FH_MODE_GREEDY 0
 #define FH_MODE_SAMPLE 1
@@ -102,8 +107,9 @@ typedef struct fh_desc {
                          or NULL to compute C = unit(mean of cluster rows)
                          (Formula 5; bf16 by round-to-nearest-even when
                          dtype is bf16); copied at prepare                 */
-  int32_t quant;      /* FH_QUANT_NONE or FH_QUANT_INT4_G128 (needs bf16,
-                         d a multiple of 128)                              */
+  int32_t quant;      /* FH_QUANT_NONE, FH_QUANT_INT4_G128 or
+                         FH_QUANT_INT4_G128_MEAN (INT4: needs bf16, d a
+                         multiple of 128)                                  */
   int32_t max_batch;  /* largest B passed to later calls (1..FH_MAX_BATCH) */
   int32_t max_p;      /* largest p passed to later calls (1..c)            */
   void* stream;       /* hipStream_t for prepare's own work                */

@@ -99,6 +99,9 @@ def test_prepare_rejects_bad_descriptors(fh):
     assert _prepare(fh, _desc(fh, c2t, quant=fh.FH_QUANT_INT4_G128)) == uns  # INT4 needs bf16
     assert _prepare(fh, _desc(fh, c2t, dtype=fh.FH_DTYPE_BF16, d=200,
                               quant=fh.FH_QUANT_INT4_G128)) == uns            # d % 128
+    assert _prepare(fh, _desc(fh, c2t, quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
+    assert _prepare(fh, _desc(fh, c2t, dtype=fh.FH_DTYPE_BF16, d=200,
+                              quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
 
 
 @pytest.mark.parametrize("kind", ["repeat", "out_of_range", "negative"])

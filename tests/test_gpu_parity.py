@@ -61,9 +61,11 @@ class Case:
         return H, ref.as_f64(H, self.dtype)
 
     def prepare(self, fh, max_batch, max_p, with_C=True, quant=None):
-        q = fh.FH_QUANT_INT4_G128 if (quant if quant is not None else
-                                      self.wl.quant == "int4_g128") \
-            else fh.FH_QUANT_NONE
+        # quant: a FH_QUANT_* code, or None for the workload's own
+        if quant is None:
+            quant = (fh.FH_QUANT_INT4_G128 if self.wl.quant == "int4_g128"
+                     else fh.FH_QUANT_NONE)
+        q = quant
         return fh.FlashHead(self.E_dev, self.head.c2t,
                             self.C_dev if with_C else None, quant=q,
                             max_batch=max_batch, max_p=max_p)
@@ -472,3 +474,57 @@ def test_tiny_sampling_homogeneity_p8(fh):
                       np.append(oc[~exp_small], oc[exp_small].sum())])
     table = table[:, table.sum(axis=0) > 0]
     assert stats.chi2_contingency(table)[1] > 1e-3
+
+
+# --------------------------------------------------------------------------
+# mean-shifted INT4 centroids
+# --------------------------------------------------------------------------
+
+def _mean_shifted(cs):
+    """The case with the oracle's mean-shifted codes in place of the plain."""
+    import copy
+    cm = copy.copy(cs)
+    cm.int4 = ref.int4_quantize(cs.C64, shift=ref.int4_mean_shift(cs.C64))
+    return cm
+
+
+def test_gemma_int4_mean_shift_codes_and_parity(fh):
+    cs = case(4)
+    cm = _mean_shifted(cs)
+    head = cs.prepare(fh, max_batch=32, max_p=1024, quant=fh.FH_QUANT_INT4_G128_MEAN)
+    codes, scales = head.int4()
+    q, s = unpack_int4(codes, scales, cs.wl.c, cs.wl.d)
+    assert np.array_equal(q, cm.int4[0])
+    assert np.array_equal(s, cm.int4[1])
+    st = Stats()
+    H, H64 = cs.hidden(8, offset=1700)
+    for i in range(8):
+        res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, 1024, "greedy")
+        check_batch(cm, res, H64[i:i + 1], 1024, stats=st, score_tol=2e-2)
+    H32, H32_64 = cs.hidden(32, offset=1800)
+    res = run_debug(fh, head, dev_tensor(H32), 32, 1024, "greedy")
+    check_batch(cm, res, H32_64, 1024, stats=st, score_tol=2e-2)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
+def test_int4_mean_shift_flips_fewer_boundary_clusters(fh):
+    # rows that share a direction (as a trained output embedding's do): the
+    # plain codes spend their range on the shared part, the shifted ones do
+    # not; count the clusters each INT4 selection swaps against the selection
+    # from the unquantized bf16 centroids
+    cs = case(4, common=8.0)
+    H, H64 = cs.hidden(32, offset=1900)
+    p = 1024
+    flips = {}
+    for name, quant in (("plain", fh.FH_QUANT_INT4_G128), ("mean", fh.FH_QUANT_INT4_G128_MEAN)):
+        head = cs.prepare(fh, max_batch=32, max_p=p, quant=quant)
+        res = run_debug(fh, head, dev_tensor(H), 32, p, "greedy")
+        n = 0
+        for r in range(32):
+            ref_set = set(ref.order_desc(cs.C64 @ H64[r])[:p].tolist())
+            n += len(set(res["clusters"][r].tolist()) - ref_set)
+        flips[name] = n / (32 * p)
+        head.close()
+    print("boundary swaps per selected cluster vs bf16:", flips)
+    assert flips["mean"] < flips["plain"]

@@ -26,6 +26,7 @@ FH_DTYPE_F32 = 0
 FH_DTYPE_BF16 = 1
 FH_QUANT_NONE = 0
 FH_QUANT_INT4_G128 = 1
+FH_QUANT_INT4_G128_MEAN = 2
 FH_MODE_GREEDY = 0
 FH_MODE_SAMPLE = 1
 

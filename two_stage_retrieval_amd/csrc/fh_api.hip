@@ -114,8 +114,11 @@ double bf16_value(uint16_t b) {
 
 // Symmetric per-group INT4 codes (groups of 128 columns): scale = bf16(amax/7),
 // code = round-half-even(x / scale) clipped to [-8, 7]; packed in 16-row tiles.
-void quantize_int4(const uint16_t* C, int c, int d, std::vector<uint8_t>& codes,
-                   std::vector<uint16_t>& scales, int* ntiles_out, int* groups_out) {
+// x = C - shift (shift: d values, or NULL for none); C - shift is exact in
+// double for bf16 C and shift.
+void quantize_int4(const uint16_t* C, const double* shift, int c, int d,
+                   std::vector<uint8_t>& codes, std::vector<uint16_t>& scales, int* ntiles_out,
+                   int* groups_out) {
   const int G = d / 128, ntiles = (c + 15) / 16;
   codes.assign((size_t)ntiles * G * 1024, 0);
   scales.assign((size_t)ntiles * G * 16, 0);
@@ -124,11 +127,16 @@ void quantize_int4(const uint16_t* C, int c, int d, std::vector<uint8_t>& codes,
     const int t = k / 16, rin = k % 16;
     for (int g = 0; g < G; ++g) {
       const uint16_t* src = C + (size_t)k * d + (size_t)g * 128;
+      const double* sh = shift ? shift + (size_t)g * 128 : nullptr;
+      double x[128];
       double amax = 0.0;
-      for (int j = 0; j < 128; ++j) amax = fmax(amax, fabs(bf16_value(src[j])));
+      for (int j = 0; j < 128; ++j) {
+        x[j] = bf16_value(src[j]) - (sh ? sh[j] : 0.0);
+        amax = fmax(amax, fabs(x[j]));
+      }
       const double s = round_bf16(amax / 7.0);
       for (int j = 0; j < 128; ++j) {
-        double qq = s > 0.0 ? nearbyint(bf16_value(src[j]) / s) : 0.0;
+        double qq = s > 0.0 ? nearbyint(x[j] / s) : 0.0;
         qq = qq < -8.0 ? -8.0 : (qq > 7.0 ? 7.0 : qq);
         q[j] = (int8_t)qq;
       }
@@ -194,13 +202,22 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
     FH_TRY(hipMemcpyAsync(h->t2row, inv.data(), (size_t)v * 4, hipMemcpyHostToDevice, s));
     FH_TRY(hipStreamSynchronize(s));  // the host vector dies at scope end
   }
-  if (h->quant == FH_QUANT_INT4_G128) {
+  if (h->quant == FH_QUANT_INT4_G128 || h->quant == FH_QUANT_INT4_G128_MEAN) {
     std::vector<uint16_t> hostC((size_t)c * d);
     FH_TRY(hipMemcpyAsync(hostC.data(), h->C, hostC.size() * 2, hipMemcpyDeviceToHost, s));
     FH_TRY(hipStreamSynchronize(s));
+    std::vector<double> mu;
+    if (h->quant == FH_QUANT_INT4_G128_MEAN) {
+      // bf16 of the column means: the sum of c bf16 values is exact in double
+      mu.assign((size_t)d, 0.0);
+      for (int k = 0; k < c; ++k)
+        for (int j = 0; j < d; ++j) mu[j] += bf16_value(hostC[(size_t)k * d + j]);
+      for (int j = 0; j < d; ++j) mu[j] = round_bf16(mu[j] / c);
+    }
     std::vector<uint8_t> codes;
     std::vector<uint16_t> scales;
-    quantize_int4(hostC.data(), c, d, codes, scales, &h->ntiles, &h->groups);
+    quantize_int4(hostC.data(), mu.empty() ? nullptr : mu.data(), c, d, codes, scales,
+                  &h->ntiles, &h->groups);
     FH_TRY(alloc(h, &h->q4, codes.size()));
     FH_TRY(alloc(h, &h->q4s, scales.size() * 2));
     FH_TRY(hipMemcpyAsync(h->q4, codes.data(), codes.size(), hipMemcpyHostToDevice, s));
@@ -272,7 +289,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   const int nchunk = (int)(h->row_bytes / 16);
 
 
-  const bool int4 = h->quant == FH_QUANT_INT4_G128;
+  const bool int4 = h->quant != FH_QUANT_NONE;
   const bool batched = B >= 2 && h->b % 16 == 0 && batched_supported(h->dtype, h->d, B, int4);
 
   // stage 1 (+ selection by each batch row's last block on the GEMV path)
@@ -515,8 +532,10 @@ int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
   if (row_bytes % 16 || (ds->lde * es) % 16 || row_bytes > FH_MAX_ROW_BYTES)
     return FH_ERR_UNSUPPORTED;
   if (!aligned16(ds->E) || (ds->C && !aligned16(ds->C))) return FH_ERR_UNSUPPORTED;
-  if (ds->quant != FH_QUANT_NONE && ds->quant != FH_QUANT_INT4_G128) return FH_ERR_UNSUPPORTED;
-  if (ds->quant == FH_QUANT_INT4_G128 && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
+  if (ds->quant != FH_QUANT_NONE && ds->quant != FH_QUANT_INT4_G128 &&
+      ds->quant != FH_QUANT_INT4_G128_MEAN)
+    return FH_ERR_UNSUPPORTED;
+  if (ds->quant != FH_QUANT_NONE && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
     return FH_ERR_UNSUPPORTED;
   // C2T must be a permutation of [0, v) (equal-size clusters, dense table)
   {
@@ -585,7 +604,7 @@ int flashhead_mc_marginal(fh_handle* h, const void* H, int32_t p, float tau,
     if (st != FH_OK) return st;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool int4 = h->quant == FH_QUANT_INT4_G128;
+  const bool int4 = h->quant != FH_QUANT_NONE;
   const int nchunk = (int)(h->row_bytes / 16);
 
   // stage 1 once: the plain scores of h into the handle's first key row
@@ -728,7 +747,7 @@ int flashhead_export_centroids(const fh_handle* h, void* dst) {
 
 int flashhead_export_int4(const fh_handle* h, uint8_t* codes, uint16_t* scales) {
   if (!h || !codes || !scales) return FH_ERR_INVALID_ARG;
-  if (h->quant != FH_QUANT_INT4_G128) return FH_ERR_UNSUPPORTED;
+  if (h->quant == FH_QUANT_NONE) return FH_ERR_UNSUPPORTED;
   const size_t tiles = (size_t)h->ntiles * h->groups;
   FH_TRY(hipMemcpy(codes, h->q4, tiles * 1024, hipMemcpyDeviceToHost));
   FH_TRY(hipMemcpy(scales, h->q4s, tiles * 16 * 2, hipMemcpyDeviceToHost));

@@ -132,8 +132,13 @@ _HEAD_CACHE: dict = {}
 
 
 def make_head(wl: Workload | int, *, v=None, d=None, c=None, b=None,
-              seed=None, cache=True) -> Head:
-    """Draw E and C2T for a workload (shape overrides give small variants)."""
+              seed=None, common=0.0, cache=True) -> Head:
+    """Draw E and C2T for a workload (shape overrides give small variants).
+
+    common > 0 adds common * m, for one unit vector m shared by all rows, to
+    every row before it is normalised: rows that share a direction, as the
+    rows of a trained output embedding do.  m comes from a stream of its
+    own, so common = 0 gives the workload's usual head."""
     if isinstance(wl, int):
         wl = WORKLOADS[wl]
     over = {k: x for k, x in dict(v=v, d=d, c=c, b=b).items() if x is not None}
@@ -144,13 +149,18 @@ def make_head(wl: Workload | int, *, v=None, d=None, c=None, b=None,
             over["v"] = over.get("c", wl.c) * over.get("b", wl.b)
         wl = dataclasses.replace(wl, **over)
     key = (wl.v, wl.d, wl.c, wl.b, wl.dtype, wl.sigma_n, wl.sigma_ln,
-           wl.data_seed, wl.centroids)
+           wl.data_seed, wl.centroids, float(common))
     if cache and key in _HEAD_CACHE:
         h = _HEAD_CACHE[key]
         return Head(wl, h.E, h.c2t, h.C_given)
     if wl.c * wl.b != wl.v:
         raise ValueError("workload needs v == c*b")
     rng = np.random.Generator(np.random.PCG64(wl.data_seed))
+    shared = None
+    if common:
+        shared = _unit_rows(np.random.Generator(np.random.PCG64(wl.data_seed + 7777))
+                            .standard_normal((1, wl.d), dtype=np.float32))[0]
+        shared *= np.float32(common)
     mu = _unit_rows(rng.standard_normal((wl.c, wl.d), dtype=np.float32))
     perm = rng.permutation(wl.v).astype(np.int32)
     c2t = perm.reshape(wl.c, wl.b).copy()
@@ -164,6 +174,8 @@ def make_head(wl: Workload | int, *, v=None, d=None, c=None, b=None,
         x = rng.standard_normal((n, wl.d), dtype=np.float32)
         x *= np.float32(wl.sigma_n)
         x += mu[ks]
+        if shared is not None:
+            x += shared
         x = _unit_rows(x) * norms[slot:slot + n, None]
         dst = perm[slot:slot + n]
         E[dst] = f32_to_bf16_bits(x) if wl.dtype == "bf16" else x
