@@ -354,46 +354,51 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
       bb = s_best[w][r] > bb ? s_best[w][r] : bb;
       ll = lse_merge(ll, Lse{s_lse[w][r].x, s_lse[w][r].y});
     }
-    a.part_best[(int64_t)blockIdx.x * B + r] = bb;
-    if (a.with_lse) a.part_lse[(int64_t)blockIdx.x * B + r] = make_float2(ll.m, ll.s);
+    // row-major partials ([row][workgroup]): the fold of a row reads them
+    // contiguously
+    a.part_best[(int64_t)r * gridDim.x + blockIdx.x] = bb;
+    if (a.with_lse) a.part_lse[(int64_t)r * gridDim.x + blockIdx.x] = make_float2(ll.m, ll.s);
   }
 }
 
-// per batch row: fold the per-block partials into the token (and lse);
-// block 0 also clears the cluster masks of this call's union
+// per batch row: fold the per-block partials (a contiguous run per row) into
+// the token (and lse), wave by wave and then the waves in order; the rows'
+// workgroups together clear the cluster masks of this call's union
 __global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblocks) {
-  __shared__ uint64_t s_b[256];
-  __shared__ float2 s_l[256];
+  __shared__ uint64_t s_b[256 / kWave];
+  __shared__ float2 s_l[256 / kWave];
   const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  const uint64_t* pb = a.part_best + (int64_t)r * nblocks;
+  const float2* pl = a.part_lse + (int64_t)r * nblocks;
   uint64_t bb = 0ull;
   Lse ll = lse_empty();
-  for (int j = threadIdx.x; j < nblocks; j += 256) {
-    const uint64_t x = a.part_best[(int64_t)j * a.B + r];
+  for (int j = t; j < nblocks; j += 256) {
+    const uint64_t x = pb[j];
     bb = x > bb ? x : bb;
-    if (a.with_lse) {
-      const float2 pl = a.part_lse[(int64_t)j * a.B + r];
-      ll = lse_merge(ll, Lse{pl.x, pl.y});
-    }
+    if (a.with_lse) ll = lse_merge(ll, Lse{pl[j].x, pl[j].y});
   }
-  s_b[threadIdx.x] = bb;
-  s_l[threadIdx.x] = make_float2(ll.m, ll.s);
+  bb = wave_max_u64(bb);
+  if (a.with_lse) ll = wave_lse(ll);
+  if ((t & (kWave - 1)) == 0) {
+    s_b[t / kWave] = bb;
+    s_l[t / kWave] = make_float2(ll.m, ll.s);
+  }
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
-      if (s_b[threadIdx.x + w] > s_b[threadIdx.x]) s_b[threadIdx.x] = s_b[threadIdx.x + w];
-      const Lse x = lse_merge(Lse{s_l[threadIdx.x].x, s_l[threadIdx.x].y},
-                              Lse{s_l[threadIdx.x + w].x, s_l[threadIdx.x + w].y});
-      s_l[threadIdx.x] = make_float2(x.m, x.s);
+  if (t == 0) {
+    uint64_t b0 = s_b[0];
+    Lse l0{s_l[0].x, s_l[0].y};
+#pragma unroll
+    for (int w = 1; w < 256 / kWave; ++w) {
+      b0 = s_b[w] > b0 ? s_b[w] : b0;
+      l0 = lse_merge(l0, Lse{s_l[w].x, s_l[w].y});
     }
-    __syncthreads();
+    a.out_tokens[r] = (int32_t)key_id(b0);
+    if (a.out_lse) a.out_lse[r] = l0.m + logf(l0.s);
   }
-  if (threadIdx.x == 0) {
-    a.out_tokens[r] = (int32_t)key_id(s_b[0]);
-    if (a.out_lse) a.out_lse[r] = s_l[0].x + logf(s_l[0].y);
-  }
-  if (r == 0 && a.masks) {
+  if (a.masks) {
     const int u = *a.ucount;
-    for (int i = threadIdx.x; i < u; i += 256) a.masks[a.ulist[i]] = 0ull;
+    for (int i = r * 256 + t; i < u; i += (int)gridDim.x * 256) a.masks[a.ulist[i]] = 0ull;
   }
 }
 
