@@ -31,7 +31,6 @@ struct fh_handle {
   uint64_t* masks = nullptr;  // c
   uint32_t* error = nullptr;  // 1
   // batched path
-  uint32_t* sel_counter = nullptr;  // select kernel's finished-block counter
   int32_t* ulist = nullptr;         // union of the selected clusters (c)
   int32_t* ucount = nullptr;
   uint64_t* part_best = nullptr;    // stage-2 partials, grid x max_batch
@@ -236,12 +235,10 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(hipMemsetAsync(h->counters, 0, (size_t)mb * kArriveWords * 4, s));
   FH_TRY(hipMemsetAsync(h->masks, 0, (size_t)(c + 1) * 8, s));
   FH_TRY(hipMemsetAsync(h->error, 0, 4, s));
-  FH_TRY(alloc(h, &h->sel_counter, (size_t)kArriveWords * 4));
   FH_TRY(alloc(h, &h->ulist, (size_t)c * 4));
   FH_TRY(alloc(h, &h->ucount, 4));
   FH_TRY(alloc(h, &h->part_best, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
-  FH_TRY(hipMemsetAsync(h->sel_counter, 0, (size_t)kArriveWords * 4, s));
   FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * key_stride(c) * 4));
   FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * key_stride(c) * 4, s));
   FH_TRY(alloc(h, &h->b1_slots, (size_t)2 * kDecodeB1SlotStride * 8));
@@ -408,7 +405,6 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.seeds = seeds;
     a.dbg_scores = ksplit > 1 && dbg ? dbg->scores : nullptr;
     if (batched) {
-      a.counter = h->sel_counter;
       a.ulist = h->ulist;
       a.ucount = h->ucount;
     }

@@ -65,8 +65,8 @@ struct SelectArgs {
   int sel_stride;
   uint64_t* masks;       // optional: per-cluster bitmask of selecting rows
   uint32_t* error;       // optional: set non-zero if a row selected != p
-  // optional union compaction by the last block (needs masks)
-  uint32_t* counter;     // kArriveWords arrival counters (zero between calls)
+  // optional union of the rows' clusters, compacted by a second launch
+  // (needs masks)
   int32_t* ulist;        // clusters with a non-zero mask, ascending
   int32_t* ucount;
 };

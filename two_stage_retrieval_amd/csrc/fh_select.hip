@@ -51,20 +51,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
   select_from_keys<kSelThreads, IPT, false>(u, a.c, a.p, a.zcut, a.sel + (int64_t)r * a.sel_stride,
                                             a.masks, r, a.error, sm);
-  if (!a.counter) return;
-  // row 0's workgroup compacts the union of the selected clusters once every
-  // other row has set its mask bits
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's mask updates have been performed
-  __syncthreads();
-  if (r != 0) {
-    if (threadIdx.x == 0) arrive(a.counter, r);
-    return;
-  }
-  if (threadIdx.x < kWave) {
-    const bool ok = wait_arrivals(a.counter, gridDim.x - 1, threadIdx.x);
-    if (!ok && threadIdx.x == 0 && a.error) atomicOr(a.error, 2u);
-  }
-  __syncthreads();
+}
+
+// The union of the rows' selected clusters (non-zero masks), ascending, as
+// the batched stage 2's work list: one workgroup, launched after the
+// selection so that every row's mask bits are in (the kernel boundary
+// orders them; no workgroup waits on another).
+template <int IPT>
+__global__ __launch_bounds__(kSelThreads) void union_kernel(SelectArgs a) {
+  __shared__ SelSmem sm;
   compact_masks_block<kSelThreads, IPT>(a.masks, a.c, a.ulist, a.ucount, sm);
 }
 
@@ -89,12 +84,21 @@ hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   const int ipt = (a.c + kSelThreads - 1) / kSelThreads;
   const dim3 grid(B), block(kSelThreads);
-  if (ipt <= 4) hipExtLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, e0, e1, 0, a);
-  else if (ipt <= 8) hipExtLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, e0, e1, 0, a);
-  else if (ipt <= 16) hipExtLaunchKernelGGL(select_kernel<16>, grid, block, 0, s, e0, e1, 0, a);
-  else if (ipt <= 32) hipExtLaunchKernelGGL(select_kernel<32>, grid, block, 0, s, e0, e1, 0, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  // with a union list, the events bracket both launches
+  hipEvent_t es = a.ulist ? nullptr : e1;
+#define FH_SEL_IPT(N)                                                                         \
+  if (ipt <= N) {                                                                             \
+    hipExtLaunchKernelGGL(select_kernel<N>, grid, block, 0, s, e0, es, 0, a);                 \
+    if (a.ulist)                                                                              \
+      hipExtLaunchKernelGGL(union_kernel<N>, dim3(1), block, 0, s, nullptr, e1, 0, a);        \
+    return hipGetLastError();                                                                 \
+  }
+  FH_SEL_IPT(4)
+  FH_SEL_IPT(8)
+  FH_SEL_IPT(16)
+  FH_SEL_IPT(32)
+#undef FH_SEL_IPT
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fh
