@@ -22,6 +22,7 @@ namespace fh {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -135,7 +136,7 @@ enum GmMode : int { kGmScores = 0, kGmFlash = 1, kGmDense = 2 };
 // KC: K per chunk (KC / 32 MFMA steps); a wave requests KC * 2 contiguous
 // bytes of each of its rows per chunk
 template <int NT, int IT, int MODE, int KC>
-__global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) {
+__global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_engine_kernel(Stage2mArgs a) {
   constexpr int kSteps = KC / 32;
   constexpr int kHRow = KC + 8;  // LDS row pitch in bf16 (16-byte pad)
   constexpr int kHP = NT * 16 * (KC / 8) / kGmThreads;  // H pieces per thread per chunk
@@ -207,7 +208,10 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 a0[IT][kSteps], a1[IT][kSteps], hreg[kHP];
+  // the H staging registers are a native vector type: as an array of uint4
+  // they were kept in scratch memory, which made every prefetch wait
+  uint4 a0[IT][kSteps], a1[IT][kSteps];
+  u32x4_t hreg[kHP];
   auto load_a = [&](uint4 (&dst)[IT][kSteps], int c) {
 #pragma unroll
     for (int i = 0; i < IT; ++i)
@@ -218,11 +222,11 @@ __global__ __launch_bounds__(kGmThreads) void gemm_engine_kernel(Stage2mArgs a) 
   auto load_h = [&](int c) {
 #pragma unroll
     for (int n = 0; n < kHP; ++n)
-      hreg[n] = *reinterpret_cast<const uint4*>(hsrc[n] + (int64_t)c * KC * 2);
+      hreg[n] = *reinterpret_cast<const u32x4_t*>(hsrc[n] + (int64_t)c * KC * 2);
   };
   auto store_h = [&](int buf) {
 #pragma unroll
-    for (int n = 0; n < kHP; ++n) s_h[buf][hdst[n]] = hreg[n];
+    for (int n = 0; n < kHP; ++n) reinterpret_cast<u32x4_t*>(s_h[buf])[hdst[n]] = hreg[n];
   };
   auto compute = [&](const uint4 (&av)[IT][kSteps], int buf) {
 #pragma unroll
@@ -410,40 +414,43 @@ bool batched_supported(int dtype, int d, int B, bool int4) {
   return d % 128 == 0;
 }
 
-// items per wave: enough reuse of each H fragment, registers for double-buffered rows
-// items per wave (measured): one column tile streams best with one item and
-// more waves per SIMD; wider batches reuse each H fragment over two items
-template <int NT> constexpr int gm_items() { return NT == 1 ? 1 : 2; }
+// Tiling (measured on the 2048-wide heads at B = 16, 32, 64): one 16-row
+// item per wave, and as long a K chunk as d allows (256, 8 MFMA steps, when
+// d % 256 == 0; else 128) for the streaming modes, where it gives each row
+// 512-byte contiguous requests.  Stage-1 scores keep 128: their K slices
+// are short.  The kernel is capped at 256 registers (two waves per SIMD):
+// with one wave per SIMD the wider tiles stalled on HBM latency.
+constexpr int kGmItems = 1;
 
-// K per chunk: 128 (4 MFMA steps).  Longer chunks (256, 512) request
-// longer contiguous runs per row but cost registers and waves per SIMD; on
-// these shapes they measured slower (one column tile) or the same (wider).
-constexpr int kGmKC = 128;
-
-template <int NT, int IT, int MODE>
+template <int NT, int MODE, int KC>
 static void launch_engine_kc(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                              hipEvent_t e1) {
-  hipExtLaunchKernelGGL((gemm_engine_kernel<NT, IT, MODE, kGmKC>), dim3(grid), dim3(kGmThreads), 0,
-                        s, e0, e1, 0, a);
+  hipExtLaunchKernelGGL((gemm_engine_kernel<NT, kGmItems, MODE, KC>), dim3(grid),
+                        dim3(kGmThreads), 0, s, e0, e1, 0, a);
 }
 
-template <int MODE>
-static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
-                                hipEvent_t e1) {
+template <int MODE, int KC>
+static hipError_t launch_engine_nt(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                                   hipEvent_t e1) {
   switch ((a.B + 15) / 16) {
-    case 1: launch_engine_kc<1, gm_items<1>(), MODE>(a, grid, s, e0, e1); break;
-    case 2: launch_engine_kc<2, gm_items<2>(), MODE>(a, grid, s, e0, e1); break;
-    case 3: launch_engine_kc<3, gm_items<3>(), MODE>(a, grid, s, e0, e1); break;
-    case 4: launch_engine_kc<4, gm_items<4>(), MODE>(a, grid, s, e0, e1); break;
+    case 1: launch_engine_kc<1, MODE, KC>(a, grid, s, e0, e1); break;
+    case 2: launch_engine_kc<2, MODE, KC>(a, grid, s, e0, e1); break;
+    case 3: launch_engine_kc<3, MODE, KC>(a, grid, s, e0, e1); break;
+    case 4: launch_engine_kc<4, MODE, KC>(a, grid, s, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-static int engine_grid(int64_t nrows16, int B) {
-  const int NT = (B + 15) / 16;
-  const int it = NT == 1 ? 1 : 2;
-  const int64_t per = (int64_t)kGmWaves * it;
+template <int MODE>
+static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1) {
+  if (a.d % 256 == 0) return launch_engine_nt<MODE, 256>(a, grid, s, e0, e1);
+  return launch_engine_nt<MODE, 128>(a, grid, s, e0, e1);
+}
+
+static int engine_grid(int64_t nrows16) {
+  const int64_t per = (int64_t)kGmWaves * kGmItems;
   const int64_t g = (nrows16 + per - 1) / per;
   return g < 1 ? 1 : (int)g;
 }
@@ -481,7 +488,8 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   m.dbg_scores = a.dbg_scores;
   // one 16-row item per wave and enough K slices to give the chip ~2 x 256
   // workgroups (slices are whole K chunks)
-  const int nchunks = a.d / kGmKC;
+  constexpr int kKC = 128;
+  const int nchunks = a.d / kKC;
   const int64_t groups = ((int64_t)(a.c + 15) / 16 + kGmWaves - 1) / kGmWaves;
   int S = (int)((512 + groups - 1) / groups);
   S = S < 1 ? 1 : (S > kMaxKSplit ? kMaxKSplit : S);
@@ -491,14 +499,7 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   *ksplit = S;
   const int64_t units = groups * S;
   const int grid = (int)(units < 4096 ? units : 4096);
-  switch (NT) {
-    case 1: launch_engine_kc<1, 1, kGmScores>(m, grid, s, e0, e1); break;
-    case 2: launch_engine_kc<2, 1, kGmScores>(m, grid, s, e0, e1); break;
-    case 3: launch_engine_kc<3, 1, kGmScores>(m, grid, s, e0, e1); break;
-    case 4: launch_engine_kc<4, 1, kGmScores>(m, grid, s, e0, e1); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_engine_nt<kGmScores, kKC>(m, grid, s, e0, e1);
 }
 
 int stage2_mfma_grid() { return 4096; }
@@ -507,7 +508,7 @@ hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s, c
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   // flash: the union is known on the device only; launch for every cluster
   const int64_t items = dense ? (a.v + 15) / 16 : (int64_t)a.c * (a.b / 16);
-  int grid = engine_grid(items, a.B);
+  int grid = engine_grid(items);
   grid = grid < stage2_mfma_grid() ? grid : stage2_mfma_grid();
   hipError_t e = dense ? launch_engine<kGmDense>(a, grid, s, e0, e1)
                        : launch_engine<kGmFlash>(a, grid, s, e0, e1);
