@@ -32,7 +32,12 @@ Readings taken where the pages are silent (each listed in the design notes):
   * INT4 stage-1 centroids: symmetric signed 4-bit codes per group of 128
     columns, scale = bf16(amax / 7), codes = round-half-even(C / scale);
   * centroids when computed: bf16 of the unit-normalised mean of the raw
-    cluster rows ([notes] Formula 5).
+    cluster rows ([notes] Formula 5);
+  * equal-size spherical k-means ([notes] Module 1): tokens are placed by
+    cosine in descending order of the (token, cluster) pairs, each into a
+    cluster with room (the unique stable capacity-b assignment); centroids
+    start from the unit rows of caller-drawn distinct token ids and stay in
+    float64 between iterations.
 """
 from __future__ import annotations
 
@@ -424,6 +429,96 @@ def mc_marginal(rows_f64: Callable, c2t, h_f64, p: int, tau: float, seeds,
         lses[i], m1s[i] = lse, m1
         Ss.append(S)
     return MCResult(per_draw.mean(axis=0), per_draw, lses, m1s, Ss)
+
+
+# --------------------------------------------------------------------------
+# equal-size spherical k-means ([notes] Module 1, Formulas 4 and 5)
+# --------------------------------------------------------------------------
+
+
+def unit_rows(X) -> np.ndarray:
+    """Rows scaled to unit L2 norm (a zero row stays zero)."""
+    X = np.asarray(X, dtype=np.float64)
+    n = np.sqrt((X * X).sum(axis=1, keepdims=True))
+    return np.divide(X, n, out=np.zeros_like(X), where=n > 0)
+
+
+def equal_size_assign(S, b: int) -> np.ndarray:
+    """Capacity-b assignment of v tokens to c clusters from the cosine table
+    S (v x c), v = c * b ([notes] Module 1: every cluster holds exactly b
+    tokens; how the pages enforce it is not stated).
+
+    Reading: the (token, cluster) pairs are taken in descending cosine
+    (ties: lower token id, then lower cluster id); a pair is kept when the
+    token is still unplaced and the cluster has room.  With tokens and
+    clusters ranking each other by the same cosine this is the unique
+    stable assignment (no token and cluster that both prefer each other to
+    what they hold).  Returns C2T, c x b, each row ascending."""
+    S = np.asarray(S, dtype=np.float64)
+    v, c = S.shape
+    assert v == c * b
+    ii, kk = np.meshgrid(np.arange(v), np.arange(c), indexing="ij")
+    order = np.lexsort((kk.ravel(), ii.ravel(), -S.ravel()))
+    owner = np.full(v, -1, dtype=np.int64)
+    room = np.full(c, b, dtype=np.int64)
+    left = v
+    for f in order:
+        i, k = divmod(int(f), c)
+        if owner[i] < 0 and room[k] > 0:
+            owner[i] = k
+            room[k] -= 1
+            left -= 1
+            if left == 0:
+                break
+    c2t = np.empty((c, b), dtype=np.int64)
+    for k in range(c):
+        c2t[k] = np.sort(np.nonzero(owner == k)[0])
+    return c2t
+
+
+def unit_cluster_means(rows_f64, c2t) -> np.ndarray:
+    """Formula 5 in float64: the mean of each cluster's raw rows, scaled to
+    unit norm (a zero mean stays zero)."""
+    rows_f64 = np.asarray(rows_f64, dtype=np.float64)
+    return unit_rows(np.stack([rows_f64[t].mean(axis=0) for t in np.asarray(c2t)]))
+
+
+@dataclass
+class KMeansResult:
+    c2t: np.ndarray        # c x b, rows ascending
+    C: np.ndarray          # c x d float64: Formula 5 centroids of c2t
+    iters: int             # assignment steps run
+    objective: float       # sum of the tokens' cosines in the last assignment
+
+
+def kmeans_equal_size(rows_f64, c: int, init, max_iter: int) -> KMeansResult:
+    """Equal-size spherical k-means ([notes] Module 1; Formula 4 objective:
+    the summed cosine of each token to its cluster's unit centroid; Formula 5
+    update), in the pages' order: cosines of the unit rows to the current
+    centroids, the equal-size assignment, then the centroid update.  The
+    initial centroids are the unit rows of the c distinct token ids `init`
+    (drawn by the caller).  Stops after max_iter assignments, or earlier
+    when an assignment repeats the previous one (the centroids are then
+    already its means)."""
+    rows_f64 = np.asarray(rows_f64, dtype=np.float64)
+    v = rows_f64.shape[0]
+    assert v % c == 0 and max_iter >= 1
+    init = np.asarray(init, dtype=np.int64)
+    assert init.shape == (c,) and len(set(init.tolist())) == c
+    assert init.min() >= 0 and init.max() < v
+    b = v // c
+    X = unit_rows(rows_f64)
+    C = X[init]
+    prev = None
+    for it in range(max_iter):
+        S = X @ C.T
+        c2t = equal_size_assign(S, b)
+        obj = float(sum(S[c2t[k], k].sum() for k in range(c)))
+        if prev is not None and np.array_equal(c2t, prev):
+            return KMeansResult(c2t, C, it + 1, obj)
+        C = unit_cluster_means(rows_f64, c2t)
+        prev = c2t
+    return KMeansResult(prev, C, max_iter, obj)
 
 
 # --------------------------------------------------------------------------

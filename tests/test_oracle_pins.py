@@ -585,3 +585,118 @@ def test_generator_tables_and_determinism():
     small = synth.make_head(1, c=32, b=16, d=128, cache=False)
     assert small.E.dtype == np.uint16 and small.E.shape == (512, 128)
     ref.validate(512, 32, 16, small.c2t)
+
+
+# --------------------------------------------------------------------------
+# equal-size spherical k-means ([notes] Module 1, Formulas 4 and 5)
+# --------------------------------------------------------------------------
+
+
+def _balanced_assignments(v, c, b):
+    """Every map of v tokens onto c clusters of exactly b (brute force)."""
+    import itertools
+    out = []
+    for lab in itertools.product(range(c), repeat=v):
+        if all(lab.count(k) == b for k in range(c)):
+            out.append(np.array(lab))
+    return out
+
+
+def _is_stable(S, lab, b):
+    """No token i and cluster k != lab[i] that both rank each other above what
+    they hold: i ranks clusters by (cosine desc, id asc), k ranks tokens by
+    (cosine desc, id asc)."""
+    v, c = S.shape
+    for i in range(v):
+        a = lab[i]
+        for k in range(c):
+            if k == a:
+                continue
+            if not (S[i, k] > S[i, a] or (S[i, k] == S[i, a] and k < a)):
+                continue
+            members = np.nonzero(lab == k)[0]
+            worst = min(members, key=lambda j: (S[j, k], -j))
+            if S[i, k] > S[worst, k] or (S[i, k] == S[worst, k] and i < worst):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed,tied", [(0, False), (1, False), (2, True), (3, True), (4, True)])
+def test_equal_size_assign_is_the_unique_stable_assignment(seed, tied):
+    rng = np.random.default_rng(seed)
+    v, c, b = 6, 3, 2
+    S = rng.integers(-2, 3, size=(v, c)).astype(np.float64) if tied else rng.standard_normal((v, c))
+    stable = [lab for lab in _balanced_assignments(v, c, b) if _is_stable(S, lab, b)]
+    assert len(stable) == 1
+    c2t = ref.equal_size_assign(S, b)
+    lab = np.empty(v, dtype=np.int64)
+    for k in range(c):
+        lab[c2t[k]] = k
+    assert np.array_equal(lab, stable[0])
+    assert all(np.all(np.diff(row) > 0) for row in c2t)
+
+
+def test_equal_size_assign_keeps_each_tokens_best_when_it_fits():
+    # every cluster is the first choice of exactly b tokens: nobody moves
+    rng = np.random.default_rng(5)
+    v, c, b = 40, 8, 5
+    want = rng.permutation(np.repeat(np.arange(c), b))
+    S = rng.uniform(-1, 0.5, size=(v, c))
+    S[np.arange(v), want] = rng.uniform(0.6, 1.0, size=v)
+    c2t = ref.equal_size_assign(S, b)
+    for k in range(c):
+        assert np.array_equal(c2t[k], np.nonzero(want == k)[0])
+
+
+def test_equal_size_assign_full_cluster_sends_the_weakest_on():
+    # all 4 tokens prefer cluster 0 (capacity 2): the two with the larger
+    # cosines (0.9, 0.7) stay, the tied pair at 0.5 both move to cluster 1
+    S = np.array([[0.9, 0.1], [0.5, 0.4], [0.7, -0.3], [0.5, 0.2]])
+    c2t = ref.equal_size_assign(S, 2)
+    assert c2t.tolist() == [[0, 2], [1, 3]]
+    # with room for three the tie at 0.5 goes to the lower token id
+    S3 = np.vstack([S, [0.1, 0.3], [0.0, 0.0]])
+    assert ref.equal_size_assign(S3, 3).tolist() == [[0, 1, 2], [3, 4, 5]]
+
+
+def test_unit_cluster_means_closed_form():
+    rows = np.array([[3.0, 4.0], [0.0, 2.0], [1.0, 0.0], [-1.0, 0.0]])
+    C = ref.unit_cluster_means(rows, np.array([[0, 1], [2, 3]]))
+    np.testing.assert_allclose(C[0], [1 / math.sqrt(5), 2 / math.sqrt(5)], rtol=1e-15)
+    assert np.array_equal(C[1], [0.0, 0.0])  # zero mean stays zero
+
+
+def test_kmeans_recovers_separated_equal_groups():
+    # c orthogonal directions, b tokens near each (random positive scales):
+    # from any one token per group the first assignment is the groups, the
+    # second repeats it, and the centroids are the unit group means
+    rng = np.random.default_rng(6)
+    c, b, d = 8, 6, 32
+    dirs = np.eye(d)[:c]
+    grp = rng.permutation(np.repeat(np.arange(c), b))
+    rows = (dirs[grp] + 0.05 * rng.standard_normal((c * b, d))) * rng.uniform(0.5, 3, (c * b, 1))
+    init = np.array([rng.choice(np.nonzero(grp == k)[0]) for k in rng.permutation(c)])
+    r = ref.kmeans_equal_size(rows, c, init, max_iter=10)
+    assert r.iters == 2
+    for k in range(c):
+        g = grp[init[k]]
+        members = np.nonzero(grp == g)[0]
+        assert np.array_equal(r.c2t[k], members)
+        m = rows[members].mean(axis=0)
+        np.testing.assert_allclose(r.C[k], m / np.linalg.norm(m), rtol=1e-12, atol=1e-15)
+    # Formula 4 objective: the summed cosine of every token to its centroid
+    cos = (rows / np.linalg.norm(rows, axis=1, keepdims=True)) @ r.C.T
+    assert r.objective == pytest.approx(sum(cos[r.c2t[k], k].sum() for k in range(c)), rel=1e-12)
+
+
+def test_kmeans_first_assignment_ignores_row_scale():
+    # the assignment ranks by cosine: scaling token rows by positive factors
+    # leaves the first assignment unchanged (Formula 4 is in cosines)
+    rng = np.random.default_rng(7)
+    rows = rng.standard_normal((96, 16))
+    init = rng.choice(96, 12, replace=False)
+    a = ref.kmeans_equal_size(rows, 12, init, max_iter=1)
+    scaled = rows * rng.uniform(0.1, 10.0, size=(96, 1))
+    b_ = ref.kmeans_equal_size(scaled, 12, init, max_iter=1)
+    assert np.array_equal(a.c2t, b_.c2t)
+    assert a.iters == 1 and sorted(a.c2t.ravel().tolist()) == list(range(96))
