@@ -228,6 +228,42 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype,
                float tau, const uint64_t* seeds, int32_t* out_tokens,
                float* out_lse, void* workspace, void* stream);
 
+/*
+ * Equal-size spherical k-means (notes, Module 1; Formula 4, the summed
+ * cosine of each token to its cluster's unit centroid; Formula 5, the
+ * centroid is the unit-normalised mean of the cluster's rows): the offline
+ * step that builds C2T from E, with every cluster holding exactly b = v / c
+ * tokens.  The pages leave the size constraint's mechanism open; the
+ * assignment here places tokens by cosine, pairs taken in descending order
+ * (ties: lower token id, then lower cluster id), each into a cluster with
+ * room: the unique stable capacity-b assignment.  Each iteration computes
+ * the cosines of the unit rows of E to the centroids, the assignment, then
+ * the Formula 5 update; it stops after max_iter assignments or when an
+ * assignment repeats the previous one.  Cosines and centroids are float64.
+ *   E          device, v x d, row stride lde elements, dtype F32 or BF16,
+ *              aligned to its element size; finite (a zero row has cosine 0
+ *              to every centroid)
+ *   c          clusters, v % c == 0, c <= FH_MAX_C, v / c <= 1024
+ *   init       host, c distinct token ids in [0, v): the initial centroids
+ *              are their unit rows (the caller draws them)
+ *   max_iter   >= 1
+ *   c2t        device out, c x b int32, each row ascending; the result can
+ *              be passed to flashhead_prepare (as fh_desc.c2t, after a copy
+ *              to the host)
+ *   centroids  device out, c x d float64 (Formula 5 of the returned c2t),
+ *              or NULL
+ *   iters_run  host out, assignments computed, or NULL
+ * Blocking: allocates its own device workspace (about 8 * v * (d + c)
+ * bytes), synchronizes `stream` and frees the workspace before returning.
+ * FH_ERR_INVALID_ARG for bad sizes, repeated or out-of-range init ids, and
+ * when a token finds no cluster (only with non-finite input); FH_ERR_OOM
+ * when the workspace does not fit.
+ */
+int flashhead_kmeans(const void* E, int64_t v, int32_t d, int32_t dtype,
+                     int64_t lde, int32_t c, const int32_t* init,
+                     int32_t max_iter, int32_t* c2t, double* centroids,
+                     int32_t* iters_run, void* stream);
+
 /* Static text for a status code. */
 const char* flashhead_status_string(int status);
 

@@ -165,3 +165,39 @@ def test_dense_workspace_size(fh):
         # best keys, counters (16-byte padded) and per-block partials
         assert n >= B * 8 + B * 4 + B * 8 and n % 8 == 0
         assert fh.dense_head_workspace_bytes(B + 1) > n
+
+
+def test_kmeans_host_checks(fh):
+    # every rejection is decided on the host before any device work
+    lib = fh.lib
+    inv, uns = fh.FH_ERR_INVALID_ARG, fh.FH_ERR_UNSUPPORTED
+    good = np.arange(0, 4096, 64, dtype=np.int32)  # 64 distinct ids
+
+    def call(E=FAKE_DEV, v=4096, d=256, dtype=fh.FH_DTYPE_F32, lde=256, c=64, init=good,
+             iters=3, c2t=FAKE_DEV):
+        n = C.c_int32(-1)
+        st = lib.flashhead_kmeans(E, v, d, dtype, lde, c,
+                                  None if init is None else init.ctypes.data, iters, c2t, None,
+                                  C.byref(n), None)
+        assert n.value == 0
+        return st
+
+    assert call(E=None) == inv
+    assert call(c2t=None) == inv
+    assert call(init=None) == inv
+    assert call(v=4000) == inv            # v % c != 0
+    assert call(iters=0) == inv
+    assert call(lde=200) == inv
+    assert call(d=0) == inv
+    dup = good.copy()
+    dup[5] = dup[4]
+    assert call(init=dup) == inv
+    out = good.copy()
+    out[0] = 4096
+    assert call(init=out) == inv
+    neg = good.copy()
+    neg[1] = -1
+    assert call(init=neg) == inv
+    assert call(dtype=9) == uns
+    assert call(E=FAKE_DEV + 2) == uns    # not aligned to its fp32 elements
+    assert call(c=2, init=good[:2]) == uns  # 2048 tokens per cluster

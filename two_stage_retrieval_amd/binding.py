@@ -36,7 +36,7 @@ EXPORTED = [
     "flashhead_status_string", "flashhead_export_centroids",
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
     "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
-    "flashhead_mc_workspace_bytes", "flashhead_mc_marginal",
+    "flashhead_mc_workspace_bytes", "flashhead_mc_marginal", "flashhead_kmeans",
 ]
 
 
@@ -106,6 +106,9 @@ def _load() -> C.CDLL:
     lib.flashhead_mc_marginal.argtypes = [vp, vp, i32, f32, vp, i32, vp, i32,
                                           vp, vp, vp, C.c_size_t, vp]
     lib.flashhead_mc_marginal.restype = C.c_int
+    lib.flashhead_kmeans.argtypes = [vp, i64, i32, i32, i64, i32, vp, i32, vp, vp,
+                                     C.POINTER(i32), vp]
+    lib.flashhead_kmeans.restype = C.c_int
     return lib
 
 
@@ -242,6 +245,22 @@ def dense_head(E, H, B: int, mode: int, tau: float, seeds, out_tokens,
     _check(lib.dense_head(_ptr(E), v, d, dtype_code(E), lde, _ptr(H), B, mode,
                           tau, _ptr(seeds), _ptr(out_tokens), _ptr(out_lse),
                           _ptr(workspace), _stream(stream)), "dense_head")
+
+
+def flashhead_kmeans(E, c: int, init, max_iter: int, out_c2t, out_centroids=None, *,
+                     v=None, d=None, lde=None, stream=None) -> int:
+    """Equal-size spherical k-means of E's rows into c clusters (blocking).
+    `init` is a host int32 array of c distinct token ids; `out_c2t` a device
+    int32 tensor of c x (v / c); returns the assignments computed."""
+    v = v if v is not None else E.shape[0]
+    d = d if d is not None else E.shape[1]
+    lde = lde if lde is not None else E.stride(0)
+    init = np.ascontiguousarray(init, dtype=np.int32)
+    iters = C.c_int32(0)
+    _check(lib.flashhead_kmeans(_ptr(E), v, d, dtype_code(E), lde, c, init.ctypes.data,
+                                max_iter, _ptr(out_c2t), _ptr(out_centroids),
+                                C.byref(iters), _stream(stream)), "flashhead_kmeans")
+    return int(iters.value)
 
 
 def flashhead_export_centroids(handle: int, out: np.ndarray) -> np.ndarray:

@@ -17,7 +17,8 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflashhead.so")
 
 SOURCES = ["fh_api.hip", "fh_stage1.hip", "fh_rowdot.hip", "fh_select.hip",
-           "fh_prepare.hip", "fh_batched.hip", "fh_mc.hip"]
+           "fh_prepare.hip", "fh_batched.hip", "fh_mc.hip",
+           "fh_kmeans.hip"]
 
 # Packed-fp32 instructions are disabled for all device code.
 HIPCC_FLAGS = [

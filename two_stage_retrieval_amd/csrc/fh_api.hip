@@ -735,6 +735,38 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   return FH_OK;
 }
 
+int flashhead_kmeans(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, int32_t c,
+                     const int32_t* init, int32_t max_iter, int32_t* c2t, double* centroids,
+                     int32_t* iters_run, void* stream) {
+  if (iters_run) *iters_run = 0;
+  if (!E || !init || !c2t) return FH_ERR_INVALID_ARG;
+  if (v < 1 || c < 1 || d < 1 || lde < d || max_iter < 1 || v % c) return FH_ERR_INVALID_ARG;
+  const int es = esize_of(dtype);
+  if (!es) return FH_ERR_UNSUPPORTED;
+  if (v > (int64_t)INT32_MAX || c > FH_MAX_C || v / c > kMaxKmB) return FH_ERR_UNSUPPORTED;
+  if ((uintptr_t)E % es) return FH_ERR_UNSUPPORTED;
+  std::vector<char> seen((size_t)v, 0);
+  for (int32_t k = 0; k < c; ++k) {
+    if (init[k] < 0 || init[k] >= v || seen[init[k]]) return FH_ERR_INVALID_ARG;
+    seen[init[k]] = 1;
+  }
+  KMeansArgs a{};
+  a.E = static_cast<const uint8_t*>(E);
+  a.lde_bytes = lde * es;
+  a.dtype = dtype;
+  a.v = v;
+  a.d = d;
+  a.c = c;
+  a.init_host = init;
+  a.max_iter = max_iter;
+  a.c2t = c2t;
+  a.centroids = centroids;
+  int iters = 0, status = 0;
+  FH_TRY(run_kmeans(a, static_cast<hipStream_t>(stream), &iters, &status));
+  if (iters_run) *iters_run = iters;
+  return status ? FH_ERR_INVALID_ARG : FH_OK;
+}
+
 int flashhead_export_centroids(const fh_handle* h, void* dst) {
   if (!h || !dst) return FH_ERR_INVALID_ARG;
   FH_TRY(hipMemcpy(dst, h->C, (size_t)h->c * h->row_bytes, hipMemcpyDeviceToHost));

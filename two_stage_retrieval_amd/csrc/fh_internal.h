@@ -223,6 +223,24 @@ hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s,
                               const Timing* tm = nullptr);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int num_cu,
                               hipStream_t s);
+// Equal-size spherical k-means (fh_kmeans.hip).  E device, init host
+// (c distinct ids), c2t device out (c x b, rows ascending), centroids device
+// out (c x d float64) or null.  Blocking: allocates its own workspace and
+// synchronizes s.  *status = 1 when a token found no cluster (only with
+// non-finite input).
+constexpr int kMaxKmB = 1024;  // tokens per cluster
+struct KMeansArgs {
+  const uint8_t* E;
+  int64_t lde_bytes;
+  int dtype;
+  int64_t v;
+  int d, c;
+  const int32_t* init_host;
+  int max_iter;
+  int32_t* c2t;
+  double* centroids;
+};
+hipError_t run_kmeans(const KMeansArgs& a, hipStream_t s, int* iters, int* status);
 hipError_t launch_cluster_major_copy(const uint8_t* E, int64_t lde_bytes, const int32_t* c2t,
                                      int64_t v, int64_t row_bytes, uint8_t* Ec, hipStream_t s);
 
