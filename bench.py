@@ -110,6 +110,10 @@ def main():
                     help="time the Monte Carlo marginal (Formula 7) with N draws "
                          "instead of the decode step; prints its own JSON line")
     ap.add_argument("--mc-tokens", type=int, default=16)
+    ap.add_argument("--kmeans", type=int, default=0, metavar="N",
+                    help="time N iterations of the equal-size spherical k-means "
+                         "(Module 1) on the workload's E instead of the decode step; "
+                         "prints its own JSON line")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run --steps cold calls and a 256 MiB copy-like kernel, then exit "
                          "(for rocprofv3 --pmc runs)")
@@ -139,6 +143,10 @@ def main():
     tau = args.tau if sample else 1.0
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.kmeans:
+        kmeans_bench(args, wl, dev)
+        return
 
     t0 = time.time()
     head = synth.make_head(wl)
@@ -428,6 +436,61 @@ def mc_bench(args, wl, head, H, H_dev, fh, evict, int4):
            "config": {"workload": f"{wl.name} mc N={N} Q={Q}", "p": wl.p, "tau": tau,
                       "timing": "cold (1 GiB read-only flush before each call)"},
            "us_per_draw": round(us / N, 4), "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
+def kmeans_bench(args, wl, dev):
+    """Module 1: equal-size spherical k-means of the workload's E into its c
+    clusters, N assignment + update iterations from c drawn token ids.  The
+    call is blocking (its rounds synchronise with the host), so it is timed
+    with the host clock.  The oracle is timed for one iteration on a smaller
+    head of the same generator and scaled by the (token, cluster) pairs,
+    which its cosine product and pair ordering grow with."""
+    import torch
+
+    from two_stage_retrieval_amd import binding as fhb
+    from two_stage_retrieval_amd import synth
+    N = args.kmeans
+    t0 = time.time()
+    head = synth.make_head(wl)
+    E = head.E
+    if E.dtype == np.uint16:
+        E_dev = torch.from_numpy(E.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        E_dev = torch.from_numpy(E).to(dev)
+    init = np.random.default_rng(41).choice(wl.v, size=wl.c, replace=False).astype(np.int32)
+    c2t = torch.empty((wl.c, wl.b), dtype=torch.int32, device=dev)
+    log(f"[bench] kmeans input {wl.name} in {time.time() - t0:.1f}s")
+    fhb.flashhead_kmeans(E_dev, wl.c, init, 1, c2t)  # warm-up (code, allocator)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    iters = fhb.flashhead_kmeans(E_dev, wl.c, init, N, c2t)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3
+    log(f"[bench] kmeans: {iters} iterations in {ms:.1f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import flashhead_ref as ref
+        cs, bs = 512, wl.b
+        small = synth.make_head(wl, c=cs, b=bs)
+        rows = ref.as_f64(small.E, wl.dtype)
+        init_s = np.random.default_rng(41).choice(cs * bs, size=cs, replace=False)
+        t = time.perf_counter()
+        ref.kmeans_equal_size(rows, cs, init_s, 1)
+        sec = time.perf_counter() - t
+        scale = (wl.v * wl.c) / (cs * bs * cs)
+        cpu = {"value": round(sec * 1e3 * scale, 1), "unit": "ms/iteration", "cores": None,
+               "kind": "oracle",
+               "sample": f"one iteration at v={cs * bs}, c={cs}, d={wl.d} ({sec:.2f} s, "
+                         f"float64 numpy oracle) scaled by the pair count v*c ({scale:.0f}x)"}
+        log(f"[bench] oracle: {sec:.2f} s for one iteration at v={cs * bs}, c={cs}")
+    res = {"metric": "equal-size spherical k-means ms/iteration (cosines, assignment, update)",
+           "value": round(ms / iters, 3), "unit": "ms/iteration", "n_gpus": 1,
+           "steps": iters, "warmup": 1, "higher_is_better": False, "dtype": "f64",
+           "data": "synthetic (seeded generator, pages' head shapes)",
+           "config": {"workload": f"{wl.name} kmeans v={wl.v} d={wl.d} c={wl.c} b={wl.b}",
+                      "iterations": iters, "timing": "host clock around the blocking call"},
+           "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
 

@@ -10,12 +10,13 @@
 // ranking each other by the same cosine that is the unique stable
 // assignment, which deferred acceptance reaches in parallel rounds:
 //   propose  every unplaced token proposes to its best cluster below the
-//            last one it proposed to (one wave scans the token's row of
-//            cosines);
-//   bucket   proposals are counted per cluster, offsets scanned, and the
-//            token ids scattered into per-cluster runs;
-//   accept   one workgroup per cluster ranks what it holds together with
-//            its new proposals by (cosine desc, token id asc), keeps the
+//            last one it proposed to (one workgroup scans the token's row of
+//            cosines) and takes a slot of that cluster's proposal block; a
+//            token that finds the block full proposes again next round
+//            (deferred acceptance ends in the same assignment whatever the
+//            order of the proposals);
+//   accept   one workgroup per cluster with proposals ranks what it holds
+//            together with them by (cosine desc, token id asc), keeps the
 //            first b and sends the rest back to the unplaced list.
 // The rounds end when every token is placed (a token can always place:
 // total room equals v).  Cosines, centroids and their sums are float64, so
@@ -95,24 +96,30 @@ __global__ __launch_bounds__(kKmThreads) void gather_rows_kernel(const double* X
   for (int j = threadIdx.x; j < d; j += kKmThreads) C[(int64_t)k * d + j] = src[j];
 }
 
-// S (v x c) = X (v x d) C^T (C c x d), float64.  64 x 64 output tile per
-// workgroup, 4 x 4 per thread, K staged through LDS 16 at a time; each
+// S (v x c) = X (v x d) C^T (C c x d), float64 on the vector units.  A
+// 128 x 128 output tile per workgroup, 8 x 8 outputs per thread at rows
+// ty + 16 p and columns tx + 16 q (so a wave's LDS reads are 4 broadcast
+// rows and 16 consecutive columns), K staged through LDS 8 at a time; each
 // output is a sum over j ascending.
-constexpr int kSimTile = 64, kSimK = 16;
+constexpr int kSimTile = 128, kSimK = 8;
 __global__ __launch_bounds__(kKmThreads) void cosine_kernel(const double* X, const double* C,
                                                             int64_t v, int c, int d, double* S) {
-  __shared__ double sa[kSimK][kSimTile + 1];
-  __shared__ double sb[kSimK][kSimTile + 1];
+  __shared__ double sa[kSimK][kSimTile];
+  __shared__ double sb[kSimK][kSimTile];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t i0 = (int64_t)blockIdx.y * kSimTile;
   const int k0 = blockIdx.x * kSimTile;
-  double acc[4][4] = {};
+  double acc[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[p][q] = 0.0;
   for (int j0 = 0; j0 < d; j0 += kSimK) {
-    // 64 rows x 16 columns of each operand: 4 elements per thread
+    // 128 rows x 8 columns of each operand: 4 elements per thread
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = threadIdx.x + q * kKmThreads;  // [0, 1024)
-      const int r = e >> 4, jj = e & 15;
+      const int r = e >> 3, jj = e & 7;
       const int64_t gi = i0 + r;
       const int gk = k0 + r;
       const int gj = j0 + jj;
@@ -122,48 +129,53 @@ __global__ __launch_bounds__(kKmThreads) void cosine_kernel(const double* X, con
     __syncthreads();
 #pragma unroll
     for (int jj = 0; jj < kSimK; ++jj) {
-      double a[4], b[4];
+      double a[8], b[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[q] = sa[jj][ty * 4 + q];
-        b[q] = sb[jj][tx * 4 + q];
+      for (int q = 0; q < 8; ++q) {
+        a[q] = sa[jj][ty + 16 * q];
+        b[q] = sb[jj][tx + 16 * q];
       }
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+      for (int p = 0; p < 8; ++p)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
+        for (int q = 0; q < 8; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int64_t gi = i0 + ty * 4 + p;
+  for (int p = 0; p < 8; ++p) {
+    const int64_t gi = i0 + ty + 16 * p;
     if (gi >= v) continue;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int gk = k0 + tx * 4 + q;
+    for (int q = 0; q < 8; ++q) {
+      const int gk = k0 + tx + 16 * q;
       if (gk < c) S[gi * c + gk] = acc[p][q];
     }
   }
 }
 
+constexpr int kKmQ = 256;  // proposal slots per cluster and round
+// counters (int32): unplaced after the round and clusters with proposals,
+// each by round parity; the no-candidate and table-changed flags
+constexpr int kCtrFree = 0, kCtrAct = 2, kCtrBad = 4, kCtrChanged = 5, kCtrWords = 8;
+
 struct Round {
   const double* S;
   int64_t v;
   int c, b;
+  int par;                // round parity: which counter pair this round uses
   const int32_t* freel;   // unplaced tokens of this round
   int32_t nfree;
   int32_t* last;          // per token: the cluster of its last proposal (-1: none)
-  int32_t* cnt;           // per cluster: proposals this round
-  int32_t* off;           // per cluster: start of its run in bucket (c + 1)
-  int32_t* fill;          // per cluster: scatter cursor
-  int32_t* bucket;        // proposals grouped by cluster
-  double* bucket_s;       // and their cosines
+  int32_t* pcnt;          // per cluster: proposals this round (may exceed kKmQ)
+  int32_t* prop;          // c x kKmQ proposal slots
+  double* prop_s;         // and their cosines
+  int32_t* act;           // clusters with proposals this round
   int32_t* holds;         // c x b: the tokens a cluster holds
   double* holds_s;        // and their cosines
   int32_t* hn;            // per cluster: how many it holds
-  int32_t* freel_next;    // tokens sent back this round
-  int32_t* counters;      // [0] unplaced after this round, [1] no-candidate flag
+  int32_t* freel_next;    // unplaced tokens for the next round
+  int32_t* counters;
 };
 
 // does (s1, id1) rank before (s2, id2): larger cosine, then lower id
@@ -171,120 +183,123 @@ __device__ __forceinline__ bool before(double s1, int id1, double s2, int id2) {
   return s1 > s2 || (s1 == s2 && id1 < id2);
 }
 
-// one wave per unplaced token: the best cluster after its last proposal in
-// its own order (cosine desc, cluster id asc)
+// one workgroup per unplaced token: the best cluster after its last
+// proposal in the token's own order (cosine desc, cluster id asc).  A whole
+// workgroup scans the row so that the late rounds, with few tokens left,
+// are not one wave's chain of loads.
+__device__ __forceinline__ void better_pair(double& bs, int& bk, double os, int ok) {
+  if (ok >= 0 && (bk < 0 || before(os, ok, bs, bk))) { bs = os; bk = ok; }
+}
+
 __global__ __launch_bounds__(kKmThreads) void propose_kernel(Round r) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kKmWaves + (threadIdx.x >> 6);
-  if (t >= r.nfree) return;  // wave-uniform
-  const int32_t i = r.freel[t];
+  __shared__ double w_s[kKmWaves];
+  __shared__ int w_k[kKmWaves];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int32_t i = r.freel[blockIdx.x];  // grid = unplaced tokens
   const double* row = r.S + (int64_t)i * r.c;
   const int lk = r.last[i];
   const double ls = lk >= 0 ? row[lk] : 0.0;
   double bs = 0.0;
   int bk = -1;
-  for (int k = lane; k < r.c; k += kWave) {
-    const double s = row[k];
-    const bool after = lk < 0 || s < ls || (s == ls && k > lk);
-    if (after && (bk < 0 || before(s, k, bs, bk))) { bs = s; bk = k; }
+  // 8 loads in flight per thread, then their comparisons
+  for (int k0 = threadIdx.x; k0 < r.c; k0 += 8 * kKmThreads) {
+    double vals[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int k = k0 + q * kKmThreads;
+      vals[q] = k < r.c ? row[k] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int k = k0 + q * kKmThreads;
+      const double sv = vals[q];
+      const bool after = lk < 0 || sv < ls || (sv == ls && k > lk);
+      if (k < r.c && after) better_pair(bs, bk, sv, k);
+    }
   }
 #pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const double os = __shfl_xor(bs, o, kWave);
-    const int ok = __shfl_xor(bk, o, kWave);
-    if (ok >= 0 && (bk < 0 || before(os, ok, bs, bk))) { bs = os; bk = ok; }
-  }
+  for (int o = kWave / 2; o > 0; o >>= 1)
+    better_pair(bs, bk, __shfl_xor(bs, o, kWave), __shfl_xor(bk, o, kWave));
   if (lane == 0) {
+    w_s[wave] = bs;
+    w_k[wave] = bk;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kKmWaves; ++w) better_pair(bs, bk, w_s[w], w_k[w]);
     if (bk < 0) {
-      r.counters[1] = 1;  // only with non-finite cosines
+      r.counters[kCtrBad] = 1;  // only with non-finite cosines
       r.last[i] = -2;
       return;
     }
-    r.last[i] = bk;
-    atomicAdd(&r.cnt[bk], 1);
+    const int slot = atomicAdd(&r.pcnt[bk], 1);
+    if (slot < kKmQ) {
+      r.prop[(int64_t)bk * kKmQ + slot] = i;
+      r.prop_s[(int64_t)bk * kKmQ + slot] = bs;
+      r.last[i] = bk;
+      if (slot == 0) r.act[atomicAdd(&r.counters[kCtrAct + r.par], 1)] = bk;
+    } else {
+      // the block is full: propose again next round (last is unchanged)
+      r.freel_next[atomicAdd(&r.counters[kCtrFree + r.par], 1)] = i;
+    }
   }
 }
 
-// exclusive scan of the per-cluster counts (one 1024-thread workgroup);
-// clears the scatter cursors
-__global__ __launch_bounds__(1024) void offsets_kernel(Round r) {
-  __shared__ int part[1024];
-  const int t = threadIdx.x;
-  const int per = (r.c + 1023) / 1024;
-  const int b0 = t * per;
-  int s = 0;
-  for (int k = b0; k < b0 + per && k < r.c; ++k) s += r.cnt[k];
-  part[t] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-    const int x = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
-  }
-  int run = part[t] - s;
-  for (int k = b0; k < b0 + per && k < r.c; ++k) {
-    r.off[k] = run;
-    run += r.cnt[k];
-    r.fill[k] = 0;
-  }
-  if (t == 1023) r.off[r.c] = part[1023];
-}
-
-__global__ __launch_bounds__(kKmThreads) void scatter_kernel(Round r) {
-  const int t = blockIdx.x * kKmThreads + threadIdx.x;
-  if (t >= r.nfree) return;
-  const int32_t i = r.freel[t];
-  const int k = r.last[i];
-  if (k < 0) return;
-  const int pos = r.off[k] + atomicAdd(&r.fill[k], 1);
-  r.bucket[pos] = i;
-  r.bucket_s[pos] = r.S[(int64_t)i * r.c + k];
-}
-
-// one workgroup per cluster with proposals: rank held + proposed tokens,
-// keep the first b (written in rank order), send back the rest
+// the clusters with proposals, grid-strided over the workgroups: rank
+// held + proposed tokens, keep the first b (written in rank order), send
+// back the rest
 __global__ __launch_bounds__(kKmThreads) void accept_kernel(Round r) {
   __shared__ int32_t sh_id[kMaxKmB];
   __shared__ double sh_s[kMaxKmB];
-  const int k = blockIdx.x;
-  const int np = r.cnt[k];
-  if (np == 0) return;
-  const int h = r.hn[k];
-  const int m = h + np;
+  const int nact = r.counters[kCtrAct + r.par];
   const int b = r.b;
-  __syncthreads();  // every wave has read hn[k] before thread 0 rewrites it
-  int32_t* hold = r.holds + (int64_t)k * b;
-  double* hold_s = r.holds_s + (int64_t)k * b;
-  const int32_t* pid = r.bucket + r.off[k];
-  const double* ps = r.bucket_s + r.off[k];
-  if (m <= b) {
-    for (int j = threadIdx.x; j < np; j += kKmThreads) {
-      hold[h + j] = pid[j];
-      hold_s[h + j] = ps[j];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    // the next round's counters (the previous round's, already read)
+    r.counters[kCtrFree + (r.par ^ 1)] = 0;
+    r.counters[kCtrAct + (r.par ^ 1)] = 0;
+  }
+  for (int a = blockIdx.x; a < nact; a += gridDim.x) {
+    const int k = r.act[a];
+    const int pc = r.pcnt[k];
+    const int np = pc < kKmQ ? pc : kKmQ;
+    const int h = r.hn[k];
+    const int m = h + np;
+    // every wave has read pcnt[k] and hn[k] before they are rewritten, and
+    // is done with the previous cluster's LDS copy
+    __syncthreads();
+    if (threadIdx.x == 0) r.pcnt[k] = 0;  // zero for the next round
+    int32_t* hold = r.holds + (int64_t)k * b;
+    double* hold_s = r.holds_s + (int64_t)k * b;
+    const int32_t* pid = r.prop + (int64_t)k * kKmQ;
+    const double* ps = r.prop_s + (int64_t)k * kKmQ;
+    if (m <= b) {
+      for (int j = threadIdx.x; j < np; j += kKmThreads) {
+        hold[h + j] = pid[j];
+        hold_s[h + j] = ps[j];
+      }
+      if (threadIdx.x == 0) r.hn[k] = m;
+      continue;
     }
-    if (threadIdx.x == 0) r.hn[k] = m;
-    return;
-  }
-  for (int j = threadIdx.x; j < h; j += kKmThreads) {
-    sh_id[j] = hold[j];
-    sh_s[j] = hold_s[j];
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < m; j += kKmThreads) {
-    const int32_t id = j < h ? sh_id[j] : pid[j - h];
-    const double s = j < h ? sh_s[j] : ps[j - h];
-    int rank = 0;
-    for (int l = 0; l < h; ++l) rank += before(sh_s[l], sh_id[l], s, id);
-    for (int l = 0; l < np; ++l) rank += before(ps[l], pid[l], s, id);
-    if (rank < b) {
-      hold[rank] = id;
-      hold_s[rank] = s;
-    } else {
-      r.freel_next[atomicAdd(&r.counters[0], 1)] = id;
+    for (int j = threadIdx.x; j < h; j += kKmThreads) {
+      sh_id[j] = hold[j];
+      sh_s[j] = hold_s[j];
     }
+    __syncthreads();
+    for (int j = threadIdx.x; j < m; j += kKmThreads) {
+      const int32_t id = j < h ? sh_id[j] : pid[j - h];
+      const double sj = j < h ? sh_s[j] : ps[j - h];
+      int rank = 0;
+      for (int l = 0; l < h; ++l) rank += before(sh_s[l], sh_id[l], sj, id);
+      for (int l = 0; l < np; ++l) rank += before(ps[l], pid[l], sj, id);
+      if (rank < b) {
+        hold[rank] = id;
+        hold_s[rank] = sj;
+      } else {
+        r.freel_next[atomicAdd(&r.counters[kCtrFree + r.par], 1)] = id;
+      }
+    }
+    if (threadIdx.x == 0) r.hn[k] = b;
   }
-  if (threadIdx.x == 0) r.hn[k] = b;
 }
 
 // each cluster's tokens ascending into c2t; flags a change from prev
@@ -361,27 +376,26 @@ hipError_t run_kmeans(const KMeansArgs& a, hipStream_t s, int* iters, int* statu
   const int64_t v = a.v;
   const int c = a.c, d = a.d, b = (int)(v / c);
   Buffers buf;
-  double *X, *C, *S, *bucket_s, *holds_s;
-  int32_t *init, *fa, *fb, *last, *cnt, *off, *fill, *bucket, *holds, *hn, *prev, *ctr;
+  double *X, *C, *S, *prop_s, *holds_s;
+  int32_t *init, *fa, *fb, *last, *pcnt, *prop, *holds, *hn, *prev, *ctr, *act;
   KM_TRY(buf.get(&X, (size_t)v * d));
   KM_TRY(buf.get(&C, (size_t)c * d));
   KM_TRY(buf.get(&S, (size_t)v * c));
-  KM_TRY(buf.get(&bucket_s, (size_t)v));
+  KM_TRY(buf.get(&prop_s, (size_t)c * kKmQ));
   KM_TRY(buf.get(&holds_s, (size_t)v));
   KM_TRY(buf.get(&init, (size_t)c));
   KM_TRY(buf.get(&fa, (size_t)v));
   KM_TRY(buf.get(&fb, (size_t)v));
   KM_TRY(buf.get(&last, (size_t)v));
-  KM_TRY(buf.get(&cnt, (size_t)c));
-  KM_TRY(buf.get(&off, (size_t)c + 1));
-  KM_TRY(buf.get(&fill, (size_t)c));
-  KM_TRY(buf.get(&bucket, (size_t)v));
+  KM_TRY(buf.get(&pcnt, (size_t)c));
+  KM_TRY(buf.get(&prop, (size_t)c * kKmQ));
   KM_TRY(buf.get(&holds, (size_t)v));
   KM_TRY(buf.get(&hn, (size_t)c));
   KM_TRY(buf.get(&prev, (size_t)v));
-  KM_TRY(buf.get(&ctr, 4));
+  KM_TRY(buf.get(&ctr, kCtrWords));
+  KM_TRY(buf.get(&act, (size_t)c));
   int32_t* host_ctr = nullptr;
-  KM_TRY(hipHostMalloc((void**)&host_ctr, 4 * sizeof(int32_t), 0));
+  KM_TRY(hipHostMalloc((void**)&host_ctr, kCtrWords * sizeof(int32_t), 0));
   struct HostFree {
     int32_t* p;
     ~HostFree() { (void)hipHostFree(p); }
@@ -403,62 +417,60 @@ hipError_t run_kmeans(const KMeansArgs& a, hipStream_t s, int* iters, int* statu
     hipLaunchKernelGGL(cosine_kernel, gsim, dim3(kKmThreads), 0, s, X, C, v, c, d, S);
     KM_TRY(hipMemsetAsync(hn, 0, (size_t)c * 4, s));
     KM_TRY(hipMemsetAsync(last, 0xFF, (size_t)v * 4, s));  // -1: no proposal yet
-    KM_TRY(hipMemsetAsync(ctr, 0, 4 * 4, s));
+    KM_TRY(hipMemsetAsync(ctr, 0, kCtrWords * 4, s));
+    KM_TRY(hipMemsetAsync(pcnt, 0, (size_t)c * 4, s));  // accept re-zeroes what it used
     hipLaunchKernelGGL(iota_kernel, dim3(blocks_for(v, 256)), dim3(256), 0, s, fa, v);
     KM_TRY(hipGetLastError());
     int32_t nfree = (int32_t)v;
     int64_t rounds = 0;
     while (nfree > 0) {
+      const int par = (int)(rounds & 1);
       Round r{};
       r.S = S;
       r.v = v;
       r.c = c;
       r.b = b;
+      r.par = par;
       r.freel = fa;
       r.nfree = nfree;
       r.last = last;
-      r.cnt = cnt;
-      r.off = off;
-      r.fill = fill;
-      r.bucket = bucket;
-      r.bucket_s = bucket_s;
+      r.pcnt = pcnt;
+      r.prop = prop;
+      r.prop_s = prop_s;
+      r.act = act;
       r.holds = holds;
       r.holds_s = holds_s;
       r.hn = hn;
       r.freel_next = fb;
       r.counters = ctr;
-      KM_TRY(hipMemsetAsync(cnt, 0, (size_t)c * 4, s));
-      KM_TRY(hipMemsetAsync(ctr, 0, 4, s));  // unplaced count of this round
-      hipLaunchKernelGGL(propose_kernel, dim3(blocks_for(nfree, kKmWaves)), dim3(kKmThreads), 0, s, r);
-      hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, s, r);
-      hipLaunchKernelGGL(scatter_kernel, dim3(blocks_for(nfree, kKmThreads)), dim3(kKmThreads), 0, s, r);
-      hipLaunchKernelGGL(accept_kernel, dim3(c), dim3(kKmThreads), 0, s, r);
+      hipLaunchKernelGGL(propose_kernel, dim3(nfree), dim3(kKmThreads), 0, s, r);
+      // at most one cluster with proposals per proposal
+      hipLaunchKernelGGL(accept_kernel, dim3(nfree < c ? nfree : c), dim3(kKmThreads), 0, s, r);
       KM_TRY(hipGetLastError());
-      KM_TRY(hipMemcpyAsync(host_ctr, ctr, 2 * 4, hipMemcpyDeviceToHost, s));
+      KM_TRY(hipMemcpyAsync(host_ctr, ctr, kCtrWords * 4, hipMemcpyDeviceToHost, s));
       KM_TRY(hipStreamSynchronize(s));
-      if (host_ctr[1]) {
+      if (host_ctr[kCtrBad]) {
         *status = 1;  // a token found no cluster: non-finite cosines
         return hipSuccess;
       }
-      nfree = host_ctr[0];
+      nfree = host_ctr[kCtrFree + par];
       int32_t* t = fa;
       fa = fb;
       fb = t;
-      // every round places or re-places at least one proposal; a token
-      // proposes to each cluster at most once
+      // every round keeps at least one proposal (a full block keeps its
+      // first kKmQ), and a token proposes to each cluster at most once
       if (++rounds > v * (int64_t)c) {
         *status = 1;
         return hipSuccess;
       }
     }
-    KM_TRY(hipMemsetAsync(ctr + 2, 0, 4, s));
     hipLaunchKernelGGL(table_kernel, dim3(c), dim3(kKmThreads), 0, s, holds, b, a.c2t,
-                       it > 0 ? prev : nullptr, ctr + 2);
+                       it > 0 ? prev : nullptr, ctr + kCtrChanged);
     KM_TRY(hipGetLastError());
-    KM_TRY(hipMemcpyAsync(host_ctr + 2, ctr + 2, 4, hipMemcpyDeviceToHost, s));
+    KM_TRY(hipMemcpyAsync(host_ctr, ctr, kCtrWords * 4, hipMemcpyDeviceToHost, s));
     KM_TRY(hipStreamSynchronize(s));
     *iters = it + 1;
-    if (it > 0 && host_ctr[2] == 0) break;  // the centroids are already its means
+    if (it > 0 && host_ctr[kCtrChanged] == 0) break;  // the centroids are already its means
     if (a.dtype == FH_DTYPE_BF16)
       hipLaunchKernelGGL(centroid_kernel<bf16_t>, dim3(c), dim3(kKmThreads), 0, s, a.E,
                          a.lde_bytes, a.c2t, b, d, C);
