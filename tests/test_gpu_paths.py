@@ -30,6 +30,25 @@ def seeds_dev(seeds):
     return torch.from_numpy(seeds.view(np.int64)).cuda()
 
 
+def test_batched_list_and_all_cluster_walks_alternate(fh):
+    # below 16 rows stage 2 walks the union list, from 16 rows on every
+    # cluster; one handle alternating between the two must find the row
+    # masks cleared by whichever ran before (greedy and sampling)
+    cs = case(1, c=400, b=16, d=256, seed=56)
+    head = cs.prepare(fh, max_batch=24, max_p=40)
+    H, H64 = cs.hidden(24, offset=7)
+    st = Stats()
+    for step, B in enumerate((24, 3, 24, 5, 16, 2)):
+        res = run_debug(fh, head, dev_tensor(H[:B]), B, 40, "greedy")
+        assert path_of(fh, head) == PATH_BATCHED
+        check_batch(cs, res, H64[:B], 40, stats=st)
+        seeds = synth.make_seeds(step, B)
+        res = run_debug(fh, head, dev_tensor(H[:B]), B, 40, "sample", 0.8, seeds_dev(seeds))
+        check_batch(cs, res, H64[:B], 40, "sample", 0.8, seeds, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
 @pytest.mark.parametrize("B", [3, 17, 33, 50])
 def test_batched_path_ragged_batches(fh, B):
     # 16-row MFMA tiles over B columns: 1, 2, 3 and 4 column tiles, each

@@ -404,7 +404,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.inv_tau = inv_tau;
     a.seeds = seeds;
     a.dbg_scores = ksplit > 1 && dbg ? dbg->scores : nullptr;
-    if (batched) {
+    if (batched && B < kUnionMinRows) {
       a.ulist = h->ulist;
       a.ucount = h->ucount;
     }
@@ -430,8 +430,11 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.p = p;
     a.H = static_cast<const uint8_t*>(H);
     a.h_bytes = h->row_bytes;
-    a.ulist = h->ulist;
-    a.ucount = h->ucount;
+    // small batches select few clusters in all: stage 2 walks their list;
+    // from kUnionMinRows rows on, the union covers most clusters and
+    // stage 2 walks all of them, skipping the ones no row selected
+    a.ulist = B < kUnionMinRows ? h->ulist : nullptr;
+    a.ucount = B < kUnionMinRows ? h->ucount : nullptr;
     a.masks = h->masks;
     a.c2t = h->c2t;
     a.sel = h->sel;

@@ -121,7 +121,9 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 //   SCORES  stage-1 keys: item rows are centroids; key = score (or score /
 //           tau + Gumbel noise) for every (batch row, centroid);
 //   FLASH   stage 2: item rows are the candidate rows of a selected cluster
-//           (cluster ulist[i / (b/16)] of the cluster-major copy of E); per
+//           (cluster ulist[i / (b/16)] of the cluster-major copy of E, or
+//           cluster i / (b/16) when there is no list, unselected ones
+//           skipped); per
 //           batch row, candidates of clusters the row selected (its bit in
 //           the cluster's mask) are folded into a running best decode key
 //           and log-sum-exp;
@@ -150,7 +152,11 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int B = a.B;
   const int sub = a.b / 16;
   const int64_t nrows_total = MODE == kGmScores ? (int64_t)a.c : a.v;
-  const int64_t nitems = MODE == kGmFlash ? (int64_t)(*a.ucount) * sub : (nrows_total + 15) / 16;
+  // FLASH walks the union list when there is one, else every cluster
+  // (skipping the ones no row selected)
+  const int64_t nitems = MODE == kGmFlash
+                             ? (a.ulist ? (int64_t)(*a.ucount) : (int64_t)a.c) * sub
+                             : (nrows_total + 15) / 16;
   const int nchunks = a.d / KC;
   uint64_t best[NT];
   Lse lse[NT];
@@ -166,6 +172,18 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __syncthreads();  // the previous group's readers of both LDS buffers are done
   const int64_t item0 = (unit / S) * kGmWaves * IT;
   const int sp = (int)(unit % S);
+  if constexpr (MODE == kGmFlash) {
+    if (!a.ulist) {
+      // a group whose clusters no row selected is skipped by the whole
+      // workgroup (every thread reads the same masks)
+      bool any = false;
+      for (int w = 0; w < kGmWaves * IT; ++w) {
+        const int64_t it = item0 + w;
+        any = any || (it < nitems && a.masks[it / sub] != 0ull);
+      }
+      if (!any) continue;
+    }
+  }
   const int cbeg = sp * nchunks / S, cend = (sp + 1) * nchunks / S;
 
   // this wave's items
@@ -178,7 +196,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const bool live = it < nitems;
     it = live ? it : nitems - 1;
     if constexpr (MODE == kGmFlash) {
-      kc[i] = a.ulist[it / sub];
+      kc[i] = a.ulist ? a.ulist[it / sub] : it / sub;
       row0[i] = kc[i] * a.b + (it % sub) * 16;
       mask[i] = live ? a.masks[kc[i]] : 0ull;
     } else {
@@ -212,7 +230,13 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // they were kept in scratch memory, which made every prefetch wait
   uint4 a0[IT][kSteps], a1[IT][kSteps];
   u32x4_t hreg[kHP];
+  // a wave whose items no row needs (a cluster no row selected, the tail)
+  // reads no rows and runs no MFMA; it still stages H for the others
+  bool wlive = false;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) wlive = wlive || mask[i] != 0ull;
   auto load_a = [&](uint4 (&dst)[IT][kSteps], int c) {
+    if (!wlive) return;
 #pragma unroll
     for (int i = 0; i < IT; ++i)
 #pragma unroll
@@ -229,6 +253,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     for (int n = 0; n < kHP; ++n) reinterpret_cast<u32x4_t*>(s_h[buf])[hdst[n]] = hreg[n];
   };
   auto compute = [&](const uint4 (&av)[IT][kSteps], int buf) {
+    if (!wlive) return;
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       uint4 bv[NT];
@@ -401,8 +426,12 @@ __global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblock
     if (a.out_lse) a.out_lse[r] = l0.m + logf(l0.s);
   }
   if (a.masks) {
-    const int u = *a.ucount;
-    for (int i = r * 256 + t; i < u; i += (int)gridDim.x * 256) a.masks[a.ulist[i]] = 0ull;
+    if (a.ulist) {
+      const int u = *a.ucount;
+      for (int i = r * 256 + t; i < u; i += (int)gridDim.x * 256) a.masks[a.ulist[i]] = 0ull;
+    } else {
+      for (int i = r * 256 + t; i < a.c; i += (int)gridDim.x * 256) a.masks[i] = 0ull;
+    }
   }
 }
 

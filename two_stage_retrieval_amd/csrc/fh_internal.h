@@ -79,8 +79,8 @@ struct Stage2mArgs {
   int b, d, B, p;
   const uint8_t* H;      // B x d bf16
   int64_t h_bytes;
-  const int32_t* ulist;  // flash: union of the selected clusters, ascending
-  const int32_t* ucount;
+  const int32_t* ulist;  // flash: union of the selected clusters, ascending,
+  const int32_t* ucount; // or null: every cluster, skipping zero masks
   uint64_t* masks;       // flash: rows that selected each cluster
   const int32_t* c2t;
   const int32_t* sel;    // flash debug: B x sel_stride ascending selections
@@ -104,6 +104,9 @@ struct Stage2mArgs {
   int64_t part_stride;   // floats between the slices' B x key_stride blocks
 };
 constexpr int kMaxKSplit = 4;
+// batched stage 2 walks the union list below this many rows, every cluster
+// (skipping unselected ones) from it on
+constexpr int kUnionMinRows = 16;
 
 struct Stage1Args {
   const uint8_t* C;       // c x d centroids (bf16 / fp32)
