@@ -121,3 +121,37 @@ def test_full_llama_shape_one_assignment_is_stable(fh):
         better = np.nonzero(cos[n] > mine + tol)[0]
         # a cluster the token prefers must hold b tokens it prefers to it
         assert np.all(worst[better] >= cos[n, better] - tol), i
+
+
+def test_kmeans_table_drives_the_head(fh):
+    # the offline step feeding the online one: C2T from flashhead_kmeans,
+    # the centroids computed by prepare (Formula 5, bf16), then greedy
+    # decoding against the oracle on the same table (ids exact where the
+    # oracle's top-2 decode margin exceeds 1e-3, else within 1e-3 of the top)
+    head = synth.make_head(1, v=4096, d=256, c=256, b=16)
+    E_dev = dev_tensor(head.E)
+    init = draw_init(4096, 256, 39)
+    c2t_dev = torch.empty((256, 16), dtype=torch.int32, device="cuda")
+    fh.flashhead_kmeans(E_dev, 256, init, 3, c2t_dev)
+    c2t = c2t_dev.cpu().numpy()
+    p = 32
+    fhh = fh.FlashHead(E_dev, c2t, None, max_batch=1, max_p=p)
+    rows = ref.rows_accessor(head.E, "bf16")
+    C64 = ref.as_f64(ref.bf16_bits_of(ref.centroid_means(rows, c2t)), "bf16")
+    H = synth.make_hidden(head, 16, offset=3)
+    out = torch.empty(1, dtype=torch.int32, device="cuda")
+    exact = 0
+    for r in range(16):
+        fhh.greedy(dev_tensor(H[r:r + 1]), p, out=out)
+        torch.cuda.synchronize()
+        tok = int(out.cpu()[0])
+        o = ref.flashhead_step(rows, c2t, ref.as_f64(H[r], "bf16"), p, C_f64=C64)
+        if o.m1 > 1e-3 and o.m2 > 1e-3:
+            assert tok == o.token
+            exact += 1
+        elif o.m1 > 1e-3:
+            # same candidates, a near tie at the top: within 1e-3 of it
+            T = o.T.tolist()
+            assert tok in T and o.z[T.index(tok)] >= o.z.max() - 1e-3
+    assert exact >= 8
+    fhh.close()
