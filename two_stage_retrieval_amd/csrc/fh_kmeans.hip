@@ -191,26 +191,27 @@ __device__ __forceinline__ void better_pair(double& bs, int& bk, double os, int 
   if (ok >= 0 && (bk < 0 || before(os, ok, bs, bk))) { bs = os; bk = ok; }
 }
 
-__global__ __launch_bounds__(kKmThreads) void propose_kernel(Round r) {
-  __shared__ double w_s[kKmWaves];
-  __shared__ int w_k[kKmWaves];
+// The best cluster of token i after its last proposal lk (cosine desc,
+// cluster id asc), by the whole workgroup; the result is valid in thread 0
+// (bk < 0: no cluster left, only with non-finite cosines).  Ends with the
+// workgroup's LDS scratch free again.
+__device__ __forceinline__ void best_after(const Round& r, int32_t i, int lk, double* w_s, int* w_k,
+                                           double& bs, int& bk) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int32_t i = r.freel[blockIdx.x];  // grid = unplaced tokens
   const double* row = r.S + (int64_t)i * r.c;
-  const int lk = r.last[i];
   const double ls = lk >= 0 ? row[lk] : 0.0;
-  double bs = 0.0;
-  int bk = -1;
-  // 8 loads in flight per thread, then their comparisons
-  for (int k0 = threadIdx.x; k0 < r.c; k0 += 8 * kKmThreads) {
-    double vals[8];
+  bs = 0.0;
+  bk = -1;
+  // 16 loads in flight per thread, then their comparisons
+  for (int k0 = threadIdx.x; k0 < r.c; k0 += 16 * kKmThreads) {
+    double vals[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int k = k0 + q * kKmThreads;
       vals[q] = k < r.c ? row[k] : 0.0;
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int k = k0 + q * kKmThreads;
       const double sv = vals[q];
       const bool after = lk < 0 || sv < ls || (sv == ls && k > lk);
@@ -225,8 +226,19 @@ __global__ __launch_bounds__(kKmThreads) void propose_kernel(Round r) {
     w_k[wave] = bk;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0)
     for (int w = 1; w < kKmWaves; ++w) better_pair(bs, bk, w_s[w], w_k[w]);
+  __syncthreads();  // w_s / w_k may be reused
+}
+
+__global__ __launch_bounds__(kKmThreads) void propose_kernel(Round r) {
+  __shared__ double w_s[kKmWaves];
+  __shared__ int w_k[kKmWaves];
+  const int32_t i = r.freel[blockIdx.x];  // grid = unplaced tokens
+  double bs;
+  int bk;
+  best_after(r, i, r.last[i], w_s, w_k, bs, bk);
+  if (threadIdx.x == 0) {
     if (bk < 0) {
       r.counters[kCtrBad] = 1;  // only with non-finite cosines
       r.last[i] = -2;
@@ -299,6 +311,68 @@ __global__ __launch_bounds__(kKmThreads) void accept_kernel(Round r) {
       }
     }
     if (threadIdx.x == 0) r.hn[k] = b;
+  }
+}
+
+// The last unplaced tokens, one workgroup, one proposal at a time (the
+// order of proposals does not change where deferred acceptance ends): the
+// token on top of the stack proposes to its best cluster after its last
+// one; a cluster with room takes it; a full cluster takes it only over its
+// weakest holder, which then takes its place on the stack.  Each token
+// proposes to a cluster at most once, so the loop ends; a budget of v * c
+// proposals guards it anyway.
+constexpr int kTailMax = 1024;  // stack capacity of the tail
+// Unplaced tokens at which the rounds hand over to the tail: a round costs
+// about as much as 6 sequential proposals (two launches and a host round
+// trip against one row scan each)
+constexpr int kTailStart = 8;
+__global__ __launch_bounds__(kKmThreads) void tail_kernel(Round r) {
+  __shared__ int32_t stack[kTailMax];
+  __shared__ int top;
+  __shared__ int stop;
+  __shared__ double w_s[kKmWaves];
+  __shared__ int w_k[kKmWaves];
+  for (int j = threadIdx.x; j < r.nfree; j += kKmThreads) stack[j] = r.freel[j];
+  if (threadIdx.x == 0) {
+    top = r.nfree;
+    stop = 0;
+  }
+  const int b = r.b;
+  int64_t budget = r.v * (int64_t)r.c;
+  __syncthreads();
+  while (top > 0 && !stop) {
+    const int32_t i = stack[top - 1];
+    double bs;
+    int bk;
+    best_after(r, i, r.last[i], w_s, w_k, bs, bk);
+    if (threadIdx.x == 0) {
+      if (bk < 0 || --budget < 0) {
+        r.counters[kCtrBad] = 1;
+        stop = 1;
+      } else {
+        r.last[i] = bk;
+        int32_t* hold = r.holds + (int64_t)bk * b;
+        double* hold_s = r.holds_s + (int64_t)bk * b;
+        const int h = r.hn[bk];
+        if (h < b) {
+          hold[h] = i;
+          hold_s[h] = bs;
+          r.hn[bk] = h + 1;
+          --top;
+        } else {
+          int wpos = 0;  // the holder that ranks last
+          for (int l = 1; l < b; ++l)
+            if (before(hold_s[wpos], hold[wpos], hold_s[l], hold[l])) wpos = l;
+          if (before(bs, i, hold_s[wpos], hold[wpos])) {
+            stack[top - 1] = hold[wpos];
+            hold[wpos] = i;
+            hold_s[wpos] = bs;
+          }
+          // else the token stays on top and proposes further down its list
+        }
+      }
+    }
+    __syncthreads();  // top, stop and the stack as thread 0 left them
   }
 }
 
@@ -443,6 +517,17 @@ hipError_t run_kmeans(const KMeansArgs& a, hipStream_t s, int* iters, int* statu
       r.hn = hn;
       r.freel_next = fb;
       r.counters = ctr;
+      if (nfree <= kTailStart) {
+        hipLaunchKernelGGL(tail_kernel, dim3(1), dim3(kKmThreads), 0, s, r);
+        KM_TRY(hipGetLastError());
+        KM_TRY(hipMemcpyAsync(host_ctr, ctr, kCtrWords * 4, hipMemcpyDeviceToHost, s));
+        KM_TRY(hipStreamSynchronize(s));
+        if (host_ctr[kCtrBad]) {
+          *status = 1;  // a token found no cluster: non-finite cosines
+          return hipSuccess;
+        }
+        break;
+      }
       hipLaunchKernelGGL(propose_kernel, dim3(nfree), dim3(kKmThreads), 0, s, r);
       // at most one cluster with proposals per proposal
       hipLaunchKernelGGL(accept_kernel, dim3(nfree < c ? nfree : c), dim3(kKmThreads), 0, s, r);
