@@ -195,24 +195,26 @@ __device__ __forceinline__ void better_pair(double& bs, int& bk, double os, int 
 // cluster id asc), by the whole workgroup; the result is valid in thread 0
 // (bk < 0: no cluster left, only with non-finite cosines).  Ends with the
 // workgroup's LDS scratch free again.
+template <int NT>
 __device__ __forceinline__ void best_after(const Round& r, int32_t i, int lk, double* w_s, int* w_k,
                                            double& bs, int& bk) {
+  constexpr int kLoads = 8192 / NT;  // loads in flight per thread (c <= 8192: one batch)
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const double* row = r.S + (int64_t)i * r.c;
   const double ls = lk >= 0 ? row[lk] : 0.0;
   bs = 0.0;
   bk = -1;
-  // 16 loads in flight per thread, then their comparisons
-  for (int k0 = threadIdx.x; k0 < r.c; k0 += 16 * kKmThreads) {
-    double vals[16];
+  // kLoads loads in flight per thread, then their comparisons
+  for (int k0 = threadIdx.x; k0 < r.c; k0 += kLoads * NT) {
+    double vals[kLoads];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int k = k0 + q * kKmThreads;
+    for (int q = 0; q < kLoads; ++q) {
+      const int k = k0 + q * NT;
       vals[q] = k < r.c ? row[k] : 0.0;
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int k = k0 + q * kKmThreads;
+    for (int q = 0; q < kLoads; ++q) {
+      const int k = k0 + q * NT;
       const double sv = vals[q];
       const bool after = lk < 0 || sv < ls || (sv == ls && k > lk);
       if (k < r.c && after) better_pair(bs, bk, sv, k);
@@ -227,7 +229,7 @@ __device__ __forceinline__ void best_after(const Round& r, int32_t i, int lk, do
   }
   __syncthreads();
   if (threadIdx.x == 0)
-    for (int w = 1; w < kKmWaves; ++w) better_pair(bs, bk, w_s[w], w_k[w]);
+    for (int w = 1; w < NT / kWave; ++w) better_pair(bs, bk, w_s[w], w_k[w]);
   __syncthreads();  // w_s / w_k may be reused
 }
 
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(kKmThreads) void propose_kernel(Round r) {
   const int32_t i = r.freel[blockIdx.x];  // grid = unplaced tokens
   double bs;
   int bk;
-  best_after(r, i, r.last[i], w_s, w_k, bs, bk);
+  best_after<kKmThreads>(r, i, r.last[i], w_s, w_k, bs, bk);
   if (threadIdx.x == 0) {
     if (bk < 0) {
       r.counters[kCtrBad] = 1;  // only with non-finite cosines
@@ -326,13 +328,16 @@ constexpr int kTailMax = 1024;  // stack capacity of the tail
 // about as much as 6 sequential proposals (two launches and a host round
 // trip against one row scan each)
 constexpr int kTailStart = 8;
-__global__ __launch_bounds__(kKmThreads) void tail_kernel(Round r) {
+constexpr int kTailThreads = 1024;  // one row scan per proposal: all loads at once
+__global__ __launch_bounds__(kTailThreads) void tail_kernel(Round r) {
   __shared__ int32_t stack[kTailMax];
-  __shared__ int top;
-  __shared__ int stop;
-  __shared__ double w_s[kKmWaves];
-  __shared__ int w_k[kKmWaves];
-  for (int j = threadIdx.x; j < r.nfree; j += kKmThreads) stack[j] = r.freel[j];
+  __shared__ int32_t h_id[kMaxKmB];  // the proposed-to cluster's holders
+  __shared__ double h_s[kMaxKmB];
+  __shared__ int top, stop, s_k, s_h;
+  __shared__ double s_s;
+  __shared__ double w_s[kTailThreads / kWave];
+  __shared__ int w_k[kTailThreads / kWave];
+  for (int j = threadIdx.x; j < r.nfree; j += kTailThreads) stack[j] = r.freel[j];
   if (threadIdx.x == 0) {
     top = r.nfree;
     stop = 0;
@@ -344,35 +349,49 @@ __global__ __launch_bounds__(kKmThreads) void tail_kernel(Round r) {
     const int32_t i = stack[top - 1];
     double bs;
     int bk;
-    best_after(r, i, r.last[i], w_s, w_k, bs, bk);
+    best_after<kTailThreads>(r, i, r.last[i], w_s, w_k, bs, bk);
     if (threadIdx.x == 0) {
       if (bk < 0 || --budget < 0) {
         r.counters[kCtrBad] = 1;
         stop = 1;
-      } else {
-        r.last[i] = bk;
-        int32_t* hold = r.holds + (int64_t)bk * b;
-        double* hold_s = r.holds_s + (int64_t)bk * b;
-        const int h = r.hn[bk];
-        if (h < b) {
-          hold[h] = i;
-          hold_s[h] = bs;
-          r.hn[bk] = h + 1;
-          --top;
-        } else {
-          int wpos = 0;  // the holder that ranks last
-          for (int l = 1; l < b; ++l)
-            if (before(hold_s[wpos], hold[wpos], hold_s[l], hold[l])) wpos = l;
-          if (before(bs, i, hold_s[wpos], hold[wpos])) {
-            stack[top - 1] = hold[wpos];
-            hold[wpos] = i;
-            hold_s[wpos] = bs;
-          }
-          // else the token stays on top and proposes further down its list
-        }
+      }
+      s_k = bk;
+      s_s = bs;
+      s_h = bk >= 0 ? r.hn[bk] : 0;
+    }
+    __syncthreads();
+    if (stop) break;
+    const int k = s_k;
+    const int h = s_h;
+    int32_t* hold = r.holds + (int64_t)k * b;
+    double* hold_s = r.holds_s + (int64_t)k * b;
+    if (h == b) {  // full: its holders into LDS, all loads at once
+      for (int j = threadIdx.x; j < b; j += kTailThreads) {
+        h_id[j] = hold[j];
+        h_s[j] = hold_s[j];
       }
     }
-    __syncthreads();  // top, stop and the stack as thread 0 left them
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      r.last[i] = k;
+      if (h < b) {
+        hold[h] = i;
+        hold_s[h] = s_s;
+        r.hn[k] = h + 1;
+        --top;
+      } else {
+        int wpos = 0;  // the holder that ranks last
+        for (int l = 1; l < b; ++l)
+          if (before(h_s[wpos], h_id[wpos], h_s[l], h_id[l])) wpos = l;
+        if (before(s_s, i, h_s[wpos], h_id[wpos])) {
+          stack[top - 1] = h_id[wpos];
+          hold[wpos] = i;
+          hold_s[wpos] = s_s;
+        }
+        // else the token stays on top and proposes further down its list
+      }
+    }
+    __syncthreads();  // top, the stack and the LDS copies as thread 0 left them
   }
 }
 
@@ -518,7 +537,7 @@ hipError_t run_kmeans(const KMeansArgs& a, hipStream_t s, int* iters, int* statu
       r.freel_next = fb;
       r.counters = ctr;
       if (nfree <= kTailStart) {
-        hipLaunchKernelGGL(tail_kernel, dim3(1), dim3(kKmThreads), 0, s, r);
+        hipLaunchKernelGGL(tail_kernel, dim3(1), dim3(kTailThreads), 0, s, r);
         KM_TRY(hipGetLastError());
         KM_TRY(hipMemcpyAsync(host_ctr, ctr, kCtrWords * 4, hipMemcpyDeviceToHost, s));
         KM_TRY(hipStreamSynchronize(s));
