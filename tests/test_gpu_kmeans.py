@@ -155,3 +155,14 @@ def test_kmeans_table_drives_the_head(fh):
             assert tok in T and o.z[T.index(tok)] >= o.z.max() - 1e-3
     assert exact >= 8
     fhh.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_shapes(fh, dtype):
+    # d = 100 (not a multiple of the cosine GEMM's K step of 8), 600 tokens
+    # and 40 clusters (partial 128-wide tiles on both sides), b = 15
+    rng = np.random.default_rng(40)
+    v, d, c = 600, 100, 40
+    X = rng.standard_normal((v, d)).astype(np.float32) * rng.uniform(0.5, 2.0, (v, 1)).astype(np.float32)
+    E = X if dtype == "f32" else synth.f32_to_bf16_bits(X)
+    check(fh, E, dtype, c, draw_init(v, c, 41), 4)
