@@ -30,8 +30,8 @@ constexpr int kMcSelThreads = 1024;
 constexpr int kMcThreads = 256;
 constexpr int kMcWaves = kMcThreads / kWave;
 
-template <int IPT>
-__global__ __launch_bounds__(kMcSelThreads) void mc_select_kernel(McArgs a) {
+template <int NT, int IPT>
+__global__ __launch_bounds__(NT) void mc_select_kernel(McArgs a) {
   __shared__ SelSmem sm;
   const int i = blockIdx.x;
   const int k0 = threadIdx.x * IPT;
@@ -49,11 +49,11 @@ __global__ __launch_bounds__(kMcSelThreads) void mc_select_kernel(McArgs a) {
         u[j4 + q] = __float_as_uint(__uint_as_float(u[j4 + q]) * a.inv_tau + gj[q]);
   }
   int32_t* out = a.sel + (int64_t)i * a.p;
-  select_from_keys<kMcSelThreads, IPT, false>(u, a.c, a.p, a.zcut, out, nullptr, 0, a.error, sm);
+  select_from_keys<NT, IPT, false>(u, a.c, a.p, a.zcut, out, nullptr, 0, a.error, sm);
   __syncthreads();  // the draw's ids are visible to the whole workgroup
   // flag the draw's clusters (plain stores of one: every writer stores the
   // same value, so no atomics)
-  for (int j = threadIdx.x; j < a.p; j += kMcSelThreads) {
+  for (int j = threadIdx.x; j < a.p; j += NT) {
     const int32_t k = out[j];
     if (k >= 0 && k < a.c) a.flags[k] = 1u;
   }
@@ -173,12 +173,16 @@ __global__ __launch_bounds__(kMcThreads) void mc_reduce_kernel(McArgs a) {
 template <typename TE, int NCH>
 static hipError_t launch_mc_t(const McArgs& a, const RowdotArgs& ra, hipStream_t s) {
   constexpr int R = NCH <= 2 ? 8 : 4;
-  const int ipt = (a.c + kMcSelThreads - 1) / kMcSelThreads;
-  const dim3 gsel(a.n), bsel(kMcSelThreads);
-  if (ipt <= 4) hipLaunchKernelGGL(mc_select_kernel<4>, gsel, bsel, 0, s, a);
-  else if (ipt <= 8) hipLaunchKernelGGL(mc_select_kernel<8>, gsel, bsel, 0, s, a);
-  else if (ipt <= 16) hipLaunchKernelGGL(mc_select_kernel<16>, gsel, bsel, 0, s, a);
-  else if (ipt <= 32) hipLaunchKernelGGL(mc_select_kernel<32>, gsel, bsel, 0, s, a);
+  // draws are independent: 512-thread workgroups (16 keys per thread up to
+  // 8192 clusters) let four draws share a compute unit
+  const int ipt512 = (a.c + 511) / 512;
+  const int ipt1k = (a.c + kMcSelThreads - 1) / kMcSelThreads;
+  const dim3 gsel(a.n);
+  if (ipt512 <= 4) hipLaunchKernelGGL((mc_select_kernel<512, 4>), gsel, dim3(512), 0, s, a);
+  else if (ipt512 <= 8) hipLaunchKernelGGL((mc_select_kernel<512, 8>), gsel, dim3(512), 0, s, a);
+  else if (ipt512 <= 16) hipLaunchKernelGGL((mc_select_kernel<512, 16>), gsel, dim3(512), 0, s, a);
+  else if (ipt1k <= 16) hipLaunchKernelGGL((mc_select_kernel<1024, 16>), gsel, dim3(1024), 0, s, a);
+  else if (ipt1k <= 32) hipLaunchKernelGGL((mc_select_kernel<1024, 32>), gsel, dim3(1024), 0, s, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
