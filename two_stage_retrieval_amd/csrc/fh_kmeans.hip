@@ -18,8 +18,10 @@
 //   accept   one workgroup per cluster with proposals ranks what it holds
 //            together with them by (cosine desc, token id asc), keeps the
 //            first b and sends the rest back to the unplaced list.
-// The rounds end when every token is placed (a token can always place:
-// total room equals v).  Cosines, centroids and their sums are float64, so
+// When 8 or fewer tokens are left unplaced, one workgroup finishes the
+// assignment one proposal at a time (a round would cost about as much as
+// 6 proposals).  It ends when every token is placed (a token can always
+// place: total room equals v).  Cosines, centroids and their sums are float64, so
 // the integer decisions rest on float64 comparisons, as in a plain CPU
 // implementation of the same definition.
 //
@@ -29,7 +31,6 @@
 // caller-chosen token ids.
 #include <hip/hip_runtime.h>
 
-#include <cstring>
 #include <vector>
 
 #include "fh_device.h"
