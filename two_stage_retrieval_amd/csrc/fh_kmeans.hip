@@ -97,62 +97,80 @@ __global__ __launch_bounds__(kKmThreads) void gather_rows_kernel(const double* X
   for (int j = threadIdx.x; j < d; j += kKmThreads) C[(int64_t)k * d + j] = src[j];
 }
 
-// S (v x c) = X (v x d) C^T (C c x d), float64 on the vector units.  A
-// 128 x 128 output tile per workgroup, 8 x 8 outputs per thread at rows
-// ty + 16 p and columns tx + 16 q (so a wave's LDS reads are 4 broadcast
-// rows and 16 consecutive columns), K staged through LDS 8 at a time; each
-// output is a sum over j ascending.
-constexpr int kSimTile = 128, kSimK = 8;
+// S (v x c) = X (v x d) C^T (C c x d), float64 on the matrix cores
+// (v_mfma_f64_16x16x4f64: lane l feeds A[l mod 16][l div 16] and
+// B[l div 16][l mod 16] and holds D[l div 16 + 4 r][l mod 16], r = 0..3).
+// A 128 x 128 output tile per workgroup, a 64 x 64 quarter (4 x 4 blocks of
+// 16 x 16) per wave, K staged through LDS 16 at a time.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSimTile = 128, kSimK = 16;
 __global__ __launch_bounds__(kKmThreads) void cosine_kernel(const double* X, const double* C,
                                                             int64_t v, int c, int d, double* S) {
-  __shared__ double sa[kSimK][kSimTile];
-  __shared__ double sb[kSimK][kSimTile];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  __shared__ double sa[kSimK][kSimTile + 1];  // [k][row]
+  __shared__ double sb[kSimK][kSimTile + 1];  // [k][column]
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;  // the wave's quarter
+  const int li = lane & 15, lk = lane >> 4;
   const int64_t i0 = (int64_t)blockIdx.y * kSimTile;
   const int k0 = blockIdx.x * kSimTile;
-  double acc[8][8];
+  f64x4_t acc[4][4];
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[p][q] = 0.0;
-  for (int j0 = 0; j0 < d; j0 += kSimK) {
-    // 128 rows x 8 columns of each operand: 4 elements per thread
+    for (int q = 0; q < 4; ++q) acc[p][q] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  // 128 rows x 16 columns of each operand per K step: 8 elements per
+  // thread, the next step's loaded into registers while this one computes
+  double na[8], nb[8];
+  auto fetch = [&](int j0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = threadIdx.x + q * kKmThreads;  // [0, 1024)
-      const int r = e >> 3, jj = e & 7;
+    for (int q = 0; q < 8; ++q) {
+      const int e = threadIdx.x + q * kKmThreads;  // [0, 2048)
+      const int r = e >> 4, jj = e & 15;
       const int64_t gi = i0 + r;
       const int gk = k0 + r;
       const int gj = j0 + jj;
-      sa[jj][r] = (gi < v && gj < d) ? X[gi * d + gj] : 0.0;
-      sb[jj][r] = (gk < c && gj < d) ? C[(int64_t)gk * d + gj] : 0.0;
+      na[q] = (gi < v && gj < d) ? X[gi * d + gj] : 0.0;
+      nb[q] = (gk < c && gj < d) ? C[(int64_t)gk * d + gj] : 0.0;
     }
-    __syncthreads();
-#pragma unroll
-    for (int jj = 0; jj < kSimK; ++jj) {
-      double a[8], b[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        a[q] = sa[jj][ty + 16 * q];
-        b[q] = sb[jj][tx + 16 * q];
-      }
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int64_t gi = i0 + ty + 16 * p;
-    if (gi >= v) continue;
+  };
+  fetch(0);
+  for (int j0 = 0; j0 < d; j0 += kSimK) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int gk = k0 + tx + 16 * q;
-      if (gk < c) S[gi * c + gk] = acc[p][q];
+      const int e = threadIdx.x + q * kKmThreads;
+      sa[e & 15][e >> 4] = na[q];
+      sb[e & 15][e >> 4] = nb[q];
     }
+    __syncthreads();
+    if (j0 + kSimK < d) fetch(j0 + kSimK);
+#pragma unroll
+    for (int k4 = 0; k4 < kSimK; k4 += 4) {
+      double a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = sa[k4 + lk][wr + 16 * q + li];
+        b[q] = sb[k4 + lk][wc + 16 * q + li];
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[p][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[p], b[q], acc[p][q], 0, 0, 0);
+    }
+    __syncthreads();
   }
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t gi = i0 + wr + 16 * p + lk + 4 * r;
+      if (gi >= v) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int gk = k0 + wc + 16 * q + li;
+        if (gk < c) S[gi * c + gk] = acc[p][q][r];
+      }
+    }
 }
 
 constexpr int kKmQ = 256;  // proposal slots per cluster and round
