@@ -21,9 +21,9 @@
 // When 8 or fewer tokens are left unplaced, one workgroup finishes the
 // assignment one proposal at a time (a round would cost about as much as
 // 6 proposals).  It ends when every token is placed (a token can always
-// place: total room equals v).  Cosines, centroids and their sums are float64, so
-// the integer decisions rest on float64 comparisons, as in a plain CPU
-// implementation of the same definition.
+// place: total room equals v).  Cosines, centroids and their sums are
+// float64, so the integer decisions rest on float64 comparisons, as in a
+// plain CPU implementation of the same definition.
 //
 // Iteration: cosines S = X C^T of the unit rows X against the centroids,
 // the assignment, then (unless it repeats the previous assignment) the
@@ -202,10 +202,7 @@ __device__ __forceinline__ bool before(double s1, int id1, double s2, int id2) {
   return s1 > s2 || (s1 == s2 && id1 < id2);
 }
 
-// one workgroup per unplaced token: the best cluster after its last
-// proposal in the token's own order (cosine desc, cluster id asc).  A whole
-// workgroup scans the row so that the late rounds, with few tokens left,
-// are not one wave's chain of loads.
+// keep (os, ok) in (bs, bk) if it ranks before it (bk < 0: nothing kept yet)
 __device__ __forceinline__ void better_pair(double& bs, int& bk, double os, int ok) {
   if (ok >= 0 && (bk < 0 || before(os, ok, bs, bk))) { bs = os; bk = ok; }
 }
@@ -252,6 +249,11 @@ __device__ __forceinline__ void best_after(const Round& r, int32_t i, int lk, do
   __syncthreads();  // w_s / w_k may be reused
 }
 
+// one workgroup per unplaced token: the best cluster after its last
+// proposal in the token's own order (cosine desc, cluster id asc), then a
+// slot in that cluster's proposal block.  A whole workgroup scans the row so
+// that the late rounds, with few tokens left, are not one wave's chain of
+// loads.
 __global__ __launch_bounds__(kKmThreads) void propose_kernel(Round r) {
   __shared__ double w_s[kKmWaves];
   __shared__ int w_k[kKmWaves];
