@@ -423,7 +423,7 @@ def mc_bench(args, wl, head, H, H_dev, fh, evict, int4):
         ref.mc_marginal(rows, head.c2t, h64, wl.p, tau, sd,
                         rng.integers(0, wl.v, size=Q), **kw)
         per_draw = (time.perf_counter() - t0) * 1e6 / n_s
-        cpu = {"value": round(per_draw * N, 1), "unit": "us/estimate", "cores": None,
+        cpu = {"value": round(per_draw * N, 1), "unit": "us/estimate", "cores": blas_threads(),
                "kind": "oracle",
                "sample": f"{n_s} draws timed ({per_draw:.0f} us/draw, float64 numpy oracle), "
                          f"scaled to {N} draws"}
@@ -479,7 +479,7 @@ def kmeans_bench(args, wl, dev):
         ref.kmeans_equal_size(rows, cs, init_s, 1)
         sec = time.perf_counter() - t
         scale = (wl.v * wl.c) / (cs * bs * cs)
-        cpu = {"value": round(sec * 1e3 * scale, 1), "unit": "ms/iteration", "cores": None,
+        cpu = {"value": round(sec * 1e3 * scale, 1), "unit": "ms/iteration", "cores": blas_threads(),
                "kind": "oracle",
                "sample": f"one iteration at v={cs * bs}, c={cs}, d={wl.d} ({sec:.2f} s, "
                          f"float64 numpy oracle) scaled by the pair count v*c ({scale:.0f}x)"}
@@ -502,6 +502,15 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def blas_threads() -> int:
+    """Threads of the host BLAS pool the oracle's NumPy calls use."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except ImportError:
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
 
 
 def cpu_baseline(head, H, wl, B, int4, sample, tau, seconds):
