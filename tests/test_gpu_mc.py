@@ -152,3 +152,26 @@ def test_mc_repeatable_and_errors(fh):
     head.mc_marginal(x, 8, 0.8, sd, bad)
     torch.cuda.synchronize()
     assert fh.flashhead_query(head.handle, 9) == 16
+
+
+def test_llama_mc_at_the_benchmarked_draw_count(fh):
+    # the bench's configuration (Llama head, p = 512, N = 10 000 draws,
+    # 16 query tokens): the oracle takes sampled draws one by one and checks
+    # their lse, and the estimate obeys what holds at any N (a probability
+    # per token, the query terms bounded by the draws that contain them)
+    cs = case(1)
+    head = cs.prepare(fh, max_batch=1, max_p=512)
+    H, H64 = cs.hidden(1, offset=1500)
+    N = 10000
+    seeds = [(21 << 32) | i for i in range(N)]
+    rng = np.random.default_rng(10)
+    o1 = oracle_mc(cs, H64[0], 512, 1.0, seeds[:1], [0])
+    toks = tokens_for(cs, o1, rng, 16)
+    prob, lse = run_mc(head, dev_tensor(H), 512, 1.0, seeds, toks)
+    assert np.all(np.isfinite(lse)) and np.all((prob >= 0) & (prob <= 1))
+    assert np.all(prob[:8] > 0)  # candidates of draw 0 are in at least that draw
+    for i in rng.choice(N, size=24, replace=False):
+        o = oracle_mc(cs, H64[0], 512, 1.0, [seeds[i]], toks)
+        if o.m1[0] >= 1e-5:
+            assert lse[i] == pytest.approx(o.lse[0], rel=1e-4, abs=1e-4)
+    assert fh.flashhead_query(head.handle, 9) == 0
