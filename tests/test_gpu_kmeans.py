@@ -166,3 +166,31 @@ def test_ragged_shapes(fh, dtype):
     X = rng.standard_normal((v, d)).astype(np.float32) * rng.uniform(0.5, 2.0, (v, 1)).astype(np.float32)
     E = X if dtype == "f32" else synth.f32_to_bf16_bits(X)
     check(fh, E, dtype, c, draw_init(v, c, 41), 4)
+
+
+def test_full_llama_shape_bench_configuration(fh):
+    # the bench's call (Llama head, up to 5 iterations from 8016 drawn ids):
+    # the returned centroids are Formula 5 of the returned table (sampled
+    # clusters), and the table is a stable assignment against the centroids
+    # it was computed with (when the call stopped on a repeat, those are the
+    # returned ones; sampled tokens, ties within 1e-12 not judged)
+    head = synth.make_head(1)
+    v, c, b, d = head.wl.v, head.wl.c, head.wl.b, head.wl.d
+    init = np.random.default_rng(41).choice(v, size=c, replace=False).astype(np.int32)
+    c2t, C, it = run_gpu(fh, dev_tensor(head.E), c, init, 5)
+    assert 1 <= it <= 5
+    assert np.array_equal(np.sort(c2t.ravel()), np.arange(v))
+    rows = ref.as_f64(head.E, "bf16")
+    rng = np.random.default_rng(42)
+    ks = rng.choice(c, size=64, replace=False)
+    np.testing.assert_allclose(C[ks], ref.unit_cluster_means(rows, c2t[ks]), rtol=0, atol=1e-12)
+    if it < 5:  # stopped on a repeat: c2t was assigned against C
+        X = ref.unit_rows(rows)
+        own = np.empty(v, dtype=np.int64)
+        own[c2t.ravel()] = np.repeat(np.arange(c), b)
+        worst = np.einsum("kjd,kd->kj", X[c2t], C).min(axis=1)
+        sample = rng.choice(v, size=256, replace=False)
+        cos = X[sample] @ C.T
+        for n, i in enumerate(sample):
+            better = np.nonzero(cos[n] > cos[n, own[i]] + 1e-12)[0]
+            assert np.all(worst[better] >= cos[n, better] - 1e-12), i
