@@ -114,6 +114,8 @@ def main():
                     help="time N iterations of the equal-size spherical k-means "
                          "(Module 1) on the workload's E instead of the decode step; "
                          "prints its own JSON line")
+    ap.add_argument("--flags", type=int, default=0,
+                    help="fh_desc.flags for the head (1: cooperative single launch)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run --steps cold calls and a 256 MiB copy-like kernel, then exit "
                          "(for rocprofv3 --pmc runs)")
@@ -165,7 +167,7 @@ def main():
     C_init = to_dev(head.C_given) if head.C_given is not None else None
     fh = fhb.FlashHead(E_dev, head.c2t, C_init,
                        quant=fhb.FH_QUANT_INT4_G128 if int4 else fhb.FH_QUANT_NONE,
-                       max_batch=B, max_p=wl.p)
+                       max_batch=B, max_p=wl.p, flags=args.flags)
     nb = nvec // B
     batches = [H_dev[i * B:(i + 1) * B] for i in range(nb)]
     out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -271,8 +273,19 @@ def main():
     time_cold(call, K)
     stage_ms, ncalls = fhb.flashhead_profile_end(fh.handle)
     kern_us = [x * 1e3 for x in stage_ms]
-    log(f"[bench] kernels us: stage1 {kern_us[0]:.2f} select {kern_us[1]:.2f} "
-        f"stage2 {kern_us[2]:.2f} over {ncalls} calls")
+    path = fhb.flashhead_query(fh.handle, 10)
+    if path == 1:  # the whole step is one kernel: there are no separate stages to time
+        log(f"[bench] kernel us: decode_b1 {kern_us[0]:.2f} over {ncalls} calls")
+    else:
+        log(f"[bench] kernels us: stage1 {kern_us[0]:.2f} select {kern_us[1]:.2f} "
+            f"stage2 {kern_us[2]:.2f} over {ncalls} calls")
+    # a bounded wait between workgroups that gave up, or a selection of the
+    # wrong size, leaves a bit in the self-check word: the timings above are
+    # then of a step that did not compute the head, and no line is printed
+    check = fhb.flashhead_query(fh.handle, 9)
+    if check:
+        log(f"[bench] FAILED: self-check word {check:#x} after the timed calls")
+        sys.exit(3)
 
     dense_cold = dense_warm = None
     if dense:
@@ -301,7 +314,6 @@ def main():
     # dominant kernel: at batch 1 the whole step is one launch (stage 1,
     # selection, stage 2 and the decode); otherwise the longer of the two
     # streaming stages
-    path = fhb.flashhead_query(fh.handle, 10)
     if path == 1:
         dom, dom_bytes, dom_name = 0, total_b, "decode_b1"
         kern_us = [kern_us[0], 0.0, 0.0]
@@ -341,7 +353,8 @@ def main():
         "data": "synthetic (seeded generator, pages' head shapes)",
         "config": {"workload": f"{wl.name} {'sample' if sample else 'greedy'} B={B}",
                    "v": wl.v, "d": wl.d, "c": wl.c, "b": wl.b, "p": wl.p,
-                   "batch": B, "timing": "cold (1 GiB read-only flush before each call)"},
+                   "batch": B, "timing": "cold (1 GiB read-only flush before each call)",
+                   "flags": args.flags},
         "achieved_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": total_b,
@@ -398,6 +411,10 @@ def mc_bench(args, wl, head, H, H_dev, fh, evict, int4):
             times.append(a.elapsed_time(b) * 1e3)
     us = statistics.median(times)
     log(f"[bench] mc: {N} draws, {Q} tokens: cold p50 {us:.1f} us")
+    check = fhb.flashhead_query(fh.handle, 9)
+    if check:
+        log(f"[bench] FAILED: self-check word {check:#x} after the timed calls")
+        sys.exit(3)
     if args.pmc_probe:
         # the copy-like kernel of known size that calibrates the counters
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)

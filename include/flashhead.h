@@ -77,6 +77,16 @@ extern "C" {
 #define FH_MODE_GREEDY 0
 #define FH_MODE_SAMPLE 1
 
+/* fh_desc.flags */
+#define FH_FLAG_COOPERATIVE 1 /* launch the single-launch batch-1 decode (see
+                                flashhead_plan_step) through the cooperative
+                                launch API, whose runtime guarantees that all
+                                its workgroups are resident together, also
+                                while other work shares the device.  Without
+                                it prepare checks with the occupancy API that
+                                they fit on the device at once, which holds
+                                when nothing else occupies it.               */
+
 /* Limits of this implementation. */
 #define FH_MAX_BATCH 64     /* rows per call                               */
 #define FH_MAX_C 32768      /* clusters                                    */
@@ -113,6 +123,7 @@ typedef struct fh_desc {
   int32_t max_batch;  /* largest B passed to later calls (1..FH_MAX_BATCH) */
   int32_t max_p;      /* largest p passed to later calls (1..c)            */
   void* stream;       /* hipStream_t for prepare's own work                */
+  int32_t flags;      /* FH_FLAG_* bits, 0 for the defaults                */
 } fh_desc;
 
 /*
@@ -291,10 +302,45 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
  * 6 max_batch, 7 max_p, 8 device bytes owned by the handle, 9 the
  * self-check word (reading it synchronises with the device and clears it;
  * bit 0: a selection produced a count other than p; bits 1-3: a bounded
- * wait between workgroups of one launch gave up), 10 the kernels the last
- * step ran (0 none yet, 1 the single-launch batch-1 decode, 2 stage 1 and
- * stage 2 as separate row-dot launches, 3 the batched matrix-core path). */
+ * wait between workgroups of one launch gave up, after about 0.4 s, and the
+ * step's output is not to be trusted; bit 4: a query token outside [0, v)
+ * in flashhead_mc_marginal), 10 the kernels the last step ran (0 none yet,
+ * 1 the single-launch batch-1 decode, 2 stage 1 and stage 2 as separate
+ * row-dot launches, 3 the batched matrix-core path), 11 the state of the
+ * single launch's buffer set that the next launch uses, read back
+ * synchronously (0 when every key reads pending, every selection entry -1,
+ * every merge slot and the set's go word zero, and the device's launch
+ * count matches the handle's; otherwise bit 0 keys, 1 selection, 2 slots,
+ * 3 go word, 4 launch count), 12 the single-launch decode kernel's
+ * workgroups that one compute unit holds at once (occupancy API, measured
+ * at prepare), 13 the device's compute units, 14 fh_desc.flags.
+ * The decode calls are asynchronous and cannot return what goes wrong
+ * inside a kernel: a caller that must know checks the self-check word (9)
+ * after synchronising, as the tests and the benchmark do. */
 int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
+
+/*
+ * The kernels a decode step of a head of this shape takes, on the host
+ * alone (no device call): returns 1 (the single-launch batch-1 decode:
+ * stage 1, selection, stage 2 and decode in one launch of *grid
+ * workgroups), 2 (stage 1 with the selection, then stage 2 with the decode,
+ * as two row-dot launches; *grid = 0) or 3 (the batched matrix-core path;
+ * *grid = 0), or FH_ERR_INVALID_ARG for sizes no step accepts.
+ *   c, b, d, dtype, quant   as in fh_desc
+ *   B, p                    as in flashhead_greedy / flashhead_sample
+ *   num_cu                  compute units of the device (flashhead_query 13)
+ *   blocks_per_cu           single-launch workgroups one compute unit holds
+ *                           at once (flashhead_query 12)
+ * The single launch's workgroups wait on one another (the selection waits
+ * for every stage-1 key, stage 2 for the selection, the merge for every
+ * partial), so it is taken only when grid <= num_cu * blocks_per_cu.  In the
+ * two-launch path one workgroup per batch row waits for the others, which
+ * never wait, so it progresses whenever the device holds more than B
+ * workgroups.  flashhead_greedy and flashhead_sample follow this plan.
+ */
+int flashhead_plan_step(int32_t c, int32_t b, int32_t d, int32_t dtype, int32_t quant,
+                        int32_t B, int32_t p, int32_t num_cu, int32_t blocks_per_cu,
+                        int32_t* grid);
 
 /*
  * Measurement reference, not part of the method: reads `bytes` (a multiple

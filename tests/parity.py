@@ -29,6 +29,14 @@ class Stats:
         self.tok_diff = 0
         self.max_logit_err = 0.0
 
+    def merge(self, o: "Stats"):
+        self.rows += o.rows
+        self.set_band += o.set_band
+        self.set_diff += o.set_diff
+        self.tok_band += o.tok_band
+        self.tok_diff += o.tok_diff
+        self.max_logit_err = max(self.max_logit_err, o.max_logit_err)
+
     def __repr__(self):
         return (f"rows={self.rows} set_in_band={self.set_band} "
                 f"set_differs={self.set_diff} tok_in_band={self.tok_band} "

@@ -66,11 +66,11 @@ def test_status_strings(fh):
 
 
 def _desc(fh, c2t, *, v=None, d=256, dtype=None, lde=None, E=FAKE_DEV, C_init=None,
-          quant=0, max_batch=1, max_p=1):
+          quant=0, max_batch=1, max_p=1, flags=0):
     c, b = c2t.shape
     dtype = fh.FH_DTYPE_F32 if dtype is None else dtype
     return fh.fh_desc(c * b if v is None else v, d, c, b, dtype, d if lde is None else lde,
-                      E, c2t.ctypes.data, C_init, quant, max_batch, max_p, None)
+                      E, c2t.ctypes.data, C_init, quant, max_batch, max_p, None, flags)
 
 
 def _prepare(fh, desc) -> int:
@@ -102,6 +102,7 @@ def test_prepare_rejects_bad_descriptors(fh):
     assert _prepare(fh, _desc(fh, c2t, quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
     assert _prepare(fh, _desc(fh, c2t, dtype=fh.FH_DTYPE_BF16, d=200,
                               quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
+    assert _prepare(fh, _desc(fh, c2t, flags=2)) == inv          # unknown flag bit
 
 
 @pytest.mark.parametrize("kind", ["repeat", "out_of_range", "negative"])
@@ -201,3 +202,49 @@ def test_kmeans_host_checks(fh):
     assert call(dtype=9) == uns
     assert call(E=FAKE_DEV + 2) == uns    # not aligned to its fp32 elements
     assert call(c=2, init=good[:2]) == uns  # 2048 tokens per cluster
+
+
+# --------------------------------------------------------------------------
+# the host-side plan: which kernels a step takes, and the residency rule of
+# the single launch (its workgroups wait on one another)
+# --------------------------------------------------------------------------
+
+def test_plan_step_paths(fh):
+    BF, F32 = fh.FH_DTYPE_BF16, fh.FH_DTYPE_F32
+    plan = fh.flashhead_plan_step
+    # the Llama-3.2-1B head shape at batch 1: one launch, one workgroup per
+    # compute unit
+    assert plan(8016, 16, 2048, BF, 0, 1, 512, 256, 1) == (1, 256)
+    # fewer compute units: the grid shrinks with them
+    assert plan(8016, 16, 2048, BF, 0, 1, 512, 80, 1) == (1, 80)
+    # a kernel no compute unit can hold: never the single launch
+    assert plan(8016, 16, 2048, BF, 0, 1, 512, 256, 0) == (2, 0)
+    # the Gemma-3-1B head with INT4 centroids
+    assert plan(16384, 16, 1152, BF, fh.FH_QUANT_INT4_G128, 1, 1024, 256, 2) == (1, 256)
+    # a small head: the grid covers its rows, not every compute unit
+    path, grid = plan(64, 64, 256, F32, 0, 1, 8, 256, 1)
+    assert path == 1 and 1 <= grid < 256
+    # batches: matrix cores for bf16 with b a multiple of 16, else row-dot
+    assert plan(8016, 16, 2048, BF, 0, 2, 512, 256, 1) == (3, 0)
+    assert plan(8016, 16, 2048, BF, 0, 64, 512, 256, 1) == (3, 0)
+    assert plan(50, 8, 128, BF, 0, 3, 7, 256, 1) == (2, 0)
+    assert plan(4096, 1, 256, F32, 0, 4, 8, 256, 1) == (2, 0)
+    # more probes than the single launch holds, or more clusters than it selects
+    assert plan(4096, 16, 128, BF, 0, 1, 3000, 256, 1) == (2, 0)
+    assert plan(20000, 2, 128, BF, 0, 1, 300, 256, 1) == (2, 0)
+
+
+def test_plan_step_rejects_bad_sizes(fh):
+    BF = fh.FH_DTYPE_BF16
+    g = C.c_int32(7)
+    inv = fh.FH_ERR_INVALID_ARG
+    lib = fh.lib
+    assert lib.flashhead_plan_step(8016, 16, 2048, BF, 0, 1, 512, 256, 1, None) == inv
+    for args in ((8016, 16, 2048, BF, 0, 1, 8017, 256, 1),   # p > c
+                 (8016, 16, 2048, BF, 0, 0, 512, 256, 1),    # B = 0
+                 (8016, 16, 2048, BF, 0, 65, 512, 256, 1),   # B > FH_MAX_BATCH
+                 (8016, 16, 2048, 5, 0, 1, 512, 256, 1),     # dtype
+                 (8016, 16, 2048, BF, 3, 1, 512, 256, 1),    # quant
+                 (8016, 16, 2048, BF, 0, 1, 512, 0, 1)):     # no compute unit
+        assert lib.flashhead_plan_step(*args, C.byref(g)) == inv
+        assert g.value == 0

@@ -75,6 +75,27 @@ class Case:
             return ref.stage1_scores_int4(self.int4[0], self.int4[1], h64)
         return ref.stage1_scores(self.C64, h64)
 
+    def oracle_scores_many(self, H64):
+        """The oracle's stage-1 scores of several rows at once: the same sums
+        (INT4: per group, integer codes times h, then times the group's
+        scale), as matrix products; the first row is also scored by the
+        oracle's own function and must agree."""
+        if self.int4 is None:
+            out = (self.C64 @ H64.T).T
+        else:
+            if not hasattr(self, "_q64"):
+                q, _ = self.int4
+                self._q64 = np.ascontiguousarray(q, dtype=np.float64)
+            q, sc = self._q64, np.asarray(self.int4[1], np.float64)
+            c, d = q.shape
+            G = d // 128
+            out = np.zeros((H64.shape[0], c))
+            for g in range(G):
+                cols = slice(128 * g, 128 * g + 128)
+                out += (q[:, cols] @ H64[:, cols].T).T * sc[:, g]
+        assert np.allclose(out[0], self.oracle_scores(H64[0]), rtol=0, atol=1e-9)
+        return out
+
 
 _CASES = {}
 
@@ -109,25 +130,65 @@ def run_debug(fhmod, head, H_dev, B, p, mode, tau=1.0, seeds=None):
     return res
 
 
+def check_one(cs, res, r, h64, p, mode="greedy", tau=1.0, seed=0, stats=None,
+              score_tol=None, scores=None):
+    """Rules R1-R4 for batch row r of one GPU step (res from run_debug)."""
+    if scores is None:
+        scores = cs.oracle_scores(h64)
+    tol = score_tol if score_tol is not None else (
+        1e-4 if cs.dtype == "f32" else 2e-2)
+    assert np.max(np.abs(res["scores"][r] - scores)) <= tol
+    keys1 = ref.select_keys(scores, mode, tau, seed)
+    check_row(gpu_token=res["tokens"][r], gpu_sel=res["clusters"][r],
+              gpu_ids=res["cand_ids"][r], gpu_logits=res["cand_logits"][r],
+              keys1=keys1, p=p, c2t=cs.head.c2t, rows=cs.rows, h64=h64,
+              dtype=cs.dtype, mode=mode, tau=tau, seed=seed, stats=stats)
+    if mode == "sample":
+        z = ref.exact_logits(cs.rows, res["cand_ids"][r], h64)
+        assert res["lse"][r] == pytest.approx(ref.logsumexp(z / tau),
+                                              abs=1e-3, rel=1e-5)
+
+
 def check_batch(cs, res, H64, p, mode="greedy", tau=1.0, seeds=None,
                 stats=None, score_tol=None):
-    B = H64.shape[0]
-    for r in range(B):
-        h64 = H64[r]
-        scores = cs.oracle_scores(h64)
-        tol = score_tol if score_tol is not None else (
-            1e-4 if cs.dtype == "f32" else 2e-2)
-        assert np.max(np.abs(res["scores"][r] - scores)) <= tol
+    for r in range(H64.shape[0]):
         seed = int(seeds[r]) if seeds is not None else 0
-        keys1 = ref.select_keys(scores, mode, tau, seed)
-        check_row(gpu_token=res["tokens"][r], gpu_sel=res["clusters"][r],
-                  gpu_ids=res["cand_ids"][r], gpu_logits=res["cand_logits"][r],
-                  keys1=keys1, p=p, c2t=cs.head.c2t, rows=cs.rows, h64=h64,
-                  dtype=cs.dtype, mode=mode, tau=tau, seed=seed, stats=stats)
-        if mode == "sample":
-            z = ref.exact_logits(cs.rows, res["cand_ids"][r], h64)
-            assert res["lse"][r] == pytest.approx(ref.logsumexp(z / tau),
-                                                  abs=1e-3, rel=1e-5)
+        check_one(cs, res, r, H64[r], p, mode, tau, seed, stats, score_tol)
+
+
+def check_steps(cs, steps, p, mode="greedy", tau=1.0, stats=None,
+                score_tol=None, workers=8):
+    """Rules R1-R4 over many GPU steps at once: steps is a list of
+    (res, H64 rows, seeds or None).  The oracle's stage-1 scores come from
+    one product per step; the per-row checks run on a pool of host threads
+    (numpy releases the interpreter lock in its kernels).  Each row gets its
+    own counters, merged in row order afterwards."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = []
+    sc = cs.oracle_scores_many(np.concatenate([H64 for _, H64, _ in steps]))
+    i = 0
+    for res, H64, seeds in steps:
+        for r in range(H64.shape[0]):
+            seed = int(seeds[r]) if seeds is not None else 0
+            jobs.append((res, r, H64[r], seed, sc[i]))
+            i += 1
+
+    def one(job):
+        res, r, h64, seed, scores = job
+        st = Stats()
+        check_one(cs, res, r, h64, p, mode, tau, seed, st, score_tol, scores)
+        return st
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(one, jobs))
+    if stats is not None:
+        for st in parts:
+            stats.merge(st)
+
+
+def report(name, st):
+    """One line per parity run, collected into the per-workload table."""
+    print(f"PARITY {name}: {st}", flush=True)
 
 
 # --------------------------------------------------------------------------
@@ -209,59 +270,97 @@ def test_llama_centroids_computed_on_device(fh):
 
 
 def test_llama_greedy_parity(fh):
+    """All 1024 hidden vectors of the Llama-shaped workload, batch 1 (the
+    single-launch decode), each call checked, self-check word included."""
     cs = case(1)
     head = cs.prepare(fh, max_batch=1, max_p=512)
     H, H64 = cs.hidden(1024)
     st = Stats()
-    for i in range(0, 1024, 16):
+    steps = []
+    for i in range(1024):
         res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, 512, "greedy")
-        check_batch(cs, res, H64[i:i + 1], 512, stats=st)
-    print(st)
+        steps.append((res, H64[i:i + 1], None))
+    assert fh.flashhead_query(head.handle, 9) == 0
+    check_steps(cs, steps, 512, stats=st)
+    report("llama3.2-1b-head greedy B=1", st)
+    assert st.rows == 1024
 
 
-def test_llama_dense_head(fh):
+@pytest.mark.parametrize("B", [64, 1])
+def test_llama_dense_head(fh, B):
+    """The in-library dense head on 64 hidden vectors: greedy, and sampled
+    at both temperatures with its lse, one batch of 64 (matrix cores) or 64
+    calls of one row (row-dot)."""
     cs = case(1)
-    dense = fh.DenseHead(cs.E_dev, max_batch=4)
-    H, H64 = cs.hidden(4, offset=100)
-    Hd = dev_tensor(H)
-    seeds = synth.make_seeds(11, 4)
-    sd = torch.from_numpy(seeds.view(np.int64)).cuda()
-    g = dense(Hd).cpu().numpy()
-    s = dense(Hd, fh.FH_MODE_SAMPLE, 1.0, sd).cpu().numpy()
-    for r in range(4):
-        z = ref.dense_logits(cs.rows, cs.wl.v, H64[r])
-        for mode, got, seed in (("greedy", g[r], 0),
-                                ("sample", s[r], int(seeds[r]))):
-            tok, m2, _, keys = ref.decode_tokens(np.arange(cs.wl.v), z, mode,
-                                                 1.0, seed)
-            if m2 > 1e-3:
-                assert got == tok
+    n = 64
+    dense = fh.DenseHead(cs.E_dev, max_batch=B)
+    H, H64 = cs.hidden(n, offset=100)
+    seeds = synth.make_seeds(11, n)
+    out = {}
+    for mode, tau in (("greedy", 1.0), ("sample", 0.7), ("sample", 1.0)):
+        toks = np.empty(n, dtype=np.int64)
+        lses = np.empty(n)
+        for lo in range(0, n, B):
+            Hd = dev_tensor(H[lo:lo + B])
+            lse = torch.empty(B, dtype=torch.float32, device="cuda")
+            if mode == "greedy":
+                t = dense(Hd, out_lse=lse)
             else:
-                assert keys[got] >= keys.max() - 1e-3
+                sd = torch.from_numpy(seeds[lo:lo + B].view(np.int64)).cuda()
+                t = dense(Hd, fh.FH_MODE_SAMPLE, tau, sd, out_lse=lse)
+            toks[lo:lo + B] = t.cpu().numpy()
+            lses[lo:lo + B] = lse.cpu().numpy()
+        out[(mode, tau)] = (toks, lses)
+    st = Stats()
+    for r in range(n):
+        z = ref.dense_logits(cs.rows, cs.wl.v, H64[r])
+        for (mode, tau), (toks, lses) in out.items():
+            st.rows += 1
+            tok, m2, lse, keys = ref.decode_tokens(np.arange(cs.wl.v), z, mode,
+                                                   tau, int(seeds[r]))
+            if m2 > 1e-3:
+                assert toks[r] == tok
+            else:
+                st.tok_band += 1
+                st.tok_diff += int(toks[r] != tok)
+                assert keys[toks[r]] >= keys.max() - 1e-3
+            assert lses[r] == pytest.approx(lse, abs=1e-3, rel=1e-5)
+    report(f"llama3.2-1b dense head greedy+sample(0.7,1.0) B={B}", st)
 
 
 @pytest.mark.parametrize("tau", [0.7, 1.0])
 def test_llama_sample_b16_parity(fh, tau):
+    """16 steps of 16 rows per temperature, a Philox key per (step, row)."""
     cs = case(3)
     head = cs.prepare(fh, max_batch=16, max_p=512)
     st = Stats()
-    for step in range(2):
+    steps = []
+    for step in range(16):
         H, H64 = cs.hidden(16, offset=16 * step)
         seeds = synth.make_seeds(step, 16)
         res = run_debug(fh, head, dev_tensor(H), 16, 512, "sample", tau,
                         torch.from_numpy(seeds.view(np.int64)).cuda())
-        check_batch(cs, res, H64, 512, "sample", tau, seeds, stats=st)
-    print(st)
+        steps.append((res, H64, seeds))
+    assert fh.flashhead_query(head.handle, 9) == 0
+    check_steps(cs, steps, 512, "sample", tau, stats=st)
+    report(f"llama3.2-1b-head-sample-b16 tau={tau} B=16", st)
+    assert st.rows == 256
 
 
 def test_llama_greedy_b64_parity(fh):
+    """16 batches of 64 rows (the batched matrix-core path)."""
     cs = case(2)
     head = cs.prepare(fh, max_batch=64, max_p=512)
-    H, H64 = cs.hidden(64)
     st = Stats()
-    res = run_debug(fh, head, dev_tensor(H), 64, 512, "greedy")
-    check_batch(cs, res, H64, 512, stats=st)
-    print(st)
+    steps = []
+    for i in range(16):
+        H, H64 = cs.hidden(64, offset=64 * i)
+        res = run_debug(fh, head, dev_tensor(H), 64, 512, "greedy")
+        steps.append((res, H64, None))
+    assert fh.flashhead_query(head.handle, 9) == 0
+    check_steps(cs, steps, 512, stats=st)
+    report("llama3.2-1b-head-b64 greedy B=64", st)
+    assert st.rows == 1024
 
 
 # --------------------------------------------------------------------------
@@ -299,15 +398,20 @@ def test_gemma_int4_codes_match_oracle(fh):
 
 @pytest.mark.parametrize("B", [1, 32])
 def test_gemma_int4_greedy_parity(fh, B):
+    """All 1024 hidden vectors at batch 1; 8 batches of 32."""
     cs = case(4)
     head = cs.prepare(fh, max_batch=B, max_p=1024)
     st = Stats()
-    n = 16 if B == 1 else 32
+    n = 1024 if B == 1 else 8 * 32
     H, H64 = cs.hidden(n)
+    steps = []
     for lo in range(0, n, B):
         res = run_debug(fh, head, dev_tensor(H[lo:lo + B]), B, 1024, "greedy")
-        check_batch(cs, res, H64[lo:lo + B], 1024, stats=st, score_tol=2e-2)
-    print(st)
+        steps.append((res, H64[lo:lo + B], None))
+    assert fh.flashhead_query(head.handle, 9) == 0
+    check_steps(cs, steps, 1024, stats=st, score_tol=2e-2)
+    report(f"gemma3-1b-head-int4 greedy B={B}", st)
+    assert st.rows == n
 
 
 # --------------------------------------------------------------------------
@@ -440,6 +544,45 @@ def test_tiny_sampling_chisquare_p_equals_c(fh):
     prob = np.exp(z - z.max())
     prob /= prob.sum()
     assert _pooled_chisq(counts, prob) > 1e-3
+
+
+@pytest.mark.parametrize("B,n", [(64, 100_000), (1, 20_000)])
+def test_tiny_head_sampling_matches_exact_marginal(fh, B, n):
+    """v = 24, c = 6, b = 4, p = 2 (fp32, d = 8): the distribution of the
+    GPU's sampled tokens against the exact marginal sum_S P(S) softmax_S(z/tau)
+    ([notes] Module 2 sampling mode and Formula 3), P(S) from enumerating the
+    ordered successive draws without replacement.  B = 64 rows per call take
+    the two-launch path, B = 1 the single launch."""
+    from scipy import special
+
+    from .test_oracle_pins import _plackett_luce_set_probs
+    head = synth.make_head(0, v=24, c=6, b=4, d=8, seed=31)
+    H = synth.make_hidden(head, 1, offset=3)
+    h64 = H[0].astype(np.float64)
+    C64 = head.C_given.astype(np.float64)
+    tau, p = 1.0, 2
+    s = ref.stage1_scores(C64, h64)
+    z = ref.exact_logits(ref.rows_accessor(head.E, "f32"), np.arange(24), h64)
+    marg = np.zeros(24)
+    for S, pS in _plackett_luce_set_probs(np.exp(s / tau), p).items():
+        T = ref.candidate_tokens(np.array(S), head.c2t)
+        marg[T] += pS * special.softmax(z[T] / tau)
+    assert marg.sum() == pytest.approx(1.0)
+    fhh = fh.FlashHead(dev_tensor(head.E), head.c2t, dev_tensor(head.C_given),
+                       max_batch=B, max_p=p)
+    Hd = dev_tensor(np.repeat(H, B, axis=0))
+    seeds = torch.from_numpy((np.arange(n, dtype=np.uint64) + (np.uint64(77) << np.uint64(32)))
+                             .view(np.int64)).cuda()
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    for lo in range(0, n, B):
+        fhh.sample(Hd, p, tau, seeds[lo:lo + B], out=out[lo:lo + B])
+    toks = out.cpu().numpy()
+    assert fh.flashhead_query(fhh.handle, 9) == 0
+    assert fh.flashhead_query(fhh.handle, 10) == (2 if B > 1 else 1)
+    counts = np.bincount(toks, minlength=24)
+    assert counts.sum() == n and np.all(counts[marg == 0] == 0)
+    assert _pooled_chisq(counts, marg) > 1e-3
+    fhh.close()
 
 
 def test_tiny_sampling_homogeneity_p8(fh):

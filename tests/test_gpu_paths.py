@@ -101,6 +101,73 @@ def test_single_launch_alternating_p(fh):
     print(st)
 
 
+def test_single_launch_buffers_stay_consistent_across_grids(fh):
+    # the single launch's grid follows p (256 workgroups at p = 512, 251 at
+    # p = 37 on this head); after every call the buffer set the next launch
+    # uses must be back in its pending state, also the merge slots of
+    # workgroups beyond the last grid; sampling with the lse checks that no
+    # stale partial reaches the merge
+    cs = case(1)
+    head = cs.prepare(fh, max_batch=1, max_p=512)
+    H, H64 = cs.hidden(8, offset=310)
+    st = Stats()
+    assert fh.flashhead_query(head.handle, 11) == 0
+    for i, p in enumerate([512, 37, 512, 1, 200, 512, 37, 512]):
+        seeds = synth.make_seeds(40 + i, 1)
+        res = run_debug(fh, head, dev_tensor(H[i:i + 1]), 1, p, "sample", 0.9,
+                        seeds_dev(seeds))
+        assert path_of(fh, head) == PATH_SINGLE_LAUNCH
+        assert fh.flashhead_query(head.handle, 11) == 0
+        check_batch(cs, res, H64[i:i + 1], p, "sample", 0.9, seeds, stats=st)
+        x = dev_tensor(H[i:i + 1])
+        head.greedy(x, p)
+        assert fh.flashhead_query(head.handle, 11) == 0
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
+def test_single_launch_plan_matches_the_device(fh):
+    # the handle's own plan inputs give the path each step takes
+    cs = case(1)
+    head = cs.prepare(fh, max_batch=4, max_p=512)
+    ncu = fh.flashhead_query(head.handle, 13)
+    bpc = fh.flashhead_query(head.handle, 12)
+    assert ncu >= 1 and bpc >= 1
+    H, _ = cs.hidden(4, offset=20)
+    for B, p in ((1, 512), (1, 37), (4, 512)):
+        head.greedy(dev_tensor(H[:B]), p)
+        path, grid = fh.flashhead_plan_step(cs.wl.c, cs.wl.b, cs.wl.d, fh.FH_DTYPE_BF16, 0,
+                                            B, p, ncu, bpc)
+        assert path_of(fh, head) == path
+        if path == PATH_SINGLE_LAUNCH:
+            assert 1 <= grid <= min(ncu, 512)
+    assert fh.flashhead_query(head.handle, 9) == 0
+
+
+def test_cooperative_launch_gives_the_same_results(fh):
+    cs = case(1)
+    plain = cs.prepare(fh, max_batch=1, max_p=512)
+    coop = fh.FlashHead(cs.E_dev, cs.head.c2t, cs.C_dev, max_batch=1, max_p=512,
+                        flags=fh.FH_FLAG_COOPERATIVE)
+    assert fh.flashhead_query(coop.handle, 14) == fh.FH_FLAG_COOPERATIVE
+    H, _ = cs.hidden(16, offset=40)
+    for i in range(16):
+        x = dev_tensor(H[i:i + 1])
+        sd = seeds_dev(synth.make_seeds(i, 1))
+        a = plain.greedy(x, 512).cpu().numpy()
+        b = coop.greedy(x, 512).cpu().numpy()
+        assert path_of(fh, coop) == PATH_SINGLE_LAUNCH
+        assert np.array_equal(a, b)
+        la = torch.empty(1, device="cuda")
+        lb = torch.empty(1, device="cuda")
+        a = plain.sample(x, 512, 0.8, sd, out_lse=la).cpu().numpy()
+        b = coop.sample(x, 512, 0.8, sd, out_lse=lb).cpu().numpy()
+        assert np.array_equal(a, b) and torch.equal(la, lb)
+    assert fh.flashhead_query(coop.handle, 9) == 0
+    assert fh.flashhead_query(coop.handle, 11) == 0
+    coop.close()
+
+
 def test_large_p_takes_the_two_launch_path(fh):
     # p above what the single launch keeps in LDS
     cs = case(1, c=4096, b=16, d=128, seed=57)

@@ -29,6 +29,7 @@ FH_QUANT_INT4_G128 = 1
 FH_QUANT_INT4_G128_MEAN = 2
 FH_MODE_GREEDY = 0
 FH_MODE_SAMPLE = 1
+FH_FLAG_COOPERATIVE = 1
 
 EXPORTED = [
     "flashhead_prepare", "flashhead_destroy", "flashhead_greedy",
@@ -37,6 +38,7 @@ EXPORTED = [
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
     "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
     "flashhead_mc_workspace_bytes", "flashhead_mc_marginal", "flashhead_kmeans",
+    "flashhead_plan_step",
 ]
 
 
@@ -45,7 +47,8 @@ class fh_desc(C.Structure):
                 ("b", C.c_int32), ("dtype", C.c_int32), ("lde", C.c_int64),
                 ("E", C.c_void_p), ("c2t", C.c_void_p), ("C", C.c_void_p),
                 ("quant", C.c_int32), ("max_batch", C.c_int32),
-                ("max_p", C.c_int32), ("stream", C.c_void_p)]
+                ("max_p", C.c_int32), ("stream", C.c_void_p),
+                ("flags", C.c_int32)]
 
 
 class fh_debug(C.Structure):
@@ -109,6 +112,9 @@ def _load() -> C.CDLL:
     lib.flashhead_kmeans.argtypes = [vp, i64, i32, i32, i64, i32, vp, i32, vp, vp,
                                      C.POINTER(i32), vp]
     lib.flashhead_kmeans.restype = C.c_int
+    lib.flashhead_plan_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        C.POINTER(i32)]
+    lib.flashhead_plan_step.restype = C.c_int
     return lib
 
 
@@ -177,7 +183,7 @@ def _debug(dbg: Optional[dict]):
 
 def flashhead_prepare(E, c2t: np.ndarray, C_init=None, *, v=None, d=None,
                       lde=None, quant: int = FH_QUANT_NONE, max_batch: int = 1,
-                      max_p: int = 1, stream=None) -> int:
+                      max_p: int = 1, flags: int = 0, stream=None) -> int:
     """Returns an opaque handle (int).  E, C_init: device tensors."""
     c2t = np.ascontiguousarray(c2t, dtype=np.int32)
     c, b = c2t.shape
@@ -186,11 +192,22 @@ def flashhead_prepare(E, c2t: np.ndarray, C_init=None, *, v=None, d=None,
     lde = lde if lde is not None else E.stride(0)
     desc = fh_desc(v, d, c, b, dtype_code(E), lde, _ptr(E),
                    c2t.ctypes.data, _ptr(C_init), quant, max_batch, max_p,
-                   _stream(stream))
+                   _stream(stream), flags)
     h = C.c_void_p()
     _check(lib.flashhead_prepare(C.byref(desc), C.byref(h)),
            "flashhead_prepare")
     return h.value
+
+
+def flashhead_plan_step(c: int, b: int, d: int, dtype: int, quant: int, B: int,
+                        p: int, num_cu: int, blocks_per_cu: int):
+    """Host-only: (path, grid) a decode step of this shape takes."""
+    g = C.c_int32()
+    st = lib.flashhead_plan_step(c, b, d, dtype, quant, B, p, num_cu, blocks_per_cu,
+                                 C.byref(g))
+    if st < 0:
+        raise FlashHeadError(st, "flashhead_plan_step")
+    return st, g.value
 
 
 def flashhead_destroy(handle: int) -> None:
@@ -304,7 +321,7 @@ class FlashHead:
     """A prepared head on the current device (see include/flashhead.h)."""
 
     def __init__(self, E, c2t, C_init=None, *, quant: int = FH_QUANT_NONE,
-                 max_batch: int = 1, max_p: int = 1, stream=None):
+                 max_batch: int = 1, max_p: int = 1, flags: int = 0, stream=None):
         self.E = E                      # borrowed: keep it alive
         self.c, self.b = np.asarray(c2t).shape
         self.v, self.d = E.shape
@@ -312,7 +329,7 @@ class FlashHead:
         self.max_batch, self.max_p = max_batch, max_p
         self.handle = flashhead_prepare(E, c2t, C_init, quant=quant,
                                         max_batch=max_batch, max_p=max_p,
-                                        stream=stream)
+                                        flags=flags, stream=stream)
 
     def close(self):
         if getattr(self, "handle", None):

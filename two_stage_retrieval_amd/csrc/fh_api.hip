@@ -37,6 +37,8 @@ struct fh_handle {
   float2* part_lse = nullptr;
   // single-launch batch-1 decode
   int num_cu = 0;
+  int b1_blocks_per_cu = 0;         // decode workgroups one compute unit holds at once
+  int flags = 0;                    // FH_FLAG_*
   float* b1_keys = nullptr;         // 2 x key_stride(c), all bits set between launches
   uint64_t* b1_slots = nullptr;     // 2 x kDecodeB1SlotStride words, zero between launches
   float2* b1_lse = nullptr;         // kDecodeB1SlotStride words
@@ -179,6 +181,8 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   hipStream_t s = static_cast<hipStream_t>(ds->stream);
   FH_TRY(hipGetDevice(&h->device));
   FH_TRY(hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device));
+  FH_TRY(decode_b1_occupancy(h->dtype, h->quant != FH_QUANT_NONE, (int)(h->row_bytes / 16),
+                             ds->c, &h->b1_blocks_per_cu));
   const int64_t v = ds->v;
   const int c = ds->c, b = ds->b, d = ds->d;
   FH_TRY(alloc(h, &h->c2t, (size_t)v * 4));
@@ -255,6 +259,28 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   return FH_OK;
 }
 
+// The kernels a step of this shape takes: 1 the single-launch batch-1 decode
+// (*grid workgroups), 2 stage 1 and stage 2 as separate row-dot launches,
+// 3 the batched matrix-core path.  The single launch's workgroups wait on
+// one another, so it is taken only when every one of them can be resident
+// at once.  The row-dot launches need no such guarantee: in each batch row
+// one workgroup waits for the others, which never wait, so they progress as
+// long as the device holds more than B workgroups.
+int plan_path(int c, int b, int d, int64_t row_bytes, int dtype, bool int4, int B, int p,
+              int num_cu, int blocks_per_cu, int* grid) {
+  *grid = 0;
+  if (B >= 2 && b % 16 == 0 && batched_supported(dtype, d, B, int4)) return 3;
+  if (B == 1 && stage1_selects(c)) {
+    const int g = decode_b1_grid(c, p, (int)(row_bytes / 16), (c + 15) / 16, (int64_t)p * b,
+                                 int4, num_cu);
+    if (g > 0 && g <= kMaxGrid && (int64_t)g <= (int64_t)num_cu * blocks_per_cu) {
+      *grid = g;
+      return 1;
+    }
+  }
+  return 2;
+}
+
 int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
               const uint64_t* seeds, int32_t* out, float* out_lse, const fh_debug* dbg,
               void* stream) {
@@ -287,7 +313,10 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
 
 
   const bool int4 = h->quant != FH_QUANT_NONE;
-  const bool batched = B >= 2 && h->b % 16 == 0 && batched_supported(h->dtype, h->d, B, int4);
+  int b1_grid = 0;
+  const int path = plan_path(h->c, h->b, h->d, h->row_bytes, h->dtype, int4, B, p, h->num_cu,
+                             h->b1_blocks_per_cu, &b1_grid);
+  const bool batched = path == 3;
 
   // stage 1 (+ selection by each batch row's last block on the GEMV path)
   Stage1Args s1{};
@@ -309,7 +338,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.sample = sample;
   s1.inv_tau = inv_tau;
   s1.seeds = seeds;
-  s1.select = (!batched && stage1_selects(h->c)) ? 1 : 0;
+  s1.select = (!batched && stage1_selects(h->c)) ? 1 : 0;  // path 1 selects inside its launch too
   s1.p = p;
   s1.zcut = select_zcut(h->c, p);
   s1.counters = h->counters;
@@ -347,7 +376,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   };
 
   // batch 1: the whole step in one launch when the shape allows it
-  if (B == 1 && !batched && s1.select) {
+  if (path == 1) {
     DecodeB1Args f{};
     f.s1 = s1;
     f.s2 = gather_args();
@@ -358,9 +387,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     f.epoch = h->b1_epoch;
     f.go = h->b1_go;
     f.slot_stride = kDecodeB1SlotStride;
-    const int grid = decode_b1_grid(f, int4, h->num_cu);
-    if (grid > 0 && grid <= kMaxGrid) {
-      FH_TRY(launch_decode_b1(f, h->dtype, int4, grid, s, t1));
+    {
+      FH_TRY(launch_decode_b1(f, h->dtype, int4, b1_grid,
+                              (h->flags & FH_FLAG_COOPERATIVE) != 0, s, t1));
       if (t2) {  // selection and stage 2 ran inside the one launch
         (void)hipEventRecord(t2->start, s);
         (void)hipEventRecord(t2->stop, s);
@@ -493,6 +522,21 @@ extern "C" {
 
 const char* flashhead_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
+int flashhead_plan_step(int32_t c, int32_t b, int32_t d, int32_t dtype, int32_t quant, int32_t B,
+                        int32_t p, int32_t num_cu, int32_t blocks_per_cu, int32_t* grid) {
+  if (!grid) return FH_ERR_INVALID_ARG;
+  *grid = 0;
+  const int es = esize_of(dtype);
+  if (c < 1 || b < 1 || d < 1 || !es || B < 1 || B > FH_MAX_BATCH || p < 1 || p > c ||
+      num_cu < 1 || blocks_per_cu < 0 || quant < FH_QUANT_NONE || quant > FH_QUANT_INT4_G128_MEAN)
+    return FH_ERR_INVALID_ARG;
+  int g = 0;
+  const int path = plan_path(c, b, d, (int64_t)d * es, dtype, quant != FH_QUANT_NONE, B, p,
+                             num_cu, blocks_per_cu, &g);
+  *grid = g;
+  return path;
+}
+
 int flashhead_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes < 16 || bytes % 16 || !aligned16(buf)) return FH_ERR_INVALID_ARG;
   int dev = 0, ncu = 0;
@@ -536,6 +580,7 @@ int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
     return FH_ERR_UNSUPPORTED;
   if (ds->quant != FH_QUANT_NONE && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
     return FH_ERR_UNSUPPORTED;
+  if (ds->flags & ~FH_FLAG_COOPERATIVE) return FH_ERR_INVALID_ARG;
   // C2T must be a permutation of [0, v) (equal-size clusters, dense table)
   {
     std::vector<uint8_t> seen((size_t)ds->v, 0);
@@ -557,6 +602,7 @@ int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
   h->max_p = ds->max_p;
   h->esize = es;
   h->row_bytes = row_bytes;
+  h->flags = ds->flags;
   const int st = prepare_impl(ds, h);
   if (st != FH_OK) {
     (void)hipStreamSynchronize(static_cast<hipStream_t>(ds->stream));
@@ -839,6 +885,36 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
     case 7: *value = h->max_p; break;
     case 8: *value = h->bytes; break;
     case 10: *value = h->last_path; break;
+    case 12: *value = h->b1_blocks_per_cu; break;
+    case 13: *value = h->num_cu; break;
+    case 14: *value = h->flags; break;
+    case 11: {  // the single launch's buffer set for the next launch
+      uint32_t ep = 0, go[2] = {0u, 0u};
+      FH_TRY(hipMemcpy(&ep, h->b1_epoch, 4, hipMemcpyDeviceToHost));
+      FH_TRY(hipMemcpy(go, h->b1_go, 8, hipMemcpyDeviceToHost));
+      const int set = (int)(ep & 1u);
+      const int64_t ks = key_stride(h->c);
+      std::vector<uint32_t> keys((size_t)ks);
+      std::vector<int32_t> sel((size_t)kDecodeB1MaxP);
+      std::vector<uint64_t> slots((size_t)kDecodeB1SlotStride);
+      FH_TRY(hipMemcpy(keys.data(), h->b1_keys + set * ks, (size_t)ks * 4,
+                       hipMemcpyDeviceToHost));
+      FH_TRY(hipMemcpy(sel.data(), h->b1_sel + set * kDecodeB1MaxP, (size_t)kDecodeB1MaxP * 4,
+                       hipMemcpyDeviceToHost));
+      FH_TRY(hipMemcpy(slots.data(), h->b1_slots + set * kDecodeB1SlotStride,
+                       (size_t)kDecodeB1SlotStride * 8, hipMemcpyDeviceToHost));
+      int64_t bits = 0;
+      for (int k = 0; k < h->c; ++k)
+        if (keys[(size_t)k] != 0xFFFFFFFFu) bits |= 1;
+      for (int i = 0; i < kDecodeB1MaxP; ++i)
+        if (sel[(size_t)i] != -1) bits |= 2;
+      for (int j = 0; j < kDecodeB1MaxGrid; ++j)
+        if (slots[(size_t)j * 16] != 0ull) bits |= 4;
+      if (go[set] != 0u) bits |= 8;
+      if ((uint64_t)ep != (h->b1_launches & 0xFFFFFFFFull)) bits |= 16;
+      *value = bits;
+      break;
+    }
     case 9: {  // selection error flag (synchronous read and clear)
       uint32_t e = 0;
       FH_TRY(hipMemcpy(&e, h->error, 4, hipMemcpyDeviceToHost));

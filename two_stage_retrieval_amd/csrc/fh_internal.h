@@ -211,9 +211,16 @@ float select_zcut(int c, int p);
 hipError_t launch_stage1(const Stage1Args& a, int dtype, bool int4, int B, hipStream_t s,
                          const Timing* tm = nullptr);
 bool stage1_selects(int c);
-// grid of the single-launch batch-1 decode (0: not available for this shape)
-int decode_b1_grid(const DecodeB1Args& a, bool int4, int num_cu);
-hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid,
+// Workgroups of the single-launch batch-1 decode for a shape (0: the shape
+// does not take it), one per compute unit at most: c clusters, p probes,
+// nchunk 16-byte chunks per row, ntiles INT4 tiles, nrows = p * b candidate
+// rows.  Pure host arithmetic.
+int decode_b1_grid(int c, int p, int nchunk, int ntiles, int64_t nrows, bool int4, int num_cu);
+// Workgroups of the decode kernel that the shape uses that one compute unit
+// holds at once (the occupancy API), in *blocks.
+hipError_t decode_b1_occupancy(int dtype, bool int4, int nchunk, int c, int* blocks);
+// coop: through the cooperative launch API (all workgroups resident together)
+hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid, bool coop,
                             hipStream_t s, const Timing* tm = nullptr);
 hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
                                  const int32_t* c2t, int c, int b, void* C, hipStream_t s);

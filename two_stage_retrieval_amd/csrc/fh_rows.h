@@ -385,10 +385,9 @@ __device__ __forceinline__ bool merge_decode(const RowdotArgs& a, int r, int nbl
 // decode): workgroups other than 0 store their partial key into their slot
 // of `slot` (zero = not yet written; a published key is never zero) after
 // their lse partial, if any, has been performed; workgroup 0's wave 0 polls
-// the slots until every one is written and folds them.  Every workgroup also
-// clears its slot of `slot_next`, the set the next launch uses.  Slot j is
-// word j * kSlotWords: one 128-byte line per writer.  Returns true in
-// workgroup 0.
+// the slots until every one is written and folds them.  Workgroup 0 also
+// clears all of `slot_next`, the set the next launch uses.  Slot j is word
+// j * kSlotWords: one 128-byte line per writer.  Returns true in workgroup 0.
 // ---------------------------------------------------------------------------
 constexpr int kSlotWords = 16;  // u64 words per slot
 template <int NT>
@@ -415,7 +414,12 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
     bb = ms.best[w] > bb ? ms.best[w] : bb;
     ll = lse_merge(ll, Lse{ms.lse[w].x, ms.lse[w].y});
   }
-  if (t == 0) slot_next[block * kSlotWords] = 0ull;
+  // Workgroup 0 clears every slot of the set the next launch uses, not only
+  // the slots of this launch's grid: the grid depends on p, so a slot beyond
+  // it may still hold a key from two launches back.  Nothing in this launch
+  // reads or writes that set.
+  if (block == 0)
+    for (int j = t; j < kDecodeB1MaxGrid; j += NT) slot_next[j * kSlotWords] = 0ull;
   if (block != 0) {
     if (t == 0) {
       if (a.out_lse) {

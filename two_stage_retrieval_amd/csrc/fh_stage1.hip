@@ -427,13 +427,14 @@ hipError_t launch_stage1(const Stage1Args& a, int dtype, bool int4, int B, hipSt
 // ---------------------------------------------------------------------------
 // single-launch batch-1 decode
 // ---------------------------------------------------------------------------
-int decode_b1_grid(const DecodeB1Args& a, bool int4, int num_cu) {
-  if (!stage1_selects(a.s1.c) || num_cu < 1 || a.s1.p > kDecodeB1MaxP) return 0;
-  const int nch = (a.s2.nchunk + kWave - 1) / kWave;
+int decode_b1_grid(int c, int p, int nchunk, int ntiles, int64_t nrows, bool int4,
+                   int num_cu) {
+  if (!stage1_selects(c) || num_cu < 1 || p < 1 || p > kDecodeB1MaxP) return 0;
+  const int nch = (nchunk + kWave - 1) / kWave;
   if (nch < 1 || nch > 8) return 0;
   const int R = nch <= 2 ? 8 : 4;
-  const int64_t units1 = int4 ? a.s1.ntiles : (a.s1.c + kS1Rows - 1) / kS1Rows;
-  const int64_t units2 = (a.s2.nrows + R - 1) / R;
+  const int64_t units1 = int4 ? ntiles : (c + kS1Rows - 1) / kS1Rows;
+  const int64_t units2 = (nrows + R - 1) / R;
   const int64_t units = units1 > units2 ? units1 : units2;
   int64_t g = (units + kS1Waves - 1) / kS1Waves;
   if (g > num_cu) g = num_cu;  // one resident workgroup per compute unit
@@ -441,46 +442,101 @@ int decode_b1_grid(const DecodeB1Args& a, bool int4, int num_cu) {
   return (int)(g < 1 ? 1 : g);
 }
 
+// One launch of the decode kernel.  COOPERATIVE: through the cooperative
+// launch API, whose runtime guarantees that all workgroups are resident
+// together (the kernel uses no grid barrier of that API; the events are then
+// recorded around the launch instead of exactly at the kernel).
+template <typename K>
+static hipError_t launch_one(K kernel, const DecodeB1Args& a, int grid, bool coop, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1) {
+  const dim3 g(grid), block(kS1Threads);
+  if (!coop) {
+    hipExtLaunchKernelGGL(kernel, g, block, 0, s, e0, e1, 0, a);
+    return hipGetLastError();
+  }
+  if (e0) (void)hipEventRecord(e0, s);
+  DecodeB1Args copy = a;
+  void* params[] = {&copy};
+  const hipError_t e =
+      hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), g, block, params, 0, s);
+  if (e != hipSuccess) return e;
+  if (e1) (void)hipEventRecord(e1, s);
+  return hipSuccess;
+}
+
 template <typename TE, int NCH, bool INT4>
-static hipError_t launch_b1_nch(const DecodeB1Args& a, int grid, hipStream_t s, hipEvent_t e0,
-                                hipEvent_t e1) {
+static hipError_t launch_b1_nch(const DecodeB1Args& a, int grid, bool coop, hipStream_t s,
+                                hipEvent_t e0, hipEvent_t e1) {
   constexpr int R = NCH <= 2 ? 8 : 4;
   const int c = a.s1.c;
-  const dim3 g(grid), block(kS1Threads);
-  if (c <= kS1Threads * 4) {
-    hipExtLaunchKernelGGL((decode_b1_kernel<TE, NCH, R, 4, INT4>), g, block, 0, s, e0, e1, 0, a);
-  } else if (c <= kS1Threads * 16) {
-    hipExtLaunchKernelGGL((decode_b1_kernel<TE, NCH, R, 16, INT4>), g, block, 0, s, e0, e1, 0, a);
-  } else if (c <= kS1Threads * 32) {
-    hipExtLaunchKernelGGL((decode_b1_kernel<TE, NCH, R, 32, INT4>), g, block, 0, s, e0, e1, 0, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (c <= kS1Threads * 4)
+    return launch_one(decode_b1_kernel<TE, NCH, R, 4, INT4>, a, grid, coop, s, e0, e1);
+  if (c <= kS1Threads * 16)
+    return launch_one(decode_b1_kernel<TE, NCH, R, 16, INT4>, a, grid, coop, s, e0, e1);
+  if (c <= kS1Threads * 32)
+    return launch_one(decode_b1_kernel<TE, NCH, R, 32, INT4>, a, grid, coop, s, e0, e1);
+  return hipErrorInvalidValue;
 }
 
 template <typename TE, bool INT4>
-static hipError_t launch_b1_t(const DecodeB1Args& a, int grid, hipStream_t s, hipEvent_t e0,
-                              hipEvent_t e1) {
+static hipError_t launch_b1_t(const DecodeB1Args& a, int grid, bool coop, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
   switch ((a.s2.nchunk + kWave - 1) / kWave) {
-    case 1: return launch_b1_nch<TE, 1, INT4>(a, grid, s, e0, e1);
-    case 2: return launch_b1_nch<TE, 2, INT4>(a, grid, s, e0, e1);
-    case 3: return launch_b1_nch<TE, 3, INT4>(a, grid, s, e0, e1);
-    case 4: return launch_b1_nch<TE, 4, INT4>(a, grid, s, e0, e1);
-    case 5: return launch_b1_nch<TE, 5, INT4>(a, grid, s, e0, e1);
-    case 6: return launch_b1_nch<TE, 6, INT4>(a, grid, s, e0, e1);
-    case 7: return launch_b1_nch<TE, 7, INT4>(a, grid, s, e0, e1);
-    case 8: return launch_b1_nch<TE, 8, INT4>(a, grid, s, e0, e1);
+    case 1: return launch_b1_nch<TE, 1, INT4>(a, grid, coop, s, e0, e1);
+    case 2: return launch_b1_nch<TE, 2, INT4>(a, grid, coop, s, e0, e1);
+    case 3: return launch_b1_nch<TE, 3, INT4>(a, grid, coop, s, e0, e1);
+    case 4: return launch_b1_nch<TE, 4, INT4>(a, grid, coop, s, e0, e1);
+    case 5: return launch_b1_nch<TE, 5, INT4>(a, grid, coop, s, e0, e1);
+    case 6: return launch_b1_nch<TE, 6, INT4>(a, grid, coop, s, e0, e1);
+    case 7: return launch_b1_nch<TE, 7, INT4>(a, grid, coop, s, e0, e1);
+    case 8: return launch_b1_nch<TE, 8, INT4>(a, grid, coop, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid,
+template <typename TE, int NCH, bool INT4>
+static hipError_t occ_nch(int c, int* blocks) {
+  constexpr int R = NCH <= 2 ? 8 : 4;
+  if (c <= kS1Threads * 4)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks, decode_b1_kernel<TE, NCH, R, 4, INT4>, kS1Threads, 0);
+  if (c <= kS1Threads * 16)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks, decode_b1_kernel<TE, NCH, R, 16, INT4>, kS1Threads, 0);
+  if (c <= kS1Threads * 32)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks, decode_b1_kernel<TE, NCH, R, 32, INT4>, kS1Threads, 0);
+  return hipSuccess;  // more clusters than the single launch selects: none
+}
+
+template <typename TE, bool INT4>
+static hipError_t occ_t(int nchunk, int c, int* blocks) {
+  switch ((nchunk + kWave - 1) / kWave) {
+    case 1: return occ_nch<TE, 1, INT4>(c, blocks);
+    case 2: return occ_nch<TE, 2, INT4>(c, blocks);
+    case 3: return occ_nch<TE, 3, INT4>(c, blocks);
+    case 4: return occ_nch<TE, 4, INT4>(c, blocks);
+    case 5: return occ_nch<TE, 5, INT4>(c, blocks);
+    case 6: return occ_nch<TE, 6, INT4>(c, blocks);
+    case 7: return occ_nch<TE, 7, INT4>(c, blocks);
+    case 8: return occ_nch<TE, 8, INT4>(c, blocks);
+    default: return hipSuccess;  // rows wider than any instantiation: none
+  }
+}
+
+hipError_t decode_b1_occupancy(int dtype, bool int4, int nchunk, int c, int* blocks) {
+  *blocks = 0;
+  if (int4) return occ_t<bf16_t, true>(nchunk, c, blocks);
+  if (dtype == FH_DTYPE_BF16) return occ_t<bf16_t, false>(nchunk, c, blocks);
+  return occ_t<float, false>(nchunk, c, blocks);
+}
+
+hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid, bool coop,
                             hipStream_t s, const Timing* tm) {
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
-  if (int4) return launch_b1_t<bf16_t, true>(a, grid, s, e0, e1);
-  if (dtype == FH_DTYPE_BF16) return launch_b1_t<bf16_t, false>(a, grid, s, e0, e1);
-  return launch_b1_t<float, false>(a, grid, s, e0, e1);
+  if (int4) return launch_b1_t<bf16_t, true>(a, grid, coop, s, e0, e1);
+  if (dtype == FH_DTYPE_BF16) return launch_b1_t<bf16_t, false>(a, grid, coop, s, e0, e1);
+  return launch_b1_t<float, false>(a, grid, coop, s, e0, e1);
 }
 
 }  // namespace fh
