@@ -240,6 +240,26 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype,
                float* out_lse, void* workspace, void* stream);
 
 /*
+ * dense_head for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that forbid hipMalloc): the same kernels and
+ * results, with the workspace in a fixed array inside the library instead
+ * of a caller's buffer.  The array holds the workspace of
+ * FH_DENSE_STATIC_MAX_BATCH rows (dense_head_workspace_bytes(16) bytes,
+ * about 2.1 MB); each device the library runs on keeps its own copy until
+ * the process ends.  The call allocates nothing; its arrival counters are
+ * cleared by a kernel on `stream` before use.  All calls on one device
+ * share that device's array, so calls that overlap in time on one device
+ * (other streams, other threads) race and must not be made.
+ *   B          1..FH_DENSE_STATIC_MAX_BATCH (FH_ERR_INVALID_ARG beyond)
+ *   the other arguments as for dense_head
+ */
+#define FH_DENSE_STATIC_MAX_BATCH 16
+int dense_head_static(const void* E, int64_t v, int32_t d, int32_t dtype,
+                      int64_t lde, const void* H, int32_t B, int32_t mode,
+                      float tau, const uint64_t* seeds, int32_t* out_tokens,
+                      float* out_lse, void* stream);
+
+/*
  * Equal-size spherical k-means (notes, Module 1; Formula 4, the summed
  * cosine of each token to its cluster's unit centroid; Formula 5, the
  * centroid is the unit-normalised mean of the cluster's rows): the offline

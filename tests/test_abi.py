@@ -248,3 +248,15 @@ def test_plan_step_rejects_bad_sizes(fh):
                  (8016, 16, 2048, BF, 0, 1, 512, 0, 1)):     # no compute unit
         assert lib.flashhead_plan_step(*args, C.byref(g)) == inv
         assert g.value == 0
+
+
+def test_dense_head_static_host_checks(fh):
+    # rejected on the host, before the library's fixed workspace is looked up
+    lib = fh.lib
+    inv = fh.FH_ERR_INVALID_ARG
+    assert fh.FH_DENSE_STATIC_MAX_BATCH == 16
+    assert fh.dense_head_workspace_bytes(16) <= 4 << 20
+    for B in (17, 64):
+        assert lib.dense_head_static(FAKE_DEV, 4096, 256, fh.FH_DTYPE_F32, 256, FAKE_DEV, B,
+                                     fh.FH_MODE_GREEDY, C.c_float(1.0), None, FAKE_DEV, None,
+                                     None) == inv

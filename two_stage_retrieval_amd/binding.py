@@ -38,8 +38,9 @@ EXPORTED = [
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
     "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
     "flashhead_mc_workspace_bytes", "flashhead_mc_marginal", "flashhead_kmeans",
-    "flashhead_plan_step",
+    "flashhead_plan_step", "dense_head_static",
 ]
+FH_DENSE_STATIC_MAX_BATCH = 16
 
 
 class fh_desc(C.Structure):
@@ -87,6 +88,9 @@ def _load() -> C.CDLL:
     lib.dense_head.argtypes = [vp, i64, i32, i32, i64, vp, i32, i32, f32, vp,
                                vp, vp, vp, vp]
     lib.dense_head.restype = C.c_int
+    lib.dense_head_static.argtypes = [vp, i64, i32, i32, i64, vp, i32, i32, f32, vp,
+                                      vp, vp, vp]
+    lib.dense_head_static.restype = C.c_int
     lib.flashhead_status_string.argtypes = [C.c_int]
     lib.flashhead_status_string.restype = C.c_char_p
     lib.flashhead_stream_read.argtypes = [vp, i64, vp, vp]
@@ -262,6 +266,17 @@ def dense_head(E, H, B: int, mode: int, tau: float, seeds, out_tokens,
     _check(lib.dense_head(_ptr(E), v, d, dtype_code(E), lde, _ptr(H), B, mode,
                           tau, _ptr(seeds), _ptr(out_tokens), _ptr(out_lse),
                           _ptr(workspace), _stream(stream)), "dense_head")
+
+
+def dense_head_static(E, H, B: int, mode: int, tau: float, seeds, out_tokens,
+                      out_lse=None, *, v=None, d=None, lde=None, stream=None) -> None:
+    """dense_head with the library's own fixed workspace (no allocation)."""
+    v = v if v is not None else E.shape[0]
+    d = d if d is not None else E.shape[1]
+    lde = lde if lde is not None else E.stride(0)
+    _check(lib.dense_head_static(_ptr(E), v, d, dtype_code(E), lde, _ptr(H), B, mode,
+                                 tau, _ptr(seeds), _ptr(out_tokens), _ptr(out_lse),
+                                 _stream(stream)), "dense_head_static")
 
 
 def flashhead_kmeans(E, c: int, init, max_iter: int, out_c2t, out_centroids=None, *,

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -518,6 +519,43 @@ static McLayout mc_layout(int c, int n, int p, int q) {
   return L;
 }
 
+namespace {
+
+int dense_impl(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, const void* H,
+               int32_t B, int32_t mode, float tau, const uint64_t* seeds, int32_t* out_tokens,
+               float* out_lse, void* workspace, bool clear_counters, void* stream);
+
+// The workspace of dense_head_static: the layout of dense_head's workspace
+// for FH_DENSE_STATIC_MAX_BATCH rows, one copy per device, held until the
+// process ends.  Host code never uses this name as an address: each
+// device's copy is found once through hipGetSymbolAddress.
+constexpr size_t kStaticScratchBytes =
+    (size_t)FH_DENSE_STATIC_MAX_BATCH * (kArriveWords * 4 + kDenseMaxGrid * 16);
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (looked up on the first
+// call on that device, with the device current).
+int static_scratch(void** out) {
+  int dev = -1;
+  FH_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return FH_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    FH_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return FH_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FH_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* flashhead_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
@@ -725,6 +763,29 @@ size_t dense_head_workspace_bytes(int32_t B) {
 int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, const void* H,
                int32_t B, int32_t mode, float tau, const uint64_t* seeds, int32_t* out_tokens,
                float* out_lse, void* workspace, void* stream) {
+  if (!workspace) return FH_ERR_INVALID_ARG;
+  return dense_impl(E, v, d, dtype, lde, H, B, mode, tau, seeds, out_tokens, out_lse,
+                    workspace, false, stream);
+}
+
+int dense_head_static(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde,
+                      const void* H, int32_t B, int32_t mode, float tau, const uint64_t* seeds,
+                      int32_t* out_tokens, float* out_lse, void* stream) {
+  if (B > FH_DENSE_STATIC_MAX_BATCH) return FH_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  const int st = static_scratch(&ws);
+  if (st != FH_OK) return st;
+  return dense_impl(E, v, d, dtype, lde, H, B, mode, tau, seeds, out_tokens, out_lse, ws, true,
+                    stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int dense_impl(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, const void* H,
+               int32_t B, int32_t mode, float tau, const uint64_t* seeds, int32_t* out_tokens,
+               float* out_lse, void* workspace, bool clear_counters, void* stream) {
   if (!E || !H || !out_tokens || !workspace) return FH_ERR_INVALID_ARG;
   if (v < 1 || d < 1 || lde < d || B < 1 || B > FH_MAX_BATCH) return FH_ERR_INVALID_ARG;
   if (mode != FH_MODE_GREEDY && mode != FH_MODE_SAMPLE) return FH_ERR_INVALID_ARG;
@@ -780,9 +841,20 @@ int dense_head(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, 
   a.seeds = seeds;
   const int gx = rowdot_grid(v, a.nchunk, kRowDense);
   if (gx > kDenseMaxGrid) return FH_ERR_UNSUPPORTED;
+  // the shared array keeps the last call's contents: its arrival counters
+  // are cleared before use (a fill kernel, which a graph may capture)
+  if (clear_counters)
+    FH_TRY(launch_fill_u32(ws_ctr, 0u, (int64_t)nb * kArriveWords,
+                           static_cast<hipStream_t>(stream)));
   FH_TRY(launch_rowdot(a, kRowDense, dtype, B, gx, static_cast<hipStream_t>(stream)));
   return FH_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+
 
 int flashhead_kmeans(const void* E, int64_t v, int32_t d, int32_t dtype, int64_t lde, int32_t c,
                      const int32_t* init, int32_t max_iter, int32_t* c2t, double* centroids,

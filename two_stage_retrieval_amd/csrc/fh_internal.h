@@ -233,6 +233,8 @@ hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s,
                               const Timing* tm = nullptr);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int num_cu,
                               hipStream_t s);
+// n words of p set to value by a kernel on s
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s);
 // Equal-size spherical k-means (fh_kmeans.hip).  E device, init host
 // (c distinct ids), c2t device out (c x b, rows ascending), centroids device
 // out (c x d float64) or null.  Blocking: allocates its own workspace and

@@ -119,4 +119,22 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fill of n 32-bit words (for memory a caller may capture into a graph,
+// where a memset node is avoided).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, uint32_t value, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t grid = (n + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)grid), dim3(256), 0, s, p, value, n);
+  return hipGetLastError();
+}
+
 }  // namespace fh
