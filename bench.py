@@ -114,8 +114,15 @@ def main():
                     help="time N iterations of the equal-size spherical k-means "
                          "(Module 1) on the workload's E instead of the decode step; "
                          "prints its own JSON line")
+    ap.add_argument("--bf16-stage1", action="store_true",
+                    help="score the centroids in bf16 even where the workload names INT4")
     ap.add_argument("--flags", type=int, default=0,
                     help="fh_desc.flags for the head (1: cooperative single launch)")
+    ap.add_argument("--timeline", type=int, default=0, metavar="N",
+                    help="load the measurement build (libflashhead_trace.so) and print the "
+                         "median timeline of N cold batch-1 calls instead of the bench line")
+    ap.add_argument("--timeline-warm", action="store_true",
+                    help="with --timeline: no cache flush before the calls")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run --steps cold calls and a 256 MiB copy-like kernel, then exit "
                          "(for rocprofv3 --pmc runs)")
@@ -126,6 +133,8 @@ def main():
               "notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.timeline:
+        os.environ["FLASHHEAD_LIB_VARIANT"] = "trace"
     import torch
 
     from two_stage_retrieval_amd import binding as fhb
@@ -140,6 +149,9 @@ def main():
         p = args.p or wl.p
         wl = dataclasses.replace(wl, name=f"{wl.name}-c{c}-b{b}-p{p}", c=c, b=b, v=c * b, p=p)
     B = args.batch or wl.batches[0]
+    if args.bf16_stage1 and wl.quant != "none":
+        import dataclasses
+        wl = dataclasses.replace(wl, name=wl.name + "-bf16-stage1", quant="none")
     int4 = wl.quant == "int4_g128"
     sample = wl.mode == "sample"
     tau = args.tau if sample else 1.0
@@ -190,6 +202,10 @@ def main():
 
     if args.mc:
         mc_bench(args, wl, head, H, H_dev, fh, evict, int4)
+        fh.close()
+        return
+    if args.timeline:
+        timeline_bench(args, wl, fh, call, evict, B)
         fh.close()
         return
 
@@ -373,6 +389,103 @@ def main():
     }
     fh.close()
     print(json.dumps(res), flush=True)
+
+
+# events of the single-launch decode's measurement build (fh_trace.h)
+_TL_BLOCK = {"start": 0, "keys_seen": 1, "sel_published": 2, "s2_entries": 3,
+             "partial_published": 4, "token": 5, "end": 6}
+_TL_WAVE = {"s1_issued": 0, "s1_done": 1, "s2_done": 2}
+_TL_SEL_POINTS = (0, 2, 3, 4, 5, 6, 7)
+
+
+def parse_timeline(words, khz):
+    """µs from the first workgroup's start for each event of one launch."""
+    nb, nw = 512, 8192
+    blk = words[:8 * nb].reshape(8, nb).astype(np.int64)
+    wav = words[8 * nb:8 * nb + 4 * nw].reshape(4, nw).astype(np.int64)
+    sel = words[8 * nb + 4 * nw:8 * nb + 4 * nw + 32].reshape(16, 2).astype(np.int64)
+    cnt = words[8 * nb + 4 * nw + 32:8 * nb + 4 * nw + 48].astype(np.int64)
+    grid = int(np.count_nonzero(blk[0]))
+    t0 = blk[0][:grid].min()
+    us = lambda t: (t - t0) * 1e3 / khz  # noqa: E731
+    waves = wav[:, :grid * 8]
+    out = {"grid": grid,
+           "last_workgroup_start": us(blk[0][:grid].max()),
+           "stage1_requests_issued_all": us(waves[0][waves[0] > 0].max()),
+           "stage1_done_median_wave": us(np.median(waves[1][waves[1] > 0])),
+           "stage1_done_all": us(waves[1][waves[1] > 0].max()),
+           "keys_seen_by_wg0": us(blk[1][0]),
+           "selection_published": us(blk[2][0]),
+           "stage2_entries_all": us(blk[3][1:grid].max()) if grid > 1 else None,
+           "stage2_done_median_wave": us(np.median(waves[2][waves[2] > 0])),
+           "stage2_done_all": us(waves[2][waves[2] > 0].max()),
+           "partials_published_all": us(blk[4][1:grid].max()) if grid > 1 else None,
+           "token_written": us(blk[5][0]),
+           "last_workgroup_end": us(blk[6][:grid].max())}
+    pts = [sel[i] for i in _TL_SEL_POINTS]
+    out["selection_phase_cycles"] = [int(pts[i + 1][0] - pts[i][0]) for i in range(len(pts) - 1)]
+    out["selection_cycles"] = int(pts[-1][0] - pts[0][0])
+    sel_rt = lambda i: us(sel[i][1]) if sel[i][1] else None  # noqa: E731
+    out["wg0_stage1_done"] = us(wav[1][:8][wav[1][:8] > 0].max())
+    out["wg0_keys_in_registers"] = us(blk[7][0])
+    out["wg0_last_reload_issued"] = sel_rt(11)
+    out["boundary_gather_cycles"] = (int(sel[8][0] - sel[4][0]) if sel[8][0] else None)
+    out["boundary_gathered_cycles"] = (int(sel[9][0] - sel[8][0]) if sel[9][0] else None)
+    out["boundary_ranked_cycles"] = (int(sel[10][0] - sel[9][0]) if sel[10][0] else None)
+    lags = []
+    for b in range(1, grid):
+        w2 = wav[2][b * 8:(b + 1) * 8]
+        w2 = w2[w2 > 0]
+        if blk[4][b] and len(w2):
+            lags.append((blk[4][b] - w2.max()) * 1e3 / khz)
+    out["publish_lag_median"] = float(np.median(lags)) if lags else None
+    out["publish_lag_max"] = float(np.max(lags)) if lags else None
+    last = int(np.argmax(blk[4][:grid]))
+    w2l = wav[2][last * 8:(last + 1) * 8]
+    out["last_publisher_stage2_done"] = us(w2l[w2l > 0].max()) if (w2l > 0).any() else None
+    out["key_poll_rounds"] = int(cnt[0])
+    out["merge_poll_rounds"] = int(cnt[1])
+    out["boundary_bin_keys"] = int(cnt[2])
+    return out
+
+
+def timeline_bench(args, wl, fh, call, evict, B):
+    """The median over N cold calls of each event of the single-launch decode
+    (the measurement build's timestamps), as one JSON line."""
+    import torch
+
+    from two_stage_retrieval_amd import binding as fhb
+    if B != 1:
+        raise SystemExit("--timeline times the single-launch batch-1 decode (--batch 1)")
+    fhb.flashhead_trace_read()  # clear
+    runs = []
+    for i in range(args.timeline + 5):
+        if not args.timeline_warm:
+            evict()
+        call(i)
+        torch.cuda.synchronize()
+        words, khz = fhb.flashhead_trace_read()
+        if i >= 5:
+            runs.append(parse_timeline(words, khz))
+    if fhb.flashhead_query(fh.handle, 10) != 1:
+        raise SystemExit("the step did not take the single launch")
+    check = fhb.flashhead_query(fh.handle, 9)
+    if check:
+        raise SystemExit(f"self-check word {check:#x}")
+    med = {}
+    for k, v in runs[0].items():
+        if isinstance(v, list):
+            med[k] = [int(statistics.median(r[k][j] for r in runs)) for j in range(len(v))]
+            continue
+        vals = [r[k] for r in runs if r[k] is not None]  # an event a launch did not reach
+        med[k] = round(float(statistics.median(vals)), 3) if vals else None
+    log("[bench] timeline (us from the first workgroup's start, median of "
+        f"{len(runs)} cold calls):")
+    for k, v in med.items():
+        log(f"    {k:32s} {v}")
+    print(json.dumps({"timeline": wl.name, "calls": len(runs), "median": med,
+                      "cache": "warm" if args.timeline_warm else "cold (1 GiB flush)",
+                      "build": "libflashhead_trace.so"}), flush=True)
 
 
 def mc_bench(args, wl, head, H, H_dev, fh, evict, int4):

@@ -385,6 +385,20 @@ int flashhead_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* 
 int flashhead_profile_begin(fh_handle* h, int32_t max_calls);
 int flashhead_profile_end(fh_handle* h, double* stage_ms, int32_t* calls);
 
+/*
+ * Timeline of the single-launch batch-1 decode, for measurement only.  The
+ * library returns FH_ERR_UNSUPPORTED (and *words = 0); its measurement build
+ * (libflashhead_trace.so, the same sources built with timeline hooks)
+ * copies the timestamps its hooks stored during the launches since the
+ * last read to host[0 .. *words) and clears them.  Layout (64-bit words):
+ * 8 workgroup events x 512 workgroups, then 4 wave events x 8192 waves, then
+ * 16 selection phases as (shader-clock cycles, device-clock time) pairs,
+ * then 16 counters; *clock_khz is the device clock's rate.  A launch
+ * overwrites the previous one's stamps; 0 means not recorded.
+ */
+int flashhead_trace_read(uint64_t* host, int64_t max_words, int64_t* words,
+                         int64_t* clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,11 @@ from typing import Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libflashhead.so")
+# FLASHHEAD_LIB_VARIANT=trace loads the measurement build (timeline hooks)
+_VARIANT = os.environ.get("FLASHHEAD_LIB_VARIANT", "")
+if _VARIANT not in ("", "trace"):
+    raise ImportError(f"unknown FLASHHEAD_LIB_VARIANT {_VARIANT!r}")
+LIB_PATH = os.path.join(_PKG, "libflashhead_trace.so" if _VARIANT else "libflashhead.so")
 
 FH_OK = 0
 FH_ERR_INVALID_ARG = -1
@@ -38,7 +42,7 @@ EXPORTED = [
     "flashhead_export_int4", "flashhead_query", "flashhead_profile_begin",
     "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
     "flashhead_mc_workspace_bytes", "flashhead_mc_marginal", "flashhead_kmeans",
-    "flashhead_plan_step", "dense_head_static",
+    "flashhead_plan_step", "dense_head_static", "flashhead_trace_read",
 ]
 FH_DENSE_STATIC_MAX_BATCH = 16
 
@@ -119,6 +123,8 @@ def _load() -> C.CDLL:
     lib.flashhead_plan_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                         C.POINTER(i32)]
     lib.flashhead_plan_step.restype = C.c_int
+    lib.flashhead_trace_read.argtypes = [vp, i64, C.POINTER(i64), C.POINTER(i64)]
+    lib.flashhead_trace_read.restype = C.c_int
     return lib
 
 
@@ -212,6 +218,16 @@ def flashhead_plan_step(c: int, b: int, d: int, dtype: int, quant: int, B: int,
     if st < 0:
         raise FlashHeadError(st, "flashhead_plan_step")
     return st, g.value
+
+
+def flashhead_trace_read():
+    """(words as a numpy uint64 array, device clock kHz) from the
+    measurement build; FlashHeadError(FH_ERR_UNSUPPORTED) from the library."""
+    n, khz = C.c_int64(), C.c_int64()
+    buf = np.zeros(1 << 16, dtype=np.uint64)
+    _check(lib.flashhead_trace_read(buf.ctypes.data, buf.size, C.byref(n), C.byref(khz)),
+           "flashhead_trace_read")
+    return buf[:n.value].copy(), khz.value
 
 
 def flashhead_destroy(handle: int) -> None:

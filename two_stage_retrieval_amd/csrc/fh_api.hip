@@ -40,7 +40,7 @@ struct fh_handle {
   int num_cu = 0;
   int b1_blocks_per_cu = 0;         // decode workgroups one compute unit holds at once
   int flags = 0;                    // FH_FLAG_*
-  float* b1_keys = nullptr;         // 2 x key_stride(c), all bits set between launches
+  float* b1_keys = nullptr;         // 2 x b1_key_stride(c), all bits set between launches
   uint64_t* b1_slots = nullptr;     // 2 x kDecodeB1SlotStride words, zero between launches
   float2* b1_lse = nullptr;         // kDecodeB1SlotStride words
   int32_t* b1_sel = nullptr;        // 2 x kDecodeB1MaxP, -1 between launches
@@ -65,6 +65,9 @@ constexpr int kDenseMaxGrid = 8192;  // dense: partial slots of the batched kern
 
 // selection keys of a batch row: c floats padded to a 16-byte multiple
 int64_t key_stride(int c) { return ((int64_t)c + 3) & ~(int64_t)3; }
+// the single launch's key buffers: padded to whole 128-byte lines, so that
+// each workgroup's run of keys fills lines of its own
+int64_t b1_key_stride(int c) { return ((int64_t)c + 31) & ~(int64_t)31; }
 
 int esize_of(int dtype) { return dtype == FH_DTYPE_F32 ? 4 : dtype == FH_DTYPE_BF16 ? 2 : 0; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -244,8 +247,8 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(alloc(h, &h->ucount, 4));
   FH_TRY(alloc(h, &h->part_best, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
-  FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * key_stride(c) * 4));
-  FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * key_stride(c) * 4, s));
+  FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * b1_key_stride(c) * 4));
+  FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * b1_key_stride(c) * 4, s));
   FH_TRY(alloc(h, &h->b1_slots, (size_t)2 * kDecodeB1SlotStride * 8));
   FH_TRY(hipMemsetAsync(h->b1_slots, 0, (size_t)2 * kDecodeB1SlotStride * 8, s));
   FH_TRY(alloc(h, &h->b1_lse, (size_t)kDecodeB1SlotStride * 8));
@@ -382,6 +385,7 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     f.s1 = s1;
     f.s2 = gather_args();
     f.s1.keys = h->b1_keys;
+    f.s1.key_stride = b1_key_stride(h->c);
     f.s2.part_best = h->b1_slots;
     f.s2.lse_part = h->b1_lse;
     f.sel = h->b1_sel;
@@ -965,7 +969,7 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
       FH_TRY(hipMemcpy(&ep, h->b1_epoch, 4, hipMemcpyDeviceToHost));
       FH_TRY(hipMemcpy(go, h->b1_go, 8, hipMemcpyDeviceToHost));
       const int set = (int)(ep & 1u);
-      const int64_t ks = key_stride(h->c);
+      const int64_t ks = b1_key_stride(h->c);
       std::vector<uint32_t> keys((size_t)ks);
       std::vector<int32_t> sel((size_t)kDecodeB1MaxP);
       std::vector<uint64_t> slots((size_t)kDecodeB1SlotStride);

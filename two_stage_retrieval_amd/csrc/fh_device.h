@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "fh_internal.h"
+#include "fh_trace.h"
 
 namespace fh {
 
@@ -142,30 +143,52 @@ constexpr uint32_t kStreamCluster = 0;
 constexpr uint32_t kStreamToken = 1;
 
 // ---------------------------------------------------------------------------
-// wave reductions
+// wave reductions.  The sums, maxima and log-sum-exp merges run on DPP
+// (row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15 and 31
+// across rows), which moves data between lanes inside the vector ALU; the
+// result is lane 63's, read into a scalar register, so every lane gets it.
+// A butterfly of cross-lane shuffles would take six dependent trips through
+// the LDS crossbar instead.  Every lane of the wave must be active; the
+// order of the operations is fixed, so the results are reproducible.
 // ---------------------------------------------------------------------------
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce_dpp(T x, T identity, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit lanes");
+  const int id = __builtin_bit_cast(int, identity);
+  T v = x;
+#define FH_DPP_STEP(ctrl, rmask)                                                           \
+  v = op(v, __builtin_bit_cast(                                                            \
+                T, __builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), ctrl, rmask, \
+                                               0xf, false)));
+  FH_DPP_STEP(0x111, 0xf)  // row_shr:1
+  FH_DPP_STEP(0x112, 0xf)  // row_shr:2
+  FH_DPP_STEP(0x114, 0xf)  // row_shr:4
+  FH_DPP_STEP(0x118, 0xf)  // row_shr:8: lane 15 of each row holds the row's result
+  FH_DPP_STEP(0x142, 0xa)  // row_bcast:15 into rows 1 and 3
+  FH_DPP_STEP(0x143, 0xc)  // row_bcast:31 into rows 2 and 3: lane 63 holds all
+#undef FH_DPP_STEP
+  return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  return wave_reduce_dpp(x, 0.0f, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  return wave_reduce_dpp(x, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o, kWave));
-  return x;
+  return wave_reduce_dpp(x, INFINITY, [](float a, float b) { return fminf(a, b); });
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce_dpp(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+// the largest 64-bit value: the largest high word, then the largest low word
+// among the lanes that hold it
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t y = __shfl_xor(x, o, kWave);
-    x = y > x ? y : x;
-  }
-  return x;
+  const uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 // inclusive prefix sum across the wave (lane order)
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
@@ -193,41 +216,6 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int x) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return v;
 }
-// max / min over the wave (every lane gets the result); disabled DPP lanes
-// take the identity through `old`
-__device__ __forceinline__ float wave_max_dpp(float x) {
-  const int id = __float_as_int(-INFINITY);
-  float v = x;
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x111, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x112, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x114, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x118, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x142, 0xa, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x143, 0xc, 0xf, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ float wave_add_dpp(float x) {
-  float v = x;
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ float wave_min_dpp(float x) {
-  const int id = __float_as_int(INFINITY);
-  float v = x;
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x111, 0xf, 0xf, false)));
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x112, 0xf, 0xf, false)));
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x114, 0xf, 0xf, false)));
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x118, 0xf, 0xf, false)));
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x142, 0xa, 0xf, false)));
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x143, 0xc, 0xf, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
 // Online log-sum-exp state (max m, scaled sum s = sum exp(x - m)).
 struct Lse {
   float m, s;
@@ -244,13 +232,27 @@ __device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
   if (a.m >= b.m) return Lse{a.m, a.s + b.s * __expf(b.m - a.m)};
   return Lse{b.m, b.s + a.s * __expf(a.m - b.m)};
 }
+// (the pairs move by DPP as in wave_reduce_dpp; a disabled source lane
+// brings the empty state)
 __device__ __forceinline__ Lse wave_lse(Lse a) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    Lse b{__shfl_xor(a.m, o, kWave), __shfl_xor(a.s, o, kWave)};
-    a = lse_merge(a, b);
+  const int ninf = __float_as_int(-INFINITY);
+#define FH_DPP_LSE(ctrl, rmask)                                                               \
+  {                                                                                           \
+    const Lse b{__int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(a.m), ctrl, \
+                                                           rmask, 0xf, false)),            \
+                __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a.s), ctrl,    \
+                                                           rmask, 0xf, false))};           \
+    a = lse_merge(a, b);                                                                      \
   }
-  return a;
+  FH_DPP_LSE(0x111, 0xf)
+  FH_DPP_LSE(0x112, 0xf)
+  FH_DPP_LSE(0x114, 0xf)
+  FH_DPP_LSE(0x118, 0xf)
+  FH_DPP_LSE(0x142, 0xa)
+  FH_DPP_LSE(0x143, 0xc)
+#undef FH_DPP_LSE
+  return Lse{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.m), 63)),
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.s), 63))};
 }
 
 // ---------------------------------------------------------------------------
@@ -271,9 +273,7 @@ __device__ __forceinline__ void arrive(uint32_t* ctr, int w) {
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  return wave_reduce_dpp(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // Called by all 64 lanes of one wave.  Returns false if the spin limit was

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kMcThreads) void mc_draw_kernel(McArgs a) {
 
 // one workgroup per query token: the mean of its terms over the draws, in a
 // fixed order (thread t sums draws t, t + 256, ... of the token's contiguous
-// row; then a fixed butterfly per wave and the waves in order)
+// row; then a fixed-order DPP reduction per wave and the waves in order)
 __global__ __launch_bounds__(kMcThreads) void mc_reduce_kernel(McArgs a) {
   __shared__ float s_part[kMcWaves];
   const int t = threadIdx.x;

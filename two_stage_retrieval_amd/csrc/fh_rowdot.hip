@@ -15,11 +15,6 @@
 // chain).
 #include "fh_rows.h"
 
-// Optional timeline hook for measurement builds (empty in the library).
-#ifndef FH_S2_TRACE
-#define FH_S2_TRACE(slot)
-#endif
-
 namespace fh {
 
 constexpr int kRowdotThreads = 256;
@@ -31,7 +26,6 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = blockIdx.y;
-  FH_S2_TRACE(0);
   float hreg[NCH][Chunk<TE>::kElems];
   load_h<TE, NCH>(a.H + (int64_t)r * a.h_bytes, a.nchunk, lane, hreg);
   const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
@@ -40,11 +34,8 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
   dot_rows<TE, NCH, R, MODE>(a, r, a.sel + (int64_t)r * a.sel_stride, hreg, seed, lane,
                                     (int64_t)blockIdx.x * kRowdotWaves + wave,
                                     (int64_t)gridDim.x * kRowdotWaves, best, lse);
-  FH_S2_TRACE(1);
   // workgroup 0 of the batch row folds every workgroup's partial
-  if (merge_decode<kRowdotThreads>(a, r, gridDim.x, blockIdx.x, 0, best, lse, ms)) {
-    FH_S2_TRACE(3);
-  }
+  merge_decode<kRowdotThreads>(a, r, gridDim.x, blockIdx.x, 0, best, lse, ms);
 }
 
 // Rows per wave per step: enough bytes in flight per wave without spilling.

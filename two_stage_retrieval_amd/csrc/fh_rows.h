@@ -8,14 +8,6 @@
 #include "fh_device.h"
 #include "fh_internal.h"
 
-// Optional timeline hooks for measurement builds (empty in the library).
-#ifndef FH_PUB_TRACE
-#define FH_PUB_TRACE()
-#endif
-#ifndef FH_MERGE_POLL_TRACE
-#define FH_MERGE_POLL_TRACE(round)
-#endif
-
 namespace fh {
 
 // h (one row of H): chunk lane + 64 i of the row, raw, then unpacked.
@@ -431,7 +423,7 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
       }
       __hip_atomic_store(slot + block * kSlotWords, bb ? bb : 1ull, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-      FH_PUB_TRACE();
+      FH_TRACE_BLOCK(4);  // partial published
     }
     return false;
   }
@@ -452,7 +444,7 @@ __device__ __forceinline__ bool merge_decode_slots(const RowdotArgs& a, int nblo
     if (j != 0 && j < nblocks) todo |= 1u << q;
   }
   for (int it = 0;; ++it) {
-    FH_MERGE_POLL_TRACE(it);
+    FH_TRACE_COUNT(1, it + 1);  // merge poll rounds
     uint64_t xs[kQ];
 #pragma unroll
     for (int q = 0; q < kQ; ++q)

@@ -28,14 +28,6 @@
 #include "fh_device.h"
 #include "fh_internal.h"
 
-// Optional phase hook for measurement builds (empty in the library).
-#ifndef FH_SEL_TRACE
-#define FH_SEL_TRACE(i)
-#endif
-#ifndef FH_SEL_STATE
-#define FH_SEL_STATE(lo, fmin, fmax, total, nb, ngt)
-#endif
-
 namespace fh {
 
 constexpr int kSelBins = 2048;
@@ -144,10 +136,10 @@ __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int 
       lsq = fmaf(f, f, lsq);
     }
   }
-  lmax = wave_max_dpp(lmax);
-  lmin = wave_min_dpp(lmin);
-  lsum = wave_add_dpp(lsum);
-  lsq = wave_add_dpp(lsq);
+  lmax = wave_max(lmax);
+  lmin = wave_min(lmin);
+  lsum = wave_sum(lsum);
+  lsq = wave_sum(lsq);
   if ((t & (kWave - 1)) == 0) {
     sm.fmax[t >> 6] = lmax;
     sm.fmin[t >> 6] = lmin;
@@ -172,7 +164,7 @@ __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int 
 // range, the histogram is redone over [min, max]; the result never depends
 // on zcut.
 template <int NT, int IPT, bool COHERENT_OUT, bool PREPARED = false>
-__device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, int32_t* out,
+__device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, int32_t* out,
                                  uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
   static_assert(IPT % 4 == 0 && IPT <= 32 && (IPT & (IPT - 1)) == 0, "items per thread");
   constexpr int NW = NT / kWave;
@@ -187,13 +179,13 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
   // ---- block min / max / moments --------------------------------------------------
   // u keeps the raw fp32 bits; the order-preserving form is made where the
   // bits themselves are compared (boundary candidates, radix passes)
-  FH_SEL_TRACE(0);
+  FH_TRACE_SEL(0);
   if constexpr (!PREPARED) {
     select_clear<NT>(c, sm);
     select_wave_range<IPT>(u, c, sm);
     __syncthreads();
   }
-  FH_SEL_TRACE(2);
+  FH_TRACE_SEL(2);
   float fmax = sm.fmax[0], fmin = sm.fmin[0], fsum = sm.fsum[0], fsq = sm.fsq[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
@@ -241,7 +233,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
       if (in) atomicAdd(&sm.hist[b], 1);
     }
     __syncthreads();
-    FH_SEL_TRACE(3);
+    FH_TRACE_SEL(3);
     int hb[BPT];
     int hs = 0;
 #pragma unroll
@@ -274,8 +266,8 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
     for (int i = t; i < kSelBins; i += NT) sm.hist[i] = 0;
     __syncthreads();
   }
-  FH_SEL_STATE(lo, fmin, fmax, sm.misc[7], nb, ngt);
-  FH_SEL_TRACE(4);
+  FH_TRACE_COUNT(2, nb);  // keys in the boundary bin
+  FH_TRACE_SEL(4);
   int need = p - ngt;  // ids still to take from the boundary bin
 
   // (branch-free: items past c carry bin 0, below every key's)
@@ -346,6 +338,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
     int base = 0;
     if (lane == kWave - 1 && wincl > 0) base = atomicAdd(&sm.misc[6], wincl);
     base = __shfl(base, kWave - 1, kWave) + wincl - cc;
+    FH_TRACE_SEL(8);
     if (cand) {
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
@@ -357,6 +350,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
       }
     }
     __syncthreads();
+    FH_TRACE_SEL(9);
     if (wave == 0) {
       // each candidate's rank in (key descending, id ascending); the `need`
       // first are taken (candidate j is read from lane j's registers)
@@ -372,6 +366,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
       if (live && rank < need) atomicOr(&sm.chosen[kk >> 5], 1u << (kk & 31));
     }
     __syncthreads();
+    FH_TRACE_SEL(10);
     // the thread's ids [k0, k0 + IPT) lie in one word of the bitmap (IPT is
     // a power of two up to 32 and k0 a multiple of it)
     if (cand) above |= cand & (sm.chosen[k0 >> 5] >> (k0 & 31));
@@ -387,12 +382,12 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
       }
     }
   }
-  FH_SEL_TRACE(5);
+  FH_TRACE_SEL(5);
 
   // ---- ascending ids -------------------------------------------------------------
   const int cnt = __popc(above);
   const int incl = sel_scan<NT>(cnt, sm, parity, lane, wave);
-  FH_SEL_TRACE(6);
+  FH_TRACE_SEL(6);
   // one step per selected id of the thread, lowest first
   int rank = incl - cnt;
   for (uint32_t m = above; m != 0u && rank < p; m &= m - 1u, ++rank) {
@@ -404,7 +399,7 @@ __device__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, i
     }
     if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k), 1ull << row);
   }
-  FH_SEL_TRACE(7);
+  FH_TRACE_SEL(7);
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);
 }
 

@@ -20,26 +20,6 @@
 #include "fh_rows.h"
 #include "fh_select.h"
 
-// Optional timeline hook for measurement builds (empty in the library).
-#ifndef FH_S1_TRACE
-#define FH_S1_TRACE(slot)
-#endif
-#ifndef FH_S1_WAVE_TRACE
-#define FH_S1_WAVE_TRACE(wave)
-#endif
-#ifndef FH_S1_ISSUE_TRACE
-#define FH_S1_ISSUE_TRACE(wave)
-#endif
-#ifndef FH_S2_WAVE_TRACE
-#define FH_S2_WAVE_TRACE(wave)
-#endif
-#ifndef FH_S1_TRACE_END
-#define FH_S1_TRACE_END()
-#endif
-#ifndef FH_S1_POLL_TRACE
-#define FH_S1_POLL_TRACE(round)
-#endif
-
 namespace fh {
 
 constexpr int kS1Threads = 512;
@@ -58,7 +38,6 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   const int lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint8_t* hrow = a.H + (int64_t)r * a.h_bytes;
-  FH_S1_TRACE(0);
   const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
   float* keys = a.keys + (int64_t)r * a.key_stride;
   float* dbg = a.dbg_scores ? a.dbg_scores + (int64_t)r * a.c : nullptr;
@@ -75,7 +54,6 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
     __syncthreads();
     score_int4_tiles<SELECT>(a, keys, nullptr, dbg, seed, s_h, lane, w0, wstride);
   }
-  FH_S1_TRACE(1);
   if constexpr (!SELECT) return;
 
   // ---- workgroup 0 of this batch row selects, once every other workgroup
@@ -92,10 +70,129 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
     if (!ok && lane == 0 && a.error) atomicOr(a.error, 2u);
   }
   __syncthreads();
-  FH_S1_TRACE(2);
   select_block<kS1Threads, IPT, true>(keys, a.c, (int)a.key_stride, a.p, a.zcut,
                                       a.sel + (int64_t)r * a.sel_stride, a.masks, r, a.error, sm);
-  FH_S1_TRACE(3);
+}
+
+// ---------------------------------------------------------------------------
+// Stage-1 shares of the single-launch decode.  In pass k workgroup b scores
+// one contiguous run of rows (32 bf16 / fp32 rows, or 64 rows of INT4
+// tiles); the scores meet in LDS (double-buffered, one barrier per pass)
+// and wave 0 forms the keys and stores them as whole 128-byte lines with one
+// device-coherent store, marks the same rows pending in the next launch's
+// key buffer and writes the debug scores.  A line stored whole by one wave
+// reaches the polling workgroup sooner than partial lines stored by several.
+// ---------------------------------------------------------------------------
+// One key of the pass: lane `i` of wave 0 owns row `row` (score in LDS).
+__device__ __forceinline__ void b1_publish_key(const Stage1Args& a, float* keys, float* keys_next,
+                                               uint64_t seed, int row, float score,
+                                               uint64_t* best_key) {
+  const float key =
+      a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
+  __hip_atomic_store(keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  keys_next[row] = __uint_as_float(kKeyPending);
+  if (a.dbg_scores) a.dbg_scores[row] = score;
+  track_best_key(best_key, key, row);
+}
+
+// bf16 / fp32 centroid rows: wave w scores the 4 rows of group
+// (k * grid + b) * 8 + w; its first group's rows are already in `data`.
+template <typename TE, int NCH>
+__device__ __forceinline__ void b1_score_rows(const Stage1Args& a, float* keys, float* keys_next,
+                                              uint64_t seed, const uint4 (&hraw)[NCH],
+                                              float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
+                                              int wave, uint4 (&data)[kS1Rows][NCH],
+                                              float (*s_stage)[kS1Waves * kS1Rows],
+                                              uint64_t* best_key) {
+  using CK = Chunk<TE>;
+  constexpr int kRun = kS1Waves * kS1Rows;  // rows per workgroup and pass
+  const int ngroups = (a.c + kS1Rows - 1) / kS1Rows;
+  const int wstride = gridDim.x * kS1Waves;
+  unpack_h<TE, NCH>(hraw, hreg);
+  for (int k = 0;; ++k) {
+    const int gbase = (k * (int)gridDim.x + (int)blockIdx.x) * kS1Waves;
+    if (gbase >= ngroups) break;  // the same in every wave of the workgroup
+    float* st = s_stage[k & 1];
+    const int g = gbase + wave;
+    if (g < ngroups) {
+      float acc[kS1Rows];
+#pragma unroll
+      for (int rr = 0; rr < kS1Rows; ++rr) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) sum = CK::dot(data[rr][i], hreg[i], sum);
+        acc[rr] = wave_sum(sum);
+      }
+      float mine = acc[0];
+#pragma unroll
+      for (int rr = 1; rr < kS1Rows; ++rr)
+        if (lane == rr) mine = acc[rr];
+      if (lane < kS1Rows) st[wave * kS1Rows + lane] = mine;
+      if (g + wstride < ngroups) load_centroid_group<TE, NCH>(a, g + wstride, lane, data);
+    }
+    __syncthreads();
+    if (wave == 0 && lane < kRun) {
+      const int row = gbase * kS1Rows + lane;
+      if (row < a.c) b1_publish_key(a, keys, keys_next, seed, row, st[lane], best_key);
+    }
+  }
+}
+
+// INT4 tiles (notes, Module 3): the two waves 2i and 2i + 1 of a workgroup
+// share tile (k * grid + b) * 4 + i, each taking half of its 128-column
+// groups (one coalesced 1 KB load per group, all issued before any is
+// used); lane l owns row l mod 16 and 32 of a group's columns, h comes from
+// LDS.  The halves' partial scores are added in LDS.
+__device__ __forceinline__ void b1_score_int4(const Stage1Args& a, float* keys, float* keys_next,
+                                              uint64_t seed, const float* s_h, int lane, int wave,
+                                              float (*s_part)[kS1Waves][16],
+                                              uint64_t* best_key) {
+  constexpr int kTilesPerPass = kS1Waves / 2;
+  constexpr int kBatch = 8;  // group loads in flight per wave
+  const int q = lane >> 4, rin = lane & 15;
+  const int G = a.groups, Gh = (G + 1) / 2;
+  const int g_lo = (wave & 1) * Gh;
+  const int g_hi = g_lo + Gh < G ? g_lo + Gh : G;
+  for (int k = 0;; ++k) {
+    const int tbase = (k * (int)gridDim.x + (int)blockIdx.x) * kTilesPerPass;
+    if (tbase >= a.ntiles) break;  // the same in every wave of the workgroup
+    const int tile = tbase + (wave >> 1);
+    if (tile < a.ntiles) {
+      const uint4* codes =
+          reinterpret_cast<const uint4*>(a.q4) + (int64_t)tile * G * kWave + lane;
+      const uint16_t* sc = a.q4s + (int64_t)tile * G * 16 + rin;
+      float acc = 0.0f;
+      for (int g0 = g_lo; g0 < g_hi; g0 += kBatch) {
+        uint4 w[kBatch];
+        uint32_t sb[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          if (g0 + i < g_hi) {
+            w[i] = codes[(int64_t)(g0 + i) * kWave];
+            sb[i] = sc[(g0 + i) * 16];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (g0 + i < g_hi)
+            acc = fmaf(__uint_as_float(sb[i] << 16),
+                       int4_dot_chunk(w[i], s_h + (g0 + i) * 128 + q * 32), acc);
+      }
+      acc += __shfl_xor(acc, 16, kWave);
+      acc += __shfl_xor(acc, 32, kWave);
+      if (q == 0) s_part[k & 1][wave][rin] = acc;
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane = 16 * (tile of the pass) + row in the tile
+      const int tl = tbase + (lane >> 4);
+      const int row = tl * 16 + (lane & 15);
+      if (tl < a.ntiles && row < a.c) {
+        const int pr = lane >> 4;
+        const float score = s_part[k & 1][2 * pr][lane & 15] + s_part[k & 1][2 * pr + 1][lane & 15];
+        b1_publish_key(a, keys, keys_next, seed, row, score, best_key);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -124,6 +221,8 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   __shared__ float s_h[INT4 ? FH_MAX_ROW_BYTES / 2 : 1];
   __shared__ MergeSmem<kS1Threads> ms;
   __shared__ int32_t s_sel[kDecodeB1MaxP];
+  __shared__ float s_stage[2][kS1Waves * kS1Rows];
+  __shared__ float s_part[INT4 ? 2 : 1][kS1Waves][16];
   const Stage1Args& a = args.s1;
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -134,7 +233,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   // h and the wave's first centroid rows are requested before anything else
   // is waited for (the buffer set and the seed are needed only when keys
   // are stored)
-  FH_S1_TRACE(0);
+  FH_TRACE_BLOCK(0);  // start
   // Straight-line prologue: bounds-checked buffer loads (a chunk past the
   // row, or a group past the last, reads as zero without a memory access),
   // so that the requests go out after one wait for the few arguments they
@@ -165,7 +264,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    FH_S1_ISSUE_TRACE(wave);
+    FH_TRACE_WAVE(0);  // stage-1 requests issued
   }
   const uint32_t epoch = __builtin_amdgcn_readfirstlane(
       __hip_atomic_load(args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -177,8 +276,8 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   const uint64_t seed = a.sample ? a.seeds[0] : 0ull;
   uint64_t best_key = 0;  // this lane's best (key, row), for the prefetch below
   if constexpr (!INT4) {
-    score_rows_from<TE, NCH, true>(a, keys, keys_next, a.dbg_scores, seed, hraw, hreg, lane, w0,
-                                   wstride, data, &best_key);
+    b1_score_rows<TE, NCH>(a, keys, keys_next, seed, hraw, hreg, lane, wave, data, s_stage,
+                           &best_key);
   } else {
     // h in LDS as floats for the INT4 tiles, written by wave 0 from its
     // registers (lane l holds bf16 elements 8 (l + 64 i) .. 8 (l + 64 i) + 7)
@@ -198,11 +297,9 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       }
     }
     __syncthreads();
-    score_int4_tiles<true>(a, keys, keys_next, a.dbg_scores, seed, s_h, lane, w0, wstride,
-                           &best_key);
+    b1_score_int4(a, keys, keys_next, seed, s_h, lane, wave, s_part, &best_key);
   }
-  FH_S1_TRACE(1);
-  FH_S1_WAVE_TRACE(wave);
+  FH_TRACE_WAVE(1);  // stage-1 share done
 
 
   // ---- B: workgroup 0 waits for all keys, selects and publishes ------------------
@@ -221,13 +318,14 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
 #pragma unroll
       for (int j = 0; j < IPT; ++j)
         if (j < nvalid && u[j] == kKeyPending) pend |= 1u << (j / 4);
-      FH_S1_POLL_TRACE(it);
+      FH_TRACE_COUNT(0, it + 1);  // key poll rounds
       if (!__any(pend != 0u)) break;
       if (it == kArriveSpinLimit) {
         if (lane == 0 && a.error) atomicOr(a.error, 2u);
         break;
       }
       poll_barrier();
+      FH_TRACE_SEL(11);  // a reload round issued (the last one counts)
 #pragma unroll
       for (int q = 0; q < IPT / 4; ++q) {
         if ((pend >> q) & 1u) {
@@ -239,20 +337,21 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
         }
       }
     }
+    FH_TRACE_BLOCK(7);  // every key in this thread's registers
     select_wave_range<IPT>(u, a.c, sm);
     __syncthreads();
     if (t == 0) {  // every key is in: the other workgroups may prefetch
       __hip_atomic_store(args.go + cur, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       args.go[1 - cur] = 0u;
     }
-    FH_S1_TRACE(2);
+    FH_TRACE_BLOCK(1);  // every key seen
     // the selection goes to LDS, then out in one coalesced device-coherent pass
     select_from_keys<kS1Threads, IPT, false, true>(u, a.c, a.p, a.zcut, s_sel, nullptr, 0, a.error,
                                                    sm);
     __syncthreads();
     for (int i = t; i < a.p; i += kS1Threads)
       __hip_atomic_store(sel + i, s_sel[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    FH_S1_TRACE(3);
+    FH_TRACE_BLOCK(2);  // selection published
   }
 
   // ---- C: stage-2 share ---------------------------------------------------------
@@ -334,7 +433,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       if (n1) s_win[lane + kWave] = e1;
     }
     __syncthreads();
-    FH_S1_TRACE(7);
+    FH_TRACE_BLOCK(3);  // stage-2 entries in LDS
   }
   uint64_t best = 0;
   Lse lse = lse_empty();
@@ -346,8 +445,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
                                            lse, a.error, s_win, wlo, wn);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS load outlives the workgroup
-  FH_S2_WAVE_TRACE(wave);
-  FH_S1_TRACE(5);
+  FH_TRACE_WAVE(2);  // stage-2 share done
 
   // ---- D: the decode merge; workgroup 0 then advances the epoch --------------------
   uint64_t* slots = args.s2.part_best + (int64_t)cur * args.slot_stride;
@@ -357,9 +455,9 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
                                      best, lse, a.error, ms) &&
       t == 0) {
     __hip_atomic_store(args.epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    FH_S1_TRACE(6);
+    FH_TRACE_BLOCK(5);  // token written
   }
-  FH_S1_TRACE_END();
+  FH_TRACE_BLOCK(6);  // end
 }
 
 int stage1_blocks(const Stage1Args& a, bool int4) {
@@ -433,7 +531,7 @@ int decode_b1_grid(int c, int p, int nchunk, int ntiles, int64_t nrows, bool int
   const int nch = (nchunk + kWave - 1) / kWave;
   if (nch < 1 || nch > 8) return 0;
   const int R = nch <= 2 ? 8 : 4;
-  const int64_t units1 = int4 ? ntiles : (c + kS1Rows - 1) / kS1Rows;
+  const int64_t units1 = int4 ? 2 * (int64_t)ntiles : (c + kS1Rows - 1) / kS1Rows;
   const int64_t units2 = (nrows + R - 1) / R;
   const int64_t units = units1 > units2 ? units1 : units2;
   int64_t g = (units + kS1Waves - 1) / kS1Waves;
@@ -540,3 +638,34 @@ hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int gri
 }
 
 }  // namespace fh
+
+// The decode kernel's timeline (the measurement build's hooks, see
+// fh_trace.h): copied to the host and cleared.
+extern "C" int flashhead_trace_read(uint64_t* host, int64_t max_words, int64_t* words,
+                                    int64_t* clock_khz) {
+  if (!words || !clock_khz) return FH_ERR_INVALID_ARG;
+  *words = 0;
+  *clock_khz = 0;
+#ifdef FH_TRACE
+  if (!host || max_words < fh::kTraceWords) return FH_ERR_INVALID_ARG;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return FH_ERR_HIP;
+  const size_t bytes = (size_t)fh::kTraceWords * 8;
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(fh::fh_trace_buf), bytes, 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return FH_ERR_HIP;
+  void* dptr = nullptr;
+  if (hipGetSymbolAddress(&dptr, HIP_SYMBOL(fh::fh_trace_buf)) != hipSuccess ||
+      hipMemset(dptr, 0, bytes) != hipSuccess)
+    return FH_ERR_HIP;
+  *words = fh::kTraceWords;
+  *clock_khz = khz;
+  return FH_OK;
+#else
+  (void)host;
+  (void)max_words;
+  return FH_ERR_UNSUPPORTED;
+#endif
+}
