@@ -429,6 +429,7 @@ def parse_timeline(words, khz):
     out["wg0_stage1_done"] = us(wav[1][:8][wav[1][:8] > 0].max())
     out["wg0_keys_in_registers"] = us(blk[7][0])
     out["wg0_last_reload_issued"] = sel_rt(11)
+    out["early_part_published"] = sel_rt(12)
     out["boundary_gather_cycles"] = (int(sel[8][0] - sel[4][0]) if sel[8][0] else None)
     out["boundary_gathered_cycles"] = (int(sel[9][0] - sel[8][0]) if sel[9][0] else None)
     out["boundary_ranked_cycles"] = (int(sel[10][0] - sel[9][0]) if sel[10][0] else None)

@@ -130,10 +130,15 @@ typedef struct fh_desc {
  * Optional debug outputs (device pointers, each may be NULL).  They cost
  * extra writes and exist for tests and analysis.
  *   scores      B x c   stage-1 scores s = C h (before any noise)
- *   clusters    B x p   selected cluster ids, ascending per row
+ *   clusters    B x p   selected cluster ids per row: ascending, except
+ *                       that the single-launch batch-1 decode lists first
+ *                       the clusters whose keys lie in the selection
+ *                       histogram's bins above its boundary bin (ascending;
+ *                       they are published before the boundary bin is
+ *                       resolved), then those taken from it (ascending)
  *   cand_ids    B x p*b candidate token ids; row r lists, for the j-th
- *                       selected cluster in ascending cluster order, its b
- *                       tokens C2T[k, 0..b) at [j*b, j*b + b)
+ *                       entry of `clusters`, its b tokens C2T[k, 0..b) at
+ *                       [j*b, j*b + b)
  *   cand_logits B x p*b exact logits of cand_ids (fp32)
  */
 typedef struct fh_debug {

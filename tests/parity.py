@@ -44,13 +44,18 @@ class Stats:
                 f"max_logit_err={self.max_logit_err:.3g}")
 
 
-def check_selection(gpu_sel, keys1, p, stats: Stats | None = None):
-    """R1 for one row; keys1 = oracle selection keys (float64, length c)."""
+def check_selection(gpu_sel, keys1, p, stats: Stats | None = None, runs: int = 1):
+    """R1 for one row; keys1 = oracle selection keys (float64, length c).
+    The GPU's list is `runs` ascending runs at most (the method leaves the
+    order open; the library lists ascending, or, in the single-launch batch-1
+    decode, the clusters published before the boundary bin, then the rest);
+    the set is what is compared."""
     c = len(keys1)
-    gsel = np.asarray(gpu_sel, dtype=np.int64)
-    assert len(gsel) == p, "wrong number of clusters"
-    assert len(np.unique(gsel)) == p, "duplicate cluster"
-    assert np.all(np.diff(gsel) > 0), "clusters not ascending"
+    glist = np.asarray(gpu_sel, dtype=np.int64)
+    assert len(glist) == p, "wrong number of clusters"
+    assert len(np.unique(glist)) == p, "duplicate cluster"
+    assert np.count_nonzero(np.diff(glist) < 0) <= runs - 1, "clusters out of order"
+    gsel = np.sort(glist)
     assert gsel.min() >= 0 and gsel.max() < c
     order = ref.order_desc(keys1)
     osel = np.sort(order[:p])
@@ -102,10 +107,10 @@ def check_token(gpu_token, gpu_ids, z, mode, tau, seed, stats=None):
 
 
 def check_row(*, gpu_token, gpu_sel, gpu_ids, gpu_logits, keys1, p, c2t,
-              rows, h64, dtype, mode="greedy", tau=1.0, seed=0, stats=None):
+              rows, h64, dtype, mode="greedy", tau=1.0, seed=0, stats=None, runs=1):
     if stats is not None:
         stats.rows += 1
-    check_selection(gpu_sel, keys1, p, stats)
+    check_selection(gpu_sel, keys1, p, stats, runs)
     check_candidates(gpu_sel, gpu_ids, c2t)
     z = check_logits(gpu_ids, gpu_logits, rows, h64, dtype, stats)
     check_token(gpu_token, gpu_ids, z, mode, tau, seed, stats)

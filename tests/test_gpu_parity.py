@@ -125,6 +125,8 @@ def run_debug(fhmod, head, H_dev, B, p, mode, tau=1.0, seeds=None):
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in dbg.items()}
     res["tokens"] = out.cpu().numpy()
+    # the single launch lists its clusters in two ascending runs
+    res["runs"] = 2 if fhmod.flashhead_query(head.handle, 10) == 1 else 1
     if lse is not None:
         res["lse"] = lse.cpu().numpy()
     return res
@@ -142,7 +144,8 @@ def check_one(cs, res, r, h64, p, mode="greedy", tau=1.0, seed=0, stats=None,
     check_row(gpu_token=res["tokens"][r], gpu_sel=res["clusters"][r],
               gpu_ids=res["cand_ids"][r], gpu_logits=res["cand_logits"][r],
               keys1=keys1, p=p, c2t=cs.head.c2t, rows=cs.rows, h64=h64,
-              dtype=cs.dtype, mode=mode, tau=tau, seed=seed, stats=stats)
+              dtype=cs.dtype, mode=mode, tau=tau, seed=seed, stats=stats,
+              runs=res.get("runs", 1))
     if mode == "sample":
         z = ref.exact_logits(cs.rows, res["cand_ids"][r], h64)
         assert res["lse"][r] == pytest.approx(ref.logsumexp(z / tau),
@@ -468,7 +471,7 @@ def test_all_equal_scores_pick_lowest_ids(fh, wid, over, p, B):
     H = np.zeros((B, cs.wl.d), dtype=cs.head.E.dtype)
     res = run_debug(fh, head, dev_tensor(H), B, p, "greedy")
     for r in range(B):
-        assert np.array_equal(res["clusters"][r], np.arange(p))
+        assert np.array_equal(np.sort(res["clusters"][r]), np.arange(p))
         T = ref.candidate_tokens(np.arange(p), cs.head.c2t)
         assert res["tokens"][r] == T.min()
     assert fh.flashhead_query(head.handle, 9) == 0

@@ -163,9 +163,19 @@ __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int 
 // histogram and the bins are finer.  If fewer than p keys fall in the
 // range, the histogram is redone over [min, max]; the result never depends
 // on zcut.
+//
+// `early` (device memory, written device-coherently; out is then the LDS
+// copy): the selection is published in two parts.  As soon as the boundary
+// bin is known, the keys in the bins above it, all selected, are written
+// ascending to out[0 .. ngt) and stored to early[0 .. ngt); the ids taken
+// from the boundary bin follow, ascending, at [ngt, p).  Readers that wait
+// for the entries they need start on most of them before the boundary bin
+// is resolved.  Without it the p ids are ascending.
 template <int NT, int IPT, bool COHERENT_OUT, bool PREPARED = false>
-__device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut, int32_t* out,
-                                 uint64_t* masks, int row, uint32_t* error, SelSmem& sm) {
+__device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut,
+                                                 int32_t* out, uint64_t* masks, int row,
+                                                 uint32_t* error, SelSmem& sm,
+                                                 int32_t* early = nullptr) {
   static_assert(IPT % 4 == 0 && IPT <= 32 && (IPT & (IPT - 1)) == 0, "items per thread");
   constexpr int NW = NT / kWave;
   constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
@@ -279,6 +289,16 @@ __device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int 
     above |= (uint32_t)(b > bb) << j;
     cand |= (uint32_t)(b == bb) << j;
   }
+  const uint32_t first = early ? above : 0u;  // published before the boundary bin
+  if (early) {  // (block-uniform)
+    const int ca = __popc(above);
+    int r = sel_scan<NT>(ca, sm, parity, lane, wave) - ca;
+    for (uint32_t mm = above; mm != 0u; mm &= mm - 1u, ++r) out[r] = k0 + __ffs(mm) - 1;
+    __syncthreads();
+    for (int i = t; i < ngt; i += NT)
+      __hip_atomic_store(early + i, out[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    FH_TRACE_SEL(12);
+  }
 
   // ---- large boundary bin: 8-bit radix passes on the key bits -----------------
   // (block-uniform control flow: need and nb are the same in every thread)
@@ -385,12 +405,14 @@ __device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int 
   FH_TRACE_SEL(5);
 
   // ---- ascending ids -------------------------------------------------------------
-  const int cnt = __popc(above);
-  const int incl = sel_scan<NT>(cnt, sm, parity, lane, wave);
+  // (with `early`: the boundary bin's ids, after the ngt already published)
+  const uint32_t rest = above & ~first;
+  const int cnt = __popc(rest);
+  const int incl = sel_scan<NT>(cnt, sm, parity, lane, wave) + (early ? ngt : 0);
   FH_TRACE_SEL(6);
   // one step per selected id of the thread, lowest first
   int rank = incl - cnt;
-  for (uint32_t m = above; m != 0u && rank < p; m &= m - 1u, ++rank) {
+  for (uint32_t m = rest; m != 0u && rank < p; m &= m - 1u, ++rank) {
     const int k = k0 + __ffs(m) - 1;
     if constexpr (COHERENT_OUT) {
       __hip_atomic_store(out + rank, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -398,6 +420,11 @@ __device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int 
       out[rank] = k;
     }
     if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k), 1ull << row);
+  }
+  if (early) {
+    __syncthreads();
+    for (int i = ngt + t; i < p; i += NT)
+      __hip_atomic_store(early + i, out[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   FH_TRACE_SEL(7);
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);

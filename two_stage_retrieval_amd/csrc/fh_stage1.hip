@@ -345,12 +345,12 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       args.go[1 - cur] = 0u;
     }
     FH_TRACE_BLOCK(1);  // every key seen
-    // the selection goes to LDS, then out in one coalesced device-coherent pass
+    // the selection goes to LDS and out in two coalesced device-coherent
+    // passes: the clusters above the boundary bin first, then the ones taken
+    // from it (stage 2 starts on the first before the second are known)
     select_from_keys<kS1Threads, IPT, false, true>(u, a.c, a.p, a.zcut, s_sel, nullptr, 0, a.error,
-                                                   sm);
-    __syncthreads();
-    for (int i = t; i < a.p; i += kS1Threads)
-      __hip_atomic_store(sel + i, s_sel[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                                   sm, sel);
+    __syncthreads();  // s_sel complete for this workgroup's own stage-2 share
     FH_TRACE_BLOCK(2);  // selection published
   }
 
