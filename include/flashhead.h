@@ -86,6 +86,12 @@ extern "C" {
                                 it prepare checks with the occupancy API that
                                 they fit on the device at once, which holds
                                 when nothing else occupies it.               */
+#define FH_FLAG_BORROW_E 2    /* stage 2 reads the rows of the caller's E
+                                through C2T (E is borrowed: it must stay
+                                allocated and unchanged while the handle
+                                lives) instead of a cluster-major copy that
+                                prepare makes (v * d elements more device
+                                memory; the handle then does not keep E)    */
 
 /* Limits of this implementation. */
 #define FH_MAX_BATCH 64     /* rows per call                               */
@@ -107,10 +113,12 @@ typedef struct fh_desc {
   int32_t b;          /* tokens per cluster                                */
   int32_t dtype;      /* FH_DTYPE_F32 or FH_DTYPE_BF16 (E, C, H)           */
   int64_t lde;        /* row stride of E in elements (>= d)                */
-  const void* E;      /* device, v x lde; read during prepare only: the
-                         handle keeps its own cluster-major copy (row
-                         k*b + j = E[C2T[k, j]], v x d), so E may be freed
-                         or changed after prepare returns                  */
+  const void* E;      /* device, v x lde.  Without FH_FLAG_BORROW_E it is
+                         read during prepare only: the handle keeps its own
+                         cluster-major copy (row k*b + j = E[C2T[k, j]],
+                         v x d), so E may be freed or changed after prepare
+                         returns.  With it, stage 2 reads E itself, which
+                         must then outlive the handle unchanged            */
   const int32_t* c2t; /* host, c x b; must be a permutation of [0, v);
                          copied at prepare                                 */
   const void* C;      /* device, c x d contiguous in dtype, unit-norm rows,

@@ -102,7 +102,7 @@ def test_prepare_rejects_bad_descriptors(fh):
     assert _prepare(fh, _desc(fh, c2t, quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
     assert _prepare(fh, _desc(fh, c2t, dtype=fh.FH_DTYPE_BF16, d=200,
                               quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
-    assert _prepare(fh, _desc(fh, c2t, flags=2)) == inv          # unknown flag bit
+    assert _prepare(fh, _desc(fh, c2t, flags=4)) == inv          # unknown flag bit
 
 
 @pytest.mark.parametrize("kind", ["repeat", "out_of_range", "negative"])

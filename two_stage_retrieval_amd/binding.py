@@ -34,6 +34,7 @@ FH_QUANT_INT4_G128_MEAN = 2
 FH_MODE_GREEDY = 0
 FH_MODE_SAMPLE = 1
 FH_FLAG_COOPERATIVE = 1
+FH_FLAG_BORROW_E = 2
 
 EXPORTED = [
     "flashhead_prepare", "flashhead_destroy", "flashhead_greedy",

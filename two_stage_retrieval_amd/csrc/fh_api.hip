@@ -19,7 +19,12 @@ struct fh_handle {
   int device = 0;
   void* C = nullptr;          // c x d
   int32_t* c2t = nullptr;     // c x b
-  uint8_t* Ec = nullptr;      // cluster-major copy of E (v x d)
+  uint8_t* Ec = nullptr;      // cluster-major copy of E (v x d), unless borrowed
+  // the rows stage 2 reads: the copy (row k*b + j = token C2T[k, j]) or, with
+  // FH_FLAG_BORROW_E, the caller's E itself (row = token)
+  const uint8_t* rows = nullptr;
+  int64_t rows_stride = 0;    // bytes between rows of `rows`
+  int borrowed = 0;
   uint8_t* q4 = nullptr;      // INT4 tiles
   uint16_t* q4s = nullptr;    // INT4 scales
   int ntiles = 0, groups = 0;
@@ -198,8 +203,15 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
     FH_TRY(hipMemcpyAsync(h->C, ds->C, (size_t)c * h->row_bytes, hipMemcpyDeviceToDevice, s));
   else
     FH_TRY(launch_centroid_means(E, lde_bytes, h->dtype, d, h->c2t, c, b, h->C, s));
-  FH_TRY(alloc(h, &h->Ec, (size_t)v * h->row_bytes));
-  FH_TRY(launch_cluster_major_copy(E, lde_bytes, h->c2t, v, h->row_bytes, h->Ec, s));
+  if (h->borrowed) {
+    h->rows = E;
+    h->rows_stride = lde_bytes;
+  } else {
+    FH_TRY(alloc(h, &h->Ec, (size_t)v * h->row_bytes));
+    FH_TRY(launch_cluster_major_copy(E, lde_bytes, h->c2t, v, h->row_bytes, h->Ec, s));
+    h->rows = h->Ec;
+    h->rows_stride = h->row_bytes;
+  }
   {
     // token -> row of the cluster-major copy (the inverse of the table)
     std::vector<int32_t> inv((size_t)v);
@@ -354,8 +366,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   // stage-2 gather over the cluster-major copy (GEMV paths)
   auto gather_args = [&]() {
     RowdotArgs a{};
-    a.base = h->Ec;
-    a.row_bytes = h->row_bytes;
+    a.base = h->rows;
+    a.row_bytes = h->rows_stride;
+    a.borrowed = h->borrowed;
     a.nchunk = nchunk;
     a.H = static_cast<const uint8_t*>(H);
     a.h_bytes = h->row_bytes;
@@ -454,8 +467,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   // stage 2: candidate logits + decode
   if (batched) {
     Stage2mArgs a{};
-    a.base = h->Ec;
-    a.row_bytes = h->row_bytes;
+    a.base = h->rows;
+    a.row_bytes = h->rows_stride;
+    a.borrowed = h->borrowed;
     a.v = h->v;
     a.c = h->c;
     a.b = h->b;
@@ -622,7 +636,7 @@ int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
     return FH_ERR_UNSUPPORTED;
   if (ds->quant != FH_QUANT_NONE && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
     return FH_ERR_UNSUPPORTED;
-  if (ds->flags & ~FH_FLAG_COOPERATIVE) return FH_ERR_INVALID_ARG;
+  if (ds->flags & ~(FH_FLAG_COOPERATIVE | FH_FLAG_BORROW_E)) return FH_ERR_INVALID_ARG;
   // C2T must be a permutation of [0, v) (equal-size clusters, dense table)
   {
     std::vector<uint8_t> seen((size_t)ds->v, 0);
@@ -645,6 +659,7 @@ int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
   h->esize = es;
   h->row_bytes = row_bytes;
   h->flags = ds->flags;
+  h->borrowed = (ds->flags & FH_FLAG_BORROW_E) != 0;
   const int st = prepare_impl(ds, h);
   if (st != FH_OK) {
     (void)hipStreamSynchronize(static_cast<hipStream_t>(ds->stream));
@@ -728,8 +743,9 @@ int flashhead_mc_marginal(fh_handle* h, const void* H, int32_t p, float tau,
   a.cl = reinterpret_cast<float2*>(ws + L.cl);
   a.H = static_cast<const uint8_t*>(H);
   a.nchunk = nchunk;
-  a.Ec = h->Ec;
-  a.row_bytes = h->row_bytes;
+  a.Ec = h->rows;
+  a.row_bytes = h->rows_stride;
+  a.borrowed = h->borrowed;
   a.b = h->b;
   a.t2row = h->t2row;
   a.v = h->v;
@@ -745,8 +761,9 @@ int flashhead_mc_marginal(fh_handle* h, const void* H, int32_t p, float tau,
 
   // a cluster's rows in the cluster-major copy, folded into (max, sum)
   RowdotArgs ra{};
-  ra.base = h->Ec;
-  ra.row_bytes = h->row_bytes;
+  ra.base = h->rows;
+  ra.row_bytes = h->rows_stride;
+  ra.borrowed = h->borrowed;
   ra.nchunk = nchunk;
   ra.nrows = h->b;
   ra.c2t = h->c2t;

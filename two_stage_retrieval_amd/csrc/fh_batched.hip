@@ -206,6 +206,9 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
     int64_t arow = row0[i] + lr;
     if constexpr (MODE != kGmFlash) arow = arow < nrows_total ? arow : nrows_total - 1;
+    if constexpr (MODE == kGmFlash) {
+      if (a.borrowed) arow = a.c2t[arow];  // the caller's E: the candidate's token row
+    }
     ap[i] = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
   }
   // H chunk staging: thread t moves kHP 16-byte pieces per chunk

@@ -20,8 +20,11 @@ enum RowdotMode : int {
 };
 
 struct RowdotArgs {
-  const uint8_t* base;   // E or C
+  const uint8_t* base;   // E (dense, or the caller's E when borrowed), C, or the
+                         // cluster-major copy of E (gather)
   int64_t row_bytes;     // stride between rows of `base`
+  int borrowed;          // gather: base is the caller's E, candidate rows are
+                         // token rows C2T[k, j] (else rows k*b + j of the copy)
   int nchunk;            // 16-byte chunks per row
   const uint8_t* H;      // B x d, row stride h_bytes
   int64_t h_bytes;
@@ -72,8 +75,10 @@ struct SelectArgs {
 };
 
 struct Stage2mArgs {
-  const uint8_t* base;   // C (scores), cluster-major copy of E (flash) or E (dense)
+  const uint8_t* base;   // C (scores), cluster-major copy of E or the caller's E
+                         // (flash, see borrowed) or E (dense)
   int64_t row_bytes;
+  int borrowed;          // flash: base is the caller's E, rows C2T[k, j]
   int64_t v;             // rows of E (dense)
   int c;                 // rows of C (scores)
   int b, d, B, p;
@@ -179,8 +184,9 @@ struct McArgs {
   float2* cl;             // c (max, sum of exp(x - max)) of z / tau over a cluster's rows
   const uint8_t* H;       // the hidden vector (d elements of E's type)
   int nchunk;             // 16-byte chunks per row
-  const uint8_t* Ec;      // cluster-major copy of E
-  int64_t row_bytes;
+  const uint8_t* Ec;      // cluster-major copy of E, or the caller's E (borrowed)
+  int64_t row_bytes;      // stride of Ec's rows
+  int borrowed;
   int b;
   const int32_t* t2row;   // v: row of each token in the cluster-major copy
   int64_t v;

@@ -92,10 +92,10 @@ __global__ __launch_bounds__(kMcThreads) void mc_query_kernel(McArgs a) {
     if (lane == 0 && a.error) atomicOr(a.error, 16u);
     tok = 0;
   }
-  const int32_t row = a.t2row[tok];
+  const int32_t row = a.t2row[tok];  // its row in the cluster-major order
   float hreg[NCH][Chunk<TE>::kElems];
   load_h<TE, NCH>(a.H, a.nchunk, lane, hreg);
-  const uint8_t* rowp = a.Ec + (int64_t)row * a.row_bytes;
+  const uint8_t* rowp = a.Ec + (int64_t)(a.borrowed ? tok : row) * a.row_bytes;
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {

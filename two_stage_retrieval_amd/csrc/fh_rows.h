@@ -239,6 +239,17 @@ __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32
         const int64_t kc = k < 0 ? 0 : (k >= a.nclusters ? a.nclusters - 1 : k);  // stay in the table
         phys[rr] = kc * (int64_t)b + slot;  // row of the cluster-major copy
       }
+      if (a.borrowed) {
+        // the caller's E: candidate row = token C2T[k, slot], looked up
+        // before the row can be requested (lane rr fetches entry rr)
+        int64_t mine = phys[0];
+#pragma unroll
+        for (int rr = 1; rr < R; ++rr)
+          if (lane == rr) mine = phys[rr];
+        const int32_t tk = lane < R ? a.c2t[mine] : 0;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) phys[rr] = (uint32_t)__builtin_amdgcn_readlane(tk, rr);
+      }
     } else {
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
@@ -264,7 +275,7 @@ __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32
       if (lane == rr) myphys = phys[rr];
     uint32_t mytok = (uint32_t)myphys;
     if constexpr (MODE == kRowGather) {
-      if (lane < R) mytok = (uint32_t)a.c2t[myphys];
+      if (lane < R && !a.borrowed) mytok = (uint32_t)a.c2t[myphys];
     }
     float acc[R];
 #pragma unroll

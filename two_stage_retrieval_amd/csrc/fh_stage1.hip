@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       uint64_t m = 0;
 #pragma unroll
       for (int w = 0; w < kS1Waves; ++w) m = s_best[w] > m ? s_best[w] : m;
-      if (m != 0) {
+      if (m != 0 && !args.s2.borrowed) {
         // waves 1 .. kS1Waves - 1 split the cluster's rows in 1 KB requests
         const int64_t k = (int64_t)(0xFFFFFFFFu - (uint32_t)m);  // < c
         const int64_t bytes = (int64_t)args.s2.b * args.s2.row_bytes;
