@@ -278,6 +278,28 @@ def select_clusters(scores, p: int, mode: str = "greedy", tau: float = 1.0,
 
 
 # --------------------------------------------------------------------------
+# adaptive probe count.  [notes] "Potential improvements" names an adaptive
+# number of probes (fewer for easy tokens, more for hard ones) and gives no
+# rule.  Reading taken: probe every cluster whose stage-1 softmax weight at
+# temperature tau is at least eps times the largest weight, that is every k
+# with s_k / tau >= max_j s_j / tau - ln(1 / eps), and clamp the count to
+# [p_min, p_max].  Greedy decoding uses tau = 1 for the rule.
+# --------------------------------------------------------------------------
+
+
+def adaptive_p(scores, tau: float, eps: float, p_min: int, p_max: int):
+    """Returns (p', margin): p' the clamped count, margin the distance (in
+    units of s / tau) from the threshold to the nearest score."""
+    if not (0.0 < eps <= 1.0) or not (1 <= p_min <= p_max):
+        raise ValueError("need 0 < eps <= 1 and 1 <= p_min <= p_max")
+    x = np.asarray(scores, dtype=np.float64) / tau
+    thr = x.max() - math.log(1.0 / eps)
+    n = int(np.count_nonzero(x >= thr))
+    margin = float(np.min(np.abs(x - thr)))
+    return min(max(n, p_min), p_max), margin
+
+
+# --------------------------------------------------------------------------
 # stage 2 ([notes] Module 1: the dense c x b table lets candidate i be found
 # by modulo arithmetic; Overall architecture: exact logits of the p*b rows)
 # --------------------------------------------------------------------------
@@ -340,21 +362,30 @@ class StepResult:
     keys2: np.ndarray        # decode keys over T
     m2: float
     lse: float
+    p: int = 0               # probes used (the adaptive count, or p)
+    ma: float = math.inf     # margin of the adaptive count (inf if fixed)
 
 
 def flashhead_step(rows_f64: Callable, c2t, h_f64, p: int, *,
                    C_f64=None, int4=None, mode: str = "greedy",
-                   tau: float = 1.0, seed: int = 0) -> StepResult:
-    """[notes] Overall architecture + Figure 1, in the pages' order."""
+                   tau: float = 1.0, seed: int = 0,
+                   adaptive=None) -> StepResult:
+    """[notes] Overall architecture + Figure 1, in the pages' order.
+    adaptive = (p_min, eps): the probe count is adaptive_p(scores, tau (1 for
+    greedy), eps, p_min, p) instead of p."""
     if int4 is not None:
         scores = stage1_scores_int4(int4[0], int4[1], h_f64)
     else:
         scores = stage1_scores(C_f64, h_f64)
+    ma = math.inf
+    if adaptive is not None:
+        p_min, eps = adaptive
+        p, ma = adaptive_p(scores, tau if mode == "sample" else 1.0, eps, p_min, p)
     S, keys1, m1 = select_clusters(scores, p, mode, tau, seed)
     T = candidate_tokens(S, c2t)
     z = exact_logits(rows_f64, T, h_f64)
     tok, m2, lse, keys2 = decode_tokens(T, z, mode, tau, seed)
-    return StepResult(tok, S, scores, keys1, m1, T, z, keys2, m2, lse)
+    return StepResult(tok, S, scores, keys1, m1, T, z, keys2, m2, lse, p, ma)
 
 
 def dense_logits(rows_f64: Callable, v: int, h_f64,

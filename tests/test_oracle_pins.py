@@ -700,3 +700,105 @@ def test_kmeans_first_assignment_ignores_row_scale():
     b_ = ref.kmeans_equal_size(scaled, 12, init, max_iter=1)
     assert np.array_equal(a.c2t, b_.c2t)
     assert a.iters == 1 and sorted(a.c2t.ravel().tolist()) == list(range(96))
+
+
+# --------------------------------------------------------------------------
+# adaptive probe count (reading of [notes] "Potential improvements": probe
+# every cluster whose softmax weight at temperature tau is at least eps times
+# the largest one, clamped to [p_min, p_max])
+# --------------------------------------------------------------------------
+
+def _adaptive_bruteforce(scores, tau, eps, p_min, p_max):
+    """The rule as a ratio of softmax weights, one cluster at a time."""
+    top = max(scores)
+    n = 0
+    for s in scores:
+        if math.exp((s - top) / tau) >= eps:
+            n += 1
+    return min(max(n, p_min), p_max)
+
+
+def test_adaptive_p_matches_the_weight_ratio_bruteforce():
+    rng = np.random.default_rng(71)
+    checked = 0
+    for trial in range(400):
+        c = int(rng.integers(2, 40))
+        s = rng.standard_normal(c) * rng.uniform(0.2, 4.0)
+        tau = float(rng.uniform(0.3, 2.0))
+        eps = float(rng.uniform(1e-4, 1.0))
+        p_min = int(rng.integers(1, c + 1))
+        p_max = int(rng.integers(p_min, c + 1))
+        p, margin = ref.adaptive_p(s, tau, eps, p_min, p_max)
+        if margin < 1e-9:
+            continue  # a score on the threshold: the two forms may round apart
+        assert p == _adaptive_bruteforce(list(s), tau, eps, p_min, p_max)
+        checked += 1
+    assert checked > 350
+
+
+def test_adaptive_p_limits_and_monotonicity():
+    rng = np.random.default_rng(72)
+    s = rng.standard_normal(500) * 2.0
+    # a vanishing eps probes every cluster: the upper clamp
+    assert ref.adaptive_p(s, 1.0, 1e-300, 3, 200)[0] == 200
+    assert ref.adaptive_p(s, 1.0, 1e-300, 3, 500)[0] == 500
+    # eps = 1 keeps only the largest score: the lower clamp
+    assert ref.adaptive_p(s, 1.0, 1.0, 1, 500)[0] == 1
+    assert ref.adaptive_p(s, 1.0, 1.0, 7, 500)[0] == 7
+    # a larger eps never probes more clusters; a higher temperature flattens
+    # the weights and never probes fewer
+    prev = 10 ** 9
+    for eps in np.geomspace(1e-6, 1.0, 40):
+        p, _ = ref.adaptive_p(s, 1.3, float(eps), 1, 500)
+        assert 1 <= p <= prev
+        prev = p
+    prev = 0
+    for tau in np.geomspace(0.1, 10.0, 40):
+        p, _ = ref.adaptive_p(s, float(tau), 0.01, 1, 500)
+        assert p >= prev
+        prev = p
+    # exact ties at the top all count
+    t = np.array([3.0, 1.0, 3.0, 3.0, -2.0])
+    assert ref.adaptive_p(t, 1.0, 1.0, 1, 5)[0] == 3
+    # invalid arguments
+    for bad in ((0.0, 1, 5), (1.5, 1, 5), (0.5, 0, 5), (0.5, 4, 3)):
+        with pytest.raises(ValueError):
+            ref.adaptive_p(t, 1.0, *bad)
+
+
+def test_adaptive_p_invariances():
+    rng = np.random.default_rng(73)
+    s = rng.standard_normal(300)
+    p0, m0 = ref.adaptive_p(s, 0.8, 0.05, 2, 250)
+    assert m0 > 1e-6
+    # a constant added to every score, or scores and tau scaled together,
+    # leave the weights' ratios and so the count unchanged
+    assert ref.adaptive_p(s + 17.25, 0.8, 0.05, 2, 250)[0] == p0
+    assert ref.adaptive_p(s * 4.0, 3.2, 0.05, 2, 250)[0] == p0
+    # one cluster far above the rest: an easy token takes the fewest probes
+    peaked = s.copy()
+    peaked[42] = 50.0
+    assert ref.adaptive_p(peaked, 1.0, 0.01, 4, 250)[0] == 4
+    # equal scores: every cluster qualifies
+    assert ref.adaptive_p(np.zeros(300), 1.0, 0.5, 1, 250)[0] == 250
+
+
+def test_adaptive_step_is_the_fixed_step_at_the_chosen_count(tiny_workload):
+    """The adaptive step probes p' clusters and is then the plain step with
+    p = p' (greedy: tau = 1 for the rule; sampling: the step's tau)."""
+    head, H = tiny_workload
+    rows = ref.rows_accessor(head.E, "f32")
+    C64 = head.C_given.astype(np.float64)
+    ps = set()
+    for i in range(8):
+        h = H[i].astype(np.float64)
+        for mode, tau, seed in (("greedy", 1.0, 0), ("sample", 0.7, 100 + i)):
+            a = ref.flashhead_step(rows, head.c2t, h, 32, C_f64=C64, mode=mode, tau=tau,
+                                   seed=seed, adaptive=(2, 0.2))
+            want, _ = ref.adaptive_p(ref.stage1_scores(C64, h), tau, 0.2, 2, 32)
+            assert a.p == want and len(a.S) == want and len(a.T) == want * head.c2t.shape[1]
+            f = ref.flashhead_step(rows, head.c2t, h, want, C_f64=C64, mode=mode, tau=tau,
+                                   seed=seed)
+            assert a.token == f.token and np.array_equal(a.S, f.S)
+            ps.add(want)
+    assert len(ps) > 1  # the count does adapt on this workload
