@@ -114,6 +114,10 @@ def main():
                     help="time N iterations of the equal-size spherical k-means "
                          "(Module 1) on the workload's E instead of the decode step; "
                          "prints its own JSON line")
+    ap.add_argument("--adaptive", type=float, default=0.0, metavar="EPS",
+                    help="adaptive probe count: clusters whose stage-1 softmax weight is at "
+                         "least EPS times the largest, clamped to [--p-min, p]")
+    ap.add_argument("--p-min", type=int, default=16)
     ap.add_argument("--bf16-stage1", action="store_true",
                     help="score the centroids in bf16 even where the workload names INT4")
     ap.add_argument("--flags", type=int, default=0,
@@ -193,9 +197,17 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] prepared in {time.time() - t0:.1f}s")
 
+    out_p = torch.empty(B, dtype=torch.int32, device=dev)
+
     def call(i):
         x = batches[i % nb]
-        if sample:
+        if args.adaptive:
+            if sample:
+                fh.sample_adaptive(x, args.p_min, wl.p, args.adaptive, tau, seeds[i % nb],
+                                   out=out, out_p=out_p)
+            else:
+                fh.greedy_adaptive(x, args.p_min, wl.p, args.adaptive, out=out, out_p=out_p)
+        elif sample:
             fh.sample(x, wl.p, tau, seeds[i % nb], out=out)
         else:
             fh.greedy(x, wl.p, out=out)
@@ -310,18 +322,40 @@ def main():
         log(f"[bench] dense cold p50 {statistics.median(dense_cold):.2f} us"
             + (f", warm {dense_warm:.2f} us" if dense_warm else ""))
 
-    # union of selected clusters per batch (U = p at batch 1)
+    # union of selected clusters per batch (U = p at batch 1; with the
+    # adaptive count, U and the bytes follow the probes each call takes)
     U = wl.p
+    p_stats = None
+    if args.adaptive:
+        counts = []
+        for i in range(nb):
+            call(i)
+            counts.append(out_p.cpu().numpy().copy())
+        counts = np.concatenate(counts)
+        p_stats = {"eps": args.adaptive, "p_min": args.p_min, "p_max": wl.p,
+                   "mean": round(float(counts.mean()), 1),
+                   "p10": int(np.percentile(counts, 10)), "p50": int(np.percentile(counts, 50)),
+                   "p90": int(np.percentile(counts, 90)), "rows": int(len(counts))}
+        log(f"[bench] adaptive probes: {p_stats}")
+        if B == 1:
+            U = int(round(counts.mean()))
     if B > 1:
         us = []
         for i in range(min(nb, 8)):
             dbg = {"clusters": torch.empty(B, wl.p, dtype=torch.int32, device=dev)}
             evict()
-            if sample:
+            if args.adaptive and sample:
+                fh.sample_adaptive(batches[i], args.p_min, wl.p, args.adaptive, tau, seeds[i],
+                                   out=out, debug=dbg)
+            elif args.adaptive:
+                fh.greedy_adaptive(batches[i], args.p_min, wl.p, args.adaptive, out=out,
+                                   debug=dbg)
+            elif sample:
                 fh.sample(batches[i], wl.p, tau, seeds[i], out=out, debug=dbg)
             else:
                 fh.greedy(batches[i], wl.p, out=out, debug=dbg)
-            us.append(len(np.unique(dbg["clusters"].cpu().numpy())))
+            cl = dbg["clusters"].cpu().numpy()
+            us.append(len(np.unique(cl[cl != 0x7FFFFFFF])))
         U = int(round(statistics.mean(us)))
     total_b, s1_b, s2_b = algorithmic_bytes(wl, B, U, int4)
     cold_p50 = statistics.median(cold)
@@ -367,7 +401,8 @@ def main():
                             "(Table 3, other hardware): context only",
         "dtype": wl.dtype if not int4 else "int4+bf16",
         "data": "synthetic (seeded generator, pages' head shapes)",
-        "config": {"workload": f"{wl.name} {'sample' if sample else 'greedy'} B={B}",
+        "config": {"workload": f"{wl.name} {'sample' if sample else 'greedy'} B={B}"
+                               + (f" adaptive eps={args.adaptive}" if args.adaptive else ""),
                    "v": wl.v, "d": wl.d, "c": wl.c, "b": wl.b, "p": wl.p,
                    "batch": B, "timing": "cold (1 GiB read-only flush before each call)",
                    "flags": args.flags},
@@ -375,6 +410,7 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": total_b,
         "union_clusters": U,
+        "adaptive_probes": p_stats,
         "cold_p90_us": round(cold_p90, 3),
         "warm_us": round(warm, 3) if warm else None,
         "streaming_read_gbs": round(stream_gbs, 1),

@@ -199,6 +199,31 @@ int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p,
                      float* out_lse, const fh_debug* dbg, void* stream);
 
 /*
+ * Adaptive probe count (the notes' "Potential improvements": fewer probes
+ * for easy tokens, more for hard ones; the pages give no rule, the rule here
+ * is this library's reading).  Per row r, p'_r = the number of clusters
+ * whose stage-1 softmax weight at temperature tau is at least eps times the
+ * largest weight, i.e. of k with s_k / tau >= max_j s_j / tau - ln(1 / eps),
+ * clamped to [p_min, p_max]; greedy decoding reads the rule at tau = 1.  The
+ * step then runs as flashhead_greedy / flashhead_sample with p = p'_r for
+ * that row (the count uses the plain scores; in sampling mode the p'_r
+ * clusters are the Gumbel-top-p'_r draws).
+ *   p_min, p_max  1 <= p_min <= p_max <= max_p
+ *   eps           0 < eps <= 1 (1: only the top score's ties; toward 0: p_max)
+ *   out_p         device, B int32 counts p'_r, or NULL
+ * The debug outputs hold p_max entries per row: entries [p'_r, p_max) of
+ * `clusters` read 0x7FFFFFFF, and candidate entries past p'_r * b are not
+ * written.  Other conventions as for flashhead_greedy / flashhead_sample.
+ */
+int flashhead_greedy_adaptive(fh_handle* h, const void* H, int32_t B, int32_t p_min,
+                              int32_t p_max, float eps, int32_t* out_tokens,
+                              int32_t* out_p, const fh_debug* dbg, void* stream);
+int flashhead_sample_adaptive(fh_handle* h, const void* H, int32_t B, int32_t p_min,
+                              int32_t p_max, float eps, float tau, const uint64_t* seeds,
+                              int32_t* out_tokens, float* out_lse, int32_t* out_p,
+                              const fh_debug* dbg, void* stream);
+
+/*
  * Monte Carlo marginal (notes, Module 4 and Formula 7): the estimate of
  * p(v | h) for each query token v as the mean over n_draws independent
  * draws S_i of
@@ -344,7 +369,7 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
  * synchronously (0 when every key reads pending, every selection entry -1,
  * every merge slot and the set's go word zero, and the device's launch
  * count matches the handle's; otherwise bit 0 keys, 1 selection, 2 slots,
- * 3 go word, 4 launch count), 12 the single-launch decode kernel's
+ * 3 go word, 4 launch count, 5 plain scores), 12 the single-launch decode kernel's
  * workgroups that one compute unit holds at once (occupancy API, measured
  * at prepare), 13 the device's compute units, 14 fh_desc.flags.
  * The decode calls are asynchronous and cannot return what goes wrong

@@ -44,6 +44,7 @@ EXPORTED = [
     "flashhead_profile_end", "flashhead_last_hip_error", "flashhead_stream_read",
     "flashhead_mc_workspace_bytes", "flashhead_mc_marginal", "flashhead_kmeans",
     "flashhead_plan_step", "dense_head_static", "flashhead_trace_read",
+    "flashhead_greedy_adaptive", "flashhead_sample_adaptive",
 ]
 FH_DENSE_STATIC_MAX_BATCH = 16
 
@@ -88,6 +89,12 @@ def _load() -> C.CDLL:
     lib.flashhead_sample.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp,
                                      C.POINTER(fh_debug), vp]
     lib.flashhead_sample.restype = C.c_int
+    lib.flashhead_greedy_adaptive.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp,
+                                              C.POINTER(fh_debug), vp]
+    lib.flashhead_greedy_adaptive.restype = C.c_int
+    lib.flashhead_sample_adaptive.argtypes = [vp, vp, i32, i32, i32, f32, f32, vp, vp, vp,
+                                              vp, C.POINTER(fh_debug), vp]
+    lib.flashhead_sample_adaptive.restype = C.c_int
     lib.dense_head_workspace_bytes.argtypes = [i32]
     lib.dense_head_workspace_bytes.restype = C.c_size_t
     lib.dense_head.argtypes = [vp, i64, i32, i32, i64, vp, i32, i32, f32, vp,
@@ -253,6 +260,27 @@ def flashhead_sample(handle: int, H, B: int, p: int, tau: float, seeds,
            "flashhead_sample")
 
 
+def flashhead_greedy_adaptive(handle: int, H, B: int, p_min: int, p_max: int, eps: float,
+                              out_tokens, out_p=None, debug: Optional[dict] = None,
+                              stream=None) -> None:
+    dbg = _debug(debug)
+    _check(lib.flashhead_greedy_adaptive(handle, _ptr(H), B, p_min, p_max, eps,
+                                         _ptr(out_tokens), _ptr(out_p),
+                                         dbg[0] if dbg else None, _stream(stream)),
+           "flashhead_greedy_adaptive")
+
+
+def flashhead_sample_adaptive(handle: int, H, B: int, p_min: int, p_max: int, eps: float,
+                              tau: float, seeds, out_tokens, out_lse=None, out_p=None,
+                              debug: Optional[dict] = None, stream=None) -> None:
+    dbg = _debug(debug)
+    _check(lib.flashhead_sample_adaptive(handle, _ptr(H), B, p_min, p_max, eps, tau,
+                                         _ptr(seeds), _ptr(out_tokens), _ptr(out_lse),
+                                         _ptr(out_p), dbg[0] if dbg else None,
+                                         _stream(stream)),
+           "flashhead_sample_adaptive")
+
+
 def flashhead_mc_workspace_bytes(handle: int, n_draws: int, p: int,
                                  n_tokens: int) -> int:
     return int(lib.flashhead_mc_workspace_bytes(handle, n_draws, p, n_tokens))
@@ -390,6 +418,26 @@ class FlashHead:
             out = torch.empty(B, dtype=torch.int32, device=H.device)
         flashhead_sample(self.handle, H, B, p, tau, seeds, out, out_lse,
                          debug, stream)
+        return out
+
+    def greedy_adaptive(self, H, p_min: int, p_max: int, eps: float, out=None, out_p=None,
+                        debug=None, stream=None):
+        torch = _torch()
+        B = H.shape[0]
+        if out is None:
+            out = torch.empty(B, dtype=torch.int32, device=H.device)
+        flashhead_greedy_adaptive(self.handle, H, B, p_min, p_max, eps, out, out_p, debug,
+                                  stream)
+        return out
+
+    def sample_adaptive(self, H, p_min: int, p_max: int, eps: float, tau: float, seeds,
+                        out=None, out_lse=None, out_p=None, debug=None, stream=None):
+        torch = _torch()
+        B = H.shape[0]
+        if out is None:
+            out = torch.empty(B, dtype=torch.int32, device=H.device)
+        flashhead_sample_adaptive(self.handle, H, B, p_min, p_max, eps, tau, seeds, out,
+                                  out_lse, out_p, debug, stream)
         return out
 
     def mc_marginal(self, H, p: int, tau: float, seeds, tokens, out=None,

@@ -19,7 +19,8 @@ OBJ_TRACE = os.path.join(ROOT, "_build", "trace")
 LIB = os.path.join(PKG, "libflashhead.so")
 LIB_TRACE = os.path.join(PKG, "libflashhead_trace.so")
 
-SOURCES = ["fh_api.hip", "fh_stage1.hip", "fh_rowdot.hip", "fh_select.hip",
+SOURCES = ["fh_api.hip", "fh_stage1.hip", "fh_decode_b1_adapt.hip", "fh_rowdot.hip",
+           "fh_select.hip",
            "fh_prepare.hip", "fh_batched.hip", "fh_mc.hip",
            "fh_kmeans.hip"]
 

@@ -46,6 +46,7 @@ struct fh_handle {
   int b1_blocks_per_cu = 0;         // decode workgroups one compute unit holds at once
   int flags = 0;                    // FH_FLAG_*
   float* b1_keys = nullptr;         // 2 x b1_key_stride(c), all bits set between launches
+  float* b1_raw = nullptr;          // 2 x b1_key_stride(c) plain scores (adaptive sampling)
   uint64_t* b1_slots = nullptr;     // 2 x kDecodeB1SlotStride words, zero between launches
   float2* b1_lse = nullptr;         // kDecodeB1SlotStride words
   int32_t* b1_sel = nullptr;        // 2 x kDecodeB1MaxP, -1 between launches
@@ -261,6 +262,8 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * b1_key_stride(c) * 4));
   FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * b1_key_stride(c) * 4, s));
+  FH_TRY(alloc(h, &h->b1_raw, (size_t)2 * b1_key_stride(c) * 4));
+  FH_TRY(hipMemsetAsync(h->b1_raw, 0xFF, (size_t)2 * b1_key_stride(c) * 4, s));
   FH_TRY(alloc(h, &h->b1_slots, (size_t)2 * kDecodeB1SlotStride * 8));
   FH_TRY(hipMemsetAsync(h->b1_slots, 0, (size_t)2 * kDecodeB1SlotStride * 8, s));
   FH_TRY(alloc(h, &h->b1_lse, (size_t)kDecodeB1SlotStride * 8));
@@ -297,11 +300,22 @@ int plan_path(int c, int b, int d, int64_t row_bytes, int dtype, bool int4, int 
   return 2;
 }
 
+// adaptive (nullable): p_min and eps of the adaptive probe count, p its upper
+// clamp, and the per-row counts' output
+struct AdaptiveCall {
+  int p_min;
+  float eps;
+  int32_t* out_p;
+};
+
 int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
               const uint64_t* seeds, int32_t* out, float* out_lse, const fh_debug* dbg,
-              void* stream) {
+              void* stream, const AdaptiveCall* adaptive = nullptr) {
   if (!h || !H || !out) return FH_ERR_INVALID_ARG;
   if (B < 1 || B > h->max_batch || p < 1 || p > h->max_p || p > h->c) return FH_ERR_INVALID_ARG;
+  if (adaptive && (adaptive->p_min < 1 || adaptive->p_min > p || !(adaptive->eps > 0.0f) ||
+                   !(adaptive->eps <= 1.0f)))
+    return FH_ERR_INVALID_ARG;
   if (mode == FH_MODE_SAMPLE && (!seeds || !(tau > 0.0f) || !isfinite(tau)))
     return FH_ERR_INVALID_ARG;
   if (!aligned16(H)) return FH_ERR_UNSUPPORTED;
@@ -326,6 +340,16 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   const bool sample = mode == FH_MODE_SAMPLE;
   const float inv_tau = sample ? 1.0f / tau : 1.0f;
   const int nchunk = (int)(h->row_bytes / 16);
+  Adaptive ad{};
+  if (adaptive) {
+    ad.on = 1;
+    ad.p_min = adaptive->p_min;
+    ad.L = (float)log(1.0 / (double)adaptive->eps);
+    ad.rt = sample ? inv_tau : 1.0f;  // greedy decoding reads the rule at tau = 1
+    ad.out_p = adaptive->out_p;
+  }
+  // adaptive sampling counts on plain scores while the keys carry noise
+  const bool raw_scores = adaptive && sample;
 
 
   const bool int4 = h->quant != FH_QUANT_NONE;
@@ -357,6 +381,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   s1.select = (!batched && stage1_selects(h->c)) ? 1 : 0;  // path 1 selects inside its launch too
   s1.p = p;
   s1.zcut = select_zcut(h->c, p);
+  s1.ad = ad;
+  s1.raw = (raw_scores && !batched) ? h->keys + s1.part_stride : nullptr;  // slice 1
+  s1.raw_keys = raw_scores && batched;
   s1.counters = h->counters;
   s1.sel = h->sel;
   s1.sel_stride = h->max_p;
@@ -399,6 +426,8 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     f.s2 = gather_args();
     f.s1.keys = h->b1_keys;
     f.s1.key_stride = b1_key_stride(h->c);
+    f.raw = h->b1_raw;
+    f.s1.raw = raw_scores ? h->b1_raw : nullptr;  // a flag here: the kernel picks the set
     f.s2.part_best = h->b1_slots;
     f.s2.lse_part = h->b1_lse;
     f.sel = h->b1_sel;
@@ -450,7 +479,10 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     a.sample = sample;
     a.inv_tau = inv_tau;
     a.seeds = seeds;
-    a.dbg_scores = ksplit > 1 && dbg ? dbg->scores : nullptr;
+    a.form_keys = s1.raw_keys;
+    a.raw = s1.raw;
+    a.ad = ad;
+    a.dbg_scores = (ksplit > 1 || a.form_keys) && dbg ? dbg->scores : nullptr;
     if (batched && B < kUnionMinRows) {
       a.ulist = h->ulist;
       a.ucount = h->ucount;
@@ -681,6 +713,23 @@ int flashhead_sample(fh_handle* h, const void* H, int32_t B, int32_t p, float ta
                      const uint64_t* seeds, int32_t* out_tokens, float* out_lse,
                      const fh_debug* dbg, void* stream) {
   return step_impl(h, H, B, p, FH_MODE_SAMPLE, tau, seeds, out_tokens, out_lse, dbg, stream);
+}
+
+int flashhead_greedy_adaptive(fh_handle* h, const void* H, int32_t B, int32_t p_min,
+                              int32_t p_max, float eps, int32_t* out_tokens, int32_t* out_p,
+                              const fh_debug* dbg, void* stream) {
+  const AdaptiveCall ad{p_min, eps, out_p};
+  return step_impl(h, H, B, p_max, FH_MODE_GREEDY, 1.0f, nullptr, out_tokens, nullptr, dbg,
+                   stream, &ad);
+}
+
+int flashhead_sample_adaptive(fh_handle* h, const void* H, int32_t B, int32_t p_min,
+                              int32_t p_max, float eps, float tau, const uint64_t* seeds,
+                              int32_t* out_tokens, float* out_lse, int32_t* out_p,
+                              const fh_debug* dbg, void* stream) {
+  const AdaptiveCall ad{p_min, eps, out_p};
+  return step_impl(h, H, B, p_max, FH_MODE_SAMPLE, tau, seeds, out_tokens, out_lse, dbg, stream,
+                   &ad);
 }
 
 size_t flashhead_mc_workspace_bytes(const fh_handle* h, int32_t n_draws, int32_t p,
@@ -1005,6 +1054,9 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
         if (slots[(size_t)j * 16] != 0ull) bits |= 4;
       if (go[set] != 0u) bits |= 8;
       if ((uint64_t)ep != (h->b1_launches & 0xFFFFFFFFull)) bits |= 16;
+      FH_TRY(hipMemcpy(keys.data(), h->b1_raw + set * ks, (size_t)ks * 4, hipMemcpyDeviceToHost));
+      for (int k = 0; k < h->c; ++k)
+        if (keys[(size_t)k] != 0xFFFFFFFFu) bits |= 32;
       *value = bits;
       break;
     }

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
       const int k = kq0 + q;
       if (k >= a.c) continue;
       const float s = tot[nt][q];
-      const float key = a.sample ? s * a.inv_tau + gq[q] : s;
+      // raw_keys: the plain score (the select forms the key after counting)
+      const float key = (a.sample && !a.raw_keys) ? s * a.inv_tau + gq[q] : s;
       a.keys[(int64_t)r * a.key_stride + k] = key;
       if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = s;
     }
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
           const int64_t k = kq0 + q;
           if (k >= a.c) continue;
           const float sc = acc[i][nt][q];
-          if (S > 1) {  // partial score over this K slice; the select sums the slices
+          if (S > 1 || a.raw_scores) {  // partial or plain score; the select forms the key
             a.keys[sp * a.part_stride + (int64_t)r * a.key_stride + k] = sc;
             continue;
           }
@@ -528,6 +529,7 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   S = S > nchunks ? nchunks : S;
   m.ksplit = S;
   m.part_stride = a.part_stride;
+  m.raw_scores = a.raw_keys;
   *ksplit = S;
   const int64_t units = groups * S;
   const int grid = (int)(units < 4096 ? units : 4096);

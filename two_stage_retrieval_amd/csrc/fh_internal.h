@@ -13,6 +13,18 @@ constexpr int kArriveCounters = 32;
 constexpr int kArriveStride = 32;  // uint32 per counter: one 128-byte line each
 constexpr int kArriveWords = kArriveCounters * kArriveStride;
 
+// Adaptive probe count (the selecting workgroup's rule, see adaptive_count in
+// fh_select.h).  `on` = 0: the call's p probes every row.
+struct Adaptive {
+  int on;
+  int p_min;          // the call's p is the upper clamp
+  float L;            // ln(1 / eps)
+  float rt;           // 1 / tau of the rule (1 for greedy decoding)
+  int32_t* out_p;     // device, B probe counts, or null
+};
+// A selection entry past a row's probe count (never a cluster id).
+constexpr int32_t kUnusedEntry = 0x7FFFFFFF;
+
 // Which rows a row-dot launch visits and what it does with each dot product.
 enum RowdotMode : int {
   kRowGather = 1,  // candidate rows C2T[sel[i / b], i % b]; decode epilogue
@@ -62,8 +74,12 @@ struct SelectArgs {
   float inv_tau;
   const uint64_t* seeds;
   float* dbg_scores;     // B x c
+  int form_keys;         // keys holds plain scores (nparts == 1 too): form the keys here
+  const float* raw;      // adaptive count on these plain scores (B x key_stride) when the
+                         // keys already carry noise; null otherwise
   int c, p;
   float zcut;            // histogram range hint (select_zcut; 0: none)
+  Adaptive ad;
   int32_t* sel;          // B x sel_stride, written ascending
   int sel_stride;
   uint64_t* masks;       // optional: per-cluster bitmask of selecting rows
@@ -107,6 +123,8 @@ struct Stage2mArgs {
   float* dbg_scores;
   int ksplit;            // K slices (scores); > 1: keys holds per-slice partial scores
   int64_t part_stride;   // floats between the slices' B x key_stride blocks
+  int raw_scores;        // scores epilogue: plain scores even at one slice (the
+                         // select then forms the keys)
 };
 constexpr int kMaxKSplit = 4;
 // batched stage 2 walks the union list below this many rows, every cluster
@@ -127,6 +145,9 @@ struct Stage1Args {
   int64_t key_stride;
   int64_t part_stride;    // batched stage 1: floats between K-slice partial blocks
   float* dbg_scores;      // optional raw scores, B x c
+  float* raw;             // adaptive sampling: B x key_stride plain scores beside the
+                          // keys (the rule counts on scores, the selection on keys)
+  int raw_keys;           // batched INT4 stage 1: store plain scores as the keys
   int sample;
   float inv_tau;
   const uint64_t* seeds;
@@ -134,6 +155,7 @@ struct Stage1Args {
   int select;
   int p;
   float zcut;             // histogram range hint (select_zcut; 0: none)
+  Adaptive ad;
   uint32_t* counters;     // B x kArriveWords arrival counters (zero between calls)
   int32_t* sel;           // B x sel_stride, written ascending
   int sel_stride;
@@ -159,8 +181,11 @@ constexpr int kDecodeB1MaxP = 2048;
 constexpr int kDecodeB1MaxGrid = 512;
 constexpr int64_t kDecodeB1SlotStride = (int64_t)kDecodeB1MaxGrid * 16;  // u64 words
 struct DecodeB1Args {
-  Stage1Args s1;
+  Stage1Args s1;         // s1.raw non-null: this launch publishes plain scores
   RowdotArgs s2;
+  float* raw;            // 2 x key_stride plain scores (adaptive sampling), every
+                         // entry pending before the first launch; a launch that
+                         // uses its set marks it pending again once it is read
   int32_t* sel;
   uint32_t* epoch;
   int64_t slot_stride;
@@ -228,6 +253,10 @@ hipError_t decode_b1_occupancy(int dtype, bool int4, int nchunk, int c, int* blo
 // coop: through the cooperative launch API (all workgroups resident together)
 hipError_t launch_decode_b1(const DecodeB1Args& a, int dtype, bool int4, int grid, bool coop,
                             hipStream_t s, const Timing* tm = nullptr);
+// the variant with the adaptive probe count (fh_decode_b1_adapt.hip)
+hipError_t launch_decode_b1_adaptive(const DecodeB1Args& a, int dtype, bool int4, int grid,
+                                     bool coop, hipStream_t s, const Timing* tm);
+hipError_t decode_b1_occupancy_adaptive(int dtype, bool int4, int nchunk, int c, int* blocks);
 hipError_t launch_centroid_means(const uint8_t* E, int64_t row_bytes, int dtype, int d,
                                  const int32_t* c2t, int c, int b, void* C, hipStream_t s);
 bool batched_supported(int dtype, int d, int B, bool int4);

@@ -31,7 +31,9 @@ __global__ __launch_bounds__(kRowdotThreads) void rowdot_kernel(RowdotArgs a) {
   const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
   uint64_t best = 0;
   Lse lse = lse_empty();
-  dot_rows<TE, NCH, R, MODE>(a, r, a.sel + (int64_t)r * a.sel_stride, hreg, seed, lane,
+  // (the gather may follow an adaptive count: entries past it are skipped)
+  dot_rows<TE, NCH, R, MODE, false, MODE == kRowGather>(a, r, a.sel + (int64_t)r * a.sel_stride,
+                                                        hreg, seed, lane,
                                     (int64_t)blockIdx.x * kRowdotWaves + wave,
                                     (int64_t)gridDim.x * kRowdotWaves, best, lse);
   // workgroup 0 of the batch row folds every workgroup's partial

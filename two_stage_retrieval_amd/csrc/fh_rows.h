@@ -49,15 +49,20 @@ constexpr uint32_t kKeyPending = 0xFFFFFFFFu;
 
 // With `keys_next`, also marks the row pending in the key buffer of the next
 // launch (single-launch batch-1 decode).
+// With `raw`, also stores the plain score there (adaptive sampling: the
+// probe count is taken on scores, the selection on keys).
 template <bool COHERENT>
 __device__ __forceinline__ float publish_key(const Stage1Args& a, float* keys, float* keys_next,
-                                             float* dbg, uint64_t seed, int row, float score) {
+                                             float* dbg, uint64_t seed, int row, float score,
+                                             float* raw = nullptr) {
   const float key =
       a.sample ? score * a.inv_tau + gumbel(seed, kStreamCluster, (uint32_t)row) : score;
   if constexpr (COHERENT) {
     __hip_atomic_store(keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (raw) __hip_atomic_store(raw + row, score, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     keys[row] = key;
+    if (raw) raw[row] = score;
   }
   if (keys_next) keys_next[row] = __uint_as_float(kKeyPending);
   if (dbg) dbg[row] = score;
@@ -105,7 +110,8 @@ __device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys
                                                 float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
                                                 int g, int wstride,
                                                 uint4 (&data)[kS1Rows][NCH],
-                                                uint64_t* best_key = nullptr) {
+                                                uint64_t* best_key = nullptr,
+                                                float* raw = nullptr) {
   using CK = Chunk<TE>;
   const int ngroups = (a.c + kS1Rows - 1) / kS1Rows;
   unpack_h<TE, NCH>(hraw, hreg);
@@ -125,7 +131,7 @@ __device__ __forceinline__ void score_rows_from(const Stage1Args& a, float* keys
       if (lane == rr) mine = acc[rr];
     if (lane < kS1Rows && row0 + lane < a.c)
       track_best_key(best_key,
-                     publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine),
+                     publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row0 + lane, mine, raw),
                      row0 + lane);
     g += wstride;
     if (g < ngroups) load_centroid_group<TE, NCH>(a, g, lane, data);
@@ -136,11 +142,11 @@ template <typename TE, int NCH, bool COHERENT>
 __device__ __forceinline__ void score_rows(const Stage1Args& a, float* keys, float* keys_next,
                                            float* dbg, uint64_t seed, const uint4 (&hraw)[NCH],
                                            float (&hreg)[NCH][Chunk<TE>::kElems], int lane,
-                                           int w0, int wstride) {
+                                           int w0, int wstride, float* raw = nullptr) {
   uint4 data[kS1Rows][NCH];
   if (w0 < (a.c + kS1Rows - 1) / kS1Rows) load_centroid_group<TE, NCH>(a, w0, lane, data);
   score_rows_from<TE, NCH, COHERENT>(a, keys, keys_next, dbg, seed, hraw, hreg, lane, w0,
-                                     wstride, data);
+                                     wstride, data, nullptr, raw);
 }
 
 // INT4 centroids (notes, Module 3): one 16-row group tile per wave step,
@@ -150,7 +156,8 @@ template <bool COHERENT>
 __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* keys,
                                                  float* keys_next, float* dbg, uint64_t seed,
                                                  const float* s_h, int lane, int w0,
-                                                 int wstride, uint64_t* best_key = nullptr) {
+                                                 int wstride, uint64_t* best_key = nullptr,
+                                                 float* raw = nullptr) {
   const int q = lane >> 4, rin = lane & 15;
   const int G = a.groups;
   for (int tile = w0; tile < a.ntiles; tile += wstride) {
@@ -167,8 +174,8 @@ __device__ __forceinline__ void score_int4_tiles(const Stage1Args& a, float* key
     acc += __shfl_xor(acc, 32, kWave);
     const int row = tile * 16 + rin;
     if (q == 0 && row < a.c)
-      track_best_key(best_key, publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc),
-                     row);
+      track_best_key(best_key,
+                     publish_key<COHERENT>(a, keys, keys_next, dbg, seed, row, acc, raw), row);
   }
 }
 
@@ -200,8 +207,9 @@ __device__ __forceinline__ int64_t selected_cluster(const int32_t* sel_row, int6
 }
 
 // `win` (optional): entries [wlo, wlo + wn) of the selection already in
-// LDS; other entries are read from sel_row.
-template <typename TE, int NCH, int R, int MODE, bool POLL = false>
+// LDS; other entries are read from sel_row.  SKIP: entries may be
+// kUnusedEntry (past an adaptive probe count); their rows are skipped.
+template <typename TE, int NCH, int R, int MODE, bool POLL = false, bool SKIP = false>
 __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32_t* sel_row,
                                          const float (&hreg)[NCH][Chunk<TE>::kElems],
                                          uint64_t seed, int lane, int64_t w0, int64_t wstride,
@@ -218,6 +226,9 @@ __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32
   for (int64_t g = w0; g < ngroups; g += wstride) {
     const int64_t row0 = g * R;
     int64_t phys[R];
+    bool live[R];  // gather: rows of an entry past the row's probe count are not
+#pragma unroll   // read or folded (their entry is kUnusedEntry)
+    for (int rr = 0; rr < R; ++rr) live[rr] = true;
     if constexpr (MODE == kRowGather) {
       // candidate i is slot i mod b of selection entry i / b (candidate
       // indices fit 32 bits: there are at most v of them); one division per
@@ -230,14 +241,22 @@ __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32
       for (int rr = 0; rr < R; ++rr) {
         if (rr > 0 && row0 + rr >= a.nrows) {
           phys[rr] = phys[rr - 1];  // tail: reread a row, result dropped
+          live[rr] = false;
           continue;
         }
         if (rr > 0 && ++slot == b) {
           slot = 0;
           k = entry(++j);
         }
+        if constexpr (SKIP) live[rr] = k >= 0 && k < a.nclusters;
         const int64_t kc = k < 0 ? 0 : (k >= a.nclusters ? a.nclusters - 1 : k);  // stay in the table
         phys[rr] = kc * (int64_t)b + slot;  // row of the cluster-major copy
+      }
+      if constexpr (SKIP) {
+        bool any = false;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) any = any || live[rr];
+        if (!any) continue;  // a group wholly past the row's probe count
       }
       if (a.borrowed) {
         // the caller's E: candidate row = token C2T[k, slot], looked up
@@ -286,11 +305,15 @@ __device__ __forceinline__ void dot_rows(const RowdotArgs& a, int r, const int32
       acc[rr] = wave_sum(s);
     }
     float mine = acc[0];
+    bool mylive = live[0];
 #pragma unroll
     for (int rr = 1; rr < R; ++rr)
-      if (lane == rr) mine = acc[rr];
+      if (lane == rr) {
+        mine = acc[rr];
+        mylive = live[rr];
+      }
     const int64_t myrow = row0 + lane;
-    if (lane < R && myrow < a.nrows) {
+    if (lane < R && myrow < a.nrows && mylive) {
       const float x = mine * a.inv_tau;
       const float kx = a.sample ? x + gumbel(seed, kStreamToken, mytok) : mine;
       const uint64_t key = decode_key(kx, mytok);

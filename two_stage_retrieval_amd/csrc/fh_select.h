@@ -42,6 +42,8 @@ struct SelSmem {
   float fmin[16], fmax[16], fsum[16], fsq[16];
   int w[2][16];                    // block-scan wave totals, alternating buffers
   int misc[8];
+  float amax[16];                  // adaptive count: wave maxima and counts
+  int acnt[16];
 };
 
 __device__ __forceinline__ float sel_from_ordered(uint32_t u) {
@@ -171,11 +173,14 @@ __device__ __forceinline__ void select_wave_range(const uint32_t (&u)[IPT], int 
 // from the boundary bin follow, ascending, at [ngt, p).  Readers that wait
 // for the entries they need start on most of them before the boundary bin
 // is resolved.  Without it the p ids are ascending.
+//
+// p_fill > p (an adaptive count p below the call's p_fill): out[p .. p_fill)
+// (and early[p .. p_fill)) are set to kUnusedEntry.
 template <int NT, int IPT, bool COHERENT_OUT, bool PREPARED = false>
 __device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int p, float zcut,
                                                  int32_t* out, uint64_t* masks, int row,
                                                  uint32_t* error, SelSmem& sm,
-                                                 int32_t* early = nullptr) {
+                                                 int32_t* early = nullptr, int p_fill = 0) {
   static_assert(IPT % 4 == 0 && IPT <= 32 && (IPT & (IPT - 1)) == 0, "items per thread");
   constexpr int NW = NT / kWave;
   constexpr int BPT = kSelBins / NT;  // histogram bins per thread in the scan
@@ -421,13 +426,66 @@ __device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int 
     }
     if (masks) atomicOr(reinterpret_cast<unsigned long long*>(masks + k), 1ull << row);
   }
+  for (int i = p + t; i < p_fill; i += NT) {  // entries past an adaptive count
+    if constexpr (COHERENT_OUT) {
+      __hip_atomic_store(out + i, kUnusedEntry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      out[i] = kUnusedEntry;
+    }
+  }
   if (early) {
     __syncthreads();
     for (int i = ngt + t; i < p; i += NT)
       __hip_atomic_store(early + i, out[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = p + t; i < p_fill; i += NT)
+      __hip_atomic_store(early + i, kUnusedEntry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   FH_TRACE_SEL(7);
   if (t == NT - 1 && incl != p && error) atomicOr(error, 1u);
+}
+
+// ---------------------------------------------------------------------------
+// The adaptive probe count of one row (reading of the notes' "Potential
+// improvements": fewer probes for easy tokens, more for hard ones; the rule
+// is the design's): every cluster whose score s satisfies
+//   s * rt >= max_k (s_k * rt) - L,   rt = 1 / tau, L = ln(1 / eps),
+// that is every cluster whose softmax weight at temperature tau is at least
+// eps times the largest, counts; the count is clamped to [p_min, p_max].
+// `us` holds the row's plain scores as thread t owns them (raw fp32 bits,
+// ids [t * IPT, t * IPT + IPT)).  Two barriers; the result is the same in
+// every thread.
+// ---------------------------------------------------------------------------
+template <int NT, int IPT>
+__device__ __forceinline__ int adaptive_count(const uint32_t (&us)[IPT], int c, const Adaptive& ad,
+                                              int p_max, SelSmem& sm) {
+  constexpr int NW = NT / kWave;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  const int k0 = t * IPT;
+  const int nvalid = c - k0 < 0 ? 0 : (c - k0 < IPT ? c - k0 : IPT);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j)
+    if (j < nvalid) mx = fmaxf(mx, __uint_as_float(us[j]) * ad.rt);
+  mx = wave_max(mx);
+  if (lane == 0) sm.amax[wave] = mx;
+  __syncthreads();
+  float m = sm.amax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.amax[w]);
+  const float thr = m - ad.L;
+  uint32_t n = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j)
+    n += (j < nvalid && __uint_as_float(us[j]) * ad.rt >= thr) ? 1u : 0u;
+  n = wave_sum_u32(n);
+  if (lane == 0) sm.acnt[wave] = (int)n;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += sm.acnt[w];
+  return tot < ad.p_min ? ad.p_min : (tot > p_max ? p_max : tot);
 }
 
 // Loads the keys and selects (see select_load_keys / select_from_keys).

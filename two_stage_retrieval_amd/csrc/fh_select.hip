@@ -15,9 +15,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int r = blockIdx.x;
   uint32_t u[IPT];
   select_load_keys<IPT, false>(a.keys + (int64_t)r * a.key_stride, (int)a.key_stride, u);
-  if (a.nparts > 1) {
-    // the scores arrive as K-slice partials: all slices are loaded before
-    // any is added, then summed in slice order; then the keys are formed
+  int p = a.p;  // the row's probe count
+  if (a.nparts > 1 || a.form_keys) {
+    // the scores arrive as K-slice partials (or, with form_keys, as plain
+    // scores): all slices are loaded before any is added, then summed in
+    // slice order; then the keys are formed
     // (sampling: score / tau + Gumbel noise of stream 0, one Philox block per
     // four consecutive ids)
     const int k0 = threadIdx.x * IPT;
@@ -33,6 +35,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 #pragma unroll
         for (int j = 0; j < IPT; ++j)
           u[j] = __float_as_uint(__uint_as_float(u[j]) + __uint_as_float(v[sp - 1][j]));
+    // the adaptive count reads the plain scores, before any noise
+    if (a.ad.on) p = adaptive_count<kSelThreads, IPT>(u, a.c, a.ad, a.p, sm);
     const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
 #pragma unroll
     for (int j4 = 0; j4 < IPT; j4 += 4) {
@@ -48,9 +52,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
         if (a.sample) u[j4 + q] = __float_as_uint(sc * a.inv_tau + gj[q]);
       }
     }
+  } else if (a.ad.on) {
+    if (a.raw) {  // the keys carry noise: count on the plain scores beside them
+      uint32_t us[IPT];
+      select_load_keys<IPT, false>(a.raw + (int64_t)r * a.key_stride, (int)a.key_stride, us);
+      p = adaptive_count<kSelThreads, IPT>(us, a.c, a.ad, a.p, sm);
+    } else {
+      p = adaptive_count<kSelThreads, IPT>(u, a.c, a.ad, a.p, sm);  // greedy: keys are scores
+    }
   }
-  select_from_keys<kSelThreads, IPT, false>(u, a.c, a.p, a.zcut, a.sel + (int64_t)r * a.sel_stride,
-                                            a.masks, r, a.error, sm);
+  if (a.ad.on && a.ad.out_p && threadIdx.x == 0) a.ad.out_p[r] = p;
+  select_from_keys<kSelThreads, IPT, false>(u, a.c, p, a.zcut, a.sel + (int64_t)r * a.sel_stride,
+                                            a.masks, r, a.error, sm, nullptr,
+                                            a.ad.on ? a.p : 0);
 }
 
 // The union of the rows' selected clusters (non-zero masks), ascending, as
