@@ -22,7 +22,7 @@ LIB_TRACE = os.path.join(PKG, "libflashhead_trace.so")
 SOURCES = ["fh_api.hip", "fh_stage1.hip", "fh_decode_b1_adapt.hip", "fh_rowdot.hip",
            "fh_select.hip",
            "fh_prepare.hip", "fh_batched.hip", "fh_mc.hip",
-           "fh_kmeans.hip"]
+           "fh_kmeans.hip", "fh_host.cpp"]
 
 # Packed-fp32 instructions are disabled for all device code.
 HIPCC_FLAGS = [

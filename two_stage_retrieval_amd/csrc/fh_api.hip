@@ -1,5 +1,6 @@
-// C ABI of libflashhead: argument validation, the prepared handle and its
-// workspace, the host INT4 quantizer, and the enqueue of each decode step.
+// C ABI of libflashhead: the prepared handle and its workspace, and the
+// enqueue of each decode step (descriptor checks and the INT4 quantizer are
+// host-only code in fh_host.cpp).
 #include <math.h>
 #include <string.h>
 
@@ -7,6 +8,7 @@
 #include <new>
 #include <vector>
 
+#include "fh_host.h"
 #include "fh_internal.h"
 
 using namespace fh;
@@ -75,8 +77,6 @@ int64_t key_stride(int c) { return ((int64_t)c + 3) & ~(int64_t)3; }
 // each workgroup's run of keys fills lines of its own
 int64_t b1_key_stride(int c) { return ((int64_t)c + 31) & ~(int64_t)31; }
 
-int esize_of(int dtype) { return dtype == FH_DTYPE_F32 ? 4 : dtype == FH_DTYPE_BF16 ? 2 : 0; }
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 void drop_profile(fh_handle* h) {
   for (hipEvent_t e : h->prof_ev) (void)hipEventDestroy(e);
@@ -100,70 +100,6 @@ hipError_t alloc(fh_handle* h, T** p, size_t bytes) {
   h->bytes += (int64_t)bytes;
   *p = static_cast<T*>(q);
   return hipSuccess;
-}
-
-// nearest bf16 value of a double (8 significant bits), ties to even
-double round_bf16(double x) {
-  if (x == 0.0 || !isfinite(x)) return x;
-  int e = 0;
-  (void)frexp(x, &e);
-  const int se = (e - 8) > -133 ? (e - 8) : -133;
-  return ldexp(nearbyint(ldexp(x, -se)), se);
-}
-uint16_t bf16_bits(double x) {
-  const float f = (float)x;
-  uint32_t u;
-  memcpy(&u, &f, 4);
-  return (uint16_t)(u >> 16);
-}
-double bf16_value(uint16_t b) {
-  const uint32_t u = (uint32_t)b << 16;
-  float f;
-  memcpy(&f, &u, 4);
-  return (double)f;
-}
-
-// Symmetric per-group INT4 codes (groups of 128 columns): scale = bf16(amax/7),
-// code = round-half-even(x / scale) clipped to [-8, 7]; packed in 16-row tiles.
-// x = C - shift (shift: d values, or NULL for none); C - shift is exact in
-// double for bf16 C and shift.
-void quantize_int4(const uint16_t* C, const double* shift, int c, int d,
-                   std::vector<uint8_t>& codes, std::vector<uint16_t>& scales, int* ntiles_out,
-                   int* groups_out) {
-  const int G = d / 128, ntiles = (c + 15) / 16;
-  codes.assign((size_t)ntiles * G * 1024, 0);
-  scales.assign((size_t)ntiles * G * 16, 0);
-  std::vector<int8_t> q(128);
-  for (int k = 0; k < c; ++k) {
-    const int t = k / 16, rin = k % 16;
-    for (int g = 0; g < G; ++g) {
-      const uint16_t* src = C + (size_t)k * d + (size_t)g * 128;
-      const double* sh = shift ? shift + (size_t)g * 128 : nullptr;
-      double x[128];
-      double amax = 0.0;
-      for (int j = 0; j < 128; ++j) {
-        x[j] = bf16_value(src[j]) - (sh ? sh[j] : 0.0);
-        amax = fmax(amax, fabs(x[j]));
-      }
-      const double s = round_bf16(amax / 7.0);
-      for (int j = 0; j < 128; ++j) {
-        double qq = s > 0.0 ? nearbyint(x[j] / s) : 0.0;
-        qq = qq < -8.0 ? -8.0 : (qq > 7.0 ? 7.0 : qq);
-        q[j] = (int8_t)qq;
-      }
-      scales[((size_t)t * G + g) * 16 + rin] = bf16_bits(s);
-      for (int quarter = 0; quarter < 4; ++quarter) {
-        const int lane = quarter * 16 + rin;
-        uint8_t* dst = codes.data() + (((size_t)t * G + g) * 64 + lane) * 16;
-        for (int j = 0; j < 16; ++j) {
-          const int col = quarter * 32 + 2 * j;
-          dst[j] = (uint8_t)((q[col] & 0xF) | ((q[col + 1] & 0xF) << 4));
-        }
-      }
-    }
-  }
-  *ntiles_out = ntiles;
-  *groups_out = G;
 }
 
 // the HIP error behind the last FH_ERR_HIP / FH_ERR_OOM of this thread
@@ -216,8 +152,7 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   {
     // token -> row of the cluster-major copy (the inverse of the table)
     std::vector<int32_t> inv((size_t)v);
-    const int32_t* t = static_cast<const int32_t*>(ds->c2t);
-    for (int64_t r = 0; r < v; ++r) inv[(size_t)t[r]] = (int32_t)r;
+    invert_permutation(ds->c2t, v, inv.data());
     FH_TRY(alloc(h, &h->t2row, (size_t)v * 4));
     FH_TRY(hipMemcpyAsync(h->t2row, inv.data(), (size_t)v * 4, hipMemcpyHostToDevice, s));
     FH_TRY(hipStreamSynchronize(s));  // the host vector dies at scope end
@@ -227,13 +162,7 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
     FH_TRY(hipMemcpyAsync(hostC.data(), h->C, hostC.size() * 2, hipMemcpyDeviceToHost, s));
     FH_TRY(hipStreamSynchronize(s));
     std::vector<double> mu;
-    if (h->quant == FH_QUANT_INT4_G128_MEAN) {
-      // bf16 of the column means: the sum of c bf16 values is exact in double
-      mu.assign((size_t)d, 0.0);
-      for (int k = 0; k < c; ++k)
-        for (int j = 0; j < d; ++j) mu[j] += bf16_value(hostC[(size_t)k * d + j]);
-      for (int j = 0; j < d; ++j) mu[j] = round_bf16(mu[j] / c);
-    }
+    if (h->quant == FH_QUANT_INT4_G128_MEAN) column_mean_shift(hostC.data(), c, d, mu);
     std::vector<uint8_t> codes;
     std::vector<uint16_t> scales;
     quantize_int4(hostC.data(), mu.empty() ? nullptr : mu.data(), c, d, codes, scales,
@@ -649,35 +578,12 @@ const char* flashhead_status_string(int status) {
 int flashhead_prepare(const fh_desc* ds, fh_handle** out) {
   if (!out) return FH_ERR_INVALID_ARG;
   *out = nullptr;
-  if (!ds || !ds->E || !ds->c2t) return FH_ERR_INVALID_ARG;
-  if (ds->c < 1 || ds->b < 1 || ds->d < 1 || ds->v != (int64_t)ds->c * ds->b)
-    return FH_ERR_INVALID_ARG;
-  if (ds->max_batch < 1 || ds->max_batch > FH_MAX_BATCH) return FH_ERR_INVALID_ARG;
-  if (ds->max_p < 1 || ds->max_p > ds->c) return FH_ERR_INVALID_ARG;
-  if (ds->lde < ds->d) return FH_ERR_INVALID_ARG;
-  if (ds->v > (int64_t)INT32_MAX) return FH_ERR_UNSUPPORTED;
-  const int es = esize_of(ds->dtype);
-  if (!es) return FH_ERR_UNSUPPORTED;
-  if (ds->c > FH_MAX_C) return FH_ERR_UNSUPPORTED;
-  const int64_t row_bytes = (int64_t)ds->d * es;
-  if (row_bytes % 16 || (ds->lde * es) % 16 || row_bytes > FH_MAX_ROW_BYTES)
-    return FH_ERR_UNSUPPORTED;
-  if (!aligned16(ds->E) || (ds->C && !aligned16(ds->C))) return FH_ERR_UNSUPPORTED;
-  if (ds->quant != FH_QUANT_NONE && ds->quant != FH_QUANT_INT4_G128 &&
-      ds->quant != FH_QUANT_INT4_G128_MEAN)
-    return FH_ERR_UNSUPPORTED;
-  if (ds->quant != FH_QUANT_NONE && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
-    return FH_ERR_UNSUPPORTED;
-  if (ds->flags & ~(FH_FLAG_COOPERATIVE | FH_FLAG_BORROW_E)) return FH_ERR_INVALID_ARG;
-  // C2T must be a permutation of [0, v) (equal-size clusters, dense table)
   {
-    std::vector<uint8_t> seen((size_t)ds->v, 0);
-    for (int64_t i = 0; i < ds->v; ++i) {
-      const int32_t t = ds->c2t[i];
-      if (t < 0 || (int64_t)t >= ds->v || seen[(size_t)t]) return FH_ERR_NOT_PERMUTATION;
-      seen[(size_t)t] = 1;
-    }
+    const int st = validate_desc(ds);
+    if (st != FH_OK) return st;
   }
+  const int es = esize_of(ds->dtype);
+  const int64_t row_bytes = (int64_t)ds->d * es;
   fh_handle* h = new (std::nothrow) fh_handle();
   if (!h) return FH_ERR_OOM;
   h->v = ds->v;
