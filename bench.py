@@ -90,6 +90,16 @@ def algorithmic_bytes(wl, B, U, int4):
     return total, stage1, stage2
 
 
+def stream_all_bytes(wl, B, int4, with_lse):
+    """Bytes the all-cluster stream moves per launch: C (or its INT4 tiles),
+    every row of E with its token id, H, the stage-1 keys it writes and one
+    record per (16-row item, batch row)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    s1 = (wl.c * wl.d // 2 + wl.c * (wl.d // 128) * 2) if int4 else wl.c * wl.d * e
+    rec = (wl.v // 16) * B * (16 if with_lse else 8)
+    return s1 + wl.v * wl.d * e + wl.v * 4 + B * wl.d * e + B * wl.c * 4 + rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +314,9 @@ def main():
     path = fhb.flashhead_query(fh.handle, 10)
     if path == 1:  # the whole step is one kernel: there are no separate stages to time
         log(f"[bench] kernel us: decode_b1 {kern_us[0]:.2f} over {ncalls} calls")
+    elif path == 4:  # stage 1 and every cluster's records in one launch, then select + fold
+        log(f"[bench] kernels us: stream_all {kern_us[0]:.2f} select_fold {kern_us[1]:.2f} "
+            f"over {ncalls} calls")
     else:
         log(f"[bench] kernels us: stage1 {kern_us[0]:.2f} select {kern_us[1]:.2f} "
             f"stage2 {kern_us[2]:.2f} over {ncalls} calls")
@@ -367,6 +380,11 @@ def main():
     if path == 1:
         dom, dom_bytes, dom_name = 0, total_b, "decode_b1"
         kern_us = [kern_us[0], 0.0, 0.0]
+    elif path == 4:
+        # the stream reads C and every cluster's rows (not only the union)
+        # and writes one record per (16-row item, batch row)
+        dom, dom_name = 0, "stream_all"
+        dom_bytes = stream_all_bytes(wl, B, int4, False)  # the bench asks for no lse
     elif kern_us[2] >= kern_us[0]:
         dom, dom_bytes, dom_name = 2, s2_b, "stage2"
     else:
@@ -415,8 +433,11 @@ def main():
         "warm_us": round(warm, 3) if warm else None,
         "streaming_read_gbs": round(stream_gbs, 1),
         "kernels_us": ({"decode_b1": round(kern_us[0], 3)} if path == 1 else
+                       {"stream_all": round(kern_us[0], 3),
+                        "select_fold": round(kern_us[1], 3)} if path == 4 else
                        {"stage1": round(kern_us[0], 3), "select": round(kern_us[1], 3),
                         "stage2": round(kern_us[2], 3)}),
+        "path": path,
         "dense_us_cold": round(dense_p50, 3) if dense_p50 else None,
         "dense_us_warm": round(dense_warm, 3) if dense_warm else None,
         "speedup_vs_dense": round(dense_p50 / cold_p50, 3) if dense_p50 else None,

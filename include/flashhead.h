@@ -92,6 +92,14 @@ extern "C" {
                                 lives) instead of a cluster-major copy that
                                 prepare makes (v * d elements more device
                                 memory; the handle then does not keep E)    */
+#define FH_FLAG_STREAM_ALL 4  /* batched steps (B >= 2) always take the
+                                all-cluster stream (flashhead_plan_step,
+                                path 4)                                      */
+#define FH_FLAG_SELECT_FIRST 8 /* batched steps always select first and then
+                                stream only the selected clusters (path 3).
+                                With neither flag the plan picks by the
+                                expected share of clusters the batch selects;
+                                setting both is FH_ERR_INVALID_ARG           */
 
 /* Limits of this implementation. */
 #define FH_MAX_BATCH 64     /* rows per call                               */
@@ -364,7 +372,8 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
  * step's output is not to be trusted; bit 4: a query token outside [0, v)
  * in flashhead_mc_marginal), 10 the kernels the last step ran (0 none yet,
  * 1 the single-launch batch-1 decode, 2 stage 1 and stage 2 as separate
- * row-dot launches, 3 the batched matrix-core path), 11 the state of the
+ * row-dot launches, 3 the batched matrix-core path that selects first,
+ * 4 the batched all-cluster stream), 11 the state of the
  * single launch's buffer set that the next launch uses, read back
  * synchronously (0 when every key reads pending, every selection entry -1,
  * every merge slot and the set's go word zero, and the device's launch
@@ -382,13 +391,25 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
  * alone (no device call): returns 1 (the single-launch batch-1 decode:
  * stage 1, selection, stage 2 and decode in one launch of *grid
  * workgroups), 2 (stage 1 with the selection, then stage 2 with the decode,
- * as two row-dot launches; *grid = 0) or 3 (the batched matrix-core path;
- * *grid = 0), or FH_ERR_INVALID_ARG for sizes no step accepts.
+ * as two row-dot launches; *grid = 0), 3 (the batched matrix-core path:
+ * stage 1, the selection, then stage 2 over the clusters some row selected;
+ * *grid = 0) or 4 (the batched all-cluster stream: one launch computes the
+ * stage-1 keys and, for every cluster and batch row, the best decode key and
+ * log-sum-exp of the cluster's candidates, while no selection exists yet;
+ * then per row the selection and the fold of its selected clusters' records;
+ * *grid = 0), or FH_ERR_INVALID_ARG for sizes no step accepts.  Paths 3 and
+ * 4 give the same tokens for the same selections: path 4 reads every
+ * cluster once instead of only the selected ones, and drops the wait for
+ * the selection.  Without a path flag, batched steps take path 4 when the
+ * expected share of clusters that at least one of B independent rows
+ * selects, 1 - (1 - p / c)^B, is at least 0.8.  A step that asks for the
+ * candidates' logits (fh_debug.cand_ids) takes path 3.
  *   c, b, d, dtype, quant   as in fh_desc
  *   B, p                    as in flashhead_greedy / flashhead_sample
  *   num_cu                  compute units of the device (flashhead_query 13)
  *   blocks_per_cu           single-launch workgroups one compute unit holds
  *                           at once (flashhead_query 12)
+ *   flags                   fh_desc.flags
  * The single launch's workgroups wait on one another (the selection waits
  * for every stage-1 key, stage 2 for the selection, the merge for every
  * partial), so it is taken only when grid <= num_cu * blocks_per_cu.  In the
@@ -398,7 +419,7 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
  */
 int flashhead_plan_step(int32_t c, int32_t b, int32_t d, int32_t dtype, int32_t quant,
                         int32_t B, int32_t p, int32_t num_cu, int32_t blocks_per_cu,
-                        int32_t* grid);
+                        int32_t flags, int32_t* grid);
 
 /*
  * Measurement reference, not part of the method: reads `bytes` (a multiple

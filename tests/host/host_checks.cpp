@@ -138,7 +138,9 @@ static void desc_checks() {
        FH_ERR_UNSUPPORTED},
       {"int4 d % 128", [](fh_desc& x) { x.quant = FH_QUANT_INT4_G128; x.d = 64; x.lde = 64; },
        FH_ERR_UNSUPPORTED},
-      {"flags unknown", [](fh_desc& x) { x.flags = 4; }, FH_ERR_INVALID_ARG},
+      {"flags unknown", [](fh_desc& x) { x.flags = 16; }, FH_ERR_INVALID_ARG},
+      {"both path flags", [](fh_desc& x) { x.flags = FH_FLAG_STREAM_ALL | FH_FLAG_SELECT_FIRST; },
+       FH_ERR_INVALID_ARG},
       {"c over max", [](fh_desc& x) { x.c = FH_MAX_C + 1; x.b = 1; x.v = x.c; x.max_p = 1; },
        FH_ERR_UNSUPPORTED},
   };
@@ -155,6 +157,10 @@ static void desc_checks() {
     x.quant = FH_QUANT_INT4_G128_MEAN;
     CHECK(fh::validate_desc(&x) == FH_OK);
     x.flags = FH_FLAG_COOPERATIVE | FH_FLAG_BORROW_E;
+    CHECK(fh::validate_desc(&x) == FH_OK);
+    x.flags = FH_FLAG_STREAM_ALL;
+    CHECK(fh::validate_desc(&x) == FH_OK);
+    x.flags = FH_FLAG_SELECT_FIRST | FH_FLAG_BORROW_E;
     CHECK(fh::validate_desc(&x) == FH_OK);
     x = base;
     x.dtype = FH_DTYPE_F32;

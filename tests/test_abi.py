@@ -102,7 +102,9 @@ def test_prepare_rejects_bad_descriptors(fh):
     assert _prepare(fh, _desc(fh, c2t, quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
     assert _prepare(fh, _desc(fh, c2t, dtype=fh.FH_DTYPE_BF16, d=200,
                               quant=fh.FH_QUANT_INT4_G128_MEAN)) == uns
-    assert _prepare(fh, _desc(fh, c2t, flags=4)) == inv          # unknown flag bit
+    assert _prepare(fh, _desc(fh, c2t, flags=16)) == inv         # unknown flag bit
+    assert _prepare(fh, _desc(fh, c2t, flags=fh.FH_FLAG_STREAM_ALL |
+                              fh.FH_FLAG_SELECT_FIRST)) == inv      # both path flags
 
 
 @pytest.mark.parametrize("kind", ["repeat", "out_of_range", "negative"])
@@ -224,9 +226,21 @@ def test_plan_step_paths(fh):
     # a small head: the grid covers its rows, not every compute unit
     path, grid = plan(64, 64, 256, F32, 0, 1, 8, 256, 1)
     assert path == 1 and 1 <= grid < 256
-    # batches: matrix cores for bf16 with b a multiple of 16, else row-dot
+    # batches: matrix cores for bf16 with b a multiple of 16, else row-dot;
+    # select first while the rows' selections are expected to leave many
+    # clusters unread (1 - (1 - p/c)^B below 0.8), else stream every cluster
     assert plan(8016, 16, 2048, BF, 0, 2, 512, 256, 1) == (3, 0)
-    assert plan(8016, 16, 2048, BF, 0, 64, 512, 256, 1) == (3, 0)
+    assert plan(8016, 16, 2048, BF, 0, 16, 512, 256, 1) == (3, 0)     # 0.65
+    assert plan(8016, 16, 2048, BF, 0, 24, 512, 256, 1) == (3, 0)     # 0.79
+    assert plan(8016, 16, 2048, BF, 0, 25, 512, 256, 1) == (4, 0)     # 0.81
+    assert plan(8016, 16, 2048, BF, 0, 64, 512, 256, 1) == (4, 0)     # 0.985
+    assert plan(16384, 16, 1152, BF, fh.FH_QUANT_INT4_G128, 32, 1024, 256, 1) == (4, 0)
+    # the path flags override the rule, for batches only
+    SF, SA = fh.FH_FLAG_SELECT_FIRST, fh.FH_FLAG_STREAM_ALL
+    assert plan(8016, 16, 2048, BF, 0, 64, 512, 256, 1, SF) == (3, 0)
+    assert plan(8016, 16, 2048, BF, 0, 2, 512, 256, 1, SA) == (4, 0)
+    assert plan(8016, 16, 2048, BF, 0, 1, 512, 256, 1, SA) == (1, 256)
+    assert plan(50, 8, 128, BF, 0, 3, 7, 256, 1, SA) == (2, 0)
     assert plan(50, 8, 128, BF, 0, 3, 7, 256, 1) == (2, 0)
     assert plan(4096, 1, 256, F32, 0, 4, 8, 256, 1) == (2, 0)
     # more probes than the single launch holds, or more clusters than it selects
@@ -239,13 +253,15 @@ def test_plan_step_rejects_bad_sizes(fh):
     g = C.c_int32(7)
     inv = fh.FH_ERR_INVALID_ARG
     lib = fh.lib
-    assert lib.flashhead_plan_step(8016, 16, 2048, BF, 0, 1, 512, 256, 1, None) == inv
-    for args in ((8016, 16, 2048, BF, 0, 1, 8017, 256, 1),   # p > c
-                 (8016, 16, 2048, BF, 0, 0, 512, 256, 1),    # B = 0
-                 (8016, 16, 2048, BF, 0, 65, 512, 256, 1),   # B > FH_MAX_BATCH
-                 (8016, 16, 2048, 5, 0, 1, 512, 256, 1),     # dtype
-                 (8016, 16, 2048, BF, 3, 1, 512, 256, 1),    # quant
-                 (8016, 16, 2048, BF, 0, 1, 512, 0, 1)):     # no compute unit
+    assert lib.flashhead_plan_step(8016, 16, 2048, BF, 0, 1, 512, 256, 1, 0, None) == inv
+    both = fh.FH_FLAG_STREAM_ALL | fh.FH_FLAG_SELECT_FIRST
+    for args in ((8016, 16, 2048, BF, 0, 1, 8017, 256, 1, 0),   # p > c
+                 (8016, 16, 2048, BF, 0, 0, 512, 256, 1, 0),    # B = 0
+                 (8016, 16, 2048, BF, 0, 65, 512, 256, 1, 0),   # B > FH_MAX_BATCH
+                 (8016, 16, 2048, 5, 0, 1, 512, 256, 1, 0),     # dtype
+                 (8016, 16, 2048, BF, 3, 1, 512, 256, 1, 0),    # quant
+                 (8016, 16, 2048, BF, 0, 1, 512, 0, 1, 0),      # no compute unit
+                 (8016, 16, 2048, BF, 0, 64, 512, 256, 1, both)):  # both path flags
         assert lib.flashhead_plan_step(*args, C.byref(g)) == inv
         assert g.value == 0
 

@@ -35,6 +35,8 @@ FH_MODE_GREEDY = 0
 FH_MODE_SAMPLE = 1
 FH_FLAG_COOPERATIVE = 1
 FH_FLAG_BORROW_E = 2
+FH_FLAG_STREAM_ALL = 4
+FH_FLAG_SELECT_FIRST = 8
 
 EXPORTED = [
     "flashhead_prepare", "flashhead_destroy", "flashhead_greedy",
@@ -128,7 +130,7 @@ def _load() -> C.CDLL:
     lib.flashhead_kmeans.argtypes = [vp, i64, i32, i32, i64, i32, vp, i32, vp, vp,
                                      C.POINTER(i32), vp]
     lib.flashhead_kmeans.restype = C.c_int
-    lib.flashhead_plan_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
+    lib.flashhead_plan_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                         C.POINTER(i32)]
     lib.flashhead_plan_step.restype = C.c_int
     lib.flashhead_trace_read.argtypes = [vp, i64, C.POINTER(i64), C.POINTER(i64)]
@@ -218,10 +220,10 @@ def flashhead_prepare(E, c2t: np.ndarray, C_init=None, *, v=None, d=None,
 
 
 def flashhead_plan_step(c: int, b: int, d: int, dtype: int, quant: int, B: int,
-                        p: int, num_cu: int, blocks_per_cu: int):
+                        p: int, num_cu: int, blocks_per_cu: int, flags: int = 0):
     """Host-only: (path, grid) a decode step of this shape takes."""
     g = C.c_int32()
-    st = lib.flashhead_plan_step(c, b, d, dtype, quant, B, p, num_cu, blocks_per_cu,
+    st = lib.flashhead_plan_step(c, b, d, dtype, quant, B, p, num_cu, blocks_per_cu, flags,
                                  C.byref(g))
     if st < 0:
         raise FlashHeadError(st, "flashhead_plan_step")

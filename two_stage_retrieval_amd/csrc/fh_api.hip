@@ -43,6 +43,9 @@ struct fh_handle {
   int32_t* ucount = nullptr;
   uint64_t* part_best = nullptr;    // stage-2 partials, grid x max_batch
   float2* part_lse = nullptr;
+  // all-cluster stream: one record per (16-row item, batch row)
+  uint64_t* all_best = nullptr;     // (v / 16) x max_batch
+  float2* all_lse = nullptr;
   // single-launch batch-1 decode
   int num_cu = 0;
   int b1_blocks_per_cu = 0;         // decode workgroups one compute unit holds at once
@@ -70,6 +73,8 @@ namespace {
 
 constexpr int kMaxGrid = 8192;       // largest grid.x of a decode launch
 constexpr int kDenseMaxGrid = 8192;  // dense: partial slots of the batched kernel (2 x 4096)
+constexpr double kStreamAllCover = 0.8;  // batched: expected selected share from which
+                                         // every cluster is streamed
 
 // selection keys of a batch row: c floats padded to a 16-byte multiple
 int64_t key_stride(int c) { return ((int64_t)c + 3) & ~(int64_t)3; }
@@ -189,6 +194,10 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   FH_TRY(alloc(h, &h->ucount, 4));
   FH_TRY(alloc(h, &h->part_best, (size_t)stage2_mfma_grid() * mb * 8));
   FH_TRY(alloc(h, &h->part_lse, (size_t)stage2_mfma_grid() * mb * 8));
+  if (mb >= 2 && h->b % 16 == 0 && batched_supported(h->dtype, d, 2, false)) {
+    FH_TRY(alloc(h, &h->all_best, (size_t)(v / 16) * mb * 8));
+    FH_TRY(alloc(h, &h->all_lse, (size_t)(v / 16) * mb * 8));
+  }
   FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * b1_key_stride(c) * 4));
   FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * b1_key_stride(c) * 4, s));
   FH_TRY(alloc(h, &h->b1_raw, (size_t)2 * b1_key_stride(c) * 4));
@@ -215,9 +224,17 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
 // one workgroup waits for the others, which never wait, so they progress as
 // long as the device holds more than B workgroups.
 int plan_path(int c, int b, int d, int64_t row_bytes, int dtype, bool int4, int B, int p,
-              int num_cu, int blocks_per_cu, int* grid) {
+              int num_cu, int blocks_per_cu, int flags, int* grid) {
   *grid = 0;
-  if (B >= 2 && b % 16 == 0 && batched_supported(dtype, d, B, int4)) return 3;
+  if (B >= 2 && b % 16 == 0 && batched_supported(dtype, d, B, int4)) {
+    if (flags & FH_FLAG_SELECT_FIRST) return 3;
+    if (flags & FH_FLAG_STREAM_ALL) return 4;
+    // expected share of clusters that at least one of B independent rows
+    // selects: when most clusters are read anyway, reading all of them
+    // without waiting for the selection costs less
+    const double cover = 1.0 - pow(1.0 - (double)p / c, (double)B);
+    return cover >= kStreamAllCover ? 4 : 3;
+  }
   if (B == 1 && stage1_selects(c)) {
     const int g = decode_b1_grid(c, p, (int)(row_bytes / 16), (c + 15) / 16, (int64_t)p * b,
                                  int4, num_cu);
@@ -283,9 +300,11 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
 
   const bool int4 = h->quant != FH_QUANT_NONE;
   int b1_grid = 0;
-  const int path = plan_path(h->c, h->b, h->d, h->row_bytes, h->dtype, int4, B, p, h->num_cu,
-                             h->b1_blocks_per_cu, &b1_grid);
-  const bool batched = path == 3;
+  int path = plan_path(h->c, h->b, h->d, h->row_bytes, h->dtype, int4, B, p, h->num_cu,
+                       h->b1_blocks_per_cu, h->flags, &b1_grid);
+  // the all-cluster stream keeps no candidate logits
+  if (path == 4 && dbg && dbg->cand_ids) path = 3;
+  const bool batched = path == 3 || path == 4;
 
   // stage 1 (+ selection by each batch row's last block on the GEMV path)
   Stage1Args s1{};
@@ -385,7 +404,72 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     }
   }
 
-  h->last_path = batched ? 3 : 2;
+  h->last_path = path;
+  if (path == 4) {
+    Stage2mArgs a{};
+    a.base = h->rows;
+    a.row_bytes = h->rows_stride;
+    a.borrowed = h->borrowed;
+    a.v = h->v;
+    a.c = h->c;
+    a.b = h->b;
+    a.d = h->d;
+    a.B = B;
+    a.p = p;
+    a.H = static_cast<const uint8_t*>(H);
+    a.h_bytes = h->row_bytes;
+    a.c2t = h->c2t;
+    a.sample = sample;
+    a.inv_tau = inv_tau;
+    a.seeds = seeds;
+    a.with_lse = out_lse != nullptr;
+    a.part_best = h->all_best;
+    a.part_lse = h->all_lse;
+    a.keys = h->keys;
+    a.key_stride = key_stride(h->c);
+    a.dbg_scores = dbg ? dbg->scores : nullptr;
+    a.raw_scores = raw_scores;
+    a.ksplit = 1;
+    a.cbase = static_cast<const uint8_t*>(h->C);
+    a.c_row_bytes = h->row_bytes;
+    a.n1 = int4 ? h->ntiles : (h->c + 15) / 16;
+    a.q4 = int4 ? h->q4 : nullptr;
+    a.q4s = int4 ? h->q4s : nullptr;
+    a.groups = h->groups;
+    SelectArgs sa{};
+    sa.keys = h->keys;
+    sa.key_stride = key_stride(h->c);
+    sa.c = h->c;
+    sa.p = p;
+    sa.zcut = s1.zcut;
+    sa.sel = h->sel;
+    sa.sel_stride = h->max_p;
+    sa.error = h->error;
+    sa.nparts = 1;
+    sa.part_stride = s1.part_stride;
+    sa.sample = sample;
+    sa.inv_tau = inv_tau;
+    sa.seeds = seeds;
+    sa.form_keys = raw_scores;
+    sa.ad = ad;
+    sa.dbg_scores = (raw_scores && dbg) ? dbg->scores : nullptr;
+    sa.fold_best = h->all_best;
+    sa.fold_lse = out_lse ? h->all_lse : nullptr;
+    sa.fold_sub = h->b / 16;
+    sa.fold_pitch = B;
+    sa.out_tokens = out;
+    sa.out_lse = out_lse;
+    FH_TRY(launch_stream_all(a, sa, s, t1, t2));
+    if (t3) {  // stage 2 ran inside the first launch
+      (void)hipEventRecord(t3->start, s);
+      (void)hipEventRecord(t3->stop, s);
+    }
+    if (dbg && dbg->clusters) {
+      FH_TRY(hipMemcpy2DAsync(dbg->clusters, (size_t)p * 4, h->sel, (size_t)h->max_p * 4,
+                              (size_t)p * 4, B, hipMemcpyDeviceToDevice, s));
+    }
+    return FH_OK;
+  }
   int ksplit = 1;
   if (batched) {
     FH_TRY(launch_stage1_mfma(s1, int4, B, s, t1, &ksplit));
@@ -540,16 +624,18 @@ extern "C" {
 const char* flashhead_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
 int flashhead_plan_step(int32_t c, int32_t b, int32_t d, int32_t dtype, int32_t quant, int32_t B,
-                        int32_t p, int32_t num_cu, int32_t blocks_per_cu, int32_t* grid) {
+                        int32_t p, int32_t num_cu, int32_t blocks_per_cu, int32_t flags,
+                        int32_t* grid) {
   if (!grid) return FH_ERR_INVALID_ARG;
   *grid = 0;
   const int es = esize_of(dtype);
   if (c < 1 || b < 1 || d < 1 || !es || B < 1 || B > FH_MAX_BATCH || p < 1 || p > c ||
       num_cu < 1 || blocks_per_cu < 0 || quant < FH_QUANT_NONE || quant > FH_QUANT_INT4_G128_MEAN)
     return FH_ERR_INVALID_ARG;
+  if ((flags & FH_FLAG_STREAM_ALL) && (flags & FH_FLAG_SELECT_FIRST)) return FH_ERR_INVALID_ARG;
   int g = 0;
   const int path = plan_path(c, b, d, (int64_t)d * es, dtype, quant != FH_QUANT_NONE, B, p,
-                             num_cu, blocks_per_cu, &g);
+                             num_cu, blocks_per_cu, flags, &g);
   *grid = g;
   return path;
 }

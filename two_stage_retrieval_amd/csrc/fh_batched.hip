@@ -44,29 +44,28 @@ __device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t w, int i) {
   return lo | hi;
 }
 
+// Scores of one INT4 tile (16 centroid rows) against the B hidden rows: lane
+// l ends with centroid rows 4 (l div 16) + q of the tile for batch rows
+// nt * 16 + (l mod 16) in tot[nt][q].
 template <int NT>
-__global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Args a, int B) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void int4_tile_scores(const uint8_t* q4, const uint16_t* q4s, int G,
+                                                 const uint8_t* H, int64_t h_bytes, int B,
+                                                 int tile, int lane, f32x4_t (&tot)[NT]) {
   const int slice = lane >> 4, lr = lane & 15;
   const uint8_t* hp[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     int j = nt * 16 + lr;
     j = j < B ? j : B - 1;
-    hp[nt] = a.H + (int64_t)j * a.h_bytes + (int64_t)(32 * slice) * 2;
+    hp[nt] = H + (int64_t)j * h_bytes + (int64_t)(32 * slice) * 2;
   }
-  const int tile = blockIdx.x * (kS1qThreads / kWave) + wave;
-  if (tile >= a.ntiles) return;
-  const int G = a.groups;
-  const uint4* codes = reinterpret_cast<const uint4*>(a.q4) + (int64_t)tile * G * kWave + lane;
-  f32x4_t tot[NT];
+  const uint4* codes = reinterpret_cast<const uint4*>(q4) + (int64_t)tile * G * kWave + lane;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) tot[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < G; ++g) {
     const uint4 w = codes[(int64_t)g * kWave];
     // scales of the 4 output rows of this lane: 4 (l div 16) + q
-    const uint2 sc2 = *reinterpret_cast<const uint2*>(a.q4s + ((int64_t)tile * G + g) * 16 + 4 * slice);
+    const uint2 sc2 = *reinterpret_cast<const uint2*>(q4s + ((int64_t)tile * G + g) * 16 + 4 * slice);
     const float sc[4] = {__uint_as_float(sc2.x << 16), __uint_as_float(sc2.x & 0xFFFF0000u),
                          __uint_as_float(sc2.y << 16), __uint_as_float(sc2.y & 0xFFFF0000u)};
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -89,6 +88,17 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 #pragma unroll
       for (int q = 0; q < 4; ++q) tot[nt][q] = fmaf(sc[q], part[nt][q], tot[nt][q]);
   }
+}
+
+template <int NT>
+__global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Args a, int B) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = lane >> 4, lr = lane & 15;
+  const int tile = blockIdx.x * (kS1qThreads / kWave) + wave;
+  if (tile >= a.ntiles) return;
+  f32x4_t tot[NT];
+  int4_tile_scores<NT>(a.q4, a.q4s, a.groups, a.H, a.h_bytes, B, tile, lane, tot);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + lr;
@@ -130,11 +140,20 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 //           and log-sum-exp;
 //   DENSE   the batched dense head: item rows are rows of E, every token a
 //           candidate for every batch row.
+//   ALL     stage 1 and stage 2 in one pass, before any selection: items
+//           [0, n1) are stage-1 items (16 centroid rows, or one INT4 tile
+//           scored by int4_tile_scores) with the SCORES epilogue; every
+//           later item is 16 candidate rows of a cluster, and each batch row
+//           gets one record per item (best decode key, and log-sum-exp), for
+//           every cluster whether or not the row will select it.  The
+//           select-and-fold kernel then keeps the records of the row's
+//           selected clusters only.
 // FLASH and DENSE write one partial per (workgroup, batch row).
 // ---------------------------------------------------------------------------
 constexpr int kGmThreads = 256;
 constexpr int kGmWaves = kGmThreads / kWave;
-enum GmMode : int { kGmScores = 0, kGmFlash = 1, kGmDense = 2 };
+enum GmMode : int { kGmScores = 0, kGmFlash = 1, kGmDense = 2, kGmAll = 3, kGmAllQ4 = 4 };
+// ALL with INT4 stage-1 tiles (kGmAllQ4) or 16-row bf16 centroid items (kGmAll)
 
 // KC: K per chunk (KC / 32 MFMA steps); a wave requests KC * 2 contiguous
 // bytes of each of its rows per chunk
@@ -152,12 +171,16 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int slice = lane >> 4, lr = lane & 15;
   const int B = a.B;
   const int sub = a.b / 16;
+  constexpr bool ALL = MODE == kGmAll || MODE == kGmAllQ4;
+  constexpr bool Q4 = MODE == kGmAllQ4;
   const int64_t nrows_total = MODE == kGmScores ? (int64_t)a.c : a.v;
   // FLASH walks the union list when there is one, else every cluster
-  // (skipping the ones no row selected)
+  // (skipping the ones no row selected); ALL walks the stage-1 items, then
+  // every cluster
   const int64_t nitems = MODE == kGmFlash
                              ? (a.ulist ? (int64_t)(*a.ucount) : (int64_t)a.c) * sub
-                             : (nrows_total + 15) / 16;
+                         : ALL ? a.n1 + (int64_t)a.c * sub
+                                          : (nrows_total + 15) / 16;
   const int nchunks = a.d / KC;
   uint64_t best[NT];
   Lse lse[NT];
@@ -196,6 +219,26 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     int64_t it = item0 + wave * IT + i;
     const bool live = it < nitems;
     it = live ? it : nitems - 1;
+    if constexpr (ALL) {
+      if (it < a.n1) {
+        // stage-1 item: 16 centroid rows (none to stream for an INT4 tile)
+        kc[i] = -1;
+        row0[i] = it * 16;
+        mask[i] = (live && !Q4) ? ~0ull : 0ull;
+        int64_t crow = row0[i] + lr;
+        crow = crow < a.c ? crow : a.c - 1;
+        ap[i] = a.cbase + crow * a.c_row_bytes + (int64_t)(8 * slice) * 2;
+      } else {
+        const int64_t ie = it - a.n1;
+        kc[i] = ie / sub;
+        row0[i] = kc[i] * a.b + (ie % sub) * 16;
+        mask[i] = live ? ~0ull : 0ull;
+        int64_t arow = row0[i] + lr;
+        if (a.borrowed) arow = a.c2t[arow];
+        ap[i] = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
+      }
+      continue;
+    }
     if constexpr (MODE == kGmFlash) {
       kc[i] = a.ulist ? a.ulist[it / sub] : it / sub;
       row0[i] = kc[i] * a.b + (it % sub) * 16;
@@ -271,10 +314,14 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
+  // a unit of INT4 stage-1 tiles only streams no rows: it skips the K walk
+  const bool unit_rows = !Q4 || item0 + kGmWaves * IT > a.n1;
+  if (unit_rows) {
   load_h(cbeg);
   load_a(a0, cbeg);
   store_h(0);
-  for (int c = cbeg; c < cend; c += 2) {
+  }
+  for (int c = cbeg; unit_rows && c < cend; c += 2) {
     // chunk c from buffer 0 / registers a0; prefetch chunk c + 1
     __syncthreads();
     if (c + 1 < cend) { load_h(c + 1); load_a(a1, c + 1); }
@@ -286,6 +333,81 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     if (c + 2 < cend) { load_h(c + 2); load_a(a0, c + 2); }
     compute(a1, 1);
     if (c + 2 < cend) store_h(0);
+  }
+
+  if constexpr (ALL) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int64_t it = item0 + wave * IT + i;  // uniform over the wave
+      if (it >= nitems) continue;
+      if (it < a.n1) {
+        // stage-1 keys of 16 centroids for every batch row
+        f32x4_t sc[NT];
+        if constexpr (Q4) {
+          int4_tile_scores<NT>(a.q4, a.q4s, a.groups, a.H, a.h_bytes, B, (int)it, lane, sc);
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sc[nt] = acc[i][nt];
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int r = nt * 16 + lr;
+          if (r >= B) continue;
+          const int64_t kq0 = it * 16 + 4 * slice;
+          const float4 g4 = (a.sample && !a.raw_scores)
+                                ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t k = kq0 + q;
+            if (k >= a.c) continue;
+            const float x = sc[nt][q];
+            if (a.raw_scores) {  // the select counts on it, then forms the key
+              a.keys[(int64_t)r * a.key_stride + k] = x;
+              continue;
+            }
+            a.keys[(int64_t)r * a.key_stride + k] = a.sample ? x * a.inv_tau + gq[q] : x;
+            if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = x;
+          }
+        }
+        continue;
+      }
+      // one record per batch row for these 16 candidates: the lane's 4
+      // tokens, then the 4 lanes that share a batch row
+      uint32_t tok[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tok[q] = (uint32_t)a.c2t[row0[i] + 4 * slice + q];
+      const int64_t rec = (it - a.n1) * a.B;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = nt * 16 + lr;
+        const uint64_t seed = (a.sample && r < B) ? a.seeds[r] : 0ull;
+        uint64_t bk = 0ull;
+        Lse ll = lse_empty();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x = acc[i][nt][q];
+          const float xs = x * a.inv_tau;
+          const float kx = a.sample ? xs + gumbel(seed, kStreamToken, tok[q]) : x;
+          const uint64_t key = decode_key(kx, tok[q]);
+          bk = key > bk ? key : bk;
+          if (a.with_lse) ll = lse_add(ll, xs);
+        }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          const uint64_t y = __shfl_xor(bk, o, kWave);
+          bk = y > bk ? y : bk;
+          if (a.with_lse) ll = lse_merge(ll, Lse{__shfl_xor(ll.m, o, kWave),
+                                                 __shfl_xor(ll.s, o, kWave)});
+        }
+        if (slice == 0 && r < B) {
+          a.part_best[rec + r] = bk;
+          if (a.with_lse) a.part_lse[rec + r] = make_float2(ll.m, ll.s);
+        }
+      }
+    }
+    continue;
   }
 
   if constexpr (MODE == kGmScores) {
@@ -363,7 +485,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   }
   }  // groups
-  if constexpr (MODE == kGmScores) return;
+  if constexpr (MODE == kGmScores || ALL) return;
   // combine the 4 lanes that share a batch column, then the waves
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -537,6 +659,20 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
 }
 
 int stage2_mfma_grid() { return 4096; }
+
+hipError_t launch_stream_all(const Stage2mArgs& a, const SelectArgs& sa, hipStream_t s,
+                             const Timing* t1, const Timing* t2) {
+  hipEvent_t e0 = t1 ? t1->start : nullptr, e1 = t1 ? t1->stop : nullptr;
+  // one unit of kGmWaves items per workgroup, stage-1 units first in the
+  // grid (the dispatcher starts them first)
+  const int64_t items = a.n1 + (int64_t)a.c * (a.b / 16);
+  int64_t grid = (items + kGmWaves * kGmItems - 1) / (kGmWaves * kGmItems);
+  grid = grid < (1 << 20) ? grid : (1 << 20);
+  const hipError_t e = a.q4 ? launch_engine<kGmAllQ4>(a, (int)grid, s, e0, e1)
+                            : launch_engine<kGmAll>(a, (int)grid, s, e0, e1);
+  if (e != hipSuccess) return e;
+  return launch_select_fold(sa, a.B, s, t2);
+}
 
 hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s, const Timing* tm) {
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;

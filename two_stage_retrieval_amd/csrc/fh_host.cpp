@@ -45,7 +45,11 @@ int validate_desc(const fh_desc* ds) {
     return FH_ERR_UNSUPPORTED;
   if (ds->quant != FH_QUANT_NONE && (ds->dtype != FH_DTYPE_BF16 || ds->d % 128))
     return FH_ERR_UNSUPPORTED;
-  if (ds->flags & ~(FH_FLAG_COOPERATIVE | FH_FLAG_BORROW_E)) return FH_ERR_INVALID_ARG;
+  if (ds->flags & ~(FH_FLAG_COOPERATIVE | FH_FLAG_BORROW_E | FH_FLAG_STREAM_ALL |
+                    FH_FLAG_SELECT_FIRST))
+    return FH_ERR_INVALID_ARG;
+  if ((ds->flags & FH_FLAG_STREAM_ALL) && (ds->flags & FH_FLAG_SELECT_FIRST))
+    return FH_ERR_INVALID_ARG;
   return check_permutation(ds->c2t, ds->v);
 }
 

@@ -88,6 +88,14 @@ struct SelectArgs {
   // (needs masks)
   int32_t* ulist;        // clusters with a non-zero mask, ascending
   int32_t* ucount;
+  // select-and-fold (the all-cluster stream): after its selection, row r
+  // folds the per-(16-row item, row) partials of its selected clusters
+  const uint64_t* fold_best;  // items x fold_pitch best decode keys
+  const float2* fold_lse;     // items x fold_pitch (max, sum) of z / tau, or null
+  int fold_sub;               // items per cluster (b / 16)
+  int fold_pitch;             // batch rows per item record
+  int32_t* out_tokens;
+  float* out_lse;
 };
 
 struct Stage2mArgs {
@@ -125,6 +133,16 @@ struct Stage2mArgs {
   int64_t part_stride;   // floats between the slices' B x key_stride blocks
   int raw_scores;        // scores epilogue: plain scores even at one slice (the
                          // select then forms the keys)
+  // the all-cluster stream (stage 1 and stage 2 in one launch): items
+  // [0, n1) are stage-1 items (16 centroid rows of cbase, or INT4 tiles when
+  // q4 is set), items from n1 on are the 16-row items of every cluster;
+  // part_best / part_lse receive one record per (item, batch row), item-major
+  const uint8_t* cbase;
+  int64_t c_row_bytes;
+  int64_t n1;
+  const uint8_t* q4;
+  const uint16_t* q4s;
+  int groups;
 };
 constexpr int kMaxKSplit = 4;
 // batched stage 2 walks the union list below this many rows, every cluster
@@ -235,6 +253,10 @@ hipError_t launch_rowdot(const RowdotArgs& a, int mode, int dtype, int B, int gr
                          hipStream_t s, const Timing* tm = nullptr);
 int rowdot_grid(int64_t nrows, int nchunk, int mode);
 hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing* tm = nullptr);
+// Selection of each batch row, then the fold of the all-cluster stream's
+// records over the row's selected clusters (the fold_* fields, out_*).
+hipError_t launch_select_fold(const SelectArgs& a, int B, hipStream_t s,
+                              const Timing* tm = nullptr);
 // The selection's histogram range hint for p of c keys: z with an upper
 // normal tail of min(1, 4 p / c), or 0 (no hint) when that tail is half or
 // more, or c is small.
@@ -264,6 +286,12 @@ bool batched_supported(int dtype, int d, int B, bool int4);
 hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t s,
                               const Timing* tm, int* ksplit);
 int stage2_mfma_grid();
+// The all-cluster stream: one launch of stage 1 and the per-(item, row)
+// partials of every cluster (a), then per batch row its selection and the
+// fold of its selected clusters' partials (sa).  Events: t1 around the
+// stream, t2 around the select-and-fold.
+hipError_t launch_stream_all(const Stage2mArgs& a, const SelectArgs& sa, hipStream_t s,
+                             const Timing* t1, const Timing* t2);
 hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s,
                               const Timing* tm = nullptr);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int num_cu,

@@ -9,10 +9,9 @@ namespace fh {
 
 constexpr int kSelThreads = 1024;
 
+// The selection of batch row r (the whole workgroup).
 template <int IPT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
-  __shared__ SelSmem sm;
-  const int r = blockIdx.x;
+__device__ __forceinline__ void select_row(const SelectArgs& a, int r, SelSmem& sm) {
   uint32_t u[IPT];
   select_load_keys<IPT, false>(a.keys + (int64_t)r * a.key_stride, (int)a.key_stride, u);
   int p = a.p;  // the row's probe count
@@ -67,6 +66,61 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
                                             a.ad.on ? a.p : 0);
 }
 
+template <int IPT>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
+  __shared__ SelSmem sm;
+  select_row<IPT>(a, blockIdx.x, sm);
+}
+
+// Selection of batch row r, then the fold of the records the all-cluster
+// stream left for its selected clusters: the best decode key (the token) and
+// the log-sum-exp over exactly the candidates of those clusters.
+template <int IPT>
+__global__ __launch_bounds__(kSelThreads) void select_fold_kernel(SelectArgs a) {
+  __shared__ SelSmem sm;
+  __shared__ uint64_t s_b[kSelThreads / kWave];
+  __shared__ float2 s_l[kSelThreads / kWave];
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  select_row<IPT>(a, r, sm);
+  __threadfence_block();  // this workgroup's writes of the row's selection
+  __syncthreads();
+  const int32_t* sr = a.sel + (int64_t)r * a.sel_stride;
+  uint64_t bb = 0ull;
+  Lse ll = lse_empty();
+  for (int j = t; j < a.p; j += kSelThreads) {
+    const int32_t k = sr[j];
+    if (k == kUnusedEntry) continue;  // past an adaptive count
+    for (int m = 0; m < a.fold_sub; ++m) {
+      const int64_t rec = ((int64_t)k * a.fold_sub + m) * a.fold_pitch + r;
+      const uint64_t x = a.fold_best[rec];
+      bb = x > bb ? x : bb;
+      if (a.fold_lse) {
+        const float2 l = a.fold_lse[rec];
+        ll = lse_merge(ll, Lse{l.x, l.y});
+      }
+    }
+  }
+  bb = wave_max_u64(bb);
+  if (a.fold_lse) ll = wave_lse(ll);
+  if ((t & (kWave - 1)) == 0) {
+    s_b[t / kWave] = bb;
+    s_l[t / kWave] = make_float2(ll.m, ll.s);
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint64_t b0 = s_b[0];
+    Lse l0{s_l[0].x, s_l[0].y};
+#pragma unroll
+    for (int w = 1; w < kSelThreads / kWave; ++w) {
+      b0 = s_b[w] > b0 ? s_b[w] : b0;
+      l0 = lse_merge(l0, Lse{s_l[w].x, s_l[w].y});
+    }
+    a.out_tokens[r] = (int32_t)key_id(b0);
+    if (a.out_lse) a.out_lse[r] = l0.m + logf(l0.s);
+  }
+}
+
 // The union of the rows' selected clusters (non-zero masks), ascending, as
 // the batched stage 2's work list: one workgroup, launched after the
 // selection so that every row's mask bits are in (the kernel boundary
@@ -92,6 +146,23 @@ float select_zcut(int c, int p) {
   const double q = 4.0 * (double)p / (double)c;
   if (q >= 0.5) return 0.0f;
   return (float)normal_upper_quantile(q);
+}
+
+hipError_t launch_select_fold(const SelectArgs& a, int B, hipStream_t s, const Timing* tm) {
+  hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
+  const int ipt = (a.c + kSelThreads - 1) / kSelThreads;
+  const dim3 grid(B), block(kSelThreads);
+#define FH_SEL_IPT(N)                                                                \
+  if (ipt <= N) {                                                                    \
+    hipExtLaunchKernelGGL(select_fold_kernel<N>, grid, block, 0, s, e0, e1, 0, a);   \
+    return hipGetLastError();                                                        \
+  }
+  FH_SEL_IPT(4)
+  FH_SEL_IPT(8)
+  FH_SEL_IPT(16)
+  FH_SEL_IPT(32)
+#undef FH_SEL_IPT
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing* tm) {
