@@ -402,8 +402,10 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
  * cluster once instead of only the selected ones, and drops the wait for
  * the selection.  Without a path flag, batched steps take path 4 when the
  * expected share of clusters that at least one of B independent rows
- * selects, 1 - (1 - p / c)^B, is at least 0.8.  A step that asks for the
- * candidates' logits (fh_debug.cand_ids) takes path 3.
+ * selects, 1 - (1 - p / c)^B, is at least 0.8.  On path 4 the candidates'
+ * debug logits (fh_debug.cand_ids / cand_logits) come from a second gather
+ * of the selected rows after the step (debug only: it does not change the
+ * step's tokens or lse).
  *   c, b, d, dtype, quant   as in fh_desc
  *   B, p                    as in flashhead_greedy / flashhead_sample
  *   num_cu                  compute units of the device (flashhead_query 13)

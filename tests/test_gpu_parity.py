@@ -60,7 +60,7 @@ class Case:
         H = synth.make_hidden(self.head, n, offset=offset)
         return H, ref.as_f64(H, self.dtype)
 
-    def prepare(self, fh, max_batch, max_p, with_C=True, quant=None):
+    def prepare(self, fh, max_batch, max_p, with_C=True, quant=None, flags=0):
         # quant: a FH_QUANT_* code, or None for the workload's own
         if quant is None:
             quant = (fh.FH_QUANT_INT4_G128 if self.wl.quant == "int4_g128"
@@ -68,7 +68,7 @@ class Case:
         q = quant
         return fh.FlashHead(self.E_dev, self.head.c2t,
                             self.C_dev if with_C else None, quant=q,
-                            max_batch=max_batch, max_p=max_p)
+                            max_batch=max_batch, max_p=max_p, flags=flags)
 
     def oracle_scores(self, h64):
         if self.int4 is not None:
@@ -350,19 +350,24 @@ def test_llama_sample_b16_parity(fh, tau):
     assert st.rows == 256
 
 
-def test_llama_greedy_b64_parity(fh):
-    """16 batches of 64 rows (the batched matrix-core path)."""
+@pytest.mark.parametrize("path", [3, 4])
+def test_llama_greedy_b64_parity(fh, path):
+    """16 batches of 64 rows on each batched matrix-core path (3: select
+    first; 4: the all-cluster stream, whose debug candidates come from a
+    second gather of the selected rows)."""
     cs = case(2)
-    head = cs.prepare(fh, max_batch=64, max_p=512)
+    flags = fh.FH_FLAG_SELECT_FIRST if path == 3 else fh.FH_FLAG_STREAM_ALL
+    head = cs.prepare(fh, max_batch=64, max_p=512, flags=flags)
     st = Stats()
     steps = []
     for i in range(16):
         H, H64 = cs.hidden(64, offset=64 * i)
         res = run_debug(fh, head, dev_tensor(H), 64, 512, "greedy")
+        assert fh.flashhead_query(head.handle, 10) == path
         steps.append((res, H64, None))
     assert fh.flashhead_query(head.handle, 9) == 0
     check_steps(cs, steps, 512, stats=st)
-    report("llama3.2-1b-head-b64 greedy B=64", st)
+    report(f"llama3.2-1b-head-b64 greedy B=64 path {path}", st)
     assert st.rows == 1024
 
 
@@ -399,11 +404,13 @@ def test_gemma_int4_codes_match_oracle(fh):
     assert np.array_equal(s, cs.int4[1])
 
 
-@pytest.mark.parametrize("B", [1, 32])
-def test_gemma_int4_greedy_parity(fh, B):
-    """All 1024 hidden vectors at batch 1; 8 batches of 32."""
+@pytest.mark.parametrize("B,flags", [(1, 0), (32, "SELECT_FIRST"), (32, "STREAM_ALL")])
+def test_gemma_int4_greedy_parity(fh, B, flags):
+    """All 1024 hidden vectors at batch 1; 8 batches of 32 on each batched
+    path."""
     cs = case(4)
-    head = cs.prepare(fh, max_batch=B, max_p=1024)
+    fl = getattr(fh, "FH_FLAG_" + flags) if flags else 0
+    head = cs.prepare(fh, max_batch=B, max_p=1024, flags=fl)
     st = Stats()
     n = 1024 if B == 1 else 8 * 32
     H, H64 = cs.hidden(n)
@@ -412,8 +419,10 @@ def test_gemma_int4_greedy_parity(fh, B):
         res = run_debug(fh, head, dev_tensor(H[lo:lo + B]), B, 1024, "greedy")
         steps.append((res, H64[lo:lo + B], None))
     assert fh.flashhead_query(head.handle, 9) == 0
+    assert fh.flashhead_query(head.handle, 10) == {0: 1, "SELECT_FIRST": 3, "STREAM_ALL": 4}[flags]
     check_steps(cs, steps, 1024, stats=st, score_tol=2e-2)
-    report(f"gemma3-1b-head-int4 greedy B={B}", st)
+    report(f"gemma3-1b-head-int4 greedy B={B}" + (f" path {fh.flashhead_query(head.handle, 10)}"
+                                                   if B > 1 else ""), st)
     assert st.rows == n
 
 

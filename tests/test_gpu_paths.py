@@ -30,35 +30,48 @@ def seeds_dev(seeds):
     return torch.from_numpy(seeds.view(np.int64)).cuda()
 
 
-def test_batched_list_and_all_cluster_walks_alternate(fh):
+@pytest.mark.parametrize("flags", ["SELECT_FIRST", None])
+def test_batched_list_and_all_cluster_walks_alternate(fh, flags):
     # below 16 rows stage 2 walks the union list, from 16 rows on every
     # cluster; one handle alternating between the two must find the row
-    # masks cleared by whichever ran before (greedy and sampling)
+    # masks cleared by whichever ran before (greedy and sampling).  Without
+    # a path flag the same handle also alternates between the select-first
+    # path and the all-cluster stream (1 - (1 - 40/400)^B: B = 24 and 16
+    # stream, B = 2, 3, 5 select first)
     cs = case(1, c=400, b=16, d=256, seed=56)
-    head = cs.prepare(fh, max_batch=24, max_p=40)
+    fl = getattr(fh, "FH_FLAG_" + flags) if flags else 0
+    head = cs.prepare(fh, max_batch=24, max_p=40, flags=fl)
     H, H64 = cs.hidden(24, offset=7)
     st = Stats()
+    seen = set()
     for step, B in enumerate((24, 3, 24, 5, 16, 2)):
         res = run_debug(fh, head, dev_tensor(H[:B]), B, 40, "greedy")
-        assert path_of(fh, head) == PATH_BATCHED
+        want = fh.flashhead_plan_step(400, 16, 256, fh.FH_DTYPE_BF16, 0, B, 40, 256, 1, fl)[0]
+        assert path_of(fh, head) == want
+        assert want == PATH_BATCHED or (not flags and want == 4)
+        seen.add(want)
         check_batch(cs, res, H64[:B], 40, stats=st)
         seeds = synth.make_seeds(step, B)
         res = run_debug(fh, head, dev_tensor(H[:B]), B, 40, "sample", 0.8, seeds_dev(seeds))
         check_batch(cs, res, H64[:B], 40, "sample", 0.8, seeds, stats=st)
     assert fh.flashhead_query(head.handle, 9) == 0
+    assert seen == ({3} if flags else {3, 4})
     print(st)
 
 
+@pytest.mark.parametrize("path", [3, 4])
 @pytest.mark.parametrize("B", [3, 17, 33, 50])
-def test_batched_path_ragged_batches(fh, B):
+def test_batched_path_ragged_batches(fh, B, path):
     # 16-row MFMA tiles over B columns: 1, 2, 3 and 4 column tiles, each
-    # with a partial last tile; c = 50 leaves a partial 16-row stage-1 tile
+    # with a partial last tile; c = 50 leaves a partial 16-row stage-1 tile;
+    # on both batched paths
     cs = case(1, c=50, b=16, d=256, seed=55)
-    head = cs.prepare(fh, max_batch=B, max_p=20)
+    flags = fh.FH_FLAG_SELECT_FIRST if path == 3 else fh.FH_FLAG_STREAM_ALL
+    head = cs.prepare(fh, max_batch=B, max_p=20, flags=flags)
     H, H64 = cs.hidden(B, offset=B)
     st = Stats()
     res = run_debug(fh, head, dev_tensor(H), B, 20, "greedy")
-    assert path_of(fh, head) == PATH_BATCHED
+    assert path_of(fh, head) == path
     check_batch(cs, res, H64, 20, stats=st)
     seeds = synth.make_seeds(5, B)
     res = run_debug(fh, head, dev_tensor(H), B, 20, "sample", 0.8, seeds_dev(seeds))
@@ -182,7 +195,7 @@ def test_large_p_takes_the_two_launch_path(fh):
     print(st)
 
 
-@pytest.mark.parametrize("B", [1, 16])
+@pytest.mark.parametrize("B", [1, 16, 64])
 def test_debug_outputs_do_not_change_results(fh, B):
     cs = case(3)
     head = cs.prepare(fh, max_batch=B, max_p=512)
@@ -273,7 +286,11 @@ def test_cp_variants_parity(fh, c, b, p):
     seeds = synth.make_seeds(6, 16)
     H16, H16_64 = cs.hidden(16, offset=1600)
     res = run_debug(fh, head, dev_tensor(H16), 16, p, "sample", 0.8, seeds_dev(seeds))
-    assert path_of(fh, head) == PATH_BATCHED
+    # 16 rows at p / c = 512 / 4008 are expected to select 89% of the
+    # clusters between them: the all-cluster stream; the others select first
+    assert path_of(fh, head) == fh.flashhead_plan_step(c, b, cs.wl.d, fh.FH_DTYPE_BF16, 0, 16,
+                                                       p, 256, 1)[0]
+    assert path_of(fh, head) in (PATH_BATCHED, 4)
     check_batch(cs, res, H16_64, p, "sample", 0.8, seeds, stats=st)
     assert fh.flashhead_query(head.handle, 9) == 0
     print(st)

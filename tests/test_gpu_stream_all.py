@@ -4,8 +4,10 @@ through the C ABI, against the oracle.
 Path 4 computes the stage-1 keys and, for every cluster and batch row, the
 best decode key and log-sum-exp of the cluster's candidates in one launch,
 before any selection exists; a second kernel selects each row's clusters and
-folds only their records.  It keeps no per-candidate logits, so rule R2 is
-not observable here: per row the tests check the stage-1 scores, R1 on the
+folds only their records.  The stream keeps no per-candidate logits (the
+debug candidates come from a second gather, covered by the parity tests of
+the B=64 and INT4 B=32 workloads), so these tests run without them: per row
+they check the stage-1 scores, R1 on the
 GPU's selection, R3 (greedy) or R4 (sampling) with the oracle decoding the
 candidates of the GPU's own selection, and the sampling lse against the
 oracle's lse over those candidates.  The paths' tokens are also compared
@@ -40,7 +42,7 @@ def seeds_dev(seeds):
 
 def run(fhmod, head, H_dev, B, p, mode, tau=1.0, seeds=None, adaptive=None):
     """One step with the scores and the selection read back (no candidate
-    logits, which would make the library take the select-first path)."""
+    logits: only what the step itself computes)."""
     dbg = {
         "scores": torch.empty(B, head.c, dtype=torch.float32, device="cuda"),
         "clusters": torch.empty(B, p, dtype=torch.int32, device="cuda"),

@@ -46,6 +46,7 @@ struct fh_handle {
   // all-cluster stream: one record per (16-row item, batch row)
   uint64_t* all_best = nullptr;     // (v / 16) x max_batch
   float2* all_lse = nullptr;
+  int32_t* dbg_tokens = nullptr;    // max_batch: the debug gather's own tokens
   // single-launch batch-1 decode
   int num_cu = 0;
   int b1_blocks_per_cu = 0;         // decode workgroups one compute unit holds at once
@@ -197,6 +198,7 @@ int prepare_impl(const fh_desc* ds, fh_handle* h) {
   if (mb >= 2 && h->b % 16 == 0 && batched_supported(h->dtype, d, 2, false)) {
     FH_TRY(alloc(h, &h->all_best, (size_t)(v / 16) * mb * 8));
     FH_TRY(alloc(h, &h->all_lse, (size_t)(v / 16) * mb * 8));
+    FH_TRY(alloc(h, &h->dbg_tokens, (size_t)mb * 4));
   }
   FH_TRY(alloc(h, &h->b1_keys, (size_t)2 * b1_key_stride(c) * 4));
   FH_TRY(hipMemsetAsync(h->b1_keys, 0xFF, (size_t)2 * b1_key_stride(c) * 4, s));
@@ -302,8 +304,6 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
   int b1_grid = 0;
   int path = plan_path(h->c, h->b, h->d, h->row_bytes, h->dtype, int4, B, p, h->num_cu,
                        h->b1_blocks_per_cu, h->flags, &b1_grid);
-  // the all-cluster stream keeps no candidate logits
-  if (path == 4 && dbg && dbg->cand_ids) path = 3;
   const bool batched = path == 3 || path == 4;
 
   // stage 1 (+ selection by each batch row's last block on the GEMV path)
@@ -463,6 +463,18 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
     if (t3) {  // stage 2 ran inside the first launch
       (void)hipEventRecord(t3->start, s);
       (void)hipEventRecord(t3->stop, s);
+    }
+    if (dbg && dbg->cand_ids) {
+      // the stream keeps one record per cluster, not the candidates: the
+      // debug output gathers the selected clusters' rows again (row-dot
+      // logits, which round apart from the stream's by the summation order)
+      // and writes its own tokens aside; the step's tokens stay the fold's
+      RowdotArgs g = gather_args();
+      g.out_tokens = h->dbg_tokens;
+      g.out_lse = nullptr;
+      const int gx = rowdot_grid(g.nrows, nchunk, kRowGather);
+      if (gx > kMaxGrid) return FH_ERR_UNSUPPORTED;
+      FH_TRY(launch_rowdot(g, kRowGather, h->dtype, B, gx, s));
     }
     if (dbg && dbg->clusters) {
       FH_TRY(hipMemcpy2DAsync(dbg->clusters, (size_t)p * 4, h->sel, (size_t)h->max_p * 4,
