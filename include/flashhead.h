@@ -375,10 +375,10 @@ int flashhead_export_int4(const fh_handle* h, uint8_t* codes_host,
  * row-dot launches, 3 the batched matrix-core path that selects first,
  * 4 the batched all-cluster stream), 11 the state of the
  * single launch's buffer set that the next launch uses, read back
- * synchronously (0 when every key reads pending, every selection entry -1,
- * every merge slot and the set's go word zero, and the device's launch
- * count matches the handle's; otherwise bit 0 keys, 1 selection, 2 slots,
- * 3 go word, 4 launch count, 5 plain scores), 12 the single-launch decode kernel's
+ * synchronously (0 when every key and plain score reads pending, every
+ * selection entry -1, and every merge slot and the set's go word zero;
+ * otherwise bit 0 keys, 1 selection, 2 slots, 3 go word, 5 plain scores;
+ * bit 4 is not used), 12 the single-launch decode kernel's
  * workgroups that one compute unit holds at once (occupancy API, measured
  * at prepare), 13 the device's compute units, 14 fh_desc.flags.
  * The decode calls are asynchronous and cannot return what goes wrong

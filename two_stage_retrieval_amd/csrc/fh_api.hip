@@ -56,7 +56,6 @@ struct fh_handle {
   uint64_t* b1_slots = nullptr;     // 2 x kDecodeB1SlotStride words, zero between launches
   float2* b1_lse = nullptr;         // kDecodeB1SlotStride words
   int32_t* b1_sel = nullptr;        // 2 x kDecodeB1MaxP, -1 between launches
-  uint64_t b1_launches = 0;         // host copy of the device epoch
   int last_path = 0;                // kernels of the last step (flashhead_query 10)
   uint32_t* b1_epoch = nullptr;     // launch counter (picks the buffer set)
   uint32_t* b1_go = nullptr;        // 2 words: all keys seen, per buffer set (0 between launches)
@@ -392,13 +391,9 @@ int step_impl(fh_handle* h, const void* H, int B, int p, int mode, float tau,
         (void)hipEventRecord(t3->stop, s);
       }
       if (dbg && dbg->clusters) {
-        // the selection of this launch sits in the set picked by the epoch
-        // before it; both sets are read back and the host-side epoch says
-        // which (one launch in flight per handle)
-        const int32_t* src = h->b1_sel + (size_t)(h->b1_launches & 1) * kDecodeB1MaxP;
-        FH_TRY(hipMemcpyAsync(dbg->clusters, src, (size_t)p * 4, hipMemcpyDeviceToDevice, s));
+        // the selection of this launch sits in the set its epoch picked
+        FH_TRY(launch_b1_copy_sel(h->b1_epoch, h->b1_sel, kDecodeB1MaxP, dbg->clusters, p, s));
       }
-      ++h->b1_launches;
       h->last_path = 1;
       return FH_OK;
     }
@@ -1057,7 +1052,6 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value) {
       for (int j = 0; j < kDecodeB1MaxGrid; ++j)
         if (slots[(size_t)j * 16] != 0ull) bits |= 4;
       if (go[set] != 0u) bits |= 8;
-      if ((uint64_t)ep != (h->b1_launches & 0xFFFFFFFFull)) bits |= 16;
       FH_TRY(hipMemcpy(keys.data(), h->b1_raw + set * ks, (size_t)ks * 4, hipMemcpyDeviceToHost));
       for (int k = 0; k < h->c; ++k)
         if (keys[(size_t)k] != 0xFFFFFFFFu) bits |= 32;

@@ -298,6 +298,9 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
                               hipStream_t s);
 // n words of p set to value by a kernel on s
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s);
+// The single launch's selection (the set below the epoch it left) into dst.
+hipError_t launch_b1_copy_sel(const uint32_t* epoch, const int32_t* sets, int64_t set_stride,
+                              int32_t* dst, int p, hipStream_t s);
 // Equal-size spherical k-means (fh_kmeans.hip).  E device, init host
 // (c distinct ids), c2t device out (c x b, rows ascending), centroids device
 // out (c x d float64) or null.  Blocking: allocates its own workspace and

@@ -137,4 +137,23 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s
   return hipGetLastError();
 }
 
+// The single launch's selection, for the debug output: the launch used the
+// buffer set its epoch picked, one below the epoch it left behind.  Read on
+// the device, so that it holds for launches replayed from a captured graph.
+__global__ __launch_bounds__(256) void b1_copy_sel_kernel(const uint32_t* epoch,
+                                                          const int32_t* sets, int64_t set_stride,
+                                                          int32_t* dst, int p) {
+  const uint32_t used = (*epoch - 1u) & 1u;
+  const int32_t* src = sets + (int64_t)used * set_stride;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < p; i += gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_b1_copy_sel(const uint32_t* epoch, const int32_t* sets, int64_t set_stride,
+                              int32_t* dst, int p, hipStream_t s) {
+  hipLaunchKernelGGL(b1_copy_sel_kernel, dim3((unsigned)((p + 255) / 256)), dim3(256), 0, s, epoch,
+                     sets, set_stride, dst, p);
+  return hipGetLastError();
+}
+
 }  // namespace fh
