@@ -296,12 +296,15 @@ __device__ __forceinline__ void select_from_keys(uint32_t (&u)[IPT], int c, int 
   }
   const uint32_t first = early ? above : 0u;  // published before the boundary bin
   if (early) {  // (block-uniform)
+    // each thread publishes its own ids at their ranks: consecutive threads
+    // hold consecutive ranks, so a wave's stores stay mostly contiguous
     const int ca = __popc(above);
     int r = sel_scan<NT>(ca, sm, parity, lane, wave) - ca;
-    for (uint32_t mm = above; mm != 0u; mm &= mm - 1u, ++r) out[r] = k0 + __ffs(mm) - 1;
-    __syncthreads();
-    for (int i = t; i < ngt; i += NT)
-      __hip_atomic_store(early + i, out[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (uint32_t mm = above; mm != 0u; mm &= mm - 1u, ++r) {
+      const int id = k0 + __ffs(mm) - 1;
+      out[r] = id;
+      __hip_atomic_store(early + r, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     FH_TRACE_SEL(12);
   }
 
