@@ -501,6 +501,17 @@ def parse_timeline(words, khz):
     last = int(np.argmax(blk[4][:grid]))
     w2l = wav[2][last * 8:(last + 1) * 8]
     out["last_publisher_stage2_done"] = us(w2l[w2l > 0].max()) if (w2l > 0).any() else None
+    # the workgroup whose stage 2 ends last: its index, when its entries
+    # arrived, and how many workgroups got their entries after the first
+    # selection publication
+    done_wg = np.array([wav[2][b * 8:(b + 1) * 8].max() for b in range(grid)])
+    lw = int(np.argmax(done_wg))
+    out["last_stage2_workgroup"] = lw
+    out["last_stage2_workgroup_entries"] = us(blk[3][lw]) if lw > 0 and blk[3][lw] else None
+    out["last_stage2_workgroup_share_us"] = (us(done_wg[lw]) - us(blk[3][lw])
+                                             if lw > 0 and blk[3][lw] else None)
+    ent = blk[3][1:grid]
+    out["entries_after_full_selection"] = int(np.count_nonzero(ent > blk[2][0])) if blk[2][0] else None
     out["key_poll_rounds"] = int(cnt[0])
     out["merge_poll_rounds"] = int(cnt[1])
     out["boundary_bin_keys"] = int(cnt[2])
@@ -541,7 +552,11 @@ def timeline_bench(args, wl, fh, call, evict, B):
         f"{len(runs)} cold calls):")
     for k, v in med.items():
         log(f"    {k:32s} {v}")
+    import collections
+    lastw = collections.Counter(r["last_stage2_workgroup"] for r in runs).most_common(4)
+    log(f"    {'last_stage2_workgroup (count)':32s} {lastw}")
     print(json.dumps({"timeline": wl.name, "calls": len(runs), "median": med,
+                      "last_stage2_workgroups": lastw,
                       "cache": "warm" if args.timeline_warm else "cold (1 GiB flush)",
                       "build": "libflashhead_trace.so"}), flush=True)
 
