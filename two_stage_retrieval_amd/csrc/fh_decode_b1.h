@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
       }
     }
     const int64_t ngroups = (args.s2.nrows + R - 1) / R;
-    const int64_t g0 = (int64_t)blockIdx.x * kS1Waves;
+    const int64_t g0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * kS1Waves;
     if (g0 < ngroups) {
       const int64_t g1 = g0 + kS1Waves < ngroups ? g0 + kS1Waves : ngroups;
       const int64_t rend = g1 * R < args.s2.nrows ? g1 * R : args.s2.nrows;
@@ -405,13 +405,17 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
     __syncthreads();
     FH_TRACE_BLOCK(3);  // stage-2 entries in LDS
   }
+  // stage-2 groups in reverse workgroup order: workgroup 0, which holds the
+  // whole selection in LDS, takes the last entries of the list (the boundary
+  // bin's, known last), and the last workgroups the first entries
   uint64_t best = 0;
   Lse lse = lse_empty();
+  const int w2 = (int)(gridDim.x - 1 - blockIdx.x) * kS1Waves + wave;
   if (blockIdx.x == 0) {
-    dot_rows<TE, NCH, R, kRowGather, true, ADAPT>(args.s2, 0, sel, hreg, seed, lane, w0, wstride,
+    dot_rows<TE, NCH, R, kRowGather, true, ADAPT>(args.s2, 0, sel, hreg, seed, lane, w2, wstride,
                                                   best, lse, a.error, s_sel, 0, a.p);
   } else {
-    dot_rows<TE, NCH, R, kRowGather, true, ADAPT>(args.s2, 0, sel, hreg, seed, lane, w0, wstride,
+    dot_rows<TE, NCH, R, kRowGather, true, ADAPT>(args.s2, 0, sel, hreg, seed, lane, w2, wstride,
                                                   best, lse, a.error, s_win, wlo, wn);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS load outlives the workgroup
