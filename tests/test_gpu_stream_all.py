@@ -212,6 +212,40 @@ def test_stream_all_ragged(fh, wid, over, B, ps):
     assert fh.flashhead_query(head.handle, 9) == 0
 
 
+@pytest.mark.parametrize("B", [50, 64])
+def test_wide_engine_ragged(fh, B):
+    """d = 2048 with four 16-column tiles of H (B = 49-64), greedy: the
+    engine's two-items-per-wave unrolled K walk, in the all-cluster stream
+    and in the dense head.  c = 47 clusters: a partial last stage-1 item and
+    a partial last unit of items; B = 50: the last tile's rows past the batch
+    (read as zeros) must not reach any output."""
+    cs = case(1, c=47, b=16, d=2048, seed=81)
+    head = prepare(fh, cs, B, 47, fh.FH_FLAG_STREAM_ALL)
+    dense = fh.DenseHead(cs.E_dev, max_batch=B)
+    H, H64 = cs.hidden(B, offset=9)
+    x = dev_tensor(H)
+    sc = cs.oracle_scores_many(H64)
+    for p in (1, 12, 47):
+        st = Stats()
+        res = run(fh, head, x, B, p, "greedy")
+        assert res["path"] == PATH_STREAM_ALL
+        for r in range(B):
+            check_row(cs, res, r, H64[r], sc[r], p, "greedy", 1.0, 0, st)
+        assert st.rows == B
+    lse = torch.empty(B, dtype=torch.float32, device="cuda")
+    toks = dense(x, out_lse=lse).cpu().numpy()
+    lses = lse.cpu().numpy()
+    for r in range(B):
+        z = ref.dense_logits(cs.rows, cs.wl.v, H64[r])
+        tok, m2, want_lse, keys = ref.decode_tokens(np.arange(cs.wl.v), z, "greedy", 1.0, 0)
+        if m2 > 1e-3:
+            assert toks[r] == tok
+        else:
+            assert keys[toks[r]] >= keys.max() - 1e-3
+        assert lses[r] == pytest.approx(want_lse, abs=1e-3, rel=1e-5)
+    assert fh.flashhead_query(head.handle, 9) == 0
+
+
 def test_stream_all_equal_scores_pick_lowest_ids(fh):
     """h = 0: every score and logit is 0; ties go to the lowest ids."""
     cs = case(1, c=50, b=16, d=256)

@@ -15,6 +15,8 @@
 // k indices to (slice, element) works as long as A and B use the same one;
 // here lane l's 16-byte load from a row covers k = 32 s + 8 (l div 16) +
 // [0, 8) at step s, so every load is a contiguous 16-byte piece of a row.
+#include <type_traits>
+
 #include "fh_device.h"
 #include "fh_internal.h"
 
@@ -151,13 +153,18 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 // FLASH and DENSE write one partial per (workgroup, batch row).
 // ---------------------------------------------------------------------------
 constexpr int kGmThreads = 256;
+// buffer resource word 3 for untyped 32-bit-element reads on gfx950
+constexpr int kBufferFlags = 0x00020000;
 constexpr int kGmWaves = kGmThreads / kWave;
 enum GmMode : int { kGmScores = 0, kGmFlash = 1, kGmDense = 2, kGmAll = 3, kGmAllQ4 = 4 };
 // ALL with INT4 stage-1 tiles (kGmAllQ4) or 16-row bf16 centroid items (kGmAll)
 
 // KC: K per chunk (KC / 32 MFMA steps); a wave requests KC * 2 contiguous
 // bytes of each of its rows per chunk
-template <int NT, int IT, int MODE, int KC>
+// NCH > 0: d = NCH * KC and one K slice; the K walk is unrolled, so the
+// buffers of every chunk are fixed at compile time and each chunk's loads
+// are issued ahead of the previous chunk's products.
+template <int NT, int IT, int MODE, int KC, int NCH = 0>
 __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_engine_kernel(Stage2mArgs a) {
   constexpr int kSteps = KC / 32;
   constexpr int kHRow = KC + 8;  // LDS row pitch in bf16 (16-byte pad)
@@ -171,6 +178,8 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int slice = lane >> 4, lr = lane & 15;
   const int B = a.B;
   const int sub = a.b / 16;
+  // the unrolled walk serves greedy calls only (its launcher checks)
+  const bool sample = NCH > 0 ? false : a.sample;
   constexpr bool ALL = MODE == kGmAll || MODE == kGmAllQ4;
   constexpr bool Q4 = MODE == kGmAllQ4;
   const int64_t nrows_total = MODE == kGmScores ? (int64_t)a.c : a.v;
@@ -186,6 +195,34 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   Lse lse[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) { best[nt] = 0ull; lse[nt] = lse_empty(); }
+
+  // combine the 4 lanes that share a batch column into the wave's LDS
+  // partials (merged with them when `merge`), and restart the running ones
+  auto fold_lanes = [&](bool merge) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const uint64_t y = __shfl_xor(best[nt], o, kWave);
+        best[nt] = y > best[nt] ? y : best[nt];
+        if (a.with_lse) lse[nt] = lse_merge(lse[nt], Lse{__shfl_xor(lse[nt].m, o, kWave),
+                                                         __shfl_xor(lse[nt].s, o, kWave)});
+      }
+      if (slice == 0) {
+        const int r = nt * 16 + lr;
+        if (merge) {
+          const uint64_t pb = s_best[wave][r];
+          best[nt] = pb > best[nt] ? pb : best[nt];
+          lse[nt] = lse_merge(lse[nt], Lse{s_lse[wave][r].x, s_lse[wave][r].y});
+        }
+        s_best[wave][r] = best[nt];
+        s_lse[wave][r] = make_float2(lse[nt].m, lse[nt].s);
+      }
+      best[nt] = 0ull;
+      lse[nt] = lse_empty();
+    }
+  };
+  if constexpr (NCH > 0 && !ALL && MODE != kGmScores) fold_lanes(false);  // empty partials
 
   // work units: groups of kGmWaves * IT items times ksplit slices of K (the
   // waves of a workgroup share the slice, so the staged H chunk is shared),
@@ -210,10 +247,14 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const int cbeg = sp * nchunks / S, cend = (sp + 1) * nchunks / S;
 
-  // this wave's items
+  // this wave's items: item i streams rows of abase[i] at the lane's byte
+  // offset aoff[i] (32 bits in the unrolled walk, whose launcher checks the
+  // matrix sizes; the base is uniform over the wave)
   int64_t row0[IT], kc[IT];
   uint64_t mask[IT];
-  const uint8_t* ap[IT];
+  const uint8_t* abase[IT];
+  using AOff = std::conditional_t<(NCH > 0), uint32_t, int64_t>;
+  AOff aoff[IT];
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     int64_t it = item0 + wave * IT + i;
@@ -227,15 +268,19 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
         mask[i] = (live && !Q4) ? ~0ull : 0ull;
         int64_t crow = row0[i] + lr;
         crow = crow < a.c ? crow : a.c - 1;
-        ap[i] = a.cbase + crow * a.c_row_bytes + (int64_t)(8 * slice) * 2;
+        abase[i] = a.cbase;
+        aoff[i] = (AOff)(crow * a.c_row_bytes + (int64_t)(8 * slice) * 2);
       } else {
+        // item ie is rows [16 ie, 16 ie + 16) of the cluster-major order
+        // (cluster ie / (b/16), its 16-row part ie % (b/16))
         const int64_t ie = it - a.n1;
-        kc[i] = ie / sub;
-        row0[i] = kc[i] * a.b + (ie % sub) * 16;
+        kc[i] = -1;
+        row0[i] = ie * 16;
         mask[i] = live ? ~0ull : 0ull;
         int64_t arow = row0[i] + lr;
         if (a.borrowed) arow = a.c2t[arow];
-        ap[i] = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
+        abase[i] = a.base;
+        aoff[i] = (AOff)(arow * a.row_bytes + (int64_t)(8 * slice) * 2);
       }
       continue;
     }
@@ -253,20 +298,32 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     if constexpr (MODE == kGmFlash) {
       if (a.borrowed) arow = a.c2t[arow];  // the caller's E: the candidate's token row
     }
-    ap[i] = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2;
+    abase[i] = a.base;
+    aoff[i] = (AOff)(arow * a.row_bytes + (int64_t)(8 * slice) * 2);
   }
-  // H chunk staging: thread t moves kHP 16-byte pieces per chunk
-  const uint8_t* hsrc[kHP];
-  int hdst[kHP];
+  // H chunk staging: thread t moves kHP 16-byte pieces per chunk; piece
+  // t + n * kGmThreads is H row j0 + n * kHStep, 16-byte column kp (rows
+  // past the batch read its last row)
+  constexpr int kHStep = kGmThreads / (KC / 8);
+  static_assert(kHStep * (KC / 8) == kGmThreads, "H staging rows");
+  const int j0 = threadIdx.x / (KC / 8), kp = threadIdx.x % (KC / 8);
+  const int hdst0 = j0 * (kHRow / 8) + kp;
+  int64_t hoff[kHP];
 #pragma unroll
   for (int n = 0; n < kHP; ++n) {
-    const int piece = threadIdx.x + n * kGmThreads;  // KC / 8 pieces per H row
-    int j = piece / (KC / 8);
-    const int kp = piece % (KC / 8);
-    hdst[n] = j * (kHRow / 8) + kp;
+    int j = j0 + n * kHStep;
     j = j < B ? j : B - 1;
-    hsrc[n] = a.H + (int64_t)j * a.h_bytes + (int64_t)kp * 16;
+    hoff[n] = (int64_t)j * a.h_bytes + (int64_t)kp * 16;
   }
+  // the unrolled walk reads H through a buffer resource that ends with row
+  // B - 1: a piece is the lane's row-j0 offset plus a uniform row offset
+  // (one register for all pieces; its launcher checks that 64 rows of H fit
+  // 31 bits), and the pieces of rows past the batch read as zeros (their
+  // columns are dropped)
+  const __amdgpu_buffer_rsrc_t hrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.H), (short)0, (int)((B - 1) * a.h_bytes + (int64_t)a.d * 2),
+      kBufferFlags);
+  const uint32_t hoff0 = (uint32_t)(j0 * a.h_bytes) + (uint32_t)kp * 16;
   f32x4_t acc[IT][NT];
 #pragma unroll
   for (int i = 0; i < IT; ++i)
@@ -279,7 +336,9 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   u32x4_t hreg[kHP];
   // a wave whose items no row needs (a cluster no row selected, the tail)
   // reads no rows and runs no MFMA; it still stages H for the others
-  bool wlive = false;
+  // (the unrolled walk serves the modes where every wave streams: its tail
+  // rows are clamped to valid ones and their results dropped)
+  bool wlive = NCH > 0;
 #pragma unroll
   for (int i = 0; i < IT; ++i) wlive = wlive || mask[i] != 0ull;
   auto load_a = [&](uint4 (&dst)[IT][kSteps], int c) {
@@ -288,16 +347,22 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     for (int i = 0; i < IT; ++i)
 #pragma unroll
       for (int u = 0; u < kSteps; ++u)
-        dst[i][u] = *reinterpret_cast<const uint4*>(ap[i] + (int64_t)c * KC * 2 + u * 64);
+        dst[i][u] = *reinterpret_cast<const uint4*>(abase[i] + aoff[i] + (int64_t)c * KC * 2 +
+                                                    u * 64);
   };
   auto load_h = [&](int c) {
 #pragma unroll
     for (int n = 0; n < kHP; ++n)
-      hreg[n] = *reinterpret_cast<const u32x4_t*>(hsrc[n] + (int64_t)c * KC * 2);
+      if constexpr (NCH > 0)
+        hreg[n] = __builtin_amdgcn_raw_buffer_load_b128(
+            hrsrc, hoff0 + (uint32_t)(c * KC * 2), (int)(n * kHStep * a.h_bytes), 0);
+      else
+        hreg[n] = *reinterpret_cast<const u32x4_t*>(a.H + hoff[n] + (int64_t)c * KC * 2);
   };
   auto store_h = [&](int buf) {
 #pragma unroll
-    for (int n = 0; n < kHP; ++n) reinterpret_cast<u32x4_t*>(s_h[buf])[hdst[n]] = hreg[n];
+    for (int n = 0; n < kHP; ++n)
+      reinterpret_cast<u32x4_t*>(s_h[buf])[hdst0 + n * kHStep * (kHRow / 8)] = hreg[n];
   };
   auto compute = [&](const uint4 (&av)[IT][kSteps], int buf) {
     if (!wlive) return;
@@ -316,6 +381,26 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
 
   // a unit of INT4 stage-1 tiles only streams no rows: it skips the K walk
   const bool unit_rows = !Q4 || item0 + kGmWaves * IT > a.n1;
+  if constexpr (NCH > 0) {
+    if (unit_rows) {
+      load_h(0);
+      load_a(a0, 0);
+      store_h(0);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        if (c + 1 < NCH) {
+          load_h(c + 1);
+          if ((c & 1) == 0) load_a(a1, c + 1); else load_a(a0, c + 1);
+        }
+        // keep the next chunk's loads ahead of this chunk's products
+        __builtin_amdgcn_sched_barrier(0);
+        if ((c & 1) == 0) compute(a0, 0); else compute(a1, 1);
+        if (c + 1 < NCH) store_h((c + 1) & 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
   if (unit_rows) {
   load_h(cbeg);
   load_a(a0, cbeg);
@@ -333,6 +418,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     if (c + 2 < cend) { load_h(c + 2); load_a(a0, c + 2); }
     compute(a1, 1);
     if (c + 2 < cend) store_h(0);
+  }
   }
 
   if constexpr (ALL) {
@@ -354,21 +440,19 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
           const int r = nt * 16 + lr;
           if (r >= B) continue;
           const int64_t kq0 = it * 16 + 4 * slice;
-          const float4 g4 = (a.sample && !a.raw_scores)
-                                ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+          // raw_scores: the plain score (the select counts on it, then forms
+          // the key)
+          const bool keyed = sample && !a.raw_scores;
+          const float4 g4 = keyed ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
           const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int64_t k = kq0 + q;
             if (k >= a.c) continue;
             const float x = sc[nt][q];
-            if (a.raw_scores) {  // the select counts on it, then forms the key
-              a.keys[(int64_t)r * a.key_stride + k] = x;
-              continue;
-            }
-            a.keys[(int64_t)r * a.key_stride + k] = a.sample ? x * a.inv_tau + gq[q] : x;
-            if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = x;
+            a.keys[(int64_t)r * a.key_stride + k] = keyed ? x * a.inv_tau + gq[q] : x;
+            if (a.dbg_scores && !a.raw_scores) a.dbg_scores[(int64_t)r * a.c + k] = x;
           }
         }
         continue;
@@ -382,14 +466,14 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int r = nt * 16 + lr;
-        const uint64_t seed = (a.sample && r < B) ? a.seeds[r] : 0ull;
+        const uint64_t seed = (sample && r < B) ? a.seeds[r] : 0ull;
         uint64_t bk = 0ull;
         Lse ll = lse_empty();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float x = acc[i][nt][q];
           const float xs = x * a.inv_tau;
-          const float kx = a.sample ? xs + gumbel(seed, kStreamToken, tok[q]) : x;
+          const float kx = sample ? xs + gumbel(seed, kStreamToken, tok[q]) : x;
           const uint64_t key = decode_key(kx, tok[q]);
           bk = key > bk ? key : bk;
           if (a.with_lse) ll = lse_add(ll, xs);
@@ -420,7 +504,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
         if (r >= B) continue;
         // the lane's 4 consecutive clusters share one Philox block
         const int64_t kq0 = row0[i] + 4 * slice;
-        const float4 g4 = (a.sample && S == 1)
+        const float4 g4 = (sample && S == 1)
                               ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
         const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -433,7 +517,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
             a.keys[sp * a.part_stride + (int64_t)r * a.key_stride + k] = sc;
             continue;
           }
-          const float key = a.sample ? sc * a.inv_tau + gq[q] : sc;
+          const float key = sample ? sc * a.inv_tau + gq[q] : sc;
           a.keys[(int64_t)r * a.key_stride + k] = key;
           if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = sc;
         }
@@ -457,14 +541,14 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
       const int r = nt * 16 + lr;
       const bool rowsel = r < B && ((mask[i] >> r) & 1ull);
       if (!rowsel) continue;
-      const uint64_t seed = a.sample ? a.seeds[r] : 0ull;
+      const uint64_t seed = sample ? a.seeds[r] : 0ull;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = row0[i] + 4 * slice + q;
         if (MODE == kGmDense && row >= a.v) continue;
         const float x = acc[i][nt][q];
         const float xs = x * a.inv_tau;
-        const float kx = a.sample ? xs + gumbel(seed, kStreamToken, tok[q]) : x;
+        const float kx = sample ? xs + gumbel(seed, kStreamToken, tok[q]) : x;
         const uint64_t key = decode_key(kx, tok[q]);
         best[nt] = key > best[nt] ? key : best[nt];
         if (a.with_lse) lse[nt] = lse_add(lse[nt], xs);
@@ -484,23 +568,14 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
       }
     }
   }
+  if constexpr (NCH > 0) {
+    // fold this unit into the wave's LDS partials, so that no running
+    // partial is held in registers across the next unit's K walk
+    fold_lanes(true);
+  }
   }  // groups
   if constexpr (MODE == kGmScores || ALL) return;
-  // combine the 4 lanes that share a batch column, then the waves
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const uint64_t y = __shfl_xor(best[nt], o, kWave);
-      best[nt] = y > best[nt] ? y : best[nt];
-      if (a.with_lse) lse[nt] = lse_merge(lse[nt], Lse{__shfl_xor(lse[nt].m, o, kWave),
-                                                       __shfl_xor(lse[nt].s, o, kWave)});
-    }
-    if (slice == 0) {
-      s_best[wave][nt * 16 + lr] = best[nt];
-      s_lse[wave][nt * 16 + lr] = make_float2(lse[nt].m, lse[nt].s);
-    }
-  }
+  if constexpr (NCH == 0) fold_lanes(false);
   __syncthreads();
   for (int r = threadIdx.x; r < B; r += kGmThreads) {
     uint64_t bb = s_best[0][r];
@@ -584,9 +659,30 @@ static void launch_engine_kc(const Stage2mArgs& a, int grid, hipStream_t s, hipE
                         dim3(kGmThreads), 0, s, e0, e1, 0, a);
 }
 
+// Four column tiles (B = 49-64) at d = 2048 in the streaming modes: two
+// items per wave with the unrolled K walk (measured on the 2048-wide head at
+// B = 64: 107 us against 118 us for one item per wave).
+constexpr int kWideItems = 2;
+static bool engine_wide(const Stage2mArgs& a, int mode) {
+  const int64_t lim = (int64_t)1 << 31;
+  return (mode == kGmDense || mode == kGmAll) && !a.sample && (a.B + 15) / 16 == 4 &&
+         a.d == 8 * 256 && (int64_t)64 * a.h_bytes < lim && a.v * a.row_bytes < lim &&
+         (int64_t)a.c * a.c_row_bytes < lim;
+}
+static int engine_items(const Stage2mArgs& a, int mode) {
+  return engine_wide(a, mode) ? kWideItems : kGmItems;
+}
+
 template <int MODE, int KC>
 static hipError_t launch_engine_nt(const Stage2mArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                                    hipEvent_t e1) {
+  if constexpr ((MODE == kGmDense || MODE == kGmAll) && KC == 256) {
+    if (engine_wide(a, MODE)) {
+      hipExtLaunchKernelGGL((gemm_engine_kernel<4, kWideItems, MODE, 256, 8>), dim3(grid),
+                            dim3(kGmThreads), 0, s, e0, e1, 0, a);
+      return hipGetLastError();
+    }
+  }
   switch ((a.B + 15) / 16) {
     case 1: launch_engine_kc<1, MODE, KC>(a, grid, s, e0, e1); break;
     case 2: launch_engine_kc<2, MODE, KC>(a, grid, s, e0, e1); break;
@@ -604,8 +700,8 @@ static hipError_t launch_engine(const Stage2mArgs& a, int grid, hipStream_t s, h
   return launch_engine_nt<MODE, 128>(a, grid, s, e0, e1);
 }
 
-static int engine_grid(int64_t nrows16) {
-  const int64_t per = (int64_t)kGmWaves * kGmItems;
+static int engine_grid(int64_t nrows16, int items_per_wave) {
+  const int64_t per = (int64_t)kGmWaves * items_per_wave;
   const int64_t g = (nrows16 + per - 1) / per;
   return g < 1 ? 1 : (int)g;
 }
@@ -666,7 +762,8 @@ hipError_t launch_stream_all(const Stage2mArgs& a, const SelectArgs& sa, hipStre
   // one unit of kGmWaves items per workgroup, stage-1 units first in the
   // grid (the dispatcher starts them first)
   const int64_t items = a.n1 + (int64_t)a.c * (a.b / 16);
-  int64_t grid = (items + kGmWaves * kGmItems - 1) / (kGmWaves * kGmItems);
+  const int per = kGmWaves * engine_items(a, a.q4 ? kGmAllQ4 : kGmAll);
+  int64_t grid = (items + per - 1) / per;
   grid = grid < (1 << 20) ? grid : (1 << 20);
   const hipError_t e = a.q4 ? launch_engine<kGmAllQ4>(a, (int)grid, s, e0, e1)
                             : launch_engine<kGmAll>(a, (int)grid, s, e0, e1);
@@ -678,7 +775,7 @@ hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s, c
   hipEvent_t e0 = tm ? tm->start : nullptr, e1 = tm ? tm->stop : nullptr;
   // flash: the union is known on the device only; launch for every cluster
   const int64_t items = dense ? (a.v + 15) / 16 : (int64_t)a.c * (a.b / 16);
-  int grid = engine_grid(items);
+  int grid = engine_grid(items, engine_items(a, dense ? kGmDense : kGmFlash));
   grid = grid < stage2_mfma_grid() ? grid : stage2_mfma_grid();
   hipError_t e = dense ? launch_engine<kGmDense>(a, grid, s, e0, e1)
                        : launch_engine<kGmFlash>(a, grid, s, e0, e1);
