@@ -196,34 +196,6 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) { best[nt] = 0ull; lse[nt] = lse_empty(); }
 
-  // combine the 4 lanes that share a batch column into the wave's LDS
-  // partials (merged with them when `merge`), and restart the running ones
-  auto fold_lanes = [&](bool merge) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const uint64_t y = __shfl_xor(best[nt], o, kWave);
-        best[nt] = y > best[nt] ? y : best[nt];
-        if (a.with_lse) lse[nt] = lse_merge(lse[nt], Lse{__shfl_xor(lse[nt].m, o, kWave),
-                                                         __shfl_xor(lse[nt].s, o, kWave)});
-      }
-      if (slice == 0) {
-        const int r = nt * 16 + lr;
-        if (merge) {
-          const uint64_t pb = s_best[wave][r];
-          best[nt] = pb > best[nt] ? pb : best[nt];
-          lse[nt] = lse_merge(lse[nt], Lse{s_lse[wave][r].x, s_lse[wave][r].y});
-        }
-        s_best[wave][r] = best[nt];
-        s_lse[wave][r] = make_float2(lse[nt].m, lse[nt].s);
-      }
-      best[nt] = 0ull;
-      lse[nt] = lse_empty();
-    }
-  };
-  if constexpr (NCH > 0 && !ALL && MODE != kGmScores) fold_lanes(false);  // empty partials
-
   // work units: groups of kGmWaves * IT items times ksplit slices of K (the
   // waves of a workgroup share the slice, so the staged H chunk is shared),
   // grid-stride (uniform per workgroup)
@@ -381,6 +353,10 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
 
   // a unit of INT4 stage-1 tiles only streams no rows: it skips the K walk
   const bool unit_rows = !Q4 || item0 + kGmWaves * IT > a.n1;
+  // ALL: the candidates' token ids of the records, loaded with the last
+  // chunk (whose next-chunk registers are free) so that the records do not
+  // wait for them
+  uint32_t tokp[IT][4];
   if constexpr (NCH > 0) {
     if (unit_rows) {
       load_h(0);
@@ -392,6 +368,14 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
         if (c + 1 < NCH) {
           load_h(c + 1);
           if ((c & 1) == 0) load_a(a1, c + 1); else load_a(a0, c + 1);
+        } else if constexpr (ALL) {
+#pragma unroll
+          for (int i = 0; i < IT; ++i) {
+            const int64_t t0 = row0[i] + 4 * slice;  // clamped to a cluster row
+            const int64_t tr = item0 + wave * IT + i < a.n1 ? 0 : t0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tokp[i][q] = (uint32_t)a.c2t[tr + q];
+          }
         }
         // keep the next chunk's loads ahead of this chunk's products
         __builtin_amdgcn_sched_barrier(0);
@@ -461,7 +445,8 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
       // tokens, then the 4 lanes that share a batch row
       uint32_t tok[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tok[q] = (uint32_t)a.c2t[row0[i] + 4 * slice + q];
+      for (int q = 0; q < 4; ++q)
+        tok[q] = NCH > 0 ? tokp[i][q] : (uint32_t)a.c2t[row0[i] + 4 * slice + q];
       const int64_t rec = (it - a.n1) * a.B;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -568,14 +553,23 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
       }
     }
   }
-  if constexpr (NCH > 0) {
-    // fold this unit into the wave's LDS partials, so that no running
-    // partial is held in registers across the next unit's K walk
-    fold_lanes(true);
-  }
   }  // groups
   if constexpr (MODE == kGmScores || ALL) return;
-  if constexpr (NCH == 0) fold_lanes(false);
+  // combine the 4 lanes that share a batch column, then the waves
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const uint64_t y = __shfl_xor(best[nt], o, kWave);
+      best[nt] = y > best[nt] ? y : best[nt];
+      if (a.with_lse) lse[nt] = lse_merge(lse[nt], Lse{__shfl_xor(lse[nt].m, o, kWave),
+                                                       __shfl_xor(lse[nt].s, o, kWave)});
+    }
+    if (slice == 0) {
+      s_best[wave][nt * 16 + lr] = best[nt];
+      s_lse[wave][nt * 16 + lr] = make_float2(lse[nt].m, lse[nt].s);
+    }
+  }
   __syncthreads();
   for (int r = threadIdx.x; r < B; r += kGmThreads) {
     uint64_t bb = s_best[0][r];
