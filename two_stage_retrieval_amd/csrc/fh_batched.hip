@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   int64_t row0[IT], kc[IT];
   uint64_t mask[IT];
   const uint8_t* abase[IT];
+  uint32_t ftok[IT][4];  // FLASH: the token ids of the item's rows for this lane
   using AOff = std::conditional_t<(NCH > 0), uint32_t, int64_t>;
   AOff aoff[IT];
 #pragma unroll
@@ -260,6 +261,10 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
       kc[i] = a.ulist ? a.ulist[it / sub] : it / sub;
       row0[i] = kc[i] * a.b + (it % sub) * 16;
       mask[i] = live ? a.masks[kc[i]] : 0ull;
+      // the candidates' token ids, loaded now so that the epilogue does not
+      // wait for them after the K walk
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ftok[i][q] = (uint32_t)a.c2t[row0[i] + 4 * slice + q];
     } else {
       kc[i] = 0;
       row0[i] = it * 16;
@@ -274,24 +279,16 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     aoff[i] = (AOff)(arow * a.row_bytes + (int64_t)(8 * slice) * 2);
   }
   // H chunk staging: thread t moves kHP 16-byte pieces per chunk; piece
-  // t + n * kGmThreads is H row j0 + n * kHStep, 16-byte column kp (rows
-  // past the batch read its last row)
+  // t + n * kGmThreads is H row j0 + n * kHStep, 16-byte column kp.  H is
+  // read through a buffer resource that ends with row B - 1: a piece is the
+  // lane's row-j0 offset plus a uniform row offset (one register for all
+  // pieces; 64 rows of at most FH_MAX_ROW_BYTES fit 31 bits), and the
+  // pieces of rows past the batch read as zeros (their columns are dropped)
   constexpr int kHStep = kGmThreads / (KC / 8);
   static_assert(kHStep * (KC / 8) == kGmThreads, "H staging rows");
+  static_assert((int64_t)64 * FH_MAX_ROW_BYTES < ((int64_t)1 << 31), "H offsets");
   const int j0 = threadIdx.x / (KC / 8), kp = threadIdx.x % (KC / 8);
   const int hdst0 = j0 * (kHRow / 8) + kp;
-  int64_t hoff[kHP];
-#pragma unroll
-  for (int n = 0; n < kHP; ++n) {
-    int j = j0 + n * kHStep;
-    j = j < B ? j : B - 1;
-    hoff[n] = (int64_t)j * a.h_bytes + (int64_t)kp * 16;
-  }
-  // the unrolled walk reads H through a buffer resource that ends with row
-  // B - 1: a piece is the lane's row-j0 offset plus a uniform row offset
-  // (one register for all pieces; its launcher checks that 64 rows of H fit
-  // 31 bits), and the pieces of rows past the batch read as zeros (their
-  // columns are dropped)
   const __amdgpu_buffer_rsrc_t hrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.H), (short)0, (int)((B - 1) * a.h_bytes + (int64_t)a.d * 2),
       kBufferFlags);
@@ -325,11 +322,8 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
   auto load_h = [&](int c) {
 #pragma unroll
     for (int n = 0; n < kHP; ++n)
-      if constexpr (NCH > 0)
-        hreg[n] = __builtin_amdgcn_raw_buffer_load_b128(
-            hrsrc, hoff0 + (uint32_t)(c * KC * 2), (int)(n * kHStep * a.h_bytes), 0);
-      else
-        hreg[n] = *reinterpret_cast<const u32x4_t*>(a.H + hoff[n] + (int64_t)c * KC * 2);
+      hreg[n] = __builtin_amdgcn_raw_buffer_load_b128(
+          hrsrc, hoff0 + (uint32_t)(c * KC * 2), (int)(n * kHStep * a.h_bytes), 0);
   };
   auto store_h = [&](int buf) {
 #pragma unroll
@@ -519,7 +513,7 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
     for (int q = 0; q < 4; ++q) {
       const int64_t row = row0[i] + 4 * slice + q;
       if constexpr (MODE == kGmDense) tok[q] = (uint32_t)row;
-      else tok[q] = (uint32_t)a.c2t[row];
+      else tok[q] = ftok[i][q];
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -660,8 +654,7 @@ constexpr int kWideItems = 2;
 static bool engine_wide(const Stage2mArgs& a, int mode) {
   const int64_t lim = (int64_t)1 << 31;
   return (mode == kGmDense || mode == kGmAll) && !a.sample && (a.B + 15) / 16 == 4 &&
-         a.d == 8 * 256 && (int64_t)64 * a.h_bytes < lim && a.v * a.row_bytes < lim &&
-         (int64_t)a.c * a.c_row_bytes < lim;
+         a.d == 8 * 256 && a.v * a.row_bytes < lim && (int64_t)a.c * a.c_row_bytes < lim;
 }
 static int engine_items(const Stage2mArgs& a, int mode) {
   return engine_wide(a, mode) ? kWideItems : kGmItems;
