@@ -92,33 +92,151 @@ __device__ __forceinline__ void int4_tile_scores(const uint8_t* q4, const uint16
   }
 }
 
-template <int NT>
+// The batched INT4 stage 1 as its own kernel.  A workgroup owns TPW
+// consecutive tiles and its 4 waves split the 128-column groups (wave w
+// takes groups [w G / 4, (w + 1) G / 4)): each H fragment a wave loads feeds
+// the products of all TPW tiles, so a workgroup reads H once, and the codes
+// and scales of a batch of kS1qGB groups of every tile are requested before
+// the first product (one round trip per batch, not one per group).  The
+// waves' partial scores meet in LDS; wave i adds them in wave order for
+// tile i and stores its keys.
+constexpr int kS1qWaves = kS1qThreads / kWave;
+constexpr int kS1qGB = 4;  // groups per batch of loads
+
+template <int NT, int TPW>
 __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Args a, int B) {
+  static_assert(TPW <= kS1qWaves, "one finishing wave per tile");
+  __shared__ f32x4_t s_red[kS1qWaves][TPW][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = lane >> 4, lr = lane & 15;
-  const int tile = blockIdx.x * (kS1qThreads / kWave) + wave;
+  const int G = a.groups;
+  const int tile0 = blockIdx.x * TPW;
+  const int g_lo = wave * G / kS1qWaves, g_hi = (wave + 1) * G / kS1qWaves;
+  // lane (slice, lr) feeds H row nt * 16 + lr, columns 128 g + 32 slice +
+  // 8 s + [0, 8) at step s (rows past the batch repeat the last one; their
+  // results are dropped); tiles past the last repeat the last one too
+  const uint8_t* hp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int j = nt * 16 + lr < B ? nt * 16 + lr : B - 1;
+    hp[nt] = a.H + (int64_t)j * a.h_bytes + (int64_t)(32 * slice) * 2;
+  }
+  const uint4* codes[TPW];
+  const uint16_t* scl[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tl = tile0 + i < a.ntiles ? tile0 + i : a.ntiles - 1;
+    codes[i] = reinterpret_cast<const uint4*>(a.q4) + (int64_t)tl * G * kWave + lane;
+    scl[i] = a.q4s + (int64_t)tl * G * 16 + 4 * slice;
+  }
+  f32x4_t tot[TPW][NT];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) tot[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the H fragments of one group (4 MFMA steps): with one or two column
+  // tiles the next group's are requested before the current group's
+  // products (two buffers), else each group's just before its own
+  constexpr int kHB = NT <= 2 ? 2 : 1;
+  uint4 hb[kHB][4][NT];
+  auto load_hg = [&](uint4 (&dst)[4][NT], int g) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        dst[s][nt] = *reinterpret_cast<const uint4*>(hp[nt] + (int64_t)(128 * g + 8 * s) * 2);
+  };
+  for (int g0 = g_lo; g0 < g_hi; g0 += kS1qGB) {
+    uint4 w[TPW][kS1qGB];
+    uint2 sc[TPW][kS1qGB];
+#pragma unroll
+    for (int gi = 0; gi < kS1qGB; ++gi) {
+      if (g0 + gi < g_hi) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          w[i][gi] = codes[i][(int64_t)(g0 + gi) * kWave];
+          // scales of the lane's 4 output rows of the tile: 4 slice + q
+          sc[i][gi] = *reinterpret_cast<const uint2*>(scl[i] + (g0 + gi) * 16);
+        }
+      }
+    }
+    if constexpr (kHB == 2) load_hg(hb[0], g0);
+#pragma unroll
+    for (int gi = 0; gi < kS1qGB; ++gi) {
+      if (g0 + gi >= g_hi) break;  // uniform over the wave
+      if constexpr (kHB == 2) {
+        if (gi + 1 < kS1qGB && g0 + gi + 1 < g_hi) load_hg(hb[(gi + 1) & 1], g0 + gi + 1);
+      } else {
+        load_hg(hb[0], g0 + gi);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the loads go out before the products
+      const uint4 (&bv)[4][NT] = hb[kHB == 2 ? (gi & 1) : 0];
+      f32x4_t part[TPW][NT];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) part[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const uint32_t ws = s == 0 ? w[i][gi].x : s == 1 ? w[i][gi].y : s == 2 ? w[i][gi].z
+                                                                                 : w[i][gi].w;
+          // the lane's codes for this step as bf16 (exact for -8..7)
+          const uint4 av = make_uint4(int4_pair_bf16(ws, 0), int4_pair_bf16(ws, 2),
+                                      int4_pair_bf16(ws, 4), int4_pair_bf16(ws, 6));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) part[i][nt] = mfma_bf16(av, bv[s][nt], part[i][nt]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const float scq[4] = {__uint_as_float(sc[i][gi].x << 16),
+                              __uint_as_float(sc[i][gi].x & 0xFFFF0000u),
+                              __uint_as_float(sc[i][gi].y << 16),
+                              __uint_as_float(sc[i][gi].y & 0xFFFF0000u)};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tot[i][nt][q] = fmaf(scq[q], part[i][nt][q], tot[i][nt][q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) s_red[wave][i][nt][lane] = tot[i][nt];
+  __syncthreads();
+  if (wave >= TPW) return;
+  const int tile = tile0 + wave;
   if (tile >= a.ntiles) return;
-  f32x4_t tot[NT];
-  int4_tile_scores<NT>(a.q4, a.q4s, a.groups, a.H, a.h_bytes, B, tile, lane, tot);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + lr;
     if (r >= B) continue;
+    f32x4_t sum = s_red[0][wave][nt][lane];
+#pragma unroll
+    for (int w = 1; w < kS1qWaves; ++w) sum += s_red[w][wave][nt][lane];
     // the lane's 4 consecutive clusters share one Philox block
     const int kq0 = tile * 16 + 4 * slice;
     const float4 g4 = a.sample ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
                                : make_float4(0.f, 0.f, 0.f, 0.f);
     const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
+    float kv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k = kq0 + q;
-      if (k >= a.c) continue;
-      const float s = tot[nt][q];
       // raw_keys: the plain score (the select forms the key after counting)
-      const float key = (a.sample && !a.raw_keys) ? s * a.inv_tau + gq[q] : s;
-      a.keys[(int64_t)r * a.key_stride + k] = key;
-      if (a.dbg_scores) a.dbg_scores[(int64_t)r * a.c + k] = s;
+      kv[q] = (a.sample && !a.raw_keys) ? sum[q] * a.inv_tau + gq[q] : sum[q];
+      if (a.dbg_scores && kq0 + q < a.c) a.dbg_scores[(int64_t)r * a.c + kq0 + q] = sum[q];
+    }
+    float* kr = a.keys + (int64_t)r * a.key_stride + kq0;
+    if (kq0 + 3 < a.c) {
+      *reinterpret_cast<float4*>(kr) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (kq0 + q < a.c) kr[q] = kv[q];
     }
   }
 }
@@ -625,6 +743,119 @@ __global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblock
 }
 
 // ---------------------------------------------------------------------------
+// Batched bf16 stage 1 in one round of loads.  A workgroup's unit is 4
+// consecutive 16-row items (one per wave) times one K slice of at most
+// kScChunks chunks of 128 columns.  Every thread requests all of its A rows'
+// pieces and its share of the slice's H before anything is waited for; H
+// goes to LDS (padded rows, one buffer per chunk), then the waves run the
+// products chunk by chunk, in the order the engine's SCORES walk uses, and
+// store the slice's partial scores (or, with one slice, the keys).
+// ---------------------------------------------------------------------------
+constexpr int kScChunks = 4;
+constexpr int kScKC = 128;
+
+template <int NT>
+__global__ __launch_bounds__(kGmThreads) void scores_mfma_kernel(Stage2mArgs a) {
+  constexpr int kSteps = kScKC / 32;
+  constexpr int kHRow = kScKC + 8;                       // LDS row pitch in bf16
+  constexpr int kHP = NT * 16 * (kScKC / 8) / kGmThreads;  // H pieces per thread per chunk
+  static_assert(kHP * kGmThreads == NT * 16 * (kScKC / 8), "H staging");
+  __shared__ uint4 s_h[kScChunks][NT * 16 * kHRow / 8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = lane >> 4, lr = lane & 15;
+  const int B = a.B;
+  const int S = a.ksplit;
+  const int unit = blockIdx.x;
+  const int sp = unit % S;
+  const int64_t item = (int64_t)(unit / S) * kGmWaves + wave;
+  const int64_t nitems = ((int64_t)a.c + 15) / 16;
+  const bool live = item < nitems;  // uniform over the wave
+  const int nchunks = a.d / kScKC;
+  const int cbeg = sp * nchunks / S, nc = (sp + 1) * nchunks / S - cbeg;  // nc <= kScChunks
+  const int64_t row0 = (live ? item : nitems - 1) * 16;
+  int64_t arow = row0 + lr;
+  arow = arow < a.c ? arow : a.c - 1;
+  const uint8_t* ap = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2 +
+                      (int64_t)cbeg * kScKC * 2;
+  // H through a buffer resource that ends with row B - 1: pieces of rows past
+  // the batch read as zeros (their columns are dropped)
+  constexpr int kHStep = kGmThreads / (kScKC / 8);
+  const int j0 = threadIdx.x / (kScKC / 8), kp = threadIdx.x % (kScKC / 8);
+  const __amdgpu_buffer_rsrc_t hrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.H), (short)0, (int)((B - 1) * a.h_bytes + (int64_t)a.d * 2),
+      kBufferFlags);
+  const uint32_t hoff0 = (uint32_t)(j0 * a.h_bytes) + (uint32_t)kp * 16 + (uint32_t)cbeg * kScKC * 2;
+  uint4 av[kScChunks][kSteps];
+  u32x4_t hreg[kScChunks][kHP];
+#pragma unroll
+  for (int c = 0; c < kScChunks; ++c) {
+    if (c < nc) {
+#pragma unroll
+      for (int n = 0; n < kHP; ++n)
+        hreg[c][n] = __builtin_amdgcn_raw_buffer_load_b128(
+            hrsrc, hoff0 + (uint32_t)(c * kScKC * 2), (int)(n * kHStep * a.h_bytes), 0);
+      if (live) {
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u)
+          av[c][u] = *reinterpret_cast<const uint4*>(ap + (int64_t)c * kScKC * 2 + u * 64);
+      }
+    }
+  }
+  const int hdst0 = j0 * (kHRow / 8) + kp;
+#pragma unroll
+  for (int c = 0; c < kScChunks; ++c)
+    if (c < nc)
+#pragma unroll
+      for (int n = 0; n < kHP; ++n)
+        reinterpret_cast<u32x4_t*>(s_h[c])[hdst0 + n * kHStep * (kHRow / 8)] = hreg[c][n];
+  __syncthreads();
+  if (!live) return;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kScChunks; ++c) {
+    if (c >= nc) break;
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      uint4 bv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bv[nt] = s_h[c][(nt * 16 + lr) * (kHRow / 8) + u * 4 + slice];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(av[c][u], bv[nt], acc[nt]);
+    }
+  }
+  // lane: centroid rows row0 + 4 slice + q for batch row nt * 16 + lr
+  const bool keyed = S == 1 && !a.raw_scores;  // else partial or plain scores (the select keys them)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + lr;
+    if (r >= B) continue;
+    const int64_t kq0 = row0 + 4 * slice;
+    // the lane's 4 consecutive clusters share one Philox block
+    const float4 g4 = (keyed && a.sample) ? gumbel4(a.seeds[r], kStreamCluster, (uint32_t)kq0 >> 2)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
+    float kv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sc = acc[nt][q];
+      kv[q] = (keyed && a.sample) ? sc * a.inv_tau + gq[q] : sc;
+      if (keyed && a.dbg_scores && kq0 + q < a.c) a.dbg_scores[(int64_t)r * a.c + kq0 + q] = sc;
+    }
+    float* kr = a.keys + (keyed ? 0 : (int64_t)sp * a.part_stride) + (int64_t)r * a.key_stride + kq0;
+    if (kq0 + 3 < a.c) {
+      *reinterpret_cast<float4*>(kr) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (kq0 + q < a.c) kr[q] = kv[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 bool batched_supported(int dtype, int d, int B, bool int4) {
@@ -699,15 +930,22 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   const int NT = (B + 15) / 16;
   *ksplit = 1;
   if (int4) {
-    const dim3 grid((a.ntiles + kS1qThreads / kWave - 1) / (kS1qThreads / kWave));
-    switch (NT) {
-      case 1: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<1>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
-      case 2: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<2>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
-      case 3: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<3>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
-      case 4: hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<4>, grid, dim3(kS1qThreads), 0, s, e0, e1, 0, a, B); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    // tiles per workgroup: as many as keep at least 256 workgroups (one per
+    // compute unit), at most 4 (2 from three column tiles on, for registers)
+    int tpw = NT <= 2 ? 4 : 2;
+    while (tpw > 1 && (a.ntiles + tpw - 1) / tpw < 256) tpw /= 2;
+    const dim3 grid((a.ntiles + tpw - 1) / tpw), block(kS1qThreads);
+#define FH_S1Q(N, T)                                                                         \
+  if (NT == N && tpw == T) {                                                                 \
+    hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<N, T>, grid, block, 0, s, e0, e1, 0, a, B); \
+    return hipGetLastError();                                                                \
+  }
+    FH_S1Q(1, 4) FH_S1Q(1, 2) FH_S1Q(1, 1)
+    FH_S1Q(2, 4) FH_S1Q(2, 2) FH_S1Q(2, 1)
+    FH_S1Q(3, 2) FH_S1Q(3, 1)
+    FH_S1Q(4, 2) FH_S1Q(4, 1)
+#undef FH_S1Q
+    return hipErrorInvalidValue;
   }
   Stage2mArgs m{};
   m.base = a.C;
@@ -736,6 +974,22 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
   m.part_stride = a.part_stride;
   m.raw_scores = a.raw_keys;
   *ksplit = S;
+  if (nchunks <= kMaxKSplit * kScChunks) {
+    // one round of loads per unit: at most kScChunks chunks per K slice
+    const int smin = (nchunks + kScChunks - 1) / kScChunks;
+    S = S < smin ? smin : S;
+    m.ksplit = S;
+    *ksplit = S;
+    const dim3 grid((unsigned)(groups * S)), block(kGmThreads);
+    switch ((B + 15) / 16) {
+      case 1: hipExtLaunchKernelGGL(scores_mfma_kernel<1>, grid, block, 0, s, e0, e1, 0, m); break;
+      case 2: hipExtLaunchKernelGGL(scores_mfma_kernel<2>, grid, block, 0, s, e0, e1, 0, m); break;
+      case 3: hipExtLaunchKernelGGL(scores_mfma_kernel<3>, grid, block, 0, s, e0, e1, 0, m); break;
+      case 4: hipExtLaunchKernelGGL(scores_mfma_kernel<4>, grid, block, 0, s, e0, e1, 0, m); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int64_t units = groups * S;
   const int grid = (int)(units < 4096 ? units : 4096);
   return launch_engine_nt<kGmScores, kKC>(m, grid, s, e0, e1);
