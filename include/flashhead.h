@@ -402,7 +402,8 @@ int flashhead_query(const fh_handle* h, int32_t what, int64_t* value);
  * cluster once instead of only the selected ones, and drops the wait for
  * the selection.  Without a path flag, batched steps take path 4 when the
  * expected share of clusters that at least one of B independent rows
- * selects, 1 - (1 - p / c)^B, is at least 0.8.  On path 4 the candidates'
+ * selects, 1 - (1 - p / c)^B, is at least 0.85 and d is a multiple of 256
+ * (the shapes where the stream was measured faster).  On path 4 the candidates'
  * debug logits (fh_debug.cand_ids / cand_logits) come from a second gather
  * of the selected rows after the step (debug only: it does not change the
  * step's tokens or lse).

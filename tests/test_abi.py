@@ -228,13 +228,17 @@ def test_plan_step_paths(fh):
     assert path == 1 and 1 <= grid < 256
     # batches: matrix cores for bf16 with b a multiple of 16, else row-dot;
     # select first while the rows' selections are expected to leave many
-    # clusters unread (1 - (1 - p/c)^B below 0.8), else stream every cluster
+    # clusters unread (1 - (1 - p/c)^B below 0.85), else stream every
+    # cluster, on heads whose width the stream walks in 256-wide chunks
     assert plan(8016, 16, 2048, BF, 0, 2, 512, 256, 1) == (3, 0)
     assert plan(8016, 16, 2048, BF, 0, 16, 512, 256, 1) == (3, 0)     # 0.65
-    assert plan(8016, 16, 2048, BF, 0, 24, 512, 256, 1) == (3, 0)     # 0.79
-    assert plan(8016, 16, 2048, BF, 0, 25, 512, 256, 1) == (4, 0)     # 0.81
+    assert plan(8016, 16, 2048, BF, 0, 28, 512, 256, 1) == (3, 0)     # 0.842
+    assert plan(8016, 16, 2048, BF, 0, 29, 512, 256, 1) == (4, 0)     # 0.853
     assert plan(8016, 16, 2048, BF, 0, 64, 512, 256, 1) == (4, 0)     # 0.985
-    assert plan(16384, 16, 1152, BF, fh.FH_QUANT_INT4_G128, 32, 1024, 256, 1) == (4, 0)
+    # d = 1152: select first at any coverage
+    assert plan(16384, 16, 1152, BF, fh.FH_QUANT_INT4_G128, 32, 1024, 256, 1) == (3, 0)
+    assert plan(16384, 16, 1152, BF, fh.FH_QUANT_INT4_G128, 64, 1024, 256, 1) == (3, 0)
+    assert plan(16384, 16, 1152, BF, 0, 64, 1024, 256, 1) == (3, 0)
     # the path flags override the rule, for batches only
     SF, SA = fh.FH_FLAG_SELECT_FIRST, fh.FH_FLAG_STREAM_ALL
     assert plan(8016, 16, 2048, BF, 0, 64, 512, 256, 1, SF) == (3, 0)

@@ -36,8 +36,8 @@ def test_batched_list_and_all_cluster_walks_alternate(fh, flags):
     # cluster; one handle alternating between the two must find the row
     # masks cleared by whichever ran before (greedy and sampling).  Without
     # a path flag the same handle also alternates between the select-first
-    # path and the all-cluster stream (1 - (1 - 40/400)^B: B = 24 and 16
-    # stream, B = 2, 3, 5 select first)
+    # path and the all-cluster stream (1 - (1 - 40/400)^B: B = 24 streams,
+    # B = 16, 2, 3, 5 select first)
     cs = case(1, c=400, b=16, d=256, seed=56)
     fl = getattr(fh, "FH_FLAG_" + flags) if flags else 0
     head = cs.prepare(fh, max_batch=24, max_p=40, flags=fl)

@@ -73,8 +73,8 @@ namespace {
 
 constexpr int kMaxGrid = 8192;       // largest grid.x of a decode launch
 constexpr int kDenseMaxGrid = 8192;  // dense: partial slots of the batched kernel (2 x 4096)
-constexpr double kStreamAllCover = 0.8;  // batched: expected selected share from which
-                                         // every cluster is streamed
+constexpr double kStreamAllCover = 0.85;  // batched: expected selected share from which
+                                          // every cluster is streamed
 
 // selection keys of a batch row: c floats padded to a 16-byte multiple
 int64_t key_stride(int c) { return ((int64_t)c + 3) & ~(int64_t)3; }
@@ -232,9 +232,13 @@ int plan_path(int c, int b, int d, int64_t row_bytes, int dtype, bool int4, int 
     if (flags & FH_FLAG_STREAM_ALL) return 4;
     // expected share of clusters that at least one of B independent rows
     // selects: when most clusters are read anyway, reading all of them
-    // without waiting for the selection costs less
+    // without waiting for the selection costs less.  Measured crossover (cold
+    // calls, one MI355X): about 0.85 at the Llama-3.2-1B head shape, whose
+    // stream walks K in 256-wide chunks (d % 256 == 0); at the Gemma-3-1B
+    // INT4 head shape (d = 1152, 128-wide chunks) selecting first was as
+    // fast or faster at every batch from 8 to 64 rows
     const double cover = 1.0 - pow(1.0 - (double)p / c, (double)B);
-    return cover >= kStreamAllCover ? 4 : 3;
+    return (cover >= kStreamAllCover && d % 256 == 0) ? 4 : 3;
   }
   if (B == 1 && stage1_selects(c)) {
     const int g = decode_b1_grid(c, p, (int)(row_bytes / 16), (c + 15) / 16, (int64_t)p * b,
