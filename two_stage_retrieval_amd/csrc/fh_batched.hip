@@ -709,7 +709,28 @@ __global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblock
   const float2* pl = a.part_lse + (int64_t)r * nblocks;
   uint64_t bb = 0ull;
   Lse ll = lse_empty();
-  for (int j = t; j < nblocks; j += 256) {
+  // every partial of the thread is requested before the first is folded
+  // (one round trip instead of one per partial), then folded in j order
+  constexpr int kPer = 16;  // the engine's grid is at most 16 * 256 workgroups
+  uint64_t xb[kPer];
+  float2 xl[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = t + 256 * i;
+    if (j < nblocks) {
+      xb[i] = pb[j];
+      if (a.with_lse) xl[i] = pl[j];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = t + 256 * i;
+    if (j < nblocks) {
+      bb = xb[i] > bb ? xb[i] : bb;
+      if (a.with_lse) ll = lse_merge(ll, Lse{xl[i].x, xl[i].y});
+    }
+  }
+  for (int j = t + 256 * kPer; j < nblocks; j += 256) {
     const uint64_t x = pb[j];
     bb = x > bb ? x : bb;
     if (a.with_lse) ll = lse_merge(ll, Lse{pl[j].x, pl[j].y});
