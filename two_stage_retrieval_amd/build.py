@@ -24,11 +24,15 @@ SOURCES = ["fh_api.hip", "fh_stage1.hip", "fh_decode_b1_adapt.hip", "fh_rowdot.h
            "fh_prepare.hip", "fh_batched.hip", "fh_mc.hip",
            "fh_kmeans.hip", "fh_host.cpp"]
 
-# Packed-fp32 instructions are disabled for all device code.
+# Packed-fp32 instructions are disabled for all device code.  Leading scalar
+# kernel arguments (up to 8 dwords) are preloaded into scalar registers by
+# the dispatcher, so a kernel's first requests need not wait for its
+# argument loads (kernels that take one argument struct are unaffected).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -162,8 +162,15 @@ __device__ __forceinline__ void b1_score_int4(const Stage1Args& a, float* keys, 
 // Every wait is bounded; running out of patience sets a bit of the error
 // word instead of hanging.
 // ---------------------------------------------------------------------------
+// The values the prologue's first requests need (h, the centroid rows and
+// their sizes) come as leading scalar arguments, which the dispatcher can
+// preload into scalar registers before the waves start; everything else is
+// read from `args`, behind those requests.
 template <typename TE, int NCH, int R, int IPT, bool INT4, bool ADAPT>
-__global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args) {
+__global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(const uint8_t* pre_H,
+                                                               const uint8_t* pre_C, int pre_c,
+                                                               int pre_row_bytes, int pre_nchunk,
+                                                               DecodeB1Args args) {
   __shared__ SelSmem sm;
   __shared__ float s_h[INT4 ? FH_MAX_ROW_BYTES / 2 : 1];
   __shared__ MergeSmem<kS1Threads> ms;
@@ -189,22 +196,21 @@ __global__ __launch_bounds__(kS1Threads) void decode_b1_kernel(DecodeB1Args args
   uint4 hraw[NCH];
   uint4 data[kS1Rows][NCH];
   {
-    const int nch2 = args.s2.nchunk;
-    const __amdgpu_buffer_rsrc_t hrs = sel_rsrc(a.H, (uint32_t)nch2 * 16u);
+    const __amdgpu_buffer_rsrc_t hrs = sel_rsrc(pre_H, (uint32_t)pre_nchunk * 16u);
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
       hraw[i] = sel_load4<false>(hrs, (uint32_t)(lane + kWave * i) * 16u);
     if constexpr (!INT4) {
-      const __amdgpu_buffer_rsrc_t crs = sel_rsrc(a.C, (uint32_t)(a.c * a.row_bytes));
-      const bool have = w0 < (a.c + kS1Rows - 1) / kS1Rows;
+      const __amdgpu_buffer_rsrc_t crs = sel_rsrc(pre_C, (uint32_t)(pre_c * pre_row_bytes));
+      const bool have = w0 < (pre_c + kS1Rows - 1) / kS1Rows;
 #pragma unroll
       for (int rr = 0; rr < kS1Rows; ++rr) {
-        const int row = w0 * kS1Rows + rr < a.c ? w0 * kS1Rows + rr : a.c - 1;
+        const int row = w0 * kS1Rows + rr < pre_c ? w0 * kS1Rows + rr : pre_c - 1;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
           const int ch = lane + kWave * i;
-          const uint32_t off = (have && ch < a.nchunk)
-                                   ? (uint32_t)(row * a.row_bytes) + (uint32_t)ch * 16u
+          const uint32_t off = (have && ch < pre_nchunk)
+                                   ? (uint32_t)(row * pre_row_bytes) + (uint32_t)ch * 16u
                                    : 0xFFFFFFF0u;
           data[rr][i] = sel_load4<false>(crs, off);
         }
@@ -450,13 +456,16 @@ template <typename K>
 hipError_t launch_one(K kernel, const DecodeB1Args& a, int grid, bool coop, hipStream_t s,
                              hipEvent_t e0, hipEvent_t e1) {
   const dim3 g(grid), block(kS1Threads);
+  const uint8_t* H = a.s1.H;
+  const uint8_t* C = a.s1.C;
+  int c = a.s1.c, row_bytes = (int)a.s1.row_bytes, nchunk = a.s1.nchunk;
   if (!coop) {
-    hipExtLaunchKernelGGL(kernel, g, block, 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(kernel, g, block, 0, s, e0, e1, 0, H, C, c, row_bytes, nchunk, a);
     return hipGetLastError();
   }
   if (e0) (void)hipEventRecord(e0, s);
   DecodeB1Args copy = a;
-  void* params[] = {&copy};
+  void* params[] = {&H, &C, &c, &row_bytes, &nchunk, &copy};
   const hipError_t e =
       hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), g, block, params, 0, s);
   if (e != hipSuccess) return e;
