@@ -80,6 +80,27 @@ def test_batched_path_ragged_batches(fh, B, path):
     print(st)
 
 
+@pytest.mark.parametrize("B", [9, 40, 64])
+def test_int4_select_first_tiles_per_workgroup(fh, B):
+    # the batched INT4 stage 1 on path 3 with several tiles per workgroup:
+    # 1025 tiles, the last with 6 rows, so four tiles per workgroup with one
+    # column tile of H and two from three column tiles on, with a last
+    # workgroup that holds one live tile; d = 384 gives 3 groups of 128
+    # columns over 4 waves, so one wave has none
+    cs = case(4, c=16390, b=16, d=384, seed=81)
+    head = cs.prepare(fh, max_batch=B, max_p=48, flags=fh.FH_FLAG_SELECT_FIRST)
+    H, H64 = cs.hidden(B, offset=3 * B)
+    st = Stats()
+    res = run_debug(fh, head, dev_tensor(H), B, 48, "greedy")
+    assert path_of(fh, head) == 3
+    check_batch(cs, res, H64, 48, stats=st)
+    seeds = synth.make_seeds(9, B)
+    res = run_debug(fh, head, dev_tensor(H), B, 48, "sample", 0.8, seeds_dev(seeds))
+    check_batch(cs, res, H64, 48, "sample", 0.8, seeds, stats=st)
+    assert fh.flashhead_query(head.handle, 9) == 0
+    print(st)
+
+
 def test_single_launch_p_equals_c_matches_dense(fh):
     # every cluster probed: the head is the dense argmax, id for id
     cs = case(1, c=50, b=16, d=256, seed=56)
