@@ -700,13 +700,18 @@ __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // per batch row: fold the per-block partials (a contiguous run per row) into
 // the token (and lse), wave by wave and then the waves in order; the rows'
 // workgroups together clear the cluster masks of this call's union
-__global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblocks) {
+// (the partials' addresses, count and the lse switch come as leading scalar
+// arguments, preloaded into scalar registers, so the partials' loads need
+// not wait for the argument struct)
+__global__ __launch_bounds__(256) void finalize_kernel(const uint64_t* part_best,
+                                                       const float2* part_lse, int nblocks,
+                                                       int with_lse, Stage2mArgs a) {
   __shared__ uint64_t s_b[256 / kWave];
   __shared__ float2 s_l[256 / kWave];
   const int r = blockIdx.x;
   const int t = threadIdx.x;
-  const uint64_t* pb = a.part_best + (int64_t)r * nblocks;
-  const float2* pl = a.part_lse + (int64_t)r * nblocks;
+  const uint64_t* pb = part_best + (int64_t)r * nblocks;
+  const float2* pl = part_lse + (int64_t)r * nblocks;
   uint64_t bb = 0ull;
   Lse ll = lse_empty();
   // every partial of the thread is requested before the first is folded
@@ -719,7 +724,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblock
     const int j = t + 256 * i;
     if (j < nblocks) {
       xb[i] = pb[j];
-      if (a.with_lse) xl[i] = pl[j];
+      if (with_lse) xl[i] = pl[j];
     }
   }
 #pragma unroll
@@ -727,16 +732,16 @@ __global__ __launch_bounds__(256) void finalize_kernel(Stage2mArgs a, int nblock
     const int j = t + 256 * i;
     if (j < nblocks) {
       bb = xb[i] > bb ? xb[i] : bb;
-      if (a.with_lse) ll = lse_merge(ll, Lse{xl[i].x, xl[i].y});
+      if (with_lse) ll = lse_merge(ll, Lse{xl[i].x, xl[i].y});
     }
   }
   for (int j = t + 256 * kPer; j < nblocks; j += 256) {
     const uint64_t x = pb[j];
     bb = x > bb ? x : bb;
-    if (a.with_lse) ll = lse_merge(ll, Lse{pl[j].x, pl[j].y});
+    if (with_lse) ll = lse_merge(ll, Lse{pl[j].x, pl[j].y});
   }
   bb = wave_max_u64(bb);
-  if (a.with_lse) ll = wave_lse(ll);
+  if (with_lse) ll = wave_lse(ll);
   if ((t & (kWave - 1)) == 0) {
     s_b[t / kWave] = bb;
     s_l[t / kWave] = make_float2(ll.m, ll.s);
@@ -1042,7 +1047,9 @@ hipError_t launch_stage2_mfma(const Stage2mArgs& a, bool dense, hipStream_t s, c
   hipError_t e = dense ? launch_engine<kGmDense>(a, grid, s, e0, e1)
                        : launch_engine<kGmFlash>(a, grid, s, e0, e1);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(256), 0, s, a, grid);
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(256), 0, s,
+                     static_cast<const uint64_t*>(a.part_best),
+                     static_cast<const float2*>(a.part_lse), grid, a.with_lse, a);
   return hipGetLastError();
 }
 

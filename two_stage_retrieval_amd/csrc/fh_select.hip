@@ -9,28 +9,39 @@ namespace fh {
 
 constexpr int kSelThreads = 1024;
 
+// The values the first loads need (the keys or K-slice partials of the
+// row) arrive as leading scalar kernel arguments, which the dispatcher
+// preloads into scalar registers, so the loads need not wait for the
+// argument struct; the rest comes in SelectArgs.
+struct SelectFirst {
+  const float* keys;
+  int key_stride, nparts, part_stride;
+};
+
 // The selection of batch row r (the whole workgroup).
 template <int IPT>
-__device__ __forceinline__ void select_row(const SelectArgs& a, int r, SelSmem& sm) {
+__device__ __forceinline__ void select_row(const SelectFirst& f, const SelectArgs& a, int r,
+                                           SelSmem& sm) {
   uint32_t u[IPT];
-  select_load_keys<IPT, false>(a.keys + (int64_t)r * a.key_stride, (int)a.key_stride, u);
+  // every slice of the row is requested before anything else is read
+  uint32_t v[kMaxKSplit - 1][IPT];
+  select_load_keys<IPT, false>(f.keys + (int64_t)r * f.key_stride, f.key_stride, u);
+#pragma unroll
+  for (int sp = 1; sp < kMaxKSplit; ++sp)
+    if (sp < f.nparts)
+      select_load_keys<IPT, false>(f.keys + (int64_t)sp * f.part_stride + (int64_t)r * f.key_stride,
+                                   f.key_stride, v[sp - 1]);
   int p = a.p;  // the row's probe count
-  if (a.nparts > 1 || a.form_keys) {
+  if (f.nparts > 1 || a.form_keys) {
     // the scores arrive as K-slice partials (or, with form_keys, as plain
-    // scores): all slices are loaded before any is added, then summed in
+    // scores): all slices were loaded before any is added, then summed in
     // slice order; then the keys are formed
     // (sampling: score / tau + Gumbel noise of stream 0, one Philox block per
     // four consecutive ids)
     const int k0 = threadIdx.x * IPT;
-    uint32_t v[kMaxKSplit - 1][IPT];
 #pragma unroll
     for (int sp = 1; sp < kMaxKSplit; ++sp)
-      if (sp < a.nparts)
-        select_load_keys<IPT, false>(a.keys + sp * a.part_stride + (int64_t)r * a.key_stride,
-                                     (int)a.key_stride, v[sp - 1]);
-#pragma unroll
-    for (int sp = 1; sp < kMaxKSplit; ++sp)
-      if (sp < a.nparts)
+      if (sp < f.nparts)
 #pragma unroll
         for (int j = 0; j < IPT; ++j)
           u[j] = __float_as_uint(__uint_as_float(u[j]) + __uint_as_float(v[sp - 1][j]));
@@ -67,22 +78,28 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, SelSmem& 
 }
 
 template <int IPT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* keys, int key_stride,
+                                                             int nparts, int part_stride,
+                                                             SelectArgs a) {
   __shared__ SelSmem sm;
-  select_row<IPT>(a, blockIdx.x, sm);
+  const SelectFirst f{keys, key_stride, nparts, part_stride};
+  select_row<IPT>(f, a, blockIdx.x, sm);
 }
 
 // Selection of batch row r, then the fold of the records the all-cluster
 // stream left for its selected clusters: the best decode key (the token) and
 // the log-sum-exp over exactly the candidates of those clusters.
 template <int IPT>
-__global__ __launch_bounds__(kSelThreads) void select_fold_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads) void select_fold_kernel(const float* keys,
+                                                                  int key_stride, int nparts,
+                                                                  int part_stride, SelectArgs a) {
+  const SelectFirst f{keys, key_stride, nparts, part_stride};
   __shared__ SelSmem sm;
   __shared__ uint64_t s_b[kSelThreads / kWave];
   __shared__ float2 s_l[kSelThreads / kWave];
   const int r = blockIdx.x;
   const int t = threadIdx.x;
-  select_row<IPT>(a, r, sm);
+  select_row<IPT>(f, a, r, sm);
   __threadfence_block();  // this workgroup's writes of the row's selection
   __syncthreads();
   const int32_t* sr = a.sel + (int64_t)r * a.sel_stride;
@@ -154,7 +171,8 @@ hipError_t launch_select_fold(const SelectArgs& a, int B, hipStream_t s, const T
   const dim3 grid(B), block(kSelThreads);
 #define FH_SEL_IPT(N)                                                                \
   if (ipt <= N) {                                                                    \
-    hipExtLaunchKernelGGL(select_fold_kernel<N>, grid, block, 0, s, e0, e1, 0, a);   \
+    hipExtLaunchKernelGGL(select_fold_kernel<N>, grid, block, 0, s, e0, e1, 0, a.keys,  \
+                          (int)a.key_stride, a.nparts, (int)a.part_stride, a);      \
     return hipGetLastError();                                                        \
   }
   FH_SEL_IPT(4)
@@ -173,7 +191,8 @@ hipError_t launch_select(const SelectArgs& a, int B, hipStream_t s, const Timing
   hipEvent_t es = a.ulist ? nullptr : e1;
 #define FH_SEL_IPT(N)                                                                         \
   if (ipt <= N) {                                                                             \
-    hipExtLaunchKernelGGL(select_kernel<N>, grid, block, 0, s, e0, es, 0, a);                 \
+    hipExtLaunchKernelGGL(select_kernel<N>, grid, block, 0, s, e0, es, 0, a.keys,             \
+                          (int)a.key_stride, a.nparts, (int)a.part_stride, a);                \
     if (a.ulist)                                                                              \
       hipExtLaunchKernelGGL(union_kernel<N>, dim3(1), block, 0, s, nullptr, e1, 0, a);        \
     return hipGetLastError();                                                                 \
