@@ -104,13 +104,15 @@ constexpr int kS1qWaves = kS1qThreads / kWave;
 constexpr int kS1qGB = 4;  // groups per batch of loads
 
 template <int NT, int TPW>
-__global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Args a, int B) {
+__global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(
+    const uint8_t* pq4, const uint16_t* pq4s, const uint8_t* pH, int ph_bytes, int pgroups,
+    int pntiles, int B, Stage1Args a) {
   static_assert(TPW <= kS1qWaves, "one finishing wave per tile");
   __shared__ f32x4_t s_red[kS1qWaves][TPW][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = lane >> 4, lr = lane & 15;
-  const int G = a.groups;
+  const int G = pgroups;
   const int tile0 = blockIdx.x * TPW;
   const int g_lo = wave * G / kS1qWaves, g_hi = (wave + 1) * G / kS1qWaves;
   // lane (slice, lr) feeds H row nt * 16 + lr, columns 128 g + 32 slice +
@@ -120,15 +122,15 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int j = nt * 16 + lr < B ? nt * 16 + lr : B - 1;
-    hp[nt] = a.H + (int64_t)j * a.h_bytes + (int64_t)(32 * slice) * 2;
+    hp[nt] = pH + (int64_t)j * ph_bytes + (int64_t)(32 * slice) * 2;
   }
   const uint4* codes[TPW];
   const uint16_t* scl[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int tl = tile0 + i < a.ntiles ? tile0 + i : a.ntiles - 1;
-    codes[i] = reinterpret_cast<const uint4*>(a.q4) + (int64_t)tl * G * kWave + lane;
-    scl[i] = a.q4s + (int64_t)tl * G * 16 + 4 * slice;
+    const int tl = tile0 + i < pntiles ? tile0 + i : pntiles - 1;
+    codes[i] = reinterpret_cast<const uint4*>(pq4) + (int64_t)tl * G * kWave + lane;
+    scl[i] = pq4s + (int64_t)tl * G * 16 + 4 * slice;
   }
   f32x4_t tot[TPW][NT];
 #pragma unroll
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kS1qThreads) void stage1_int4_mfma_kernel(Stage1Arg
   __syncthreads();
   if (wave >= TPW) return;
   const int tile = tile0 + wave;
-  if (tile >= a.ntiles) return;
+  if (tile >= pntiles) return;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + lr;
@@ -781,7 +783,9 @@ constexpr int kScChunks = 4;
 constexpr int kScKC = 128;
 
 template <int NT>
-__global__ __launch_bounds__(kGmThreads) void scores_mfma_kernel(Stage2mArgs a) {
+__global__ __launch_bounds__(kGmThreads) void scores_mfma_kernel(
+    const uint8_t* pbase, const uint8_t* pH, int prow_bytes, int ph_bytes, int pc, int pd, int pB,
+    int pS, Stage2mArgs a) {
   constexpr int kSteps = kScKC / 32;
   constexpr int kHRow = kScKC + 8;                       // LDS row pitch in bf16
   constexpr int kHP = NT * 16 * (kScKC / 8) / kGmThreads;  // H pieces per thread per chunk
@@ -790,28 +794,28 @@ __global__ __launch_bounds__(kGmThreads) void scores_mfma_kernel(Stage2mArgs a) 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = lane >> 4, lr = lane & 15;
-  const int B = a.B;
-  const int S = a.ksplit;
+  const int B = pB;
+  const int S = pS;
   const int unit = blockIdx.x;
   const int sp = unit % S;
   const int64_t item = (int64_t)(unit / S) * kGmWaves + wave;
-  const int64_t nitems = ((int64_t)a.c + 15) / 16;
+  const int64_t nitems = ((int64_t)pc + 15) / 16;
   const bool live = item < nitems;  // uniform over the wave
-  const int nchunks = a.d / kScKC;
+  const int nchunks = pd / kScKC;
   const int cbeg = sp * nchunks / S, nc = (sp + 1) * nchunks / S - cbeg;  // nc <= kScChunks
   const int64_t row0 = (live ? item : nitems - 1) * 16;
   int64_t arow = row0 + lr;
-  arow = arow < a.c ? arow : a.c - 1;
-  const uint8_t* ap = a.base + arow * a.row_bytes + (int64_t)(8 * slice) * 2 +
+  arow = arow < pc ? arow : pc - 1;
+  const uint8_t* ap = pbase + arow * prow_bytes + (int64_t)(8 * slice) * 2 +
                       (int64_t)cbeg * kScKC * 2;
   // H through a buffer resource that ends with row B - 1: pieces of rows past
   // the batch read as zeros (their columns are dropped)
   constexpr int kHStep = kGmThreads / (kScKC / 8);
   const int j0 = threadIdx.x / (kScKC / 8), kp = threadIdx.x % (kScKC / 8);
   const __amdgpu_buffer_rsrc_t hrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.H), (short)0, (int)((B - 1) * a.h_bytes + (int64_t)a.d * 2),
+      const_cast<uint8_t*>(pH), (short)0, (int)((B - 1) * ph_bytes + (int64_t)pd * 2),
       kBufferFlags);
-  const uint32_t hoff0 = (uint32_t)(j0 * a.h_bytes) + (uint32_t)kp * 16 + (uint32_t)cbeg * kScKC * 2;
+  const uint32_t hoff0 = (uint32_t)(j0 * ph_bytes) + (uint32_t)kp * 16 + (uint32_t)cbeg * kScKC * 2;
   uint4 av[kScChunks][kSteps];
   u32x4_t hreg[kScChunks][kHP];
 #pragma unroll
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(kGmThreads) void scores_mfma_kernel(Stage2mArgs a) 
 #pragma unroll
       for (int n = 0; n < kHP; ++n)
         hreg[c][n] = __builtin_amdgcn_raw_buffer_load_b128(
-            hrsrc, hoff0 + (uint32_t)(c * kScKC * 2), (int)(n * kHStep * a.h_bytes), 0);
+            hrsrc, hoff0 + (uint32_t)(c * kScKC * 2), (int)(n * kHStep * ph_bytes), 0);
       if (live) {
 #pragma unroll
         for (int u = 0; u < kSteps; ++u)
@@ -868,15 +872,15 @@ __global__ __launch_bounds__(kGmThreads) void scores_mfma_kernel(Stage2mArgs a) 
     for (int q = 0; q < 4; ++q) {
       const float sc = acc[nt][q];
       kv[q] = (keyed && a.sample) ? sc * a.inv_tau + gq[q] : sc;
-      if (keyed && a.dbg_scores && kq0 + q < a.c) a.dbg_scores[(int64_t)r * a.c + kq0 + q] = sc;
+      if (keyed && a.dbg_scores && kq0 + q < pc) a.dbg_scores[(int64_t)r * pc + kq0 + q] = sc;
     }
     float* kr = a.keys + (keyed ? 0 : (int64_t)sp * a.part_stride) + (int64_t)r * a.key_stride + kq0;
-    if (kq0 + 3 < a.c) {
+    if (kq0 + 3 < pc) {
       *reinterpret_cast<float4*>(kr) = make_float4(kv[0], kv[1], kv[2], kv[3]);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (kq0 + q < a.c) kr[q] = kv[q];
+        if (kq0 + q < pc) kr[q] = kv[q];
     }
   }
 }
@@ -963,7 +967,8 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
     const dim3 grid((a.ntiles + tpw - 1) / tpw), block(kS1qThreads);
 #define FH_S1Q(N, T)                                                                         \
   if (NT == N && tpw == T) {                                                                 \
-    hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<N, T>, grid, block, 0, s, e0, e1, 0, a, B); \
+    hipExtLaunchKernelGGL(stage1_int4_mfma_kernel<N, T>, grid, block, 0, s, e0, e1, 0, a.q4,   \
+                          a.q4s, a.H, (int)a.h_bytes, a.groups, a.ntiles, B, a);              \
     return hipGetLastError();                                                                \
   }
     FH_S1Q(1, 4) FH_S1Q(1, 2) FH_S1Q(1, 1)
@@ -1007,13 +1012,16 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, bool int4, int B, hipStream_t
     m.ksplit = S;
     *ksplit = S;
     const dim3 grid((unsigned)(groups * S)), block(kGmThreads);
+    // the values the first loads need, as leading scalar arguments
+#define SC_ARGS m.base, m.H, (int)m.row_bytes, (int)m.h_bytes, m.c, m.d, m.B, m.ksplit, m
     switch ((B + 15) / 16) {
-      case 1: hipExtLaunchKernelGGL(scores_mfma_kernel<1>, grid, block, 0, s, e0, e1, 0, m); break;
-      case 2: hipExtLaunchKernelGGL(scores_mfma_kernel<2>, grid, block, 0, s, e0, e1, 0, m); break;
-      case 3: hipExtLaunchKernelGGL(scores_mfma_kernel<3>, grid, block, 0, s, e0, e1, 0, m); break;
-      case 4: hipExtLaunchKernelGGL(scores_mfma_kernel<4>, grid, block, 0, s, e0, e1, 0, m); break;
+      case 1: hipExtLaunchKernelGGL(scores_mfma_kernel<1>, grid, block, 0, s, e0, e1, 0, SC_ARGS); break;
+      case 2: hipExtLaunchKernelGGL(scores_mfma_kernel<2>, grid, block, 0, s, e0, e1, 0, SC_ARGS); break;
+      case 3: hipExtLaunchKernelGGL(scores_mfma_kernel<3>, grid, block, 0, s, e0, e1, 0, SC_ARGS); break;
+      case 4: hipExtLaunchKernelGGL(scores_mfma_kernel<4>, grid, block, 0, s, e0, e1, 0, SC_ARGS); break;
       default: return hipErrorInvalidValue;
     }
+#undef SC_ARGS
     return hipGetLastError();
   }
   const int64_t units = groups * S;
