@@ -30,8 +30,14 @@ constexpr int kMcSelThreads = 1024;
 constexpr int kMcThreads = 256;
 constexpr int kMcWaves = kMcThreads / kWave;
 
+// Each draw's selection is a chain of short dependent steps, so draws on one
+// compute unit overlap: up to 16 keys per thread the registers are held to
+// 80, six waves per SIMD (three 512-thread draws per compute unit instead
+// of two; 10 000 draws at the Llama-3.2-1B head shape: 350 -> 323 us per
+// estimate), without spilling.
 template <int NT, int IPT>
-__global__ __launch_bounds__(NT) void mc_select_kernel(McArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IPT <= 16 ? 6 : 1)))
+void mc_select_kernel(McArgs a) {
   __shared__ SelSmem sm;
   const int i = blockIdx.x;
   const int k0 = threadIdx.x * IPT;
